@@ -1,0 +1,169 @@
+"""fp64 CPU oracle of the Mamba-2 mixer hot path (ctypes wrapper of m2_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the parity tests, the smoke check and the
+benchmark's CPU-baseline leg may use this package; the product path never
+does.  It neither imports nor loads the HIP library, and the HIP library
+shares no code with it.
+
+All arrays are numpy float64, C-contiguous, in the layouts documented in
+m2_oracle.c.  Functions return new arrays and never modify their inputs
+(the step copies ``ring`` and ``state`` before updating them).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "m2_oracle.c")
+_LIB = os.path.join(_HERE, "libm2oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C99, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fopenmp",
+                               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        f64 = ctypes.c_double
+        lib.oracle_conv1d.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, i64, dp, dp]
+        lib.oracle_conv1d.restype = None
+        lib.oracle_ssd_scan.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64, dp, dp, dp]
+        lib.oracle_ssd_scan.restype = None
+        lib.oracle_ssd_step.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64, dp, i64, dp, dp]
+        lib.oracle_ssd_step.restype = None
+        lib.oracle_softplus.argtypes = [f64]
+        lib.oracle_softplus.restype = f64
+        _lib = lib
+    return _lib
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError("oracle: expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def softplus(v: float) -> float:
+    return _load().oracle_softplus(float(v))
+
+
+def conv1d(x, w, bias=None, ring_in=None, ring_in_step: int = 0, want_ring: bool = True):
+    """Causal depthwise conv1d + SiLU.  x [B,L,Cd], w [Cd,W] -> (out [B,L,Cd], ring_out [B,W,Cd])."""
+    x = _f64(x)
+    Bn, L, Cd = x.shape
+    w = _f64(w)
+    W = w.shape[1]
+    w = _f64(w, (Cd, W))
+    bias = _f64(bias, (Cd,))
+    ring_in = _f64(ring_in, (Bn, W, Cd))
+    out = np.empty_like(x)
+    ring_out = np.empty((Bn, W, Cd)) if want_ring else None
+    _load().oracle_conv1d(Bn, L, Cd, W, _p(x), _p(w), _p(bias), _p(ring_in), int(ring_in_step),
+                          _p(ring_out), _p(out))
+    return out, ring_out
+
+
+def ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None,
+             dt_min: float = 0.0, dt_max: float = float("inf")):
+    """Sequential selective-SSM recurrence.
+
+    x [B,L,H,P], Bm/Cm [B,L,G,N], dt_raw [B,L,H] -> (y [B,L,H,P], state_out [B,H,P,N])."""
+    x = _f64(x)
+    Bn, L, H, P = x.shape
+    Bm = _f64(Bm)
+    G, N = Bm.shape[2], Bm.shape[3]
+    Bm = _f64(Bm, (Bn, L, G, N))
+    Cm = _f64(Cm, (Bn, L, G, N))
+    dt_raw = _f64(dt_raw, (Bn, L, H))
+    dt_bias = _f64(dt_bias, (H,))
+    A = _f64(A, (H,))
+    D = _f64(D, (H,))
+    state_in = _f64(state_in, (Bn, H, P, N))
+    if H % G:
+        raise ValueError("oracle: nheads must be a multiple of n_groups")
+    y = np.empty_like(x)
+    state_out = np.empty((Bn, H, P, N))
+    _load().oracle_ssd_scan(Bn, L, H, P, N, G, _p(x), _p(Bm), _p(Cm), _p(dt_raw), _p(dt_bias), _p(A),
+                            _p(D), float(dt_min), float(dt_max), _p(state_in), _p(y), _p(state_out))
+    return y, state_out
+
+
+def ssd_step(xbc_tok, dt_tok, w, bias, dt_bias, A, D, ring, step: int, state,
+             H: int, P: int, N: int, G: int = 1,
+             dt_min: float = 0.0, dt_max: float = float("inf")):
+    """One decode token: xbc_tok [B,Cd], dt_tok [B,H], ring [B,W,Cd], state [B,H,P,N].
+
+    Returns (y [B,H*P], ring_new, state_new)."""
+    xbc_tok = _f64(xbc_tok)
+    Bn, Cd = xbc_tok.shape
+    if Cd != H * P + 2 * G * N or H % G:
+        raise ValueError("oracle: inconsistent step dims")
+    w = _f64(w)
+    W = w.shape[1]
+    w = _f64(w, (Cd, W))
+    bias = _f64(bias, (Cd,))
+    dt_tok = _f64(dt_tok, (Bn, H))
+    dt_bias = _f64(dt_bias, (H,))
+    A = _f64(A, (H,))
+    D = _f64(D, (H,))
+    ring = np.array(_f64(ring, (Bn, W, Cd)), copy=True)
+    state = np.array(_f64(state, (Bn, H, P, N)), copy=True)
+    y = np.empty((Bn, H * P))
+    _load().oracle_ssd_step(Bn, H, P, N, G, W, _p(xbc_tok), _p(dt_tok), _p(w), _p(bias), _p(dt_bias),
+                            _p(A), _p(D), float(dt_min), float(dt_max), _p(ring), int(step), _p(state), _p(y))
+    return y, ring, state
+
+
+def split_act(act, H: int, P: int, N: int, G: int = 1):
+    """Channel split of a conv output [..., Cd] into x [..., H, P], B and C [..., G, N]."""
+    Di = H * P
+    x = act[..., :Di].reshape(act.shape[:-1] + (H, P))
+    b = act[..., Di:Di + G * N].reshape(act.shape[:-1] + (G, N))
+    c = act[..., Di + G * N:Di + 2 * G * N].reshape(act.shape[:-1] + (G, N))
+    return x, b, c
+
+
+def mixer_prefill(xbc, dt_raw, conv_w, conv_b, dt_bias, A, D, H, P, N, G=1,
+                  ring_in=None, ring_in_step=0, state_in=None):
+    """conv1d + SiLU -> split -> scan, all in fp64.  Returns (y, state_out, ring_out, act)."""
+    act, ring_out = conv1d(xbc, conv_w, conv_b, ring_in, ring_in_step)
+    x, b, c = split_act(act, H, P, N, G)
+    y, s = ssd_scan(x, b, c, dt_raw, dt_bias, A, D, state_in)
+    return y, s, ring_out, act
+
+
+def max_rel_err(got, ref) -> float:
+    """max_i |g_i - o_i| / max(|o_i|, rms(o)) over the compared tensor (floored relative error)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError("shape mismatch %s vs %s" % (got.shape, ref.shape))
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    den = np.maximum(np.abs(ref), rms if rms > 0 else 1e-300)
+    return float(np.max(np.abs(got - ref) / den))
