@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput of the Mamba-2 mixer hot path on one MI355X.
+
+Headline (`value`): prefill tokens/s of one step = conv1d+SiLU then the chunked SSD
+scan over a batch-1, 32768-token prompt at the Zamba2-2.7B mixer shape (d_model 2560,
+expand 2 -> 80 heads of headdim 64, d_state 64, one B/C group, conv width 4), bf16
+activations and fp32 state, inputs resident in HBM.  The same run also times the
+fused decode step on 256 sequences (the `decode` object).  Each kernel's average
+launch time comes from HIP events recorded on the stream the kernels run on, and is
+turned into a roofline fraction with the algorithmic bytes each launch must move.
+The fp64 CPU oracle is timed on a bounded sample of the same prefill on the host
+cores (`cpu_baseline`).
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD mixer tokens/s at 2.7B shape (32k prefill, decode) + % HBM roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    return ap.parse_args()
+
+
+def prefill_bytes(B, L, H, P, N, G, W, Cd, with_state_in, with_state_out):
+    """Algorithmic HBM bytes of one launch of each prefill kernel (bf16 activations)."""
+    conv = B * L * Cd * 2 * 2 + Cd * W * 4 + Cd * 4 + B * W * Cd * 2  # read xBC, write act, params, ring out
+    scan = B * L * (H * P * 2 + 2 * G * N * 2 + H * 2 + H * P * 2) + 3 * H * 4
+    scan += (B * H * P * N * 4) * (int(with_state_in) + int(with_state_out))
+    return conv, scan
+
+
+def step_bytes(B, H, P, N, G, W, Cd):
+    """Algorithmic HBM bytes of one decode-step launch: state read+write, ring W-1 reads + 1 write,
+    the new token, dt, y, parameters."""
+    return (B * H * P * N * 4 * 2 + B * (W - 1) * Cd * 2 + B * Cd * 2 + B * Cd * 2 + B * H * 2 + B * H * P * 2
+            + Cd * (W + 1) * 4 + 3 * H * 4)
+
+
+def time_events(torch, fns, steps, warmup):
+    """Run the callables in order `steps` times after `warmup` passes; per-callable mean ms from
+    event pairs on the current stream, plus the wall ms of the whole timed region."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+           for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            evs[s][i][0].record()
+            f()
+            evs[s][i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    per = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps for i in range(len(fns))]
+    return per, start.elapsed_time(end), wall
+
+
+def roofline(bytes_per_launch, ms):
+    gbs = bytes_per_launch / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+
+
+def bench_prefill(torch, m2, workloads, args):
+    cfg = workloads.CONFIGS[3]
+    d = cfg.dims
+    inp = workloads.config_inputs(3)
+    B, L, H, P, N, G, W, Cd = d.batch, d.seqlen, d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = m2.make_dims(B, L, d.d_model, d.expand, P, N, G, W, d.chunk_size, d.io)
+    bf = torch.bfloat16
+    xbc = torch.from_numpy(inp.xbc).to("cuda", bf)
+    dt = torch.from_numpy(inp.dt_raw).to("cuda", bf)
+    cw, cb, dtb, A, D = (torch.from_numpy(a).cuda() for a in (inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D))
+    act = torch.empty((B, L, Cd), device="cuda", dtype=bf)
+    ring_out = torch.empty((B, W, Cd), device="cuda", dtype=bf)
+    y = torch.empty((B, L, H * P), device="cuda", dtype=bf)
+    s_out = torch.empty((B, H, P, N), device="cuda")
+    nws = m2.m2_ssd_scan_workspace(dims)
+    ws = torch.empty(max(nws, 1), device="cuda", dtype=torch.uint8) if nws else None
+    xv, bv, cv = act[:, :, :H * P], act[:, :, H * P:H * P + G * N], act[:, :, H * P + G * N:]
+    del inp
+
+    def conv():
+        m2.m2_conv1d_fwd(dims, xbc, cw, cb, act, None, 0, ring_out)
+
+    def scan():
+        m2.m2_ssd_scan_fwd(dims, xv, bv, cv, dt, dtb, A, D, y, None, s_out, workspace=ws)
+
+    (t_conv, t_scan), total_ms, wall_ms = time_events(torch, [conv, scan], args.steps, args.warmup)
+    conv_b, scan_b = prefill_bytes(B, L, H, P, N, G, W, Cd, False, True)
+    step_ms = total_ms / args.steps
+    tok = B * L
+    return {
+        "tokens_per_s": tok / (step_ms * 1e-3), "ms_per_step": step_ms, "wall_ms": wall_ms,
+        "kernels": {"conv1d": {"ms": t_conv, "bytes": conv_b, "roofline": roofline(conv_b, t_conv)},
+                    "ssd_scan": {"ms": t_scan, "bytes": scan_b, "roofline": roofline(scan_b, t_scan)}},
+        "path_roofline_frac": round((conv_b + scan_b) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "config": {"workload": "zamba2-2.7b mixer prefill, batch 1 x 32768 tokens (conv1d+SiLU -> SSD scan)",
+                   "batch": B, "seqlen": L, "d_model": d.d_model, "expand": d.expand, "nheads": H,
+                   "headdim": P, "d_state": N, "n_groups": G, "d_conv": W,
+                   "chunk_size": d.chunk_size or "library default", "state": "fp32, zero initial, final returned"},
+    }
+
+
+def bench_decode(torch, m2, workloads, args):
+    cfg = workloads.CONFIGS[4]
+    d = cfg.dims
+    steps = args.decode_steps
+    inp = workloads.generate(d, 1004, True, steps)
+    B, H, P, N, G, W, Cd = d.batch, d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = m2.make_dims(B, 1, d.d_model, d.expand, P, N, G, W, 0, d.io)
+    bf = torch.bfloat16
+    xt = torch.from_numpy(inp.xbc).to("cuda", bf)
+    dtt = torch.from_numpy(inp.dt_raw).to("cuda", bf)
+    cw, cb, dtb, A, D = (torch.from_numpy(a).cuda() for a in (inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D))
+    ring = torch.from_numpy(inp.ring0).to("cuda", bf)
+    state = torch.from_numpy(inp.state0).cuda()
+    y = torch.empty((B, H * P), device="cuda", dtype=bf)
+    del inp
+    counter = [0]
+
+    def step():
+        t = counter[0] % steps
+        m2.m2_ssd_step(dims, xt[t], dtt[t], cw, cb, dtb, A, D, ring, counter[0], state, y)
+        counter[0] += 1
+
+    warm = min(args.warmup, steps)
+    (t_step,), total_ms, wall_ms = time_events(torch, [step], steps, warm)
+    sb = step_bytes(B, H, P, N, G, W, Cd)
+    step_ms = total_ms / steps
+    return {
+        "tokens_per_s": B / (step_ms * 1e-3), "ms_per_step": step_ms, "kernel_ms": t_step, "wall_ms": wall_ms,
+        "steps": steps, "roofline": roofline(sb, t_step), "bytes_per_launch": sb,
+        "config": {"workload": "zamba2-2.7b mixer decode, 256 sequences x %d chained tokens" % steps,
+                   "batch": B, "nheads": H, "headdim": P, "d_state": N, "d_conv": W,
+                   "state": "fp32 80x64x64 per sequence, N(0,0.1)", "ring": "bf16 4 x 5248, N(0,0.1)"},
+    }
+
+
+def cpu_baseline(workloads, seconds_target):
+    """The fp64 oracle (untuned) on the first T tokens of the same 32k prefill, T grown until the
+    run takes about `seconds_target` seconds."""
+    cores = len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(cores)
+    import oracle
+    d = workloads.CONFIGS[3].dims
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    T = 64
+    full = workloads.config_inputs(3, d.replace(seqlen=8192))
+    while True:
+        t0 = time.perf_counter()
+        oracle.mixer_prefill(full.xbc[:, :T], full.dt_raw[:, :T], full.conv_w, full.conv_b, full.dt_bias, full.A,
+                             full.D, H, P, N, G)
+        dt = time.perf_counter() - t0
+        if dt >= seconds_target / 2 or T >= 8192:
+            break
+        T *= 2
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d tokens of a batch-1 prefill drawn with the 32k workload's recipe and shape "
+                      "(conv1d+SiLU then scan, all 80 heads, fp64), %.2f s" % (T, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import selective_state_space_mixer_amd as m2
+    import workloads
+
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": None}
+    pre = dec = None
+    if args.only in ("all", "prefill"):
+        pre = bench_prefill(torch, m2, workloads, args)
+        print("prefill: %.3f ms/step, %.3e tok/s, conv %.1f us, scan %.1f us" % (
+            pre["ms_per_step"], pre["tokens_per_s"], pre["kernels"]["conv1d"]["ms"] * 1e3,
+            pre["kernels"]["ssd_scan"]["ms"] * 1e3), file=sys.stderr, flush=True)
+        out["value"] = round(pre["tokens_per_s"], 1)
+        out["ms_per_step"] = round(pre["ms_per_step"], 4)
+        out["config"] = pre["config"]
+        k = pre["kernels"]
+        dom = max(k, key=lambda n: k[n]["ms"])
+        out["roofline"] = dict(k[dom]["roofline"], kernel=dom)
+        out["prefill_kernels"] = {n: {"us": round(v["ms"] * 1e3, 2), "bytes": v["bytes"],
+                                      "frac": v["roofline"]["frac"], "achieved_GBs": v["roofline"]["achieved"]}
+                                  for n, v in k.items()}
+        out["prefill_path_roofline_frac"] = pre["path_roofline_frac"]
+    if args.only in ("all", "decode"):
+        dec = bench_decode(torch, m2, workloads, args)
+        print("decode: %.1f us/step, %.3e tok/s" % (dec["ms_per_step"] * 1e3, dec["tokens_per_s"]),
+              file=sys.stderr, flush=True)
+        out["decode"] = {"value": round(dec["tokens_per_s"], 1), "unit": "tokens/s",
+                         "us_per_step": round(dec["ms_per_step"] * 1e3, 2), "kernel_us": round(dec["kernel_ms"] * 1e3, 2),
+                         "steps": dec["steps"], "roofline": dict(dec["roofline"], kernel="ssd_step"),
+                         "config": dec["config"]}
+        if pre is None:
+            out["value"] = round(dec["tokens_per_s"], 1)
+            out["ms_per_step"] = round(dec["ms_per_step"], 4)
+            out["config"] = dec["config"]
+            out["roofline"] = out["decode"]["roofline"]
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(workloads, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

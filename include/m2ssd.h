@@ -1,0 +1,164 @@
+/*
+ * m2ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 mixer hot path.
+ *
+ * The three compute entry points are the steps that the Zamba2 article
+ * ("Transformers 中 Zamba2 混合架构模型解析", §三 "Mamba2 Mixer") places between the
+ * mixer's input projection and its gated norm:
+ *
+ *   m2_conv1d_fwd    causal depthwise conv1d of width mamba_d_conv, then SiLU,
+ *                    over a prompt (groups = conv_dim; §五: use_conv_bias)
+ *   m2_ssd_scan_fwd  the selective state-space scan over a prompt, computed in
+ *                    chunks (§三: intra-chunk + inter-chunk scan, chunk_size)
+ *   m2_ssd_step      the single-token recurrent update used when a cached state
+ *                    exists and the new sequence length is 1 (§三); it also
+ *                    advances the cached conv state (§三: the cache holds each
+ *                    layer's conv state and recurrent state)
+ *
+ * The recurrence, per batch element b and head h, for t = 0..L-1:
+ *     dt_t = softplus(dt_raw_t + dt_bias[h])        (then clamped to [dt_min, dt_max])
+ *     S_t  = exp(dt_t * A[h]) * S_{t-1} + dt_t * x_t (outer) B_t     S is headdim x d_state, fp32
+ *     y_t  = S_t . C_t + D[h] * x_t
+ * with S_{-1} = state_in (zero if NULL); head h reads group g(h) = h / (nheads / n_groups).
+ *
+ * Conventions
+ *   - Every pointer argument except `stream` is DEVICE memory owned by the caller.
+ *     The library allocates nothing, keeps no state between calls and never
+ *     synchronises: each call only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL = the default stream) and returns.  Calls are thread-safe.
+ *   - Activations (xBC, x, B, C, dt, y, conv ring) are stored in dims.io (bf16 or
+ *     fp32); fp32 accumulation everywhere.  Parameters (conv w/bias, dt_bias, A, D)
+ *     and the SSM state are always fp32.
+ *   - Strides are in ELEMENTS.  A "token stride" is the distance between tokens t
+ *     and t+1 of one sequence; the batch stride is seqlen * token stride.
+ *   - Errors: arguments are validated on the host before anything is enqueued; a
+ *     nonzero m2_status means nothing was launched, except M2_ERR_LAUNCH (the
+ *     runtime refused a launch).  NaN/Inf in the data are propagated, not reported.
+ *     Not checked: A <= 0 and finiteness of the inputs.
+ *   - Device pointers must be 16-byte aligned and strides multiples of 16 bytes /
+ *     element size where noted; otherwise M2_ERR_UNSUPPORTED.
+ */
+#ifndef M2SSD_H
+#define M2SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define M2SSD_ABI_VERSION 1
+
+typedef enum {
+    M2_OK = 0,
+    M2_ERR_NULL = 1,         /* a required pointer is NULL */
+    M2_ERR_SHAPE = 2,        /* non-positive or inconsistent sizes, stride below row width */
+    M2_ERR_DTYPE = 3,        /* dims.io is not a supported storage type */
+    M2_ERR_ALIAS = 4,        /* an output overlaps an input it must not overlap */
+    M2_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than m2_ssd_scan_workspace() */
+    M2_ERR_UNSUPPORTED = 6,  /* valid but not built: headdim/d_state/alignment outside the kernels' set */
+    M2_ERR_LAUNCH = 7        /* the HIP runtime reported an error at launch */
+} m2_status;
+
+typedef enum { M2_F32 = 0, M2_BF16 = 1 } m2_dtype;
+
+/* Mixer dimensions (the Zamba2 configuration names of article §五 in brackets).
+ * Derived: d_inner = expand * d_model, nheads = d_inner / headdim,
+ *          conv_dim = d_inner + 2 * n_groups * d_state.                        */
+typedef struct {
+    int64_t batch;       /* sequences */
+    int64_t seqlen;      /* tokens per sequence (ignored by m2_ssd_step) */
+    int32_t d_model;     /* [hidden_size] */
+    int32_t expand;      /* [mamba_expand] */
+    int32_t headdim;     /* [mamba_headdim]  P */
+    int32_t d_state;     /* [mamba_d_state]  N */
+    int32_t n_groups;    /* [mamba_ngroups]  G, must divide nheads */
+    int32_t d_conv;      /* [mamba_d_conv]   W, 2..4 */
+    int32_t chunk_size;  /* [chunk_size]     0 = library choice; else 16, 32 or 64 */
+    int32_t io;          /* m2_dtype of the activations */
+} m2_dims;
+
+/* Causal depthwise conv1d + SiLU over a prompt.
+ *   out[b,t,c] = SiLU(bias[c] + sum_{k<W} w[c,k] * x[b, t-(W-1)+k, c]),  SiLU(v) = v / (1 + e^-v)
+ * xbc      [batch, seqlen, conv_dim] io, token stride xbc_tok_stride (>= conv_dim);
+ *          channel order x (d_inner) | B (n_groups*d_state) | C (n_groups*d_state)
+ * w        [conv_dim, W] fp32;  bias [conv_dim] fp32 or NULL (no bias)
+ * ring_in  [batch, W, conv_dim] io or NULL (zero history): the conv state of the tokens
+ *          before t = 0, as a ring at phase ring_in_step: the token j places before
+ *          t = 0 (j = 1..W-1) is in slot (ring_in_step - j) mod W
+ * ring_out [batch, W, conv_dim] io or NULL: receives the last W tokens as a ring at
+ *          phase 0 (slot j = token seqlen-W+j, taken from ring_in when negative);
+ *          must not overlap ring_in or xbc
+ * out      [batch, seqlen, conv_dim] io, token stride out_tok_stride; must not overlap xbc
+ * seqlen may be 0 (then only ring_out is written, as a copy of the history). */
+m2_status m2_conv1d_fwd(const m2_dims* dims,
+                        const void* xbc, int64_t xbc_tok_stride,
+                        const float* w, const float* bias,
+                        const void* ring_in, int64_t ring_in_step,
+                        void* ring_out,
+                        void* out, int64_t out_tok_stride,
+                        void* stream);
+
+/* Workspace bytes m2_ssd_scan_fwd needs for these dims (0 if none). */
+size_t m2_ssd_scan_workspace(const m2_dims* dims);
+
+/* Chunked selective state-space scan over a prompt (the recurrence above for t = 0..seqlen-1).
+ * x        [batch, seqlen, nheads, headdim] io, token stride x_tok_stride (>= d_inner)
+ * B, C     [batch, seqlen, n_groups, d_state] io, token stride bc_tok_stride (>= n_groups*d_state)
+ * dt       [batch, seqlen, nheads] io (raw, before bias and softplus), token stride dt_tok_stride
+ * dt_bias, A [nheads] fp32;  D [nheads] fp32 or NULL (no skip term)
+ * dt_min, dt_max  clamp of dt after softplus; pass 0 and +INFINITY for none
+ * state_in  [batch, nheads, headdim, d_state] fp32 or NULL (zero initial state)
+ * state_out [batch, nheads, headdim, d_state] fp32 or NULL; must not overlap state_in
+ * y        [batch, seqlen, nheads*headdim] io, token stride y_tok_stride; must not overlap
+ *          x, B, C or dt
+ * workspace device scratch of at least m2_ssd_scan_workspace(dims) bytes (NULL if 0);
+ *          its contents on entry do not matter.
+ * x/B/C may be strided views into one conv1d output (token stride conv_dim). */
+m2_status m2_ssd_scan_fwd(const m2_dims* dims,
+                          const void* x, int64_t x_tok_stride,
+                          const void* B, const void* C, int64_t bc_tok_stride,
+                          const void* dt, int64_t dt_tok_stride,
+                          const float* dt_bias, const float* A, const float* D,
+                          float dt_min, float dt_max,
+                          const float* state_in, float* state_out,
+                          void* y, int64_t y_tok_stride,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* One decode token for every sequence, fused: conv window (W-1 cached tokens + the new
+ * one) -> SiLU -> split x | B | C -> dt -> state update -> output.
+ * xbc_tok  [batch, conv_dim] io, batch stride xbc_stride (>= conv_dim)
+ * dt_tok   [batch, nheads] io (raw), batch stride dt_stride (>= nheads)
+ * w, bias  conv parameters as in m2_conv1d_fwd;  dt_bias, A, D, dt_min, dt_max as in the scan
+ * ring     [batch, W, conv_dim] io, IN PLACE: a ring at phase `step` (after a prefill that
+ *          wrote ring_out, step counts the decode tokens since, from 0).  The new token
+ *          is written into slot step mod W, the slot that just left the window.
+ * state    [batch, nheads, headdim, d_state] fp32, IN PLACE
+ * y        [batch, nheads*headdim] io; must not overlap the other arguments
+ * step >= 0.  dims.seqlen is ignored. */
+m2_status m2_ssd_step(const m2_dims* dims,
+                      const void* xbc_tok, int64_t xbc_stride,
+                      const void* dt_tok, int64_t dt_stride,
+                      const float* w, const float* bias,
+                      const float* dt_bias, const float* A, const float* D,
+                      float dt_min, float dt_max,
+                      void* ring, int64_t step,
+                      float* state, void* y,
+                      void* stream);
+
+/* Static text for a status code. */
+const char* m2_status_str(m2_status status);
+
+/* M2SSD_ABI_VERSION of the built library. */
+int m2_abi_version(void);
+
+/* Name of the HIP runtime error behind the calling thread's most recent M2_ERR_LAUNCH
+ * ("hipSuccess" if none).  Static text. */
+const char* m2_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M2SSD_H */

@@ -1,0 +1,204 @@
+// api.cpp -- the C ABI of include/m2ssd.h: argument validation and dispatch.
+//
+// Everything here runs on the host before any launch.  A call that fails
+// validation enqueues nothing.  No allocation, no synchronisation, no state.
+#include "m2ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "m2_launch.h"
+
+namespace {
+
+struct Derived {
+    int64_t batch, L;
+    int d_inner, H, P, N, G, W, Cd, Q;
+    bool bf16;
+    int esize;
+};
+
+m2_status derive(const m2_dims* d, Derived& o) {
+    if (!d) return M2_ERR_NULL;
+    if (d->io != M2_F32 && d->io != M2_BF16) return M2_ERR_DTYPE;
+    if (d->batch < 0 || d->seqlen < 0 || d->d_model < 1 || d->expand < 1 || d->headdim < 1 ||
+        d->d_state < 1 || d->n_groups < 1 || d->chunk_size < 0)
+        return M2_ERR_SHAPE;
+    if (d->d_conv < 2 || d->d_conv > 4) return M2_ERR_UNSUPPORTED;
+    const int64_t d_inner = (int64_t)d->expand * d->d_model;
+    if (d_inner % d->headdim) return M2_ERR_SHAPE;
+    const int64_t H = d_inner / d->headdim;
+    if (H % d->n_groups) return M2_ERR_SHAPE;
+    const int64_t Cd = d_inner + 2 * (int64_t)d->n_groups * d->d_state;
+    if (Cd > (int64_t)1 << 30) return M2_ERR_SHAPE;
+    o.batch = d->batch;
+    o.L = d->seqlen;
+    o.d_inner = (int)d_inner;
+    o.H = (int)H;
+    o.P = d->headdim;
+    o.N = d->d_state;
+    o.G = d->n_groups;
+    o.W = d->d_conv;
+    o.Cd = (int)Cd;
+    o.Q = d->chunk_size;
+    o.bf16 = d->io == M2_BF16;
+    o.esize = o.bf16 ? 2 : 4;
+    return M2_OK;
+}
+
+// Byte range of a [rows, row_elems] view with `stride` elements between rows.
+struct Range { uintptr_t lo, hi; };
+Range span(const void* p, int64_t rows, int64_t stride, int64_t row_elems, int esize) {
+    if (!p || rows <= 0 || row_elems <= 0) return {0, 0};
+    const uintptr_t lo = (uintptr_t)p;
+    return {lo, lo + (uintptr_t)(((rows - 1) * stride + row_elems) * esize)};
+}
+bool overlap(Range a, Range b) { return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+m2_status launched(hipError_t e) {
+    if (e == hipSuccess) return M2_OK;
+    g_last_hip_error = e;
+    return M2_ERR_LAUNCH;
+}
+
+}  // namespace
+
+namespace m2 {
+void note_hip_error(hipError_t e) { g_last_hip_error = e; }
+}  // namespace m2
+
+extern "C" {
+
+const char* m2_status_str(m2_status s) {
+    switch (s) {
+        case M2_OK: return "ok";
+        case M2_ERR_NULL: return "a required pointer is NULL";
+        case M2_ERR_SHAPE: return "invalid or inconsistent sizes or strides";
+        case M2_ERR_DTYPE: return "unsupported activation storage type";
+        case M2_ERR_ALIAS: return "an output overlaps an input";
+        case M2_ERR_WORKSPACE: return "workspace missing or too small";
+        case M2_ERR_UNSUPPORTED: return "shape, width or alignment not supported by the built kernels";
+        case M2_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int m2_abi_version(void) { return M2SSD_ABI_VERSION; }
+
+const char* m2_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
+
+m2_status m2_conv1d_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_stride, const float* w,
+                        const float* bias, const void* ring_in, int64_t ring_in_step, void* ring_out, void* out,
+                        int64_t out_tok_stride, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    const int64_t rows = d.batch * d.L;
+    if (!w) return M2_ERR_NULL;
+    if (rows > 0 && (!xbc || !out)) return M2_ERR_NULL;
+    if (rows > 0 && (xbc_tok_stride < d.Cd || out_tok_stride < d.Cd)) return M2_ERR_SHAPE;
+    if (d.batch == 0 || (d.L == 0 && !ring_out)) return M2_OK;
+    const Range rx = span(xbc, rows, xbc_tok_stride, d.Cd, d.esize);
+    const Range ro = span(out, rows, out_tok_stride, d.Cd, d.esize);
+    const Range rri = span(ring_in, d.batch * d.W, d.Cd, d.Cd, d.esize);
+    const Range rro = span(ring_out, d.batch * d.W, d.Cd, d.Cd, d.esize);
+    if (overlap(rx, ro) || overlap(rri, rro) || overlap(rro, rx) || overlap(rro, ro) || overlap(ro, rri))
+        return M2_ERR_ALIAS;
+    m2::ConvArgs a;
+    a.xbc = xbc; a.xs = xbc_tok_stride; a.L = d.L; a.Cd = d.Cd; a.W = d.W; a.batch = d.batch;
+    a.w = w; a.bias = bias; a.ring_in = ring_in;
+    a.ring_phase = (int)(((ring_in_step % d.W) + d.W) % d.W);
+    a.ring_out = ring_out; a.out = out; a.os = out_tok_stride; a.bf16 = d.bf16;
+    const int vec = d.bf16 ? 8 : 4;
+    a.vec = (d.Cd % vec == 0) && (rows == 0 || (xbc_tok_stride % vec == 0 && out_tok_stride % vec == 0 &&
+                                                 aligned16(xbc) && aligned16(out))) &&
+            aligned16(ring_in) && aligned16(ring_out);
+    if (d.L == 0) { a.xbc = nullptr; a.out = nullptr; }
+    return launched(m2::launch_conv1d(a, (hipStream_t)stream));
+}
+
+size_t m2_ssd_scan_workspace(const m2_dims* dims) {
+    Derived d;
+    if (derive(dims, d) != M2_OK) return 0;
+    const int Q = d.Q ? d.Q : m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
+    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
+}
+
+m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B, const void* C,
+                          int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
+                          const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
+                          float* state_out, void* y, int64_t y_tok_stride, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    const int64_t rows = d.batch * d.L;
+    if (!dt_bias || !A) return M2_ERR_NULL;
+    if (rows > 0 && (!x || !B || !C || !dt || !y)) return M2_ERR_NULL;
+    const int GN = d.G * d.N;
+    if (rows > 0 && (x_tok_stride < d.d_inner || bc_tok_stride < GN || dt_tok_stride < d.H ||
+                     y_tok_stride < d.d_inner))
+        return M2_ERR_SHAPE;
+    if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return M2_ERR_SHAPE;
+    const int Q = d.Q ? d.Q : m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
+    if (!(Q == 16 || Q == 32 || Q == 64)) return M2_ERR_UNSUPPORTED;
+    if (!m2::ssd_scan_supported(d.P, d.N, Q, d.bf16)) return M2_ERR_UNSUPPORTED;
+    if (d.batch == 0) return M2_OK;
+    const Range ry = span(y, rows, y_tok_stride, d.d_inner, d.esize);
+    const Range rs_in = span(state_in, d.batch * d.H, (int64_t)d.P * d.N, (int64_t)d.P * d.N, 4);
+    const Range rs_out = span(state_out, d.batch * d.H, (int64_t)d.P * d.N, (int64_t)d.P * d.N, 4);
+    if (overlap(ry, span(x, rows, x_tok_stride, d.d_inner, d.esize)) ||
+        overlap(ry, span(B, rows, bc_tok_stride, GN, d.esize)) ||
+        overlap(ry, span(C, rows, bc_tok_stride, GN, d.esize)) ||
+        overlap(ry, span(dt, rows, dt_tok_stride, d.H, d.esize)) || overlap(rs_in, rs_out) ||
+        overlap(rs_out, ry))
+        return M2_ERR_ALIAS;
+    if (!aligned16(state_in) || !aligned16(state_out)) return M2_ERR_UNSUPPORTED;
+    const size_t need = m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return M2_ERR_WORKSPACE;
+    m2::ScanArgs a;
+    a.batch = d.batch; a.L = d.L; a.H = d.H; a.P = d.P; a.N = d.N; a.G = d.G; a.Q = Q;
+    a.x = x; a.xs = x_tok_stride; a.B = B; a.C = C; a.bcs = bc_tok_stride; a.dt = dt; a.dts = dt_tok_stride;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.dt_min = dt_min; a.dt_max = dt_max;
+    a.state_in = state_in; a.state_out = state_out; a.y = y; a.ys = y_tok_stride;
+    a.ws = workspace; a.ws_bytes = workspace_bytes; a.bf16 = d.bf16;
+    return launched(m2::launch_ssd_scan(a, (hipStream_t)stream));
+}
+
+m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stride, const void* dt_tok,
+                      int64_t dt_stride, const float* w, const float* bias, const float* dt_bias, const float* A,
+                      const float* D, float dt_min, float dt_max, void* ring, int64_t step, float* state, void* y,
+                      void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    if (!w || !dt_bias || !A) return M2_ERR_NULL;
+    if (d.batch > 0 && (!xbc_tok || !dt_tok || !ring || !state || !y)) return M2_ERR_NULL;
+    if (step < 0) return M2_ERR_SHAPE;
+    if (d.batch > 0 && (xbc_stride < d.Cd || dt_stride < d.H)) return M2_ERR_SHAPE;
+    if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return M2_ERR_SHAPE;
+    if (!m2::ssd_step_supported(d.P, d.N)) return M2_ERR_UNSUPPORTED;
+    if (d.batch == 0) return M2_OK;
+    const Range ry = span(y, d.batch, d.d_inner, d.d_inner, d.esize);
+    const Range rr = span(ring, d.batch * d.W, d.Cd, d.Cd, d.esize);
+    const Range rs = span(state, d.batch * d.H, (int64_t)d.P * d.N, (int64_t)d.P * d.N, 4);
+    const Range rx = span(xbc_tok, d.batch, xbc_stride, d.Cd, d.esize);
+    const Range rd = span(dt_tok, d.batch, dt_stride, d.H, d.esize);
+    if (overlap(ry, rr) || overlap(ry, rs) || overlap(ry, rx) || overlap(ry, rd) || overlap(rr, rs) ||
+        overlap(rr, rx) || overlap(rr, rd) || overlap(rs, rx) || overlap(rs, rd))
+        return M2_ERR_ALIAS;
+    if (!aligned16(state)) return M2_ERR_UNSUPPORTED;
+    m2::StepArgs a;
+    a.batch = d.batch; a.H = d.H; a.P = d.P; a.N = d.N; a.G = d.G; a.W = d.W; a.Cd = d.Cd;
+    a.xbc = xbc_tok; a.xbs = xbc_stride; a.dt = dt_tok; a.dts = dt_stride;
+    a.w = w; a.bias = bias; a.dt_bias = dt_bias; a.A = A; a.D = D; a.dt_min = dt_min; a.dt_max = dt_max;
+    a.ring = ring; a.step = step; a.state = state; a.y = y; a.bf16 = d.bf16;
+    return launched(m2::launch_ssd_step(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// conv1d.hip -- causal depthwise conv1d + SiLU over a prompt (gfx950).
+//
+// The mixer's depthwise conv (article "Transformers 中 Zamba2 混合架构模型解析", §三:
+// groups = conv_dim, kernel width mamba_d_conv, SiLU on the output):
+//     out[b,t,c] = SiLU(bias[c] + sum_{k<W} w[c,k] * x[b, t-(W-1)+k, c])
+//
+// Pure HBM stream (3 flop per byte).  Each lane owns VEC adjacent channels (one
+// 16-byte load per token) and walks TT consecutive tokens, keeping the last W
+// inputs in registers, so every input is read from HBM once (plus a W-1 token
+// halo per tile).  A wave covers 64*VEC contiguous channels of one token, so each
+// load and store instruction moves one contiguous 1 KiB row segment.
+#include "m2_device.h"
+#include "m2_launch.h"
+
+namespace m2 {
+
+template <typename T, int VEC> struct Vec;
+template <> struct Vec<bf16_t, 8> {
+    uint4 raw;
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t wd = (&raw.x)[i >> 1];
+        return __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
+    }
+    __device__ __forceinline__ void set2(int i, float lo, float hi) {
+        (&raw.x)[i >> 1] = (uint32_t)f32_to_bits(lo) | ((uint32_t)f32_to_bits(hi) << 16);
+    }
+};
+template <> struct Vec<float, 4> {
+    float4 raw;
+    __device__ __forceinline__ float get(int i) const { return (&raw.x)[i]; }
+    __device__ __forceinline__ void set2(int i, float lo, float hi) { (&raw.x)[i] = lo; (&raw.x)[i + 1] = hi; }
+};
+template <typename T> struct Vec<T, 1> {
+    T raw;
+    __device__ __forceinline__ float get(int) const { return to_f32(raw); }
+};
+
+template <typename T, int VEC>
+__device__ __forceinline__ Vec<T, VEC> load_vec(const T* p) {
+    Vec<T, VEC> v;
+    v.raw = *reinterpret_cast<const decltype(v.raw)*>(p);
+    return v;
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void store_vals(T* p, const float (&o)[VEC]) {
+    if constexpr (VEC == 1) {
+        *p = from_f32<T>(o[0]);
+    } else {
+        Vec<T, VEC> v;
+#pragma unroll
+        for (int i = 0; i < VEC; i += 2) v.set2(i, o[i], o[i + 1]);
+        *reinterpret_cast<decltype(v.raw)*>(p) = v.raw;
+    }
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void load_vals(const T* p, float (&o)[VEC]) {
+    Vec<T, VEC> v = load_vec<T, VEC>(p);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = v.get(i);
+}
+
+constexpr int kConvTileTokens = 64;   // tokens per lane
+constexpr int kConvWavesPerBlock = 4; // one token tile per wave
+constexpr int kConvUnroll = 4;        // loads issued back to back
+
+template <typename T, int VEC, int W>
+__global__ __launch_bounds__(256) void conv1d_silu_kernel(
+    const T* __restrict__ xbc, int64_t xs, int64_t L, int Cd,
+    const float* __restrict__ w, const float* __restrict__ bias,
+    const T* __restrict__ ring_in, int ring_phase,
+    T* __restrict__ ring_out, T* __restrict__ out, int64_t os)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int c0 = (blockIdx.x * kWave + lane) * VEC;
+    if (c0 >= Cd) return;
+    const int64_t tile = (int64_t)blockIdx.y * kConvWavesPerBlock + wave;
+    const int64_t t0 = tile * kConvTileTokens;
+    if (t0 >= L && !(L == 0 && tile == 0)) return;
+    const int64_t b = blockIdx.z;
+    const T* xb = xbc + b * L * xs + c0;
+    T* ob = out + b * L * os + c0;
+
+    float wr[VEC][W], br[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) wr[i][k] = w[(int64_t)(c0 + i) * W + k];
+        br[i] = bias ? bias[c0 + i] : 0.0f;
+    }
+
+    // win[k] holds token (next - W + k); win[W-1] is the newest
+    float win[W][VEC];
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const int64_t tau = t0 - W + k;
+        if (tau >= 0) {
+            if (k > 0) load_vals<T, VEC>(xb + tau * xs, win[k]);
+            else {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) win[k][i] = 0.0f;  // never enters a sum
+            }
+        } else if (ring_in) {
+            const int slot = (int)(((ring_phase + tau) % W + W) % W);
+            load_vals<T, VEC>(ring_in + (b * W + slot) * (int64_t)Cd + c0, win[k]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) win[k][i] = 0.0f;
+        }
+    }
+
+    const int64_t t_end = t0 + kConvTileTokens < L ? t0 + kConvTileTokens : L;
+    for (int64_t t = t0; t < t_end; t += kConvUnroll) {
+        float nx[kConvUnroll][VEC];
+#pragma unroll
+        for (int u = 0; u < kConvUnroll; ++u)
+            if (t + u < t_end) load_vals<T, VEC>(xb + (t + u) * xs, nx[u]);
+#pragma unroll
+        for (int u = 0; u < kConvUnroll; ++u) {
+            if (t + u < t_end) {
+#pragma unroll
+                for (int k = 0; k < W - 1; ++k)
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) win[k][i] = win[k + 1][i];
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) win[W - 1][i] = nx[u][i];
+                float o[VEC];
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    float v = br[i];
+#pragma unroll
+                    for (int k = 0; k < W; ++k) v = fmaf(wr[i][k], win[k][i], v);
+                    o[i] = silu(v);
+                }
+                store_vals<T, VEC>(ob + (t + u) * os, o);
+            }
+        }
+    }
+
+    // the tile holding the last token writes the ring (phase 0: slot j = token L-W+j)
+    if (ring_out && t_end == L && (t0 < L || L == 0)) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) store_vals<T, VEC>(ring_out + (b * W + k) * (int64_t)Cd + c0, win[k]);
+    }
+}
+
+template <typename T, int VEC, int W>
+static hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
+    const int64_t tiles = a.L > 0 ? (a.L + kConvTileTokens - 1) / kConvTileTokens : 1;
+    dim3 grid((unsigned)((a.Cd / VEC + kWave - 1) / kWave),
+              (unsigned)((tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock),
+              (unsigned)a.batch);
+    return launch_kernel(conv1d_silu_kernel<T, VEC, W>, grid, dim3(kWave * kConvWavesPerBlock), 0, s,
+                       (const T*)a.xbc, a.xs, a.L, a.Cd, a.w, a.bias, (const T*)a.ring_in, a.ring_phase,
+                       (T*)a.ring_out, (T*)a.out, a.os);
+}
+
+template <typename T, int VEC>
+static hipError_t launch_conv_w(const ConvArgs& a, hipStream_t s) {
+    switch (a.W) {
+        case 2: return launch_conv<T, VEC, 2>(a, s);
+        case 3: return launch_conv<T, VEC, 3>(a, s);
+        default: return launch_conv<T, VEC, 4>(a, s);
+    }
+}
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s) {
+    if (a.bf16) return a.vec ? launch_conv_w<bf16_t, 8>(a, s) : launch_conv_w<bf16_t, 1>(a, s);
+    return a.vec ? launch_conv_w<float, 4>(a, s) : launch_conv_w<float, 1>(a, s);
+}
+
+}  // namespace m2

@@ -1,0 +1,74 @@
+// m2_launch.h -- host-side launch descriptors passed from the C ABI layer to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m2 {
+
+struct ConvArgs {
+    const void* xbc; int64_t xs;      // [batch, L, Cd], token stride xs
+    int64_t L; int Cd; int W; int64_t batch;
+    const float* w; const float* bias;
+    const void* ring_in; int ring_phase;
+    void* ring_out;
+    void* out; int64_t os;
+    bool bf16;  // storage type of activations
+    bool vec;   // 16-byte vector path (alignment checked by the caller)
+};
+
+struct ScanArgs {
+    int64_t batch, L;
+    int H, P, N, G, Q;
+    const void* x; int64_t xs;
+    const void* B; const void* C; int64_t bcs;
+    const void* dt; int64_t dts;
+    const float* dt_bias; const float* A; const float* D;
+    float dt_min, dt_max;
+    const float* state_in; float* state_out;
+    void* y; int64_t ys;
+    void* ws; size_t ws_bytes;
+    bool bf16;
+};
+
+struct StepArgs {
+    int64_t batch;
+    int H, P, N, G, W, Cd;
+    const void* xbc; int64_t xbs;
+    const void* dt; int64_t dts;
+    const float* w; const float* bias;
+    const float* dt_bias; const float* A; const float* D;
+    float dt_min, dt_max;
+    void* ring; int64_t step;
+    float* state; void* y;
+    bool bf16;
+};
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
+hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s);
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16);
+bool ssd_scan_supported(int P, int N, int Q, bool bf16);
+int ssd_scan_default_chunk(int P, int N, bool bf16);
+hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
+bool ssd_step_supported(int P, int N);
+
+}  // namespace m2
+
+namespace m2 {
+
+template <class T> struct ident { using type = T; };
+
+// Launch through hipLaunchKernel so the returned status is this launch's own
+// (hipGetLastError would also report an earlier, unrelated failure of the thread).
+template <typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, size_t shmem, hipStream_t s,
+                                typename ident<Args>::type... args) {
+    void* argv[] = {(void*)&args...};
+    return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, s);
+}
+
+// Name of the last HIP error a call of this thread saw ("hipSuccess" if none).
+void note_hip_error(hipError_t e);
+
+}  // namespace m2

@@ -1,0 +1,137 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/m2ssd.h declares, and
+reject invalid arguments with the documented status before anything is
+enqueued.  All argument sets used here fail validation, so no device memory is
+touched (the pointers are placeholders that are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m2ssd.h")
+
+m2 = pytest.importorskip("selective_state_space_mixer_amd")
+
+FAKE = 0x7000_0000_0000   # placeholder device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(m2_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(m2.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(m2.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert m2.m2_abi_version() == m2.ABI_VERSION
+    for s in range(8):
+        assert m2.m2_status_str(s)
+    assert m2.m2_status_str(99) == "unknown status"
+
+
+def dims(**kw):
+    base = dict(batch=2, seqlen=128, d_model=2560, expand=2, headdim=64, d_state=64, n_groups=1, d_conv=4,
+                chunk_size=0, io=m2.M2_BF16)
+    base.update(kw)
+    return m2.M2Dims(**base)
+
+
+def conv(d, xbc=FAKE, xs=None, w=FAKE + 0x100000, bias=None, ring_in=None, step=0, ring_out=None,
+         out=FAKE + 0x4000_0000, os_=None):
+    lib = m2.lib()
+    cd = d.conv_dim if d.expand > 0 else 1
+    return lib.m2_conv1d_fwd(ctypes.byref(d) if d is not None else None, xbc, xs or cd, w, bias, ring_in, step,
+                             ring_out, out, os_ or cd, None)
+
+
+def scan(d, x=FAKE, xs=None, B=FAKE + 0x10000000, C=FAKE + 0x10000100, bcs=None, dt=FAKE + 0x20000000, dts=None,
+         dt_bias=FAKE + 0x30000000, A=FAKE + 0x30001000, D=None, dt_min=0.0, dt_max=float("inf"),
+         s_in=None, s_out=None, y=FAKE + 0x4000_0000_00, ys=None, ws=None, ws_bytes=0):
+    lib = m2.lib()
+    di = d.expand * d.d_model
+    return lib.m2_ssd_scan_fwd(ctypes.byref(d), x, xs or di, B, C, bcs or d.n_groups * d.d_state, dt,
+                               dts or max(di // max(d.headdim, 1), 1), dt_bias, A, D, dt_min, dt_max, s_in, s_out,
+                               y, ys or di, ws, ws_bytes, None)
+
+
+def step(d, xbc=FAKE, xs=None, dt=FAKE + 0x1000000, dts=None, w=FAKE + 0x2000000, bias=None,
+         dt_bias=FAKE + 0x3000000, A=FAKE + 0x3001000, D=None, ring=FAKE + 0x4000000, stepi=0,
+         state=FAKE + 0x1_0000_0000, y=FAKE + 0x9_0000_0000, dt_min=0.0, dt_max=float("inf")):
+    lib = m2.lib()
+    return lib.m2_ssd_step(ctypes.byref(d), xbc, xs or d.conv_dim, dt, dts or d.nheads, w, bias, dt_bias, A, D,
+                           dt_min, dt_max, ring, stepi, state, y, None)
+
+
+def test_null_dims():
+    assert m2.lib().m2_conv1d_fwd(None, FAKE, 1, FAKE, None, None, 0, None, FAKE, 1, None) == m2.M2_ERR_NULL
+    assert m2.lib().m2_ssd_scan_workspace(None) == 0
+
+
+def test_conv_validation():
+    assert conv(dims(io=7)) == m2.M2_ERR_DTYPE
+    assert conv(dims(batch=-1)) == m2.M2_ERR_SHAPE
+    assert conv(dims(d_conv=5)) == m2.M2_ERR_UNSUPPORTED
+    assert conv(dims(d_conv=1)) == m2.M2_ERR_UNSUPPORTED
+    assert conv(dims(headdim=48)) == m2.M2_ERR_SHAPE            # 5120 % 48 != 0
+    assert conv(dims(n_groups=3)) == m2.M2_ERR_SHAPE            # 80 heads % 3 != 0
+    assert conv(dims(), w=None) == m2.M2_ERR_NULL
+    assert conv(dims(), xbc=None) == m2.M2_ERR_NULL
+    assert conv(dims(), out=None) == m2.M2_ERR_NULL
+    d = dims()
+    assert conv(d, xs=d.conv_dim - 1) == m2.M2_ERR_SHAPE
+    assert conv(d, os_=d.conv_dim - 8) == m2.M2_ERR_SHAPE
+    assert conv(d, out=FAKE + 64) == m2.M2_ERR_ALIAS             # out overlaps xbc
+    assert conv(d, ring_in=FAKE + 0x2000_0000_0, ring_out=FAKE + 0x2000_0000_0 + 16) == m2.M2_ERR_ALIAS
+
+
+def test_empty_batch_is_a_no_op():
+    assert conv(dims(batch=0), xbc=None, out=None) == m2.M2_OK
+    assert scan(dims(batch=0), x=None, B=None, C=None, dt=None, y=None) == m2.M2_OK
+    assert step(dims(batch=0), xbc=None, dt=None, ring=None, state=None, y=None) == m2.M2_OK
+
+
+def test_scan_validation():
+    assert scan(dims(), dt_bias=None) == m2.M2_ERR_NULL
+    assert scan(dims(), A=None) == m2.M2_ERR_NULL
+    assert scan(dims(), y=None) == m2.M2_ERR_NULL
+    assert scan(dims(), xs=100) == m2.M2_ERR_SHAPE
+    assert scan(dims(), dts=79) == m2.M2_ERR_SHAPE
+    assert scan(dims(), dt_min=1.0, dt_max=0.5) == m2.M2_ERR_SHAPE
+    assert scan(dims(), dt_min=float("nan")) == m2.M2_ERR_SHAPE
+    assert scan(dims(chunk_size=48)) == m2.M2_ERR_UNSUPPORTED
+    assert scan(dims(d_state=24, d_model=2560)) == m2.M2_ERR_UNSUPPORTED
+    assert scan(dims(), y=FAKE + 128) == m2.M2_ERR_ALIAS                       # y overlaps x
+    assert scan(dims(), s_in=FAKE + 0x5_0000_0000, s_out=FAKE + 0x5_0000_0000) == m2.M2_ERR_ALIAS
+    assert scan(dims(), s_in=FAKE + 0x5_0000_0004) == m2.M2_ERR_UNSUPPORTED    # misaligned state
+
+
+def test_scan_workspace_required_when_reported():
+    d = dims(batch=1, seqlen=32768)
+    need = m2.m2_ssd_scan_workspace(d)
+    if need == 0:
+        pytest.skip("no workspace needed at this shape")
+    assert scan(d, ws=None) == m2.M2_ERR_WORKSPACE
+    assert scan(d, ws=FAKE + 0x8_0000_0000, ws_bytes=need - 1) == m2.M2_ERR_WORKSPACE
+
+
+def test_step_validation():
+    assert step(dims(), stepi=-1) == m2.M2_ERR_SHAPE
+    assert step(dims(), ring=None) == m2.M2_ERR_NULL
+    assert step(dims(), state=None) == m2.M2_ERR_NULL
+    assert step(dims(), xs=100) == m2.M2_ERR_SHAPE
+    assert step(dims(d_state=24, d_model=2560)) == m2.M2_ERR_UNSUPPORTED
+    assert step(dims(), y=FAKE + 0x4000000 + 64) == m2.M2_ERR_ALIAS           # y overlaps ring
+    assert step(dims(), state=FAKE + 0x1_0000_0008) == m2.M2_ERR_UNSUPPORTED  # misaligned state

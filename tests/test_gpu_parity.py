@@ -1,0 +1,366 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Every case feeds both sides the same seeded inputs (workloads/, values exactly
+representable in the storage type).  Floating outputs must agree within the
+floored max-relative-error bound: 2e-2 for bf16 activations with fp32 state,
+1e-4 for fp32 activations.  Conv ring contents are copies of inputs and must be
+bit-identical.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads
+from workloads import Dims
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import selective_state_space_mixer_amd as m2
+    from gpu_util import dev, dev32, dims_of, host, nan_like, tol_for, workspace
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+
+
+# ----------------------------------------------------------------------------- conv1d
+
+CONV_CASES = [
+    # (config index, dims overrides, use ring history, ring phase)
+    (0, {}, False, 0),
+    (1, dict(batch=2, seqlen=300), False, 0),
+    (2, dict(batch=2, seqlen=130), True, 0),
+    (2, dict(batch=2, seqlen=130), True, 3),
+    (2, dict(batch=2, seqlen=2), True, 1),
+    (2, dict(batch=3, seqlen=0), True, 2),
+    (0, dict(seqlen=65, d_conv=3), False, 0),
+    (0, dict(seqlen=40, d_conv=2), False, 0),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "cfg%d-%s-ring%d-ph%d" % (c[0], c[1], c[2], c[3]))
+def test_conv1d_parity(case):
+    _need_gpu()
+    idx, over, use_ring, phase = case
+    cfg = workloads.CONFIGS[idx]
+    d = cfg.dims.replace(**over)
+    inp = workloads.generate(d, 1000 + idx, use_ring)
+    io = d.io
+    Bn, L, Cd, W = d.batch, d.seqlen, d.conv_dim, d.d_conv
+    ring_in = inp.ring0 if use_ring else None
+    ref, ref_ring = oracle.conv1d(inp.xbc, inp.conv_w, inp.conv_b, ring_in, phase)
+    dims = dims_of(d)
+    out = nan_like((Bn, L, Cd), io)
+    ring_out = nan_like((Bn, W, Cd), io)
+    m2.m2_conv1d_fwd(dims, dev(inp.xbc, io), dev32(inp.conv_w), dev32(inp.conv_b), out,
+                     dev(ring_in, io), phase, ring_out)
+    torch.cuda.synchronize()
+    if L > 0:
+        assert oracle.max_rel_err(host(out), ref) <= tol_for(io)
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
+
+
+def test_conv1d_strided_unaligned_views_and_no_bias():
+    """Token stride not a multiple of the vector width -> scalar path; bias NULL."""
+    _need_gpu()
+    d = Dims(2, 77, 16, 2, 16, 16, 1, 4, 0, "bf16")
+    inp = workloads.generate(d, 7, True)
+    Cd = d.conv_dim
+    big = np.zeros((2, 77, Cd + 3), np.float32)
+    big[:, :, 1:Cd + 1] = inp.xbc
+    xbig = dev(big, "bf16")
+    x_view = xbig[:, :, 1:Cd + 1]
+    out_big = nan_like((2, 77, Cd + 5), "bf16")
+    out_view = out_big[:, :, 2:Cd + 2]
+    ref, ref_ring = oracle.conv1d(inp.xbc, inp.conv_w, None, inp.ring0, 1)
+    ring_out = nan_like((2, 4, Cd), "bf16")
+    m2.m2_conv1d_fwd(dims_of(d), x_view, dev32(inp.conv_w), None, out_view, dev(inp.ring0, "bf16"), 1, ring_out)
+    torch.cuda.synchronize()
+    assert oracle.max_rel_err(host(out_view), ref) <= 2e-2
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
+    # the padding around the view is untouched
+    assert torch.isnan(out_big[:, :, :2]).all() and torch.isnan(out_big[:, :, Cd + 2:]).all()
+
+
+# ----------------------------------------------------------------------------- scan
+
+def _scan_inputs(d, seed, cached):
+    inp = workloads.generate(d, seed, cached)
+    x, b, c = inp.split()
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    lead = (d.batch, d.seqlen)
+    return (inp, x.reshape(lead + (H, P)), b.reshape(lead + (G, N)), c.reshape(lead + (G, N)))
+
+
+def _run_scan(d, inp, x, b, c, state_in, strided=False):
+    io = d.io
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    Bn, L = d.batch, d.seqlen
+    dims = dims_of(d)
+    if strided:
+        # x, B, C as views into one conv-output-like buffer; dt as a view into a wider buffer
+        buf = np.concatenate([x.reshape(Bn, L, H * P), b.reshape(Bn, L, G * N), c.reshape(Bn, L, G * N)], -1)
+        tb = dev(buf, io)
+        xg = tb[:, :, :H * P].unflatten(-1, (H, P))
+        bg = tb[:, :, H * P:H * P + G * N].unflatten(-1, (G, N))
+        cg = tb[:, :, H * P + G * N:].unflatten(-1, (G, N))
+        dtb = dev(np.concatenate([np.zeros((Bn, L, 3), np.float32), inp.dt_raw, np.zeros((Bn, L, 5), np.float32)],
+                                 -1), io)
+        dtg = dtb[:, :, 3:3 + H]
+    else:
+        xg, bg, cg, dtg = dev(x, io), dev(b, io), dev(c, io), dev(inp.dt_raw, io)
+    y = nan_like((Bn, L, H * P), io)
+    s_out = torch.full((Bn, H, P, N), float("nan"), device="cuda")
+    m2.m2_ssd_scan_fwd(dims, xg, bg, cg, dtg, dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y,
+                       dev32(state_in), s_out, workspace=workspace(dims))
+    torch.cuda.synchronize()
+    return host(y).reshape(Bn, L, H, P), host(s_out)
+
+
+SCAN_CASES = [
+    # (config index, dims overrides, cached initial state, strided views)
+    (0, {}, False, False),
+    (0, dict(seqlen=100), True, True),          # ragged: 100 = 6*16 + 4
+    (1, dict(batch=2, seqlen=200), False, False),
+    (2, dict(batch=2, seqlen=300), True, True),
+    (2, dict(batch=1, seqlen=1), True, False),
+    (2, dict(batch=2, seqlen=0), True, False),
+    (2, dict(batch=1, seqlen=130, chunk_size=32), True, False),
+    (2, dict(batch=1, seqlen=130, chunk_size=16), True, False),
+    (0, dict(d_model=64, headdim=32, d_state=16, n_groups=2, seqlen=70, io="bf16"), True, False),
+    (0, dict(d_model=64, headdim=16, d_state=32, n_groups=4, seqlen=50), True, False),
+]
+
+
+@pytest.mark.parametrize("case", SCAN_CASES, ids=lambda c: "cfg%d-%s-init%d-str%d" % c)
+def test_ssd_scan_parity(case):
+    _need_gpu()
+    idx, over, cached, strided = case
+    d = workloads.CONFIGS[idx].dims.replace(**over)
+    inp, x, b, c = _scan_inputs(d, 2000 + idx, cached)
+    y, s = _run_scan(d, inp, x, b, c, inp.state0, strided)
+    yr, sr = oracle.ssd_scan(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0)
+    tol = tol_for(d.io)
+    if d.seqlen > 0:
+        assert oracle.max_rel_err(y, yr) <= tol
+    assert oracle.max_rel_err(s, sr) <= tol
+
+
+def test_ssd_scan_chunk_size_invariance():
+    """Results do not depend on the chunk length (up to rounding)."""
+    _need_gpu()
+    d = workloads.CONFIGS[2].dims.replace(batch=1, seqlen=333)
+    inp, x, b, c = _scan_inputs(d, 31, True)
+    outs = [_run_scan(d.replace(chunk_size=q), inp, x, b, c, inp.state0) for q in (16, 32, 64)]
+    for y, s in outs[1:]:
+        assert oracle.max_rel_err(y, outs[0][0]) <= 2e-2
+        assert oracle.max_rel_err(s, outs[0][1]) <= 2e-2
+
+
+def test_ssd_scan_split_prefill_invariance():
+    """Chunked prefill (two calls, state handed over) == one call (Zamba2 article §七)."""
+    _need_gpu()
+    d = workloads.CONFIGS[2].dims.replace(batch=2, seqlen=200)
+    inp, x, b, c = _scan_inputs(d, 32, True)
+    y, s = _run_scan(d, inp, x, b, c, inp.state0)
+    k = 77
+    d1, d2 = d.replace(seqlen=k), d.replace(seqlen=d.seqlen - k)
+
+    class Part:
+        pass
+
+    p1, p2 = Part(), Part()
+    for p, sl in ((p1, slice(0, k)), (p2, slice(k, None))):
+        p.dt_raw, p.dt_bias, p.A, p.D = inp.dt_raw[:, sl], inp.dt_bias, inp.A, inp.D
+    y1, s1 = _run_scan(d1, p1, x[:, :k], b[:, :k], c[:, :k], inp.state0)
+    y2, s2 = _run_scan(d2, p2, x[:, k:], b[:, k:], c[:, k:], s1.astype(np.float32))
+    assert oracle.max_rel_err(np.concatenate([y1, y2], 1), y) <= 2e-2
+    assert oracle.max_rel_err(s2, s) <= 2e-2
+
+
+def test_ssd_scan_deterministic():
+    _need_gpu()
+    d = workloads.CONFIGS[2].dims.replace(batch=2, seqlen=257)
+    inp, x, b, c = _scan_inputs(d, 33, True)
+    y1, s1 = _run_scan(d, inp, x, b, c, inp.state0)
+    y2, s2 = _run_scan(d, inp, x, b, c, inp.state0)
+    np.testing.assert_array_equal(y1, y2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+# ----------------------------------------------------------------------------- decode step
+
+def _gpu_chain(d, inp, steps, ring0, state0, first_step=0):
+    io = d.io
+    Bn, H, P, N, W, Cd = d.batch, d.nheads, d.headdim, d.d_state, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    ring = dev(ring0, io) if ring0 is not None else torch.zeros((Bn, W, Cd), device="cuda", dtype=torch.bfloat16
+                                                                if io == "bf16" else torch.float32)
+    state = dev32(state0) if state0 is not None else torch.zeros((Bn, H, P, N), device="cuda")
+    xt = dev(inp.xbc, io)
+    dtt = dev(inp.dt_raw, io)
+    w, cb, dtb, A, D = (dev32(a) for a in (inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D))
+    ys = []
+    for t in range(steps):
+        y = nan_like((Bn, H * P), io)
+        m2.m2_ssd_step(dims, xt[t], dtt[t], w, cb, dtb, A, D, ring, first_step + t, state, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    return np.stack([host(y) for y in ys]), host(ring), host(state)
+
+
+@pytest.mark.parametrize("over,steps", [(dict(batch=3), 6), (dict(batch=2, d_conv=3), 5),
+                                        (dict(batch=1, d_model=64, headdim=16, d_state=32, n_groups=2), 7)])
+def test_ssd_step_chain_parity(over, steps):
+    _need_gpu()
+    d = workloads.CONFIGS[4].dims.replace(**over)
+    inp = workloads.generate(d, 1004, True, steps)
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    ys, ring, state = _gpu_chain(d, inp, steps, inp.ring0, inp.state0)
+    r_ring, r_state = inp.ring0.astype(np.float64), inp.state0.astype(np.float64)
+    for t in range(steps):
+        yr, r_ring, r_state = oracle.ssd_step(inp.xbc[t], inp.dt_raw[t], inp.conv_w, inp.conv_b, inp.dt_bias,
+                                              inp.A, inp.D, r_ring, t, r_state, H, P, N, G)
+        assert oracle.max_rel_err(ys[t], yr) <= 2e-2, "step %d" % t
+    assert oracle.max_rel_err(state, r_state) <= 2e-2
+    np.testing.assert_array_equal(ring, r_ring)
+
+
+def test_ssd_step_fp32_chain_parity():
+    _need_gpu()
+    d = workloads.CONFIGS[0].dims.replace(batch=2, seqlen=1)
+    steps = 64
+    inp = workloads.generate(d, 1000, True, steps)
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    ys, ring, state = _gpu_chain(d, inp, steps, inp.ring0, inp.state0, first_step=5)
+    r_ring, r_state = inp.ring0.astype(np.float64), inp.state0.astype(np.float64)
+    yref = []
+    for t in range(steps):
+        yr, r_ring, r_state = oracle.ssd_step(inp.xbc[t], inp.dt_raw[t], inp.conv_w, inp.conv_b, inp.dt_bias,
+                                              inp.A, inp.D, r_ring, 5 + t, r_state, H, P, N, G)
+        yref.append(yr)
+    assert oracle.max_rel_err(ys, np.stack(yref)) <= 1e-4
+    assert oracle.max_rel_err(state, r_state) <= 1e-4
+    np.testing.assert_array_equal(ring, r_ring)
+
+
+def test_decode_chain_equals_prefill():
+    """Token-by-token decode path == chunked prefill path (Zamba2 article §七), both on the GPU."""
+    _need_gpu()
+    L = 45
+    d = workloads.CONFIGS[2].dims.replace(batch=2, seqlen=L)
+    inp = workloads.generate(d, 41, True)
+    io = d.io
+    Bn, H, P, N, G, W, Cd = d.batch, d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    # prefill: conv (ring history at phase 0) -> scan, both through the ABI
+    act = nan_like((Bn, L, Cd), io)
+    ring_out = nan_like((Bn, W, Cd), io)
+    m2.m2_conv1d_fwd(dims, dev(inp.xbc, io), dev32(inp.conv_w), dev32(inp.conv_b), act, dev(inp.ring0, io), 0,
+                     ring_out)
+    y = nan_like((Bn, L, H * P), io)
+    s_out = torch.empty((Bn, H, P, N), device="cuda")
+    dt = dev(inp.dt_raw, io)
+    m2.m2_ssd_scan_fwd(dims, act[:, :, :H * P], act[:, :, H * P:H * P + G * N], act[:, :, H * P + G * N:], dt,
+                       dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(inp.state0), s_out,
+                       workspace=workspace(dims))
+    torch.cuda.synchronize()
+
+    class Tok:
+        pass
+
+    tok = Tok()
+    tok.xbc = np.ascontiguousarray(inp.xbc.transpose(1, 0, 2))
+    tok.dt_raw = np.ascontiguousarray(inp.dt_raw.transpose(1, 0, 2))
+    tok.conv_w, tok.conv_b, tok.dt_bias, tok.A, tok.D = inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D
+    ys, ring, state = _gpu_chain(d, tok, L, inp.ring0, inp.state0)
+    assert oracle.max_rel_err(state, host(s_out)) <= 2e-2
+    assert oracle.max_rel_err(ys.transpose(1, 0, 2), host(y)) <= 2e-2
+    ro = host(ring_out)
+    for j in range(1, W + 1):
+        np.testing.assert_array_equal(ring[:, (L - j) % W], ro[:, W - j])
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def _sampled_scan_check(idx, heads, batches):
+    cfg = workloads.CONFIGS[idx]
+    d = cfg.dims
+    inp = workloads.config_inputs(idx)
+    io = d.io
+    Bn, L, H, P, N, G, W, Cd = d.batch, d.seqlen, d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    act = torch.empty((Bn, L, Cd), device="cuda", dtype=torch.bfloat16)
+    ring_out = torch.empty((Bn, W, Cd), device="cuda", dtype=torch.bfloat16)
+    xbc = dev(inp.xbc, io)
+    m2.m2_conv1d_fwd(dims, xbc, dev32(inp.conv_w), dev32(inp.conv_b), act, dev(inp.ring0, io), 0, ring_out)
+    y = torch.empty((Bn, L, H * P), device="cuda", dtype=torch.bfloat16)
+    s_out = torch.empty((Bn, H, P, N), device="cuda")
+    m2.m2_ssd_scan_fwd(dims, act[:, :, :H * P], act[:, :, H * P:H * P + G * N], act[:, :, H * P + G * N:],
+                       dev(inp.dt_raw, io), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y,
+                       dev32(inp.state0), s_out, workspace=workspace(dims))
+    torch.cuda.synchronize()
+    del xbc
+    # conv: sampled channels against the oracle (x, B and C channels)
+    chans = np.array([0, 1, H * P - 1, H * P, H * P + N - 1, Cd - 1])
+    for b in batches:
+        ring_b = None if inp.ring0 is None else inp.ring0[b:b + 1][:, :, chans]
+        ref, ref_ring = oracle.conv1d(inp.xbc[b:b + 1][:, :, chans], inp.conv_w[chans], inp.conv_b[chans], ring_b, 0)
+        got = host(act[b:b + 1][:, :, torch.as_tensor(chans, device="cuda")])
+        assert oracle.max_rel_err(got, ref) <= 2e-2
+        np.testing.assert_array_equal(host(ring_out[b:b + 1][:, :, torch.as_tensor(chans, device="cuda")]),
+                                      ref_ring)
+    # scan: whole sequences of sampled (b, h), fed the GPU's own conv output (per-kernel parity)
+    for b in batches:
+        a_b = host(act[b])
+        for h in heads:
+            g = h // (H // G)
+            xs = a_b[:, h * P:(h + 1) * P].reshape(1, L, 1, P)
+            bs = a_b[:, H * P + g * N:H * P + (g + 1) * N].reshape(1, L, 1, N)
+            cs = a_b[:, H * P + G * N + g * N:H * P + G * N + (g + 1) * N].reshape(1, L, 1, N)
+            s0 = None if inp.state0 is None else inp.state0[b:b + 1, h:h + 1]
+            yr, sr = oracle.ssd_scan(xs, bs, cs, inp.dt_raw[b:b + 1, :, h:h + 1], inp.dt_bias[h:h + 1],
+                                     inp.A[h:h + 1], inp.D[h:h + 1], s0)
+            got_y = host(y[b, :, h * P:(h + 1) * P]).reshape(1, L, 1, P)
+            assert oracle.max_rel_err(got_y, yr) <= 2e-2, (b, h)
+            assert oracle.max_rel_err(host(s_out[b:b + 1, h:h + 1]), sr) <= 2e-2, (b, h)
+
+
+def test_full_size_prefill_b8_l4096_sampled():
+    _need_gpu()
+    _sampled_scan_check(2, heads=[0, 37, 79], batches=[0, 7])
+
+
+def test_full_size_prefill_b1_l32768_sampled():
+    _need_gpu()
+    _sampled_scan_check(3, heads=[0, 52, 79], batches=[0])
+
+
+def test_full_size_prefill_130m_sampled():
+    _need_gpu()
+    _sampled_scan_check(1, heads=[0, 23], batches=[0, 3])
+
+
+def test_full_size_decode_b256_sampled():
+    """256 sequences, a few chained steps; sampled sequences against the oracle chain."""
+    _need_gpu()
+    cfg = workloads.CONFIGS[4]
+    d = cfg.dims
+    steps = 3
+    inp = workloads.generate(d, 1004, True, steps)
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    ys, ring, state = _gpu_chain(d, inp, steps, inp.ring0, inp.state0)
+    for b in (0, 131, 255):
+        r_ring = inp.ring0[b:b + 1].astype(np.float64)
+        r_state = inp.state0[b:b + 1].astype(np.float64)
+        for t in range(steps):
+            yr, r_ring, r_state = oracle.ssd_step(inp.xbc[t, b:b + 1], inp.dt_raw[t, b:b + 1], inp.conv_w,
+                                                  inp.conv_b, inp.dt_bias, inp.A, inp.D, r_ring, t, r_state,
+                                                  H, P, N, G)
+            assert oracle.max_rel_err(ys[t, b:b + 1], yr) <= 2e-2
+        assert oracle.max_rel_err(state[b:b + 1], r_state) <= 2e-2
+        np.testing.assert_array_equal(ring[b:b + 1], r_ring)
