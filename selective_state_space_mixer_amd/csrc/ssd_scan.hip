@@ -1,143 +1,627 @@
-// ssd_scan.hip -- selective state-space scan over a prompt (gfx950).
+// ssd_scan.hip -- chunked selective state-space scan over a prompt (gfx950, MFMA).
 //
-// First version: one block per (sequence, head) walks the tokens in order with the
-// P x N fp32 state held in registers (16-byte slices per lane), exactly the
-// recurrence S_t = exp(dt_t A) S_{t-1} + dt_t x_t B_t^T, y_t = S_t C_t + D x_t.
-// Inputs of token t+1 are prefetched while token t is applied.
+// The Zamba2 mixer's prompt path (article "Transformers 中 Zamba2 混合架构模型解析",
+// §三: the sequence is cut into chunks of chunk_size and scanned with an intra-chunk
+// plus an inter-chunk pass).  For a chunk of Q tokens starting after state S_prev,
+// with a_t = dt_t * A and Lam_t = the sum of a over the chunk up to and including t:
+//
+//   y_t   = exp(Lam_t) * (S_prev . C_t)                                   (state part)
+//         + sum_{s<=t} exp(Lam_t - Lam_s) * dt_s * (C_t . B_s) * x_s       (intra-chunk part)
+//         + D * x_t
+//   S_new = exp(Lam_end) * S_prev + sum_s exp(Lam_end - Lam_s) * dt_s * x_s (outer) B_s
+//
+// which is the token recurrence S_t = exp(dt_t A) S_{t-1} + dt_t x_t B_t^T, y_t = S_t C_t + D x_t
+// unrolled over the chunk (exactly, up to rounding).
+//
+// One workgroup walks the chunks of one (sequence, head, segment) in order and keeps
+// the fp32 state in MFMA accumulator registers for the whole walk.  Per chunk, four
+// contractions run on v_mfma_f32_16x16x32_bf16 (fp32 activations: v_mfma_f32_16x16x4f32):
+//   G^T[s][t] = sum_n B[s][n] C[t][n]            -> masked and scaled -> M[t][s] in LDS
+//                                                   (bf16: as a hi + lo pair, see below)
+//   Y^T[p][t] = sum_n S[p][n] (e^Lam_t C[t][n])   (state part, state as the A operand)
+//   Y^T[p][t]+= sum_s X[s][p] M[t][s]             (intra-chunk part)
+//   S^T[n][p] = e^Lam_end S^T[n][p] + sum_s (w_s B[s][n]) X[s][p],  w_s = e^(Lam_end-Lam_s) dt_s
+// Wave w owns p-block(s) w of the state and of the output, so the state never leaves
+// its registers; only M (the same for every p-block) goes through LDS.  Operands whose
+// contraction index runs down the rows of a row-major LDS tile (X and B over tokens) are
+// read with ds_read_b64_tr_b16, which hands each lane four consecutive rows of one column.
+//
+// M carries the whole intra-chunk weight of a token on itself and its neighbours; where the
+// decay is strong those terms are large and cancel, so a single bf16 rounding of M costs
+// several percent of y.  M is therefore stored as bf16 hi = rn(M) and lo = rn(M - hi) and the
+// intra contraction runs twice, which leaves M's error near 2^-17.
+//
+// Long sequences with few (sequence, head) pairs are split into segments that run in
+// parallel: a first pass computes each segment's end state from a zero start, a small
+// pass chains those into each segment's true initial state, and the main pass then
+// walks every segment from its initial state.
 #include "m2_device.h"
 #include "m2_launch.h"
 
 namespace m2 {
 
-constexpr int kScanThreads = 256;
+#define M2_LDS __attribute__((address_space(3)))
 
-template <typename T, int N, int K>
-__global__ __launch_bounds__(kScanThreads) void ssd_scan_seq_kernel(
-    const T* __restrict__ x, int64_t xs, const T* __restrict__ Bm, const T* __restrict__ Cm, int64_t bcs,
-    const T* __restrict__ dtr, int64_t dts, const float* __restrict__ dt_bias, const float* __restrict__ Aa,
-    const float* __restrict__ Dd, float dt_min, float dt_max, const float* __restrict__ state_in,
-    float* __restrict__ state_out, T* __restrict__ y, int64_t ys, int64_t L, int H, int P, int G)
-{
-    constexpr int TPR = N / 4;
-    __shared__ float buf[2][512 + 2 * 256];
-    const int h = blockIdx.x;
-    const int64_t b = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int g = h / (H / G);
-    const int nvec = P * TPR;
-    const int nld = P + 2 * N;  // elements loaded per token
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-    float4 s[K];
-    const int64_t soff = ((b * H + h) * (int64_t)P) * N;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int i = tid + k * kScanThreads;
-        s[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (state_in && i < nvec) s[k] = reinterpret_cast<const float4*>(state_in + soff)[i];
-    }
-    const float bias_h = dt_bias[h], A_h = Aa[h], D_h = Dd ? Dd[h] : 0.0f;
+// ----------------------------------------------------------------------------------------------
+// element types
 
-    // element j of a token: x[p] (j < P), B[n], C[n]
-    auto src = [&](int64_t t, int j) -> float {
-        const int64_t bt = b * L + t;
-        if (j < P) return to_f32(x[bt * xs + (int64_t)h * P + j]);
-        if (j < P + N) return to_f32(Bm[bt * bcs + (int64_t)g * N + (j - P)]);
-        return to_f32(Cm[bt * bcs + (int64_t)g * N + (j - P - N)]);
-    };
-    float pre0 = 0.f, pre1 = 0.f, pdt = 0.f;
-    if (L > 0) {
-        if (tid < nld) pre0 = src(0, tid);
-        if (tid + kScanThreads < nld) pre1 = src(0, tid + kScanThreads);
-        pdt = to_f32(dtr[(b * L) * dts + h]);
+template <typename T> struct Lds;
+template <> struct Lds<bf16_t> { using E = uint16_t; static constexpr int PAD = 8; };
+template <> struct Lds<float> { using E = float; static constexpr int PAD = 4; };
+
+// Eight k-values of one lane for a K=32 MFMA step: chunk 0 holds k = kbase+4q+{0..3},
+// chunk 1 holds k = kbase+16+4q+{0..3} (q = lane/16).  Both operands of a product use the
+// same assignment, so the sum runs over every k exactly once.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+    uint32_t w[4];
+    __device__ __forceinline__ void set(int c, float a0, float a1, float a2, float a3) {
+        w[2 * c] = (uint32_t)f32_to_bits(a0) | ((uint32_t)f32_to_bits(a1) << 16);
+        w[2 * c + 1] = (uint32_t)f32_to_bits(a2) | ((uint32_t)f32_to_bits(a3) << 16);
     }
-    for (int64_t t = 0; t < L; ++t) {
-        float* cur = buf[t & 1];
-        if (tid < nld) cur[tid] = pre0;
-        if (tid + kScanThreads < nld) cur[tid + kScanThreads] = pre1;
-        const float dt = dt_of(pdt, bias_h, dt_min, dt_max);
-        if (t + 1 < L) {
-            if (tid < nld) pre0 = src(t + 1, tid);
-            if (tid + kScanThreads < nld) pre1 = src(t + 1, tid + kScanThreads);
-            pdt = to_f32(dtr[(b * L + t + 1) * dts + h]);
-        }
-        __syncthreads();
-        const float decay = fast_exp(dt * A_h);
-        const float* xv = cur;
-        const float* Bv = cur + P;
-        const float* Cv = cur + P + N;
-        T* yt = y + (b * L + t) * ys + (int64_t)h * P;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int i = tid + k * kScanThreads;
-            const int p = i / TPR, n0 = (i % TPR) * 4;
-            float part = 0.0f;
-            if (i < nvec) {
-                const float dx = dt * xv[p];
-                float4 v = s[k];
-                v.x = fmaf(decay, v.x, dx * Bv[n0 + 0]);
-                v.y = fmaf(decay, v.y, dx * Bv[n0 + 1]);
-                v.z = fmaf(decay, v.z, dx * Bv[n0 + 2]);
-                v.w = fmaf(decay, v.w, dx * Bv[n0 + 3]);
-                s[k] = v;
-                part = v.x * Cv[n0] + v.y * Cv[n0 + 1] + v.z * Cv[n0 + 2] + v.w * Cv[n0 + 3];
-            }
-#pragma unroll
-            for (int off = 1; off < TPR; off <<= 1) part += __shfl_xor(part, off, kWave);
-            if (i < nvec && (i % TPR) == 0) yt[p] = from_f32<T>(part + D_h * xv[p]);
-        }
+    __device__ __forceinline__ float get(int c, int e) const {
+        const uint32_t v = w[2 * c + (e >> 1)];
+        return __uint_as_float((e & 1) ? (v & 0xffff0000u) : (v << 16));
     }
-    if (state_out) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int i = tid + k * kScanThreads;
-            if (i < nvec) reinterpret_cast<float4*>(state_out + soff)[i] = s[k];
-        }
+};
+template <> struct Frag<float> {
+    float v[8];
+    __device__ __forceinline__ void set(int c, float a0, float a1, float a2, float a3) {
+        v[4 * c] = a0; v[4 * c + 1] = a1; v[4 * c + 2] = a2; v[4 * c + 3] = a3;
     }
+    __device__ __forceinline__ float get(int c, int e) const { return v[4 * c + e]; }
+};
+
+__device__ __forceinline__ void mfma(f32x4& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.w),
+                                                  __builtin_bit_cast(bf16x8_t, b.w), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
-template <typename T, int N, int K>
-static hipError_t launch_scan_nk(const ScanArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)a.H, (unsigned)a.batch);
-    return launch_kernel(ssd_scan_seq_kernel<T, N, K>, grid, dim3(kScanThreads), 0, s,
-                       (const T*)a.x, a.xs, (const T*)a.B, (const T*)a.C, a.bcs, (const T*)a.dt, a.dts,
-                       a.dt_bias, a.A, a.D, a.dt_min, a.dt_max, a.state_in, a.state_out, (T*)a.y, a.ys, a.L,
-                       a.H, a.P, a.G);
+// chunk c of a fragment from a row-major LDS tile whose k index runs along the row
+__device__ __forceinline__ void chunk_row(Frag<bf16_t>& f, int c, const uint16_t* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    f.w[2 * c] = v.x;
+    f.w[2 * c + 1] = v.y;
+}
+__device__ __forceinline__ void chunk_row(Frag<float>& f, int c, const float* p) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    f.set(c, v.x, v.y, v.z, v.w);
 }
 
-template <typename T, int N>
-static hipError_t launch_scan_n(const ScanArgs& a, hipStream_t s) {
-    const int K = (a.P * (N / 4) + kScanThreads - 1) / kScanThreads;
-    switch (K) {
-        case 1: return launch_scan_nk<T, N, 1>(a, s);
-        case 2: return launch_scan_nk<T, N, 2>(a, s);
-        case 3: case 4: return launch_scan_nk<T, N, 4>(a, s);
-        default: return launch_scan_nk<T, N, 8>(a, s);
-    }
+// Fragment with k along a row: the lane supplies `row`, k = kbase + 4q (+16); kext = k extent.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_row(const typename Lds<T>::E* tile, int stride, int row, int kbase,
+                                            int kext, int q) {
+    Frag<T> f;
+    chunk_row(f, 0, tile + row * stride + kbase + 4 * q);
+    if (kbase + 16 < kext) chunk_row(f, 1, tile + row * stride + kbase + 16 + 4 * q);
+    else f.set(1, 0.f, 0.f, 0.f, 0.f);
+    return f;
+}
+
+// Chunk c of a fragment whose k index runs down the rows: lane (q, i) gets rows r0+4q..r0+4q+3
+// of column col0+i.  bf16: one ds_read_b64_tr_b16 (lane i addresses row i/4, columns 4(i%4)..+3
+// of its 16-lane group's 4x16 block and receives column i of the block).
+__device__ __forceinline__ void chunk_col(Frag<bf16_t>& f, int c, const uint16_t* tile, int stride, int r0, int col0,
+                                          int q, int i) {
+    const uint16_t* p = tile + (r0 + 4 * q + (i >> 2)) * stride + col0 + 4 * (i & 3);
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((M2_LDS i16x4_t*)(p));
+    const uint2 u = __builtin_bit_cast(uint2, v);
+    f.w[2 * c] = u.x;
+    f.w[2 * c + 1] = u.y;
+}
+__device__ __forceinline__ void chunk_col(Frag<float>& f, int c, const float* tile, int stride, int r0, int col0,
+                                          int q, int i) {
+    const float* p = tile + (r0 + 4 * q) * stride + col0 + i;
+    f.set(c, p[0], p[stride], p[2 * stride], p[3 * stride]);
 }
 
 template <typename T>
-static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
-    switch (a.N) {
-        case 16: return launch_scan_n<T, 16>(a, s);
-        case 32: return launch_scan_n<T, 32>(a, s);
-        case 64: return launch_scan_n<T, 64>(a, s);
-        default: return launch_scan_n<T, 128>(a, s);
+__device__ __forceinline__ Frag<T> frag_col(const typename Lds<T>::E* tile, int stride, int kbase, int kext,
+                                            int col0, int q, int i) {
+    Frag<T> f;
+    chunk_col(f, 0, tile, stride, kbase, col0, q, i);
+    if (kbase + 16 < kext) chunk_col(f, 1, tile, stride, kbase + 16, col0, q, i);
+    else f.set(1, 0.f, 0.f, 0.f, 0.f);
+    return f;
+}
+
+// four consecutive elements of a row as fp32, and back
+__device__ __forceinline__ void row4(const uint16_t* p, float (&o)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void row4(const float* p, float (&o)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void put4(uint16_t* p, float a0, float a1, float a2, float a3) {
+    uint2 v;
+    v.x = (uint32_t)f32_to_bits(a0) | ((uint32_t)f32_to_bits(a1) << 16);
+    v.y = (uint32_t)f32_to_bits(a2) | ((uint32_t)f32_to_bits(a3) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+}
+__device__ __forceinline__ void put4(float* p, float a0, float a1, float a2, float a3) {
+    *reinterpret_cast<float4*>(p) = make_float4(a0, a1, a2, a3);
+}
+__device__ __forceinline__ void put4g(bf16_t* p, float a0, float a1, float a2, float a3) {
+    put4(reinterpret_cast<uint16_t*>(p), a0, a1, a2, a3);
+}
+__device__ __forceinline__ void put4g(float* p, float a0, float a1, float a2, float a3) { put4(p, a0, a1, a2, a3); }
+
+// ----------------------------------------------------------------------------------------------
+// kernel parameters
+
+struct ScanK {
+    const void* x; const void* B; const void* C; const void* dt;
+    int64_t xs, bcs, dts, ys;
+    const float* dt_bias; const float* A; const float* D;
+    float dt_min, dt_max;
+    const float* state_in; float* state_out;
+    void* y;
+    float* ws_state;   // [nseg][batch*H][P*N]: segment end states, then segment initial states
+    float* ws_lam;     // [nseg][batch*H]: summed log-decay of each segment
+    int64_t L;
+    int batch, H, G;
+    int nseg, cps;     // segments per sequence, chunks per segment
+    int nblocks;       // blocks in this launch
+};
+
+// Block -> logical unit.  Consecutive blocks are dealt round-robin to the 8 XCDs; the remap
+// gives each XCD a contiguous run of logical units (the heads of one sequence and segment),
+// so the B/C rows those heads share are fetched into one L2.
+__device__ __forceinline__ int logical_block(int nblocks) {
+    const int i = blockIdx.x;
+    if (nblocks % 8) return i;
+    return (i % 8) * (nblocks / 8) + i / 8;
+}
+
+constexpr int scan_threads(int P) { return 64 * (P / 16 >= 4 ? 4 : P / 16); }
+
+template <typename T, int Q, int P, int N>
+struct Cfg {
+    using E = typename Lds<T>::E;
+    static constexpr int NPB = P / 16;
+    static constexpr int NW = NPB >= 4 ? 4 : NPB;  // waves
+    static constexpr int PBW = NPB / NW;           // p-blocks per wave
+    static constexpr int NNB = N / 16;
+    static constexpr int NTB = Q / 16;
+    static constexpr int THREADS = 64 * NW;
+    static_assert(THREADS == scan_threads(P), "thread count");
+    static constexpr int XST = P + Lds<T>::PAD;    // LDS row strides (elements)
+    static constexpr int BST = N + Lds<T>::PAD;
+    static constexpr int MST = Q + Lds<T>::PAD;
+    static constexpr int EPU = 16 / (int)sizeof(E);  // elements per 16-byte unit
+    static constexpr int XU = P / EPU, BU = N / EPU;
+    static constexpr int KS_N = (N + 31) / 32;     // K=32 steps over d_state
+    static constexpr int KS_Q = (Q + 31) / 32;     // K=32 steps over tokens
+};
+
+// ----------------------------------------------------------------------------------------------
+// chunk walk.  kStateOnly: segment end state from a zero start (no C, no output).
+
+template <typename T, int Q, int P, int N, bool kStateOnly>
+__global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k)
+{
+    using Cf = Cfg<T, Q, P, N>;
+    using E = typename Cf::E;
+    constexpr int THREADS = Cf::THREADS, XST = Cf::XST, BST = Cf::BST, MST = Cf::MST;
+    constexpr int RU = Cf::XU + Cf::BU * (kStateOnly ? 1 : 2);  // 16-byte units per token
+    constexpr int UPT = (Q * RU + THREADS - 1) / THREADS;         // units per thread per chunk
+
+    __shared__ __attribute__((aligned(16))) E Xs[Q * XST];
+    __shared__ __attribute__((aligned(16))) E Bs[Q * BST];
+    __shared__ __attribute__((aligned(16))) E Cs[kStateOnly ? 8 : Q * BST];
+    constexpr bool kSplitM = sizeof(E) == 2;  // bf16 tiles: M as hi + lo
+    __shared__ __attribute__((aligned(16))) E Ms[kStateOnly ? 8 : Q * MST];
+    __shared__ __attribute__((aligned(16))) E Ml[kStateOnly || !kSplitM ? 8 : Q * MST];
+    __shared__ __attribute__((aligned(16))) float sLam[Q];
+    __shared__ __attribute__((aligned(16))) float sDt[Q];
+    __shared__ __attribute__((aligned(16))) float sW[Q];
+    __shared__ __attribute__((aligned(16))) float sExpL[Q];
+    __shared__ float sEnd;
+
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, li = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so tile ownership is a scalar branch
+    const int unit = logical_block(k.nblocks);
+    const int BH = k.batch * k.H;
+    const int seg = unit / BH;
+    const int bh = unit % BH;
+    const int64_t b = bh / k.H;
+    const int h = bh % k.H;
+    const int g = h / (k.H / k.G);
+    const int64_t nchunks = (k.L + Q - 1) / Q;
+    const int64_t c_begin = (int64_t)seg * k.cps;
+    const int64_t c_end = c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks;
+
+    const T* xg = reinterpret_cast<const T*>(k.x) + b * k.L * k.xs + (int64_t)h * P;
+    const T* bg = reinterpret_cast<const T*>(k.B) + b * k.L * k.bcs + (int64_t)g * N;
+    const T* cg = reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N;
+    const T* dtg = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
+    const float bias_h = k.dt_bias[h], A_h = k.A[h];
+    const float D_h = k.D ? k.D[h] : 0.0f;
+
+    // state tiles in accumulator layout: accS[pb][nb][j] = S[p = pblk*16 + li][n = nb*16 + 4q + j]
+    f32x4 accS[Cf::PBW][Cf::NNB];
+    {
+        const float* src = nullptr;
+        if (!kStateOnly) {
+            if (seg == 0) src = k.state_in ? k.state_in + (int64_t)bh * P * N : nullptr;
+            else src = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
+        }
+#pragma unroll
+        for (int pb = 0; pb < Cf::PBW; ++pb) {
+            const int p = (wave * Cf::PBW + pb) * 16 + li;
+#pragma unroll
+            for (int nb = 0; nb < Cf::NNB; ++nb) {
+                if (src) {
+                    const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)p * N + nb * 16 + 4 * q);
+                    accS[pb][nb] = f32x4{v.x, v.y, v.z, v.w};
+                } else {
+                    accS[pb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    }
+
+    // Register prefetch of one chunk: UPT 16-byte units per thread (+ raw dt, one token per lane of
+    // wave 0).  Loads are issued without branches (indices clamped into the chunk) and stay raw
+    // until commit(), so nothing waits on them before the next chunk starts; commit() zeroes the
+    // tokens past the end of the sequence.
+    uint4 pre[UPT];
+    T pre_dt;
+    auto prefetch = [&](int64_t c) {
+        const int64_t t0 = c * Q;
+        const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            int idx = tid + u * THREADS;
+            if (Q * RU % THREADS != 0) idx = idx < Q * RU ? idx : Q * RU - 1;
+            int t = idx / RU;
+            const int r = idx % RU;
+            t = t < valid ? t : valid - 1;
+            const T* src;
+            if (r < Cf::XU) src = xg + (t0 + t) * k.xs + r * Cf::EPU;
+            else if (r < Cf::XU + Cf::BU) src = bg + (t0 + t) * k.bcs + (r - Cf::XU) * Cf::EPU;
+            else src = cg + (t0 + t) * k.bcs + (r - Cf::XU - Cf::BU) * Cf::EPU;
+            pre[u] = *reinterpret_cast<const uint4*>(src);
+        }
+        if (wave == 0) pre_dt = dtg[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
+    };
+    auto commit = [&](int64_t c) {
+        const int valid = (int)(k.L - c * Q < Q ? k.L - c * Q : Q);
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int idx = tid + u * THREADS;
+            const int t = idx / RU, r = idx % RU;
+            if (idx < Q * RU) {
+                E* dst;
+                if (r < Cf::XU) dst = Xs + t * XST + r * Cf::EPU;
+                else if (r < Cf::XU + Cf::BU) dst = Bs + t * BST + (r - Cf::XU) * Cf::EPU;
+                else dst = Cs + t * BST + (r - Cf::XU - Cf::BU) * Cf::EPU;
+                *reinterpret_cast<uint4*>(dst) = t < valid ? pre[u] : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        if (wave == 0) {
+            // dt and the cumulative log-decay over the chunk (inclusive prefix sum across lanes)
+            const float dtv = lane < valid ? dt_of(to_f32(pre_dt), bias_h, k.dt_min, k.dt_max) : 0.0f;
+            float lam = dtv * A_h;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(lam, off, 64);
+                if (lane >= off) lam += o;
+            }
+            const float lam_end = __shfl(lam, Q - 1, 64);
+            if (lane < Q) {
+                sLam[lane] = lam;
+                sDt[lane] = dtv;
+                sW[lane] = fast_exp(lam_end - lam) * dtv;
+                sExpL[lane] = fast_exp(lam);
+            }
+            if (lane == 0) sEnd = lam_end;
+        }
+    };
+
+    float lam_seg = 0.0f;  // summed log-decay of the segment (state-only pass)
+    if (c_begin < c_end) prefetch(c_begin);
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        commit(c);
+        __syncthreads();  // tiles and chunk statistics in LDS
+        if (c + 1 < c_end) prefetch(c + 1);
+        const int64_t t0 = c * Q;
+        const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+        const float lam_end = sEnd;
+        lam_seg += lam_end;
+
+        // X fragments (k = token s, column p): A operand of the intra part, B operand of the update
+        Frag<T> xf[Cf::PBW][Cf::KS_Q];
+#pragma unroll
+        for (int pb = 0; pb < Cf::PBW; ++pb)
+#pragma unroll
+            for (int ks = 0; ks < Cf::KS_Q; ++ks)
+                xf[pb][ks] = frag_col<T>(Xs, XST, 32 * ks, Q, (wave * Cf::PBW + pb) * 16, q, li);
+
+        f32x4 accY[Cf::PBW][Cf::NTB];
+        if constexpr (!kStateOnly) {
+            // ---- G^T tiles (s-block sb <= t-block tb), masked and scaled into M[t][s]
+            int tile = 0;
+#pragma unroll
+            for (int tb = 0; tb < Cf::NTB; ++tb) {
+#pragma unroll
+                for (int sb = 0; sb <= tb; ++sb, ++tile) {
+                    if (tile % Cf::NW != wave) continue;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < Cf::KS_N; ++ks) {
+                        const Frag<T> fa = frag_row<T>(Bs, BST, sb * 16 + li, 32 * ks, N, q);
+                        const Frag<T> fb = frag_row<T>(Cs, BST, tb * 16 + li, 32 * ks, N, q);
+                        mfma(acc, fa, fb);
+                    }
+                    const int t = tb * 16 + li;
+                    const int s0 = sb * 16 + 4 * q;
+                    const float lt = sLam[t];
+                    const float4 ls = *reinterpret_cast<const float4*>(sLam + s0);
+                    const float4 ds = *reinterpret_cast<const float4*>(sDt + s0);
+                    const float m0 = s0 + 0 <= t ? acc[0] * fast_exp(lt - ls.x) * ds.x : 0.0f;
+                    const float m1 = s0 + 1 <= t ? acc[1] * fast_exp(lt - ls.y) * ds.y : 0.0f;
+                    const float m2 = s0 + 2 <= t ? acc[2] * fast_exp(lt - ls.z) * ds.z : 0.0f;
+                    const float m3 = s0 + 3 <= t ? acc[3] * fast_exp(lt - ls.w) * ds.w : 0.0f;
+                    if constexpr (kSplitM) {
+                        const float h0 = bits_to_f32(f32_to_bits(m0)), h1 = bits_to_f32(f32_to_bits(m1));
+                        const float h2 = bits_to_f32(f32_to_bits(m2)), h3 = bits_to_f32(f32_to_bits(m3));
+                        put4(Ms + t * MST + s0, h0, h1, h2, h3);
+                        put4(Ml + t * MST + s0, m0 - h0, m1 - h1, m2 - h2, m3 - h3);
+                    } else {
+                        put4(Ms + t * MST + s0, m0, m1, m2, m3);
+                    }
+                }
+            }
+            // tiles above the diagonal that a K=32 step still covers are zero
+#pragma unroll
+            for (int tb = 0; tb + 1 < Cf::NTB; tb += 2) {
+                if ((tb / 2) % Cf::NW == wave) {
+                    put4(Ms + (tb * 16 + li) * MST + (tb + 1) * 16 + 4 * q, 0.f, 0.f, 0.f, 0.f);
+                    if constexpr (kSplitM) put4(Ml + (tb * 16 + li) * MST + (tb + 1) * 16 + 4 * q, 0.f, 0.f, 0.f, 0.f);
+                }
+            }
+
+            // ---- state part: Y^T[p][t] = sum_n S[p][n] * (e^Lam_t C[t][n])
+#pragma unroll
+            for (int pb = 0; pb < Cf::PBW; ++pb)
+#pragma unroll
+                for (int tb = 0; tb < Cf::NTB; ++tb) accY[pb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < Cf::KS_N; ++ks) {
+                Frag<T> sa[Cf::PBW];
+#pragma unroll
+                for (int pb = 0; pb < Cf::PBW; ++pb) {
+                    const f32x4 s0v = accS[pb][2 * ks];
+                    sa[pb].set(0, s0v[0], s0v[1], s0v[2], s0v[3]);
+                    if (2 * ks + 1 < Cf::NNB) {
+                        const f32x4 s1v = accS[pb][2 * ks + 1];
+                        sa[pb].set(1, s1v[0], s1v[1], s1v[2], s1v[3]);
+                    } else {
+                        sa[pb].set(1, 0.f, 0.f, 0.f, 0.f);
+                    }
+                }
+#pragma unroll
+                for (int tb = 0; tb < Cf::NTB; ++tb) {
+                    const int t = tb * 16 + li;
+                    Frag<T> cf = frag_row<T>(Cs, BST, t, 32 * ks, N, q);
+                    const float el = sExpL[t];
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+                        cf.set(cc, cf.get(cc, 0) * el, cf.get(cc, 1) * el, cf.get(cc, 2) * el, cf.get(cc, 3) * el);
+#pragma unroll
+                    for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accY[pb][tb], sa[pb], cf);
+                }
+            }
+        }
+        __syncthreads();  // M complete
+
+        if constexpr (!kStateOnly) {
+            // ---- intra-chunk part: Y^T[p][t] += sum_s X[s][p] M[t][s]
+#pragma unroll
+            for (int tb = 0; tb < Cf::NTB; ++tb) {
+#pragma unroll
+                for (int ks = 0; ks < Cf::KS_Q; ++ks) {
+                    if (32 * ks > tb * 16 + 15) continue;
+                    const Frag<T> mf = frag_row<T>(Ms, MST, tb * 16 + li, 32 * ks, Q, q);
+#pragma unroll
+                    for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accY[pb][tb], xf[pb][ks], mf);
+                    if constexpr (kSplitM) {
+                        const Frag<T> ml = frag_row<T>(Ml, MST, tb * 16 + li, 32 * ks, Q, q);
+#pragma unroll
+                        for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accY[pb][tb], xf[pb][ks], ml);
+                    }
+                }
+            }
+            // ---- D skip and store: the lane holds y[t = tb*16+li][p = pblk*16+4q .. +3]
+            T* yb = reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P;
+#pragma unroll
+            for (int tb = 0; tb < Cf::NTB; ++tb) {
+                const int t = tb * 16 + li;
+                if (t < valid) {
+#pragma unroll
+                    for (int pb = 0; pb < Cf::PBW; ++pb) {
+                        const int p0 = (wave * Cf::PBW + pb) * 16 + 4 * q;
+                        float xv[4];
+                        row4(Xs + t * XST + p0, xv);
+                        const f32x4 a = accY[pb][tb];
+                        put4g(yb + (t0 + t) * k.ys + p0, a[0] + D_h * xv[0], a[1] + D_h * xv[1],
+                              a[2] + D_h * xv[2], a[3] + D_h * xv[3]);
+                    }
+                }
+            }
+        }
+
+        // ---- state update: S^T[n][p] = e^Lam_end S^T[n][p] + sum_s (w_s B[s][n]) X[s][p]
+        const float decay = fast_exp(lam_end);
+#pragma unroll
+        for (int pb = 0; pb < Cf::PBW; ++pb)
+#pragma unroll
+            for (int nb = 0; nb < Cf::NNB; ++nb) accS[pb][nb] *= decay;
+#pragma unroll
+        for (int nb = 0; nb < Cf::NNB; ++nb) {
+#pragma unroll
+            for (int ks = 0; ks < Cf::KS_Q; ++ks) {
+                Frag<T> bw = frag_col<T>(Bs, BST, 32 * ks, Q, nb * 16, q, li);
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int s0 = 32 * ks + 16 * cc + 4 * q;
+                    if (s0 < Q) {
+                        const float4 wv = *reinterpret_cast<const float4*>(sW + s0);
+                        bw.set(cc, bw.get(cc, 0) * wv.x, bw.get(cc, 1) * wv.y, bw.get(cc, 2) * wv.z,
+                               bw.get(cc, 3) * wv.w);
+                    }
+                }
+#pragma unroll
+                for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accS[pb][nb], bw, xf[pb][ks]);
+            }
+        }
+        __syncthreads();  // LDS tiles free for the next chunk
+    }
+
+    // ---- write the state: S[p][n..n+3] per lane
+    float* dst = nullptr;
+    if (kStateOnly) dst = k.ws_state + ((int64_t)seg * BH + bh) * P * N;
+    else if (seg == k.nseg - 1) dst = k.state_out ? k.state_out + (int64_t)bh * P * N : nullptr;
+    if (dst) {
+#pragma unroll
+        for (int pb = 0; pb < Cf::PBW; ++pb) {
+            const int p = (wave * Cf::PBW + pb) * 16 + li;
+#pragma unroll
+            for (int nb = 0; nb < Cf::NNB; ++nb) {
+                const f32x4 v = accS[pb][nb];
+                *reinterpret_cast<float4*>(dst + (int64_t)p * N + nb * 16 + 4 * q) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+    if (kStateOnly && tid == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+}
+
+// Chain the segments: S_in[seg+1] = exp(lam[seg]) * S_in[seg] + S_end_local[seg], written over
+// S_end_local[seg] (so that segment seg+1 finds its initial state at index seg).
+__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(const float* __restrict__ state_in,
+                                                                float* __restrict__ ws_state,
+                                                                const float* __restrict__ ws_lam, int BH, int nseg,
+                                                                int PN)
+{
+    const int bh = blockIdx.y;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= PN) return;
+    float s = state_in ? state_in[(int64_t)bh * PN + i] : 0.0f;
+    for (int seg = 0; seg + 1 < nseg; ++seg) {
+        float* slot = ws_state + ((int64_t)seg * BH + bh) * PN + i;
+        s = fast_exp(ws_lam[(int64_t)seg * BH + bh]) * s + *slot;
+        *slot = s;
     }
 }
 
-bool ssd_scan_supported(int P, int N, int Q, bool) {
-    (void)Q;
-    if (!(N == 16 || N == 32 || N == 64 || N == 128)) return false;
-    if (P + 2 * N > 512) return false;
-    return (int64_t)P * (N / 4) <= 8 * kScanThreads;
+// ----------------------------------------------------------------------------------------------
+// host side
+
+struct Plan {
+    int nseg, cps;
+    size_t ws_bytes;
+};
+
+static Plan plan_for(int64_t batch, int64_t L, int H, int P, int N, int Q) {
+    Plan pl;
+    const int64_t nchunks = (L + Q - 1) / Q;
+    const int64_t units = batch * H;
+    // enough workgroups for about two per compute unit on 256 CUs
+    const int64_t target = 512;
+    int64_t nseg = units > 0 ? (target + units - 1) / units : 1;
+    if (nseg > nchunks) nseg = nchunks;
+    if (nseg < 1) nseg = 1;
+    const int64_t cps = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 1;
+    nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
+    pl.nseg = (int)nseg;
+    pl.cps = (int)cps;
+    pl.ws_bytes = nseg > 1 ? (size_t)(nseg * units) * ((size_t)P * N + 1) * sizeof(float) + 256 : 0;
+    return pl;
 }
 
-int ssd_scan_default_chunk(int, int, bool) { return 64; }
+template <typename T, int Q, int P, int N>
+static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
+    const Plan pl = plan_for(a.batch, a.L, a.H, a.P, a.N, Q);
+    ScanK k;
+    k.x = a.x; k.B = a.B; k.C = a.C; k.dt = a.dt;
+    k.xs = a.xs; k.bcs = a.bcs; k.dts = a.dts; k.ys = a.ys;
+    k.dt_bias = a.dt_bias; k.A = a.A; k.D = a.D; k.dt_min = a.dt_min; k.dt_max = a.dt_max;
+    k.state_in = a.state_in; k.state_out = a.state_out; k.y = a.y;
+    k.L = a.L; k.batch = (int)a.batch; k.H = a.H; k.G = a.G;
+    k.nseg = pl.nseg; k.cps = pl.cps;
+    const int BH = (int)(a.batch * a.H);
+    k.ws_state = nullptr;
+    k.ws_lam = nullptr;
+    if (pl.nseg > 1) {
+        k.ws_state = reinterpret_cast<float*>(a.ws);
+        k.ws_lam = k.ws_state + (size_t)pl.nseg * BH * P * N;
+    }
+    constexpr int THREADS = Cfg<T, Q, P, N>::THREADS;
+    hipError_t e;
+    if (pl.nseg > 1) {
+        k.nblocks = (pl.nseg - 1) * BH;
+        e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, true>, dim3(k.nblocks), dim3(THREADS), 0, s, k);
+        if (e != hipSuccess) return e;
+        dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH);
+        e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, a.state_in, k.ws_state,
+                          (const float*)k.ws_lam, BH, pl.nseg, P * N);
+        if (e != hipSuccess) return e;
+    }
+    k.nblocks = pl.nseg * BH;
+    return launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(THREADS), 0, s, k);
+}
 
-size_t ssd_scan_workspace_bytes(int64_t, int64_t, int, int, int, int, int, bool) { return 0; }
+template <typename T, int Q>
+static hipError_t dispatch_pn(const ScanArgs& a, hipStream_t s) {
+#define M2_PN(PP, NN) if (a.P == PP && a.N == NN) return run_scan<T, Q, PP, NN>(a, s);
+    M2_PN(16, 16) M2_PN(16, 32) M2_PN(16, 64) M2_PN(32, 16) M2_PN(32, 32) M2_PN(32, 64)
+    M2_PN(64, 16) M2_PN(64, 32) M2_PN(64, 64) M2_PN(64, 128)
+    if constexpr (sizeof(T) == 2) {
+        M2_PN(128, 64) M2_PN(128, 128)
+    }
+#undef M2_PN
+    return hipErrorInvalidValue;
+}
+
+bool ssd_scan_supported(int P, int N, int Q, bool bf16) {
+    if (!(Q == 16 || Q == 32 || Q == 64)) return false;
+    if (!bf16 && Q == 64) return false;  // fp32 tiles are kept to 32 tokens (LDS budget)
+    const bool small = (P == 16 || P == 32 || P == 64) && (N == 16 || N == 32 || N == 64 || (N == 128 && P == 64));
+    const bool large = bf16 && P == 128 && (N == 64 || N == 128);
+    return small || large;
+}
+
+int ssd_scan_default_chunk(int, int, bool bf16) { return bf16 ? 64 : 32; }
+
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int, int Q, bool) {
+    return plan_for(batch, L, H, P, N, Q).ws_bytes;
+}
 
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s) {
-    return a.bf16 ? launch_scan_t<bf16_t>(a, s) : launch_scan_t<float>(a, s);
+    if (a.bf16) {
+        switch (a.Q) {
+            case 16: return dispatch_pn<bf16_t, 16>(a, s);
+            case 32: return dispatch_pn<bf16_t, 32>(a, s);
+            default: return dispatch_pn<bf16_t, 64>(a, s);
+        }
+    }
+    switch (a.Q) {
+        case 16: return dispatch_pn<float, 16>(a, s);
+        default: return dispatch_pn<float, 32>(a, s);
+    }
 }
 
 }  // namespace m2
