@@ -35,8 +35,31 @@ __device__ __forceinline__ float fast_exp(float v) { return __builtin_amdgcn_exp
 // SiLU(v) = v / (1 + e^-v)
 __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + fast_exp(-v)); }
 
-// softplus(v) = log(1 + e^v); above 20 it equals v to within 2e-9 relative
-__device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+// softplus(v) = log(1 + e^v) from the hardware base-2 exp and log, with x = e^v:
+//   v > 20        -> v                          (the remainder is below 2e-9 relative)
+//   x < 1/64      -> x (1 - x/2 + x^2/3)        (log1p series; relative error below x^3/4 < 1e-6)
+//   otherwise     -> ln2 * log2(1 + x)          (1+x >= 1+1/64: rounding costs < 4e-6 relative)
+__device__ __forceinline__ float softplus(float v) {
+    const float x = fast_exp(v);
+    const float series = x * (1.0f - x * (0.5f - x * (1.0f / 3.0f)));
+    const float direct = 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + x);
+    return v > 20.0f ? v : (x < 0.015625f ? series : direct);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: DPP shifts inside each 16-lane row, then
+// the row totals are read back as scalars and added to the later rows.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    float x = v;
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+    const int row = (int)(threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? r0 : 0.0f) + (row >= 2 ? r1 : 0.0f) + (row >= 3 ? r2 : 0.0f);
+}
 
 // dt = softplus(raw + bias) clamped to [dt_min, dt_max] (NaN passes through)
 __device__ __forceinline__ float dt_of(float raw, float bias, float dt_min, float dt_max) {

@@ -20,7 +20,10 @@
 //                                                   (bf16: as a hi + lo pair, see below)
 //   Y^T[p][t] = sum_n S[p][n] (e^Lam_t C[t][n])   (state part, state as the A operand)
 //   Y^T[p][t]+= sum_s X[s][p] M[t][s]             (intra-chunk part)
-//   S^T[n][p] = e^Lam_end S^T[n][p] + sum_s (w_s B[s][n]) X[s][p],  w_s = e^(Lam_end-Lam_s) dt_s
+//   S^T[n][p] = e^Lam_end S^T[n][p] + sum_s B[s][n] (w_s X[s][p]),  w_s = e^(Lam_end-Lam_s) dt_s
+// The e^Lam_t factor of the state part is applied to the output tile, w_s scales the X fragments
+// already in registers, and the D skip is folded into M's diagonal, so the per-element work
+// outside the MFMAs is one pass over M.
 // Wave w owns p-block(s) w of the state and of the output, so the state never leaves
 // its registers; only M (the same for every p-block) goes through LDS.  Operands whose
 // contraction index runs down the rows of a row-major LDS tile (X and B over tokens) are
@@ -44,6 +47,7 @@ namespace m2 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // native vector: stays in registers
 
 // ----------------------------------------------------------------------------------------------
 // element types
@@ -203,24 +207,41 @@ struct Cfg {
     static constexpr int XU = P / EPU, BU = N / EPU;
     static constexpr int KS_N = (N + 31) / 32;     // K=32 steps over d_state
     static constexpr int KS_Q = (Q + 31) / 32;     // K=32 steps over tokens
+    // s-blocks that t-block tb's K=32 steps over tokens read: sb < 2*(tb/2)+2 (and < NTB)
+    static constexpr int tiles_in_row(int tb) { return 2 * (tb / 2) + 2 < NTB ? 2 * (tb / 2) + 2 : NTB; }
+    static constexpr int count_tiles() {
+        int n = 0;
+        for (int tb = 0; tb < NTB; ++tb) n += tiles_in_row(tb);
+        return n;
+    }
+    static constexpr int NTILES = count_tiles();
 };
 
 // ----------------------------------------------------------------------------------------------
 // chunk walk.  kStateOnly: segment end state from a zero start (no C, no output).
 
+// Loads of one [Q x width] tile in 16-byte units: U units per row, RPP rows per pass, NP passes.
+template <int U, int THREADS, int Q>
+struct TilePlan {
+    static constexpr int RPP = THREADS / U;
+    static constexpr int NP = (Q + RPP - 1) / RPP;
+    static constexpr bool kGuard = (Q % RPP) != 0;  // some passes run past the last row
+};
+
 template <typename T, int Q, int P, int N, bool kStateOnly>
-__global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k)
+__global__ __launch_bounds__(scan_threads(P)) __attribute__((amdgpu_waves_per_eu(3)))
+void ssd_chunk_scan_kernel(ScanK k)
 {
     using Cf = Cfg<T, Q, P, N>;
     using E = typename Cf::E;
-    constexpr int THREADS = Cf::THREADS, XST = Cf::XST, BST = Cf::BST, MST = Cf::MST;
-    constexpr int RU = Cf::XU + Cf::BU * (kStateOnly ? 1 : 2);  // 16-byte units per token
-    constexpr int UPT = (Q * RU + THREADS - 1) / THREADS;         // units per thread per chunk
+    constexpr int THREADS = Cf::THREADS, XST = Cf::XST, BST = Cf::BST, MST = Cf::MST, EPU = Cf::EPU;
+    using PX = TilePlan<Cf::XU, THREADS, Q>;
+    using PB = TilePlan<Cf::BU, THREADS, Q>;
+    constexpr bool kSplitM = sizeof(E) == 2;  // bf16 tiles: M as hi + lo
 
     __shared__ __attribute__((aligned(16))) E Xs[Q * XST];
     __shared__ __attribute__((aligned(16))) E Bs[Q * BST];
     __shared__ __attribute__((aligned(16))) E Cs[kStateOnly ? 8 : Q * BST];
-    constexpr bool kSplitM = sizeof(E) == 2;  // bf16 tiles: M as hi + lo
     __shared__ __attribute__((aligned(16))) E Ms[kStateOnly ? 8 : Q * MST];
     __shared__ __attribute__((aligned(16))) E Ml[kStateOnly || !kSplitM ? 8 : Q * MST];
     __shared__ __attribute__((aligned(16))) float sLam[Q];
@@ -230,7 +251,7 @@ __global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k
     __shared__ float sEnd;
 
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, li = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so tile ownership is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile ownership is a scalar branch
     const int unit = logical_block(k.nblocks);
     const int BH = k.batch * k.H;
     const int seg = unit / BH;
@@ -241,13 +262,16 @@ __global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k
     const int64_t nchunks = (k.L + Q - 1) / Q;
     const int64_t c_begin = (int64_t)seg * k.cps;
     const int64_t c_end = c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks;
-
-    const T* xg = reinterpret_cast<const T*>(k.x) + b * k.L * k.xs + (int64_t)h * P;
-    const T* bg = reinterpret_cast<const T*>(k.B) + b * k.L * k.bcs + (int64_t)g * N;
-    const T* cg = reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N;
-    const T* dtg = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
     const float bias_h = k.dt_bias[h], A_h = k.A[h];
     const float D_h = k.D ? k.D[h] : 0.0f;
+
+    // per-thread tile coordinates and global base pointers (row r0 of the sequence, unit column)
+    const int xr0 = tid / Cf::XU, xc = (tid % Cf::XU) * EPU;
+    const int br0 = tid / Cf::BU, bc = (tid % Cf::BU) * EPU;
+    const T* xg = reinterpret_cast<const T*>(k.x) + b * k.L * k.xs + (int64_t)h * P + xc;
+    const T* bgp = reinterpret_cast<const T*>(k.B) + b * k.L * k.bcs + (int64_t)g * N + bc;
+    const T* cgp = reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N + bc;
+    const T* dtg = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
 
     // state tiles in accumulator layout: accS[pb][nb][j] = S[p = pblk*16 + li][n = nb*16 + 4q + j]
     f32x4 accS[Cf::PBW][Cf::NNB];
@@ -272,54 +296,64 @@ __global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k
         }
     }
 
-    // Register prefetch of one chunk: UPT 16-byte units per thread (+ raw dt, one token per lane of
-    // wave 0).  Loads are issued without branches (indices clamped into the chunk) and stay raw
-    // until commit(), so nothing waits on them before the next chunk starts; commit() zeroes the
-    // tokens past the end of the sequence.
-    uint4 pre[UPT];
+    // Register prefetch of one chunk (+ raw dt, one token per lane of wave 0).  Both helpers are
+    // forced inline: a prefetch array left in scratch memory would make every load synchronous.  Loads are issued
+    // without divergent branches (rows clamped into the sequence on the last, partial chunk) and
+    // stay raw until commit(), so nothing waits on them until the next chunk starts; commit()
+    // zeroes the rows past the end of the sequence.
+    u32x4_t px[PX::NP], pbv[PB::NP], pcv[kStateOnly ? 1 : PB::NP];
     T pre_dt;
-    auto prefetch = [&](int64_t c) {
+    auto prefetch = [&](int64_t c) __attribute__((always_inline)) {
         const int64_t t0 = c * Q;
         const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+        const bool full = valid == Q;
 #pragma unroll
-        for (int u = 0; u < UPT; ++u) {
-            int idx = tid + u * THREADS;
-            if (Q * RU % THREADS != 0) idx = idx < Q * RU ? idx : Q * RU - 1;
-            int t = idx / RU;
-            const int r = idx % RU;
-            t = t < valid ? t : valid - 1;
-            const T* src;
-            if (r < Cf::XU) src = xg + (t0 + t) * k.xs + r * Cf::EPU;
-            else if (r < Cf::XU + Cf::BU) src = bg + (t0 + t) * k.bcs + (r - Cf::XU) * Cf::EPU;
-            else src = cg + (t0 + t) * k.bcs + (r - Cf::XU - Cf::BU) * Cf::EPU;
-            pre[u] = *reinterpret_cast<const uint4*>(src);
+        for (int i = 0; i < PX::NP; ++i) {
+            int r = xr0 + i * PX::RPP;
+            if (PX::kGuard && r >= Q) r = Q - 1;
+            if (!full) r = r < valid ? r : valid - 1;
+            px[i] = *reinterpret_cast<const u32x4_t*>(xg + (t0 + r) * k.xs);
+        }
+#pragma unroll
+        for (int i = 0; i < PB::NP; ++i) {
+            int r = br0 + i * PB::RPP;
+            if (PB::kGuard && r >= Q) r = Q - 1;
+            if (!full) r = r < valid ? r : valid - 1;
+            pbv[i] = *reinterpret_cast<const u32x4_t*>(bgp + (t0 + r) * k.bcs);
+            if constexpr (!kStateOnly) pcv[i] = *reinterpret_cast<const u32x4_t*>(cgp + (t0 + r) * k.bcs);
         }
         if (wave == 0) pre_dt = dtg[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
     };
-    auto commit = [&](int64_t c) {
+    auto commit = [&](int64_t c) __attribute__((always_inline)) {
         const int valid = (int)(k.L - c * Q < Q ? k.L - c * Q : Q);
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        if (valid < Q) {  // the last chunk of the sequence: zero the rows past its end
 #pragma unroll
-        for (int u = 0; u < UPT; ++u) {
-            const int idx = tid + u * THREADS;
-            const int t = idx / RU, r = idx % RU;
-            if (idx < Q * RU) {
-                E* dst;
-                if (r < Cf::XU) dst = Xs + t * XST + r * Cf::EPU;
-                else if (r < Cf::XU + Cf::BU) dst = Bs + t * BST + (r - Cf::XU) * Cf::EPU;
-                else dst = Cs + t * BST + (r - Cf::XU - Cf::BU) * Cf::EPU;
-                *reinterpret_cast<uint4*>(dst) = t < valid ? pre[u] : make_uint4(0u, 0u, 0u, 0u);
+            for (int i = 0; i < PX::NP; ++i) px[i] = xr0 + i * PX::RPP < valid ? px[i] : zero;
+#pragma unroll
+            for (int i = 0; i < PB::NP; ++i) {
+                pbv[i] = br0 + i * PB::RPP < valid ? pbv[i] : zero;
+                if constexpr (!kStateOnly) pcv[i] = br0 + i * PB::RPP < valid ? pcv[i] : zero;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PX::NP; ++i) {
+            const int r = xr0 + i * PX::RPP;
+            if (!PX::kGuard || r < Q) *reinterpret_cast<u32x4_t*>(Xs + r * XST + xc) = px[i];
+        }
+#pragma unroll
+        for (int i = 0; i < PB::NP; ++i) {
+            const int r = br0 + i * PB::RPP;
+            if (!PB::kGuard || r < Q) {
+                *reinterpret_cast<u32x4_t*>(Bs + r * BST + bc) = pbv[i];
+                if constexpr (!kStateOnly) *reinterpret_cast<u32x4_t*>(Cs + r * BST + bc) = pcv[i];
             }
         }
         if (wave == 0) {
             // dt and the cumulative log-decay over the chunk (inclusive prefix sum across lanes)
             const float dtv = lane < valid ? dt_of(to_f32(pre_dt), bias_h, k.dt_min, k.dt_max) : 0.0f;
-            float lam = dtv * A_h;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(lam, off, 64);
-                if (lane >= off) lam += o;
-            }
-            const float lam_end = __shfl(lam, Q - 1, 64);
+            const float lam = wave_prefix_sum(dtv * A_h);
+            const float lam_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), Q - 1));
             if (lane < Q) {
                 sLam[lane] = lam;
                 sDt[lane] = dtv;
@@ -351,49 +385,57 @@ __global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k
 
         f32x4 accY[Cf::PBW][Cf::NTB];
         if constexpr (!kStateOnly) {
-            // ---- G^T tiles (s-block sb <= t-block tb), masked and scaled into M[t][s]
-            int tile = 0;
+            // ---- G^T tiles, masked and scaled into M[t][s], with D on the diagonal.  The tiles a
+            // t-block's K=32 steps read are sb < 2*(tb/2)+2; those above the diagonal come out zero from
+            // the mask.  Every wave takes the same number of tiles (the last one repeated), so the
+            // loop has no branches and the compiler can overlap the tiles' LDS reads and MFMAs.
+            constexpr int NT = Cf::NTILES;
+            constexpr int TPW = (NT + Cf::NW - 1) / Cf::NW;
 #pragma unroll
-            for (int tb = 0; tb < Cf::NTB; ++tb) {
+            for (int i = 0; i < TPW; ++i) {
+                int id = wave + Cf::NW * i;
+                id = id < NT ? id : NT - 1;
+                int tb = 0, base = 0;
 #pragma unroll
-                for (int sb = 0; sb <= tb; ++sb, ++tile) {
-                    if (tile % Cf::NW != wave) continue;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < Cf::KS_N; ++ks) {
-                        const Frag<T> fa = frag_row<T>(Bs, BST, sb * 16 + li, 32 * ks, N, q);
-                        const Frag<T> fb = frag_row<T>(Cs, BST, tb * 16 + li, 32 * ks, N, q);
-                        mfma(acc, fa, fb);
-                    }
-                    const int t = tb * 16 + li;
-                    const int s0 = sb * 16 + 4 * q;
-                    const float lt = sLam[t];
-                    const float4 ls = *reinterpret_cast<const float4*>(sLam + s0);
-                    const float4 ds = *reinterpret_cast<const float4*>(sDt + s0);
-                    const float m0 = s0 + 0 <= t ? acc[0] * fast_exp(lt - ls.x) * ds.x : 0.0f;
-                    const float m1 = s0 + 1 <= t ? acc[1] * fast_exp(lt - ls.y) * ds.y : 0.0f;
-                    const float m2 = s0 + 2 <= t ? acc[2] * fast_exp(lt - ls.z) * ds.z : 0.0f;
-                    const float m3 = s0 + 3 <= t ? acc[3] * fast_exp(lt - ls.w) * ds.w : 0.0f;
-                    if constexpr (kSplitM) {
-                        const float h0 = bits_to_f32(f32_to_bits(m0)), h1 = bits_to_f32(f32_to_bits(m1));
-                        const float h2 = bits_to_f32(f32_to_bits(m2)), h3 = bits_to_f32(f32_to_bits(m3));
-                        put4(Ms + t * MST + s0, h0, h1, h2, h3);
-                        put4(Ml + t * MST + s0, m0 - h0, m1 - h1, m2 - h2, m3 - h3);
-                    } else {
-                        put4(Ms + t * MST + s0, m0, m1, m2, m3);
-                    }
+                for (int tt = 0; tt < Cf::NTB; ++tt) {
+                    const int cnt = Cf::tiles_in_row(tt);
+                    if (id >= base + cnt) { tb = tt + 1; base += cnt; }
                 }
-            }
-            // tiles above the diagonal that a K=32 step still covers are zero
+                const int sb = id - base;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tb = 0; tb + 1 < Cf::NTB; tb += 2) {
-                if ((tb / 2) % Cf::NW == wave) {
-                    put4(Ms + (tb * 16 + li) * MST + (tb + 1) * 16 + 4 * q, 0.f, 0.f, 0.f, 0.f);
-                    if constexpr (kSplitM) put4(Ml + (tb * 16 + li) * MST + (tb + 1) * 16 + 4 * q, 0.f, 0.f, 0.f, 0.f);
+                for (int ks = 0; ks < Cf::KS_N; ++ks) {
+                    const Frag<T> fa = frag_row<T>(Bs, BST, sb * 16 + li, 32 * ks, N, q);
+                    const Frag<T> fb = frag_row<T>(Cs, BST, tb * 16 + li, 32 * ks, N, q);
+                    mfma(acc, fa, fb);
+                }
+                const int t = tb * 16 + li;
+                const int s0 = sb * 16 + 4 * q;
+                const float lt = sLam[t];
+                const float4 ls = *reinterpret_cast<const float4*>(sLam + s0);
+                const float4 ds = *reinterpret_cast<const float4*>(sDt + s0);
+                const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+                float m[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v = acc[j] * fast_exp(lt - lsv[j]) * dsv[j];
+                    m[j] = (s0 + j <= t ? v : 0.0f) + (s0 + j == t ? D_h : 0.0f);
+                }
+                if constexpr (kSplitM) {
+                    float hi[4], lo[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        hi[j] = bits_to_f32(f32_to_bits(m[j]));
+                        lo[j] = m[j] - hi[j];
+                    }
+                    put4(Ms + t * MST + s0, hi[0], hi[1], hi[2], hi[3]);
+                    put4(Ml + t * MST + s0, lo[0], lo[1], lo[2], lo[3]);
+                } else {
+                    put4(Ms + t * MST + s0, m[0], m[1], m[2], m[3]);
                 }
             }
 
-            // ---- state part: Y^T[p][t] = sum_n S[p][n] * (e^Lam_t C[t][n])
+            // ---- state part: Y^T[p][t] = e^Lam_t * sum_n S[p][n] C[t][n]
 #pragma unroll
             for (int pb = 0; pb < Cf::PBW; ++pb)
 #pragma unroll
@@ -414,21 +456,22 @@ __global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k
                 }
 #pragma unroll
                 for (int tb = 0; tb < Cf::NTB; ++tb) {
-                    const int t = tb * 16 + li;
-                    Frag<T> cf = frag_row<T>(Cs, BST, t, 32 * ks, N, q);
-                    const float el = sExpL[t];
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc)
-                        cf.set(cc, cf.get(cc, 0) * el, cf.get(cc, 1) * el, cf.get(cc, 2) * el, cf.get(cc, 3) * el);
+                    const Frag<T> cf = frag_row<T>(Cs, BST, tb * 16 + li, 32 * ks, N, q);
 #pragma unroll
                     for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accY[pb][tb], sa[pb], cf);
                 }
+            }
+#pragma unroll
+            for (int tb = 0; tb < Cf::NTB; ++tb) {
+                const float el = sExpL[tb * 16 + li];
+#pragma unroll
+                for (int pb = 0; pb < Cf::PBW; ++pb) accY[pb][tb] *= el;
             }
         }
         __syncthreads();  // M complete
 
         if constexpr (!kStateOnly) {
-            // ---- intra-chunk part: Y^T[p][t] += sum_s X[s][p] M[t][s]
+            // ---- intra-chunk part (with the D skip on M's diagonal): Y^T[p][t] += sum_s X[s][p] M[t][s]
 #pragma unroll
             for (int tb = 0; tb < Cf::NTB; ++tb) {
 #pragma unroll
@@ -444,26 +487,37 @@ __global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k
                     }
                 }
             }
-            // ---- D skip and store: the lane holds y[t = tb*16+li][p = pblk*16+4q .. +3]
-            T* yb = reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P;
+            // ---- store: the lane holds y[t = tb*16+li][p = pblk*16+4q .. +3]
+            T* yb = reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P + t0 * k.ys;
 #pragma unroll
             for (int tb = 0; tb < Cf::NTB; ++tb) {
                 const int t = tb * 16 + li;
                 if (t < valid) {
 #pragma unroll
                     for (int pb = 0; pb < Cf::PBW; ++pb) {
-                        const int p0 = (wave * Cf::PBW + pb) * 16 + 4 * q;
-                        float xv[4];
-                        row4(Xs + t * XST + p0, xv);
                         const f32x4 a = accY[pb][tb];
-                        put4g(yb + (t0 + t) * k.ys + p0, a[0] + D_h * xv[0], a[1] + D_h * xv[1],
-                              a[2] + D_h * xv[2], a[3] + D_h * xv[3]);
+                        put4g(yb + t * k.ys + (wave * Cf::PBW + pb) * 16 + 4 * q, a[0], a[1], a[2], a[3]);
                     }
                 }
             }
         }
 
-        // ---- state update: S^T[n][p] = e^Lam_end S^T[n][p] + sum_s (w_s B[s][n]) X[s][p]
+        // ---- state update: S^T[n][p] = e^Lam_end S^T[n][p] + sum_s B[s][n] (w_s X[s][p])
+        Frag<T> xw[Cf::PBW][Cf::KS_Q];
+#pragma unroll
+        for (int ks = 0; ks < Cf::KS_Q; ++ks) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int s0 = 32 * ks + 16 * cc + 4 * q;
+                const float4 wv = s0 < Q ? *reinterpret_cast<const float4*>(sW + s0) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int pb = 0; pb < Cf::PBW; ++pb) {
+                    if (cc == 0) xw[pb][ks] = xf[pb][ks];
+                    xw[pb][ks].set(cc, xf[pb][ks].get(cc, 0) * wv.x, xf[pb][ks].get(cc, 1) * wv.y,
+                                   xf[pb][ks].get(cc, 2) * wv.z, xf[pb][ks].get(cc, 3) * wv.w);
+                }
+            }
+        }
         const float decay = fast_exp(lam_end);
 #pragma unroll
         for (int pb = 0; pb < Cf::PBW; ++pb)
@@ -473,18 +527,9 @@ __global__ __launch_bounds__(scan_threads(P)) void ssd_chunk_scan_kernel(ScanK k
         for (int nb = 0; nb < Cf::NNB; ++nb) {
 #pragma unroll
             for (int ks = 0; ks < Cf::KS_Q; ++ks) {
-                Frag<T> bw = frag_col<T>(Bs, BST, 32 * ks, Q, nb * 16, q, li);
+                const Frag<T> bf = frag_col<T>(Bs, BST, 32 * ks, Q, nb * 16, q, li);
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int s0 = 32 * ks + 16 * cc + 4 * q;
-                    if (s0 < Q) {
-                        const float4 wv = *reinterpret_cast<const float4*>(sW + s0);
-                        bw.set(cc, bw.get(cc, 0) * wv.x, bw.get(cc, 1) * wv.y, bw.get(cc, 2) * wv.z,
-                               bw.get(cc, 3) * wv.w);
-                    }
-                }
-#pragma unroll
-                for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accS[pb][nb], bw, xf[pb][ks]);
+                for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accS[pb][nb], bf, xw[pb][ks]);
             }
         }
         __syncthreads();  // LDS tiles free for the next chunk
@@ -539,8 +584,8 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int P, int N, int Q) {
     Plan pl;
     const int64_t nchunks = (L + Q - 1) / Q;
     const int64_t units = batch * H;
-    // enough workgroups for about two per compute unit on 256 CUs
-    const int64_t target = 512;
+    // about one round of resident workgroups: three per compute unit on 256 CUs
+    const int64_t target = 768;
     int64_t nseg = units > 0 ? (target + units - 1) / units : 1;
     if (nseg > nchunks) nseg = nchunks;
     if (nseg < 1) nseg = 1;
