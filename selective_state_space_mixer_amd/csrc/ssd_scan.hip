@@ -180,101 +180,124 @@ struct ScanK {
 };
 
 // Block -> logical unit.  Consecutive blocks are dealt round-robin to the 8 XCDs; the remap
-// gives each XCD a contiguous run of logical units (the heads of one sequence and segment),
-// so the B/C rows those heads share are fetched into one L2.
+// gives each XCD a contiguous run of logical units (the head groups of one sequence and
+// segment), so the B/C rows those heads share are fetched into one L2.
 __device__ __forceinline__ int logical_block(int nblocks) {
     const int i = blockIdx.x;
     if (nblocks % 8) return i;
     return (i % 8) * (nblocks / 8) + i / 8;
 }
 
-constexpr int scan_threads(int P) { return 64 * (P / 16 >= 4 ? 4 : P / 16); }
+constexpr int kScanThreads = 256;  // four waves
 
+// Work split: each wave owns PW p-blocks of one head, so its share of the state (PW x NNB
+// accumulator tiles) stays within 64 registers; WPH waves cover a head and the block holds
+// HPW = 4 / WPH heads of one B/C group, which share the B and C tiles and G = B C^T.
 template <typename T, int Q, int P, int N>
 struct Cfg {
     using E = typename Lds<T>::E;
     static constexpr int NPB = P / 16;
-    static constexpr int NW = NPB >= 4 ? 4 : NPB;  // waves
-    static constexpr int PBW = NPB / NW;           // p-blocks per wave
     static constexpr int NNB = N / 16;
     static constexpr int NTB = Q / 16;
-    static constexpr int THREADS = 64 * NW;
-    static_assert(THREADS == scan_threads(P), "thread count");
-    static constexpr int XST = P + Lds<T>::PAD;    // LDS row strides (elements)
+    static constexpr int PW = NPB < (16 / NNB > 0 ? 16 / NNB : 1) ? NPB : (16 / NNB > 0 ? 16 / NNB : 1);
+    static constexpr int WPH = NPB / PW;          // waves per head
+    static constexpr int HPW = 4 / WPH;           // heads per block
+    static_assert(WPH >= 1 && WPH <= 4 && HPW * WPH == 4, "work split");
+    static constexpr int XST = P + Lds<T>::PAD;   // LDS row strides (elements)
     static constexpr int BST = N + Lds<T>::PAD;
-    static constexpr int MST = Q + Lds<T>::PAD;
     static constexpr int EPU = 16 / (int)sizeof(E);  // elements per 16-byte unit
     static constexpr int XU = P / EPU, BU = N / EPU;
-    static constexpr int KS_N = (N + 31) / 32;     // K=32 steps over d_state
-    static constexpr int KS_Q = (Q + 31) / 32;     // K=32 steps over tokens
+    static constexpr int KS_N = (N + 31) / 32;    // K=32 steps over d_state
+    static constexpr int KS_Q = (Q + 31) / 32;    // K=32 steps over tokens
     // s-blocks that t-block tb's K=32 steps over tokens read: sb < 2*(tb/2)+2 (and < NTB)
     static constexpr int tiles_in_row(int tb) { return 2 * (tb / 2) + 2 < NTB ? 2 * (tb / 2) + 2 : NTB; }
-    static constexpr int count_tiles() {
+    static constexpr int row_base(int tb) {
         int n = 0;
-        for (int tb = 0; tb < NTB; ++tb) n += tiles_in_row(tb);
+        for (int r = 0; r < tb; ++r) n += tiles_in_row(r);
         return n;
     }
-    static constexpr int NTILES = count_tiles();
+    static constexpr int NTILES = row_base(NTB);
+};
+
+// Loads of a tile in 16-byte units: U units per row, RPP rows per pass, NP passes over R rows.
+template <int U, int R>
+struct TilePlan {
+    static constexpr int RPP = kScanThreads / U;
+    static constexpr int NP = (R + RPP - 1) / RPP;
+    static constexpr bool kGuard = (R % RPP) != 0;  // some passes run past the last row
 };
 
 // ----------------------------------------------------------------------------------------------
 // chunk walk.  kStateOnly: segment end state from a zero start (no C, no output).
 
-// Loads of one [Q x width] tile in 16-byte units: U units per row, RPP rows per pass, NP passes.
-template <int U, int THREADS, int Q>
-struct TilePlan {
-    static constexpr int RPP = THREADS / U;
-    static constexpr int NP = (Q + RPP - 1) / RPP;
-    static constexpr bool kGuard = (Q % RPP) != 0;  // some passes run past the last row
-};
-
 template <typename T, int Q, int P, int N, bool kStateOnly>
-__global__ __launch_bounds__(scan_threads(P)) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void ssd_chunk_scan_kernel(ScanK k)
 {
     using Cf = Cfg<T, Q, P, N>;
     using E = typename Cf::E;
-    constexpr int THREADS = Cf::THREADS, XST = Cf::XST, BST = Cf::BST, MST = Cf::MST, EPU = Cf::EPU;
-    using PX = TilePlan<Cf::XU, THREADS, Q>;
-    using PB = TilePlan<Cf::BU, THREADS, Q>;
-    constexpr bool kSplitM = sizeof(E) == 2;  // bf16 tiles: M as hi + lo
+    constexpr int XST = Cf::XST, BST = Cf::BST, EPU = Cf::EPU, HPW = Cf::HPW, PW = Cf::PW;
+    using PX = TilePlan<Cf::XU * HPW, Q>;  // the block's heads are adjacent in a token row
+    using PB = TilePlan<Cf::BU, Q>;
+    constexpr bool kSplitM = sizeof(E) == 2;  // bf16 operands: M as hi + lo
 
-    __shared__ __attribute__((aligned(16))) E Xs[Q * XST];
+    __shared__ __attribute__((aligned(16))) E Xs[HPW * Q * XST];
     __shared__ __attribute__((aligned(16))) E Bs[Q * BST];
     __shared__ __attribute__((aligned(16))) E Cs[kStateOnly ? 8 : Q * BST];
-    __shared__ __attribute__((aligned(16))) E Ms[kStateOnly ? 8 : Q * MST];
-    __shared__ __attribute__((aligned(16))) E Ml[kStateOnly || !kSplitM ? 8 : Q * MST];
-    __shared__ __attribute__((aligned(16))) float sLam[Q];
-    __shared__ __attribute__((aligned(16))) float sDt[Q];
-    __shared__ __attribute__((aligned(16))) float sW[Q];
-    __shared__ __attribute__((aligned(16))) float sExpL[Q];
-    __shared__ float sEnd;
+    __shared__ __attribute__((aligned(16))) float Gs[kStateOnly ? 4 : Cf::NTILES * 256];
+    __shared__ __attribute__((aligned(16))) float sLam[HPW * Q];
+    __shared__ __attribute__((aligned(16))) float sDt[HPW * Q];
+    __shared__ __attribute__((aligned(16))) float sW[HPW * Q];
+    __shared__ __attribute__((aligned(16))) float sExpL[HPW * Q];
+    __shared__ float sEnd[HPW];
 
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, li = lane & 15;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile ownership is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hw = wave / Cf::WPH;                  // head slot of this wave
+    const int pblk0 = (wave % Cf::WPH) * PW;        // first p-block of this wave
+    const bool stats_writer = (wave % Cf::WPH) == 0;
+
+    // logical unit -> (segment, sequence, head group)
     const int unit = logical_block(k.nblocks);
+    const int hpg = k.H / k.G;
+    const int upg = (hpg + HPW - 1) / HPW;          // head units per group
+    const int nhu = k.G * upg;
+    const int hu = unit % nhu;
+    const int sb_ = unit / nhu;
+    const int64_t b = sb_ % k.batch;
+    const int seg = sb_ / k.batch;
+    const int g = hu / upg;
+    const int h0 = g * hpg + (hu % upg) * HPW;
+    const int hcount = hpg - (hu % upg) * HPW < HPW ? hpg - (hu % upg) * HPW : HPW;  // heads present
+    const int h = h0 + (hw < hcount ? hw : hcount - 1);  // waves past the last head repeat it (results unused)
+    const bool hvalid = hw < hcount;
+    const int bh = (int)b * k.H + h;
     const int BH = k.batch * k.H;
-    const int seg = unit / BH;
-    const int bh = unit % BH;
-    const int64_t b = bh / k.H;
-    const int h = bh % k.H;
-    const int g = h / (k.H / k.G);
     const int64_t nchunks = (k.L + Q - 1) / Q;
     const int64_t c_begin = (int64_t)seg * k.cps;
     const int64_t c_end = c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks;
     const float bias_h = k.dt_bias[h], A_h = k.A[h];
     const float D_h = k.D ? k.D[h] : 0.0f;
 
-    // per-thread tile coordinates and global base pointers (row r0 of the sequence, unit column)
-    const int xr0 = tid / Cf::XU, xc = (tid % Cf::XU) * EPU;
+    // per-thread tile coordinates and global base pointers
+    const int xr0 = tid / (Cf::XU * HPW), xu = tid % (Cf::XU * HPW);
+    int xh = xu / Cf::XU;                                  // head slot of this thread's X unit
+    xh = xh < hcount ? xh : hcount - 1;
+    const int xc = (xu % Cf::XU) * EPU;
     const int br0 = tid / Cf::BU, bc = (tid % Cf::BU) * EPU;
-    const T* xg = reinterpret_cast<const T*>(k.x) + b * k.L * k.xs + (int64_t)h * P + xc;
+    const T* xg = reinterpret_cast<const T*>(k.x) + b * k.L * k.xs + (int64_t)(h0 + xh) * P + xc;
     const T* bgp = reinterpret_cast<const T*>(k.B) + b * k.L * k.bcs + (int64_t)g * N + bc;
     const T* cgp = reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N + bc;
     const T* dtg = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
+    E* const xdst = Xs + (xu / Cf::XU) * Q * XST + xc;      // this thread's X column in its head's tile
+    const E* const Xh = Xs + hw * Q * XST;                  // this wave's head tile
+    float* const lamh = sLam + hw * Q;
+    float* const dth = sDt + hw * Q;
+    float* const wh = sW + hw * Q;
+    float* const elh = sExpL + hw * Q;
 
-    // state tiles in accumulator layout: accS[pb][nb][j] = S[p = pblk*16 + li][n = nb*16 + 4q + j]
-    f32x4 accS[Cf::PBW][Cf::NNB];
+    // state tiles in accumulator layout: accS[pw][nb][j] = S[p = (pblk0+pw)*16 + li][n = nb*16 + 4q + j]
+    f32x4 accS[PW][Cf::NNB];
     {
         const float* src = nullptr;
         if (!kStateOnly) {
@@ -282,25 +305,24 @@ void ssd_chunk_scan_kernel(ScanK k)
             else src = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
         }
 #pragma unroll
-        for (int pb = 0; pb < Cf::PBW; ++pb) {
-            const int p = (wave * Cf::PBW + pb) * 16 + li;
+        for (int pw = 0; pw < PW; ++pw) {
+            const int p = (pblk0 + pw) * 16 + li;
 #pragma unroll
             for (int nb = 0; nb < Cf::NNB; ++nb) {
                 if (src) {
                     const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)p * N + nb * 16 + 4 * q);
-                    accS[pb][nb] = f32x4{v.x, v.y, v.z, v.w};
+                    accS[pw][nb] = f32x4{v.x, v.y, v.z, v.w};
                 } else {
-                    accS[pb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    accS[pw][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
         }
     }
 
-    // Register prefetch of one chunk (+ raw dt, one token per lane of wave 0).  Both helpers are
-    // forced inline: a prefetch array left in scratch memory would make every load synchronous.  Loads are issued
-    // without divergent branches (rows clamped into the sequence on the last, partial chunk) and
-    // stay raw until commit(), so nothing waits on them until the next chunk starts; commit()
-    // zeroes the rows past the end of the sequence.
+    // Register prefetch of one chunk (+ raw dt, one token per lane of every wave).  Loads are
+    // issued without divergent branches (rows clamped into the sequence on the last chunk) and
+    // stay raw until commit(), so nothing waits on them before the next chunk starts.  Both
+    // helpers are forced inline: a prefetch array left in scratch would make every load synchronous.
     u32x4_t px[PX::NP], pbv[PB::NP], pcv[kStateOnly ? 1 : PB::NP];
     T pre_dt;
     auto prefetch = [&](int64_t c) __attribute__((always_inline)) {
@@ -322,7 +344,7 @@ void ssd_chunk_scan_kernel(ScanK k)
             pbv[i] = *reinterpret_cast<const u32x4_t*>(bgp + (t0 + r) * k.bcs);
             if constexpr (!kStateOnly) pcv[i] = *reinterpret_cast<const u32x4_t*>(cgp + (t0 + r) * k.bcs);
         }
-        if (wave == 0) pre_dt = dtg[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
+        pre_dt = dtg[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
     };
     auto commit = [&](int64_t c) __attribute__((always_inline)) {
         const int valid = (int)(k.L - c * Q < Q ? k.L - c * Q : Q);
@@ -339,7 +361,7 @@ void ssd_chunk_scan_kernel(ScanK k)
 #pragma unroll
         for (int i = 0; i < PX::NP; ++i) {
             const int r = xr0 + i * PX::RPP;
-            if (!PX::kGuard || r < Q) *reinterpret_cast<u32x4_t*>(Xs + r * XST + xc) = px[i];
+            if (!PX::kGuard || r < Q) *reinterpret_cast<u32x4_t*>(xdst + r * XST) = px[i];
         }
 #pragma unroll
         for (int i = 0; i < PB::NP; ++i) {
@@ -349,18 +371,18 @@ void ssd_chunk_scan_kernel(ScanK k)
                 if constexpr (!kStateOnly) *reinterpret_cast<u32x4_t*>(Cs + r * BST + bc) = pcv[i];
             }
         }
-        if (wave == 0) {
-            // dt and the cumulative log-decay over the chunk (inclusive prefix sum across lanes)
-            const float dtv = lane < valid ? dt_of(to_f32(pre_dt), bias_h, k.dt_min, k.dt_max) : 0.0f;
-            const float lam = wave_prefix_sum(dtv * A_h);
-            const float lam_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), Q - 1));
+        // dt and the cumulative log-decay of this wave's head over the chunk
+        const float dtv = lane < valid ? dt_of(to_f32(pre_dt), bias_h, k.dt_min, k.dt_max) : 0.0f;
+        const float lam = wave_prefix_sum(dtv * A_h);
+        const float lam_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), Q - 1));
+        if (stats_writer) {
             if (lane < Q) {
-                sLam[lane] = lam;
-                sDt[lane] = dtv;
-                sW[lane] = fast_exp(lam_end - lam) * dtv;
-                sExpL[lane] = fast_exp(lam);
+                lamh[lane] = lam;
+                dth[lane] = dtv;
+                wh[lane] = fast_exp(lam_end - lam) * dtv;
+                elh[lane] = fast_exp(lam);
             }
-            if (lane == 0) sEnd = lam_end;
+            if (lane == 0) sEnd[hw] = lam_end;
         }
     };
 
@@ -372,35 +394,23 @@ void ssd_chunk_scan_kernel(ScanK k)
         if (c + 1 < c_end) prefetch(c + 1);
         const int64_t t0 = c * Q;
         const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
-        const float lam_end = sEnd;
+        const float lam_end = sEnd[hw];
         lam_seg += lam_end;
 
-        // X fragments (k = token s, column p): A operand of the intra part, B operand of the update
-        Frag<T> xf[Cf::PBW][Cf::KS_Q];
-#pragma unroll
-        for (int pb = 0; pb < Cf::PBW; ++pb)
-#pragma unroll
-            for (int ks = 0; ks < Cf::KS_Q; ++ks)
-                xf[pb][ks] = frag_col<T>(Xs, XST, 32 * ks, Q, (wave * Cf::PBW + pb) * 16, q, li);
-
-        f32x4 accY[Cf::PBW][Cf::NTB];
         if constexpr (!kStateOnly) {
-            // ---- G^T tiles, masked and scaled into M[t][s], with D on the diagonal.  The tiles a
-            // t-block's K=32 steps read are sb < 2*(tb/2)+2; those above the diagonal come out zero from
-            // the mask.  Every wave takes the same number of tiles (the last one repeated), so the
-            // loop has no branches and the compiler can overlap the tiles' LDS reads and MFMAs.
-            constexpr int NT = Cf::NTILES;
-            constexpr int TPW = (NT + Cf::NW - 1) / Cf::NW;
+            // ---- G^T[s][t] = sum_n B[s][n] C[t][n] for the tiles the K=32 token steps read, shared by
+            // the block's heads; stored in accumulator layout (lane l owns 4 consecutive floats).
+            constexpr int TPW = (Cf::NTILES + 3) / 4;
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
-                int id = wave + Cf::NW * i;
-                id = id < NT ? id : NT - 1;
-                int tb = 0, base = 0;
+                int id = wave + 4 * i;
+                id = id < Cf::NTILES ? id : Cf::NTILES - 1;
+                int tb = 0;
 #pragma unroll
-                for (int tt = 0; tt < Cf::NTB; ++tt) {
-                    const int cnt = Cf::tiles_in_row(tt);
-                    if (id >= base + cnt) { tb = tt + 1; base += cnt; }
-                }
+                for (int tt = 1; tt < Cf::NTB; ++tt) tb += id >= Cf::row_base(tt) ? 1 : 0;
+                int base = 0;
+#pragma unroll
+                for (int tt = 1; tt < Cf::NTB; ++tt) base = id >= Cf::row_base(tt) ? Cf::row_base(tt) : base;
                 const int sb = id - base;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -409,127 +419,128 @@ void ssd_chunk_scan_kernel(ScanK k)
                     const Frag<T> fb = frag_row<T>(Cs, BST, tb * 16 + li, 32 * ks, N, q);
                     mfma(acc, fa, fb);
                 }
-                const int t = tb * 16 + li;
-                const int s0 = sb * 16 + 4 * q;
-                const float lt = sLam[t];
-                const float4 ls = *reinterpret_cast<const float4*>(sLam + s0);
-                const float4 ds = *reinterpret_cast<const float4*>(sDt + s0);
-                const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
-                float m[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float v = acc[j] * fast_exp(lt - lsv[j]) * dsv[j];
-                    m[j] = (s0 + j <= t ? v : 0.0f) + (s0 + j == t ? D_h : 0.0f);
-                }
-                if constexpr (kSplitM) {
-                    float hi[4], lo[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        hi[j] = bits_to_f32(f32_to_bits(m[j]));
-                        lo[j] = m[j] - hi[j];
-                    }
-                    put4(Ms + t * MST + s0, hi[0], hi[1], hi[2], hi[3]);
-                    put4(Ml + t * MST + s0, lo[0], lo[1], lo[2], lo[3]);
-                } else {
-                    put4(Ms + t * MST + s0, m[0], m[1], m[2], m[3]);
-                }
-            }
-
-            // ---- state part: Y^T[p][t] = e^Lam_t * sum_n S[p][n] C[t][n]
-#pragma unroll
-            for (int pb = 0; pb < Cf::PBW; ++pb)
-#pragma unroll
-                for (int tb = 0; tb < Cf::NTB; ++tb) accY[pb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < Cf::KS_N; ++ks) {
-                Frag<T> sa[Cf::PBW];
-#pragma unroll
-                for (int pb = 0; pb < Cf::PBW; ++pb) {
-                    const f32x4 s0v = accS[pb][2 * ks];
-                    sa[pb].set(0, s0v[0], s0v[1], s0v[2], s0v[3]);
-                    if (2 * ks + 1 < Cf::NNB) {
-                        const f32x4 s1v = accS[pb][2 * ks + 1];
-                        sa[pb].set(1, s1v[0], s1v[1], s1v[2], s1v[3]);
-                    } else {
-                        sa[pb].set(1, 0.f, 0.f, 0.f, 0.f);
-                    }
-                }
-#pragma unroll
-                for (int tb = 0; tb < Cf::NTB; ++tb) {
-                    const Frag<T> cf = frag_row<T>(Cs, BST, tb * 16 + li, 32 * ks, N, q);
-#pragma unroll
-                    for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accY[pb][tb], sa[pb], cf);
-                }
-            }
-#pragma unroll
-            for (int tb = 0; tb < Cf::NTB; ++tb) {
-                const float el = sExpL[tb * 16 + li];
-#pragma unroll
-                for (int pb = 0; pb < Cf::PBW; ++pb) accY[pb][tb] *= el;
+                *reinterpret_cast<f32x4*>(Gs + id * 256 + lane * 4) = acc;
             }
         }
-        __syncthreads();  // M complete
+
+        // X fragments of this wave's head (k = token s, column p): A operand of the intra part
+        Frag<T> xf[PW][Cf::KS_Q];
+#pragma unroll
+        for (int pw = 0; pw < PW; ++pw)
+#pragma unroll
+            for (int ks = 0; ks < Cf::KS_Q; ++ks)
+                xf[pw][ks] = frag_col<T>(Xh, XST, 32 * ks, Q, (pblk0 + pw) * 16, q, li);
 
         if constexpr (!kStateOnly) {
-            // ---- intra-chunk part (with the D skip on M's diagonal): Y^T[p][t] += sum_s X[s][p] M[t][s]
+            __syncthreads();  // G complete
+            // state as the A operand of the state part: sa[pw][ks] covers n = 32ks .. 32ks+31
+            Frag<T> sa[PW][Cf::KS_N];
+#pragma unroll
+            for (int pw = 0; pw < PW; ++pw)
+#pragma unroll
+                for (int ks = 0; ks < Cf::KS_N; ++ks) {
+                    const f32x4 s0v = accS[pw][2 * ks];
+                    sa[pw][ks].set(0, s0v[0], s0v[1], s0v[2], s0v[3]);
+                    if (2 * ks + 1 < Cf::NNB) {
+                        const f32x4 s1v = accS[pw][2 * ks + 1];
+                        sa[pw][ks].set(1, s1v[0], s1v[1], s1v[2], s1v[3]);
+                    } else {
+                        sa[pw][ks].set(1, 0.f, 0.f, 0.f, 0.f);
+                    }
+                }
+            T* yb = reinterpret_cast<T*>(k.y) + (b * k.L + t0) * k.ys + (int64_t)h * P;
 #pragma unroll
             for (int tb = 0; tb < Cf::NTB; ++tb) {
+                const int t = tb * 16 + li;
+                f32x4 accY[PW];
+#pragma unroll
+                for (int pw = 0; pw < PW; ++pw) accY[pw] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // state part: Y^T[p][t] = e^Lam_t * sum_n S[p][n] C[t][n]
+#pragma unroll
+                for (int ks = 0; ks < Cf::KS_N; ++ks) {
+                    const Frag<T> cf = frag_row<T>(Cs, BST, t, 32 * ks, N, q);
+#pragma unroll
+                    for (int pw = 0; pw < PW; ++pw) mfma(accY[pw], sa[pw][ks], cf);
+                }
+                const float lt = lamh[t];
+                const float el = elh[t];
+#pragma unroll
+                for (int pw = 0; pw < PW; ++pw) accY[pw] *= el;
+                // intra part: M[t][s] = G[t][s] e^(Lam_t - Lam_s) dt_s for s <= t, + D on the diagonal
 #pragma unroll
                 for (int ks = 0; ks < Cf::KS_Q; ++ks) {
                     if (32 * ks > tb * 16 + 15) continue;
-                    const Frag<T> mf = frag_row<T>(Ms, MST, tb * 16 + li, 32 * ks, Q, q);
+                    Frag<T> mh, ml;
 #pragma unroll
-                    for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accY[pb][tb], xf[pb][ks], mf);
-                    if constexpr (kSplitM) {
-                        const Frag<T> ml = frag_row<T>(Ml, MST, tb * 16 + li, 32 * ks, Q, q);
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const int sb = 2 * ks + cc;
+                        if (sb >= Cf::tiles_in_row(tb)) {  // no such s-block
+                            mh.set(cc, 0.f, 0.f, 0.f, 0.f);
+                            ml.set(cc, 0.f, 0.f, 0.f, 0.f);
+                            continue;
+                        }
+                        const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + (Cf::row_base(tb) + sb) * 256 + lane * 4);
+                        const int s0 = sb * 16 + 4 * q;
+                        const float4 ls = *reinterpret_cast<const float4*>(lamh + s0);
+                        const float4 ds = *reinterpret_cast<const float4*>(dth + s0);
+                        const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+                        float m[4];
 #pragma unroll
-                        for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accY[pb][tb], xf[pb][ks], ml);
+                        for (int j = 0; j < 4; ++j) {
+                            const float v = gv[j] * fast_exp(lt - lsv[j]) * dsv[j];
+                            if (sb < tb) m[j] = v;
+                            else m[j] = (s0 + j <= t ? v : 0.0f) + (s0 + j == t ? D_h : 0.0f);
+                        }
+                        if constexpr (kSplitM) {
+                            float hi[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) hi[j] = bits_to_f32(f32_to_bits(m[j]));
+                            mh.set(cc, hi[0], hi[1], hi[2], hi[3]);
+                            ml.set(cc, m[0] - hi[0], m[1] - hi[1], m[2] - hi[2], m[3] - hi[3]);
+                        } else {
+                            mh.set(cc, m[0], m[1], m[2], m[3]);
+                        }
+                    }
+#pragma unroll
+                    for (int pw = 0; pw < PW; ++pw) {
+                        mfma(accY[pw], xf[pw][ks], mh);
+                        if constexpr (kSplitM) mfma(accY[pw], xf[pw][ks], ml);
                     }
                 }
-            }
-            // ---- store: the lane holds y[t = tb*16+li][p = pblk*16+4q .. +3]
-            T* yb = reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P + t0 * k.ys;
+                // store: the lane holds y[t][p = (pblk0+pw)*16 + 4q .. +3]
+                if (hvalid && t < valid) {
 #pragma unroll
-            for (int tb = 0; tb < Cf::NTB; ++tb) {
-                const int t = tb * 16 + li;
-                if (t < valid) {
-#pragma unroll
-                    for (int pb = 0; pb < Cf::PBW; ++pb) {
-                        const f32x4 a = accY[pb][tb];
-                        put4g(yb + t * k.ys + (wave * Cf::PBW + pb) * 16 + 4 * q, a[0], a[1], a[2], a[3]);
+                    for (int pw = 0; pw < PW; ++pw) {
+                        const f32x4 a = accY[pw];
+                        put4g(yb + t * k.ys + (pblk0 + pw) * 16 + 4 * q, a[0], a[1], a[2], a[3]);
                     }
                 }
             }
         }
 
         // ---- state update: S^T[n][p] = e^Lam_end S^T[n][p] + sum_s B[s][n] (w_s X[s][p])
-        Frag<T> xw[Cf::PBW][Cf::KS_Q];
+        const float decay = fast_exp(lam_end);
+#pragma unroll
+        for (int pw = 0; pw < PW; ++pw)
+#pragma unroll
+            for (int nb = 0; nb < Cf::NNB; ++nb) accS[pw][nb] *= decay;
 #pragma unroll
         for (int ks = 0; ks < Cf::KS_Q; ++ks) {
+            Frag<T> xw[PW];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int s0 = 32 * ks + 16 * cc + 4 * q;
-                const float4 wv = s0 < Q ? *reinterpret_cast<const float4*>(sW + s0) : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 wv = s0 < Q ? *reinterpret_cast<const float4*>(wh + s0) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int pb = 0; pb < Cf::PBW; ++pb) {
-                    if (cc == 0) xw[pb][ks] = xf[pb][ks];
-                    xw[pb][ks].set(cc, xf[pb][ks].get(cc, 0) * wv.x, xf[pb][ks].get(cc, 1) * wv.y,
-                                   xf[pb][ks].get(cc, 2) * wv.z, xf[pb][ks].get(cc, 3) * wv.w);
-                }
+                for (int pw = 0; pw < PW; ++pw)
+                    xw[pw].set(cc, xf[pw][ks].get(cc, 0) * wv.x, xf[pw][ks].get(cc, 1) * wv.y,
+                               xf[pw][ks].get(cc, 2) * wv.z, xf[pw][ks].get(cc, 3) * wv.w);
             }
-        }
-        const float decay = fast_exp(lam_end);
 #pragma unroll
-        for (int pb = 0; pb < Cf::PBW; ++pb)
-#pragma unroll
-            for (int nb = 0; nb < Cf::NNB; ++nb) accS[pb][nb] *= decay;
-#pragma unroll
-        for (int nb = 0; nb < Cf::NNB; ++nb) {
-#pragma unroll
-            for (int ks = 0; ks < Cf::KS_Q; ++ks) {
+            for (int nb = 0; nb < Cf::NNB; ++nb) {
                 const Frag<T> bf = frag_col<T>(Bs, BST, 32 * ks, Q, nb * 16, q, li);
 #pragma unroll
-                for (int pb = 0; pb < Cf::PBW; ++pb) mfma(accS[pb][nb], bf, xw[pb][ks]);
+                for (int pw = 0; pw < PW; ++pw) mfma(accS[pw][nb], bf, xw[pw]);
             }
         }
         __syncthreads();  // LDS tiles free for the next chunk
@@ -539,19 +550,19 @@ void ssd_chunk_scan_kernel(ScanK k)
     float* dst = nullptr;
     if (kStateOnly) dst = k.ws_state + ((int64_t)seg * BH + bh) * P * N;
     else if (seg == k.nseg - 1) dst = k.state_out ? k.state_out + (int64_t)bh * P * N : nullptr;
-    if (dst) {
+    if (dst && hvalid) {
 #pragma unroll
-        for (int pb = 0; pb < Cf::PBW; ++pb) {
-            const int p = (wave * Cf::PBW + pb) * 16 + li;
+        for (int pw = 0; pw < PW; ++pw) {
+            const int p = (pblk0 + pw) * 16 + li;
 #pragma unroll
             for (int nb = 0; nb < Cf::NNB; ++nb) {
-                const f32x4 v = accS[pb][nb];
+                const f32x4 v = accS[pw][nb];
                 *reinterpret_cast<float4*>(dst + (int64_t)p * N + nb * 16 + 4 * q) =
                     make_float4(v[0], v[1], v[2], v[3]);
             }
         }
     }
-    if (kStateOnly && tid == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+    if (kStateOnly && hvalid && (wave % Cf::WPH) == 0 && lane == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
 }
 
 // Chain the segments: S_in[seg+1] = exp(lam[seg]) * S_in[seg] + S_end_local[seg], written over
@@ -576,30 +587,41 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(const float* __r
 // host side
 
 struct Plan {
-    int nseg, cps;
+    int nseg, cps, nhu;
     size_t ws_bytes;
 };
 
-static Plan plan_for(int64_t batch, int64_t L, int H, int P, int N, int Q) {
+// Heads per block for the (P, N) work split (see Cfg).
+static int heads_per_block(int P, int N) {
+    const int npb = P / 16, nnb = N / 16;
+    const int cap = 16 / nnb > 0 ? 16 / nnb : 1;
+    const int pw = npb < cap ? npb : cap;
+    return 4 / (npb / pw);
+}
+
+static Plan plan_for(int64_t batch, int64_t L, int H, int G, int P, int N, int Q) {
     Plan pl;
     const int64_t nchunks = (L + Q - 1) / Q;
-    const int64_t units = batch * H;
-    // about one round of resident workgroups: three per compute unit on 256 CUs
-    const int64_t target = 768;
-    int64_t nseg = units > 0 ? (target + units - 1) / units : 1;
+    const int hpw = heads_per_block(P, N);
+    const int hpg = H / G;
+    pl.nhu = G * ((hpg + hpw - 1) / hpw);
+    const int64_t units = batch * pl.nhu;
+    // one round of resident blocks: two per compute unit on 256 CUs
+    const int64_t target = 512;
+    int64_t nseg = units > 0 ? target / units : 1;
     if (nseg > nchunks) nseg = nchunks;
     if (nseg < 1) nseg = 1;
     const int64_t cps = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 1;
     nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
     pl.nseg = (int)nseg;
     pl.cps = (int)cps;
-    pl.ws_bytes = nseg > 1 ? (size_t)(nseg * units) * ((size_t)P * N + 1) * sizeof(float) + 256 : 0;
+    pl.ws_bytes = nseg > 1 ? (size_t)(nseg * batch * H) * ((size_t)P * N + 1) * sizeof(float) + 256 : 0;
     return pl;
 }
 
 template <typename T, int Q, int P, int N>
 static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
-    const Plan pl = plan_for(a.batch, a.L, a.H, a.P, a.N, Q);
+    const Plan pl = plan_for(a.batch, a.L, a.H, a.G, a.P, a.N, Q);
     ScanK k;
     k.x = a.x; k.B = a.B; k.C = a.C; k.dt = a.dt;
     k.xs = a.xs; k.bcs = a.bcs; k.dts = a.dts; k.ys = a.ys;
@@ -614,19 +636,19 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
         k.ws_state = reinterpret_cast<float*>(a.ws);
         k.ws_lam = k.ws_state + (size_t)pl.nseg * BH * P * N;
     }
-    constexpr int THREADS = Cfg<T, Q, P, N>::THREADS;
     hipError_t e;
+    const int per_seg = (int)a.batch * pl.nhu;
     if (pl.nseg > 1) {
-        k.nblocks = (pl.nseg - 1) * BH;
-        e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, true>, dim3(k.nblocks), dim3(THREADS), 0, s, k);
+        k.nblocks = (pl.nseg - 1) * per_seg;
+        e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, true>, dim3(k.nblocks), dim3(kScanThreads), 0, s, k);
         if (e != hipSuccess) return e;
         dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH);
         e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, a.state_in, k.ws_state,
                           (const float*)k.ws_lam, BH, pl.nseg, P * N);
         if (e != hipSuccess) return e;
     }
-    k.nblocks = pl.nseg * BH;
-    return launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(THREADS), 0, s, k);
+    k.nblocks = pl.nseg * per_seg;
+    return launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(kScanThreads), 0, s, k);
 }
 
 template <typename T, int Q>
@@ -649,10 +671,10 @@ bool ssd_scan_supported(int P, int N, int Q, bool bf16) {
     return small || large;
 }
 
-int ssd_scan_default_chunk(int, int, bool bf16) { return bf16 ? 64 : 32; }
+int ssd_scan_default_chunk(int, int, bool) { return 32; }
 
-size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int, int Q, bool) {
-    return plan_for(batch, L, H, P, N, Q).ws_bytes;
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool) {
+    return plan_for(batch, L, H, G, P, N, Q).ws_bytes;
 }
 
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s) {
