@@ -5,10 +5,11 @@
 //     out[b,t,c] = SiLU(bias[c] + sum_{k<W} w[c,k] * x[b, t-(W-1)+k, c])
 //
 // Pure HBM stream (3 flop per byte).  Each lane owns VEC adjacent channels (one
-// 16-byte load per token) and walks TT consecutive tokens, keeping the last W
+// 16-byte load per token) and walks 64 consecutive tokens, keeping the last W
 // inputs in registers, so every input is read from HBM once (plus a W-1 token
 // halo per tile).  A wave covers 64*VEC contiguous channels of one token, so each
-// load and store instruction moves one contiguous 1 KiB row segment.
+// load and store instruction moves one contiguous 1 KiB row segment; loads run one
+// group of 8 tokens ahead of the arithmetic.
 #include "m2_device.h"
 #include "m2_launch.h"
 
@@ -61,25 +62,49 @@ __device__ __forceinline__ void load_vals(const T* p, float (&o)[VEC]) {
     for (int i = 0; i < VEC; ++i) o[i] = v.get(i);
 }
 
-constexpr int kConvTileTokens = 64;   // tokens per lane
-constexpr int kConvWavesPerBlock = 4; // one token tile per wave
-constexpr int kConvUnroll = 4;        // loads issued back to back
+constexpr int kConvTileTokens = 64;  // tokens per lane
+constexpr int kConvGroup = 8;        // tokens per load group (one group in flight while the previous computes)
+constexpr int kConvThreads = 256;
 
+template <typename T, int VEC> struct Raw;
+template <> struct Raw<bf16_t, 8> { using type = u32x4; };
+template <> struct Raw<float, 4> { using type = u32x4; };
+template <typename T> struct Raw<T, 1> { using type = T; };
+
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack(const typename Raw<T, VEC>::type& r, float (&o)[VEC]) {
+    if constexpr (VEC == 1) {
+        o[0] = to_f32(r);
+    } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const uint32_t wd = r[i >> 1];
+            o[i] = __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = __uint_as_float(r[i]);
+    }
+}
+
+// Lane <-> (token tile, channel group): the channel group runs fastest, so a wave covers 64
+// adjacent 16-byte channel groups of one token row (a contiguous 1 KiB) and every lane has work
+// whatever conv_dim is.  Each lane walks kConvTileTokens tokens of its VEC channels.
 template <typename T, int VEC, int W>
-__global__ __launch_bounds__(256) void conv1d_silu_kernel(
+__global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     const T* __restrict__ xbc, int64_t xs, int64_t L, int Cd,
     const float* __restrict__ w, const float* __restrict__ bias,
     const T* __restrict__ ring_in, int ring_phase,
     T* __restrict__ ring_out, T* __restrict__ out, int64_t os)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int c0 = (blockIdx.x * kWave + lane) * VEC;
-    if (c0 >= Cd) return;
-    const int64_t tile = (int64_t)blockIdx.y * kConvWavesPerBlock + wave;
-    const int64_t t0 = tile * kConvTileTokens;
-    if (t0 >= L && !(L == 0 && tile == 0)) return;
-    const int64_t b = blockIdx.z;
+    using R = typename Raw<T, VEC>::type;
+    const int CG = Cd / VEC;
+    const int64_t ntiles = L > 0 ? (L + kConvTileTokens - 1) / kConvTileTokens : 1;
+    const int64_t item = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
+    if (item >= ntiles * CG) return;
+    const int c0 = (int)(item % CG) * VEC;
+    const int64_t t0 = (item / CG) * kConvTileTokens;
+    const int64_t b = blockIdx.y;
     const T* xb = xbc + b * L * xs + c0;
     T* ob = out + b * L * os + c0;
 
@@ -87,74 +112,77 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
 #pragma unroll
-        for (int k = 0; k < W; ++k) wr[i][k] = w[(int64_t)(c0 + i) * W + k];
+        for (int kk = 0; kk < W; ++kk) wr[i][kk] = w[(int64_t)(c0 + i) * W + kk];
         br[i] = bias ? bias[c0 + i] : 0.0f;
     }
 
-    // win[k] holds token (next - W + k); win[W-1] is the newest
+    // win[kk] holds token (next - W + kk); win[W-1] is the newest
     float win[W][VEC];
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-        const int64_t tau = t0 - W + k;
-        if (tau >= 0) {
-            if (k > 0) load_vals<T, VEC>(xb + tau * xs, win[k]);
-            else {
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) win[k][i] = 0.0f;  // never enters a sum
-            }
-        } else if (ring_in) {
+    for (int kk = 0; kk < W; ++kk) {
+        const int64_t tau = t0 - W + kk;
+        if (tau >= 0 && kk > 0) {
+            load_vals<T, VEC>(xb + tau * xs, win[kk]);
+        } else if (tau < 0 && ring_in) {
             const int slot = (int)(((ring_phase + tau) % W + W) % W);
-            load_vals<T, VEC>(ring_in + (b * W + slot) * (int64_t)Cd + c0, win[k]);
+            load_vals<T, VEC>(ring_in + (b * W + slot) * (int64_t)Cd + c0, win[kk]);
         } else {
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) win[k][i] = 0.0f;
+            for (int i = 0; i < VEC; ++i) win[kk][i] = 0.0f;  // no history, or never enters a sum
         }
     }
 
     const int64_t t_end = t0 + kConvTileTokens < L ? t0 + kConvTileTokens : L;
-    for (int64_t t = t0; t < t_end; t += kConvUnroll) {
-        float nx[kConvUnroll][VEC];
+    const int n = (int)(t_end - t0);
+    R cur[kConvGroup], nxt[kConvGroup];
+    auto load_group = [&](R (&dst)[kConvGroup], int base) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < kConvUnroll; ++u)
-            if (t + u < t_end) load_vals<T, VEC>(xb + (t + u) * xs, nx[u]);
+        for (int u = 0; u < kConvGroup; ++u) {
+            const int tt = base + u < n ? base + u : n - 1;  // clamped: rows past the end are never used
+            dst[u] = *reinterpret_cast<const R*>(xb + (t0 + tt) * xs);
+        }
+    };
+    if (n > 0) load_group(cur, 0);
+    for (int base = 0; base < n; base += kConvGroup) {
+        if (base + kConvGroup < n) load_group(nxt, base + kConvGroup);
 #pragma unroll
-        for (int u = 0; u < kConvUnroll; ++u) {
-            if (t + u < t_end) {
+        for (int u = 0; u < kConvGroup; ++u) {
+            if (base + u < n) {
 #pragma unroll
-                for (int k = 0; k < W - 1; ++k)
+                for (int kk = 0; kk < W - 1; ++kk)
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) win[k][i] = win[k + 1][i];
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) win[W - 1][i] = nx[u][i];
+                    for (int i = 0; i < VEC; ++i) win[kk][i] = win[kk + 1][i];
+                unpack<T, VEC>(cur[u], win[W - 1]);
                 float o[VEC];
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
                     float v = br[i];
 #pragma unroll
-                    for (int k = 0; k < W; ++k) v = fmaf(wr[i][k], win[k][i], v);
+                    for (int kk = 0; kk < W; ++kk) v = fmaf(wr[i][kk], win[kk][i], v);
                     o[i] = silu(v);
                 }
-                store_vals<T, VEC>(ob + (t + u) * os, o);
+                store_vals<T, VEC>(ob + (t0 + base + u) * os, o);
             }
         }
+#pragma unroll
+        for (int u = 0; u < kConvGroup; ++u) cur[u] = nxt[u];
     }
 
     // the tile holding the last token writes the ring (phase 0: slot j = token L-W+j)
-    if (ring_out && t_end == L && (t0 < L || L == 0)) {
+    if (ring_out && t_end == L) {
 #pragma unroll
-        for (int k = 0; k < W; ++k) store_vals<T, VEC>(ring_out + (b * W + k) * (int64_t)Cd + c0, win[k]);
+        for (int kk = 0; kk < W; ++kk) store_vals<T, VEC>(ring_out + (b * W + kk) * (int64_t)Cd + c0, win[kk]);
     }
 }
 
 template <typename T, int VEC, int W>
 static hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
     const int64_t tiles = a.L > 0 ? (a.L + kConvTileTokens - 1) / kConvTileTokens : 1;
-    dim3 grid((unsigned)((a.Cd / VEC + kWave - 1) / kWave),
-              (unsigned)((tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock),
-              (unsigned)a.batch);
-    return launch_kernel(conv1d_silu_kernel<T, VEC, W>, grid, dim3(kWave * kConvWavesPerBlock), 0, s,
-                       (const T*)a.xbc, a.xs, a.L, a.Cd, a.w, a.bias, (const T*)a.ring_in, a.ring_phase,
-                       (T*)a.ring_out, (T*)a.out, a.os);
+    const int64_t items = tiles * (a.Cd / VEC);
+    dim3 grid((unsigned)((items + kConvThreads - 1) / kConvThreads), (unsigned)a.batch);
+    return launch_kernel(conv1d_silu_kernel<T, VEC, W>, grid, dim3(kConvThreads), 0, s,
+                         (const T*)a.xbc, a.xs, a.L, a.Cd, a.w, a.bias, (const T*)a.ring_in, a.ring_phase,
+                         (T*)a.ring_out, (T*)a.out, a.os);
 }
 
 template <typename T, int VEC>

@@ -9,6 +9,7 @@ namespace m2 {
 constexpr int kWave = 64;  // CDNA wavefront width
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Storage types of activations.  bf16 is kept as raw 16-bit patterns in memory.
 struct bf16_t { uint16_t bits; };

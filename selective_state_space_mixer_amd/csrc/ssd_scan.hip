@@ -181,25 +181,33 @@ struct ScanK {
 
 // Block -> logical unit.  Consecutive blocks are dealt round-robin to the 8 XCDs; the remap
 // gives each XCD a contiguous run of logical units (the head groups of one sequence and
-// segment), so the B/C rows those heads share are fetched into one L2.
+// segment), so the B/C rows those heads share are fetched into one L2.  XCD x receives
+// n/8 blocks, plus one if x < n%8; its run starts after those of XCDs 0..x-1.
 __device__ __forceinline__ int logical_block(int nblocks) {
     const int i = blockIdx.x;
-    if (nblocks % 8) return i;
-    return (i % 8) * (nblocks / 8) + i / 8;
+    const int x = i % 8, per = nblocks / 8, extra = nblocks % 8;
+    return x * per + (x < extra ? x : extra) + i / 8;
 }
 
 constexpr int kScanThreads = 256;  // four waves
+#ifndef M2_SCAN_STATE_TILES
+#define M2_SCAN_STATE_TILES 16
+#endif
+constexpr int kStateTiles = M2_SCAN_STATE_TILES;  // 16x16 state tiles per wave (PW * NNB)
 
 // Work split: each wave owns PW p-blocks of one head, so its share of the state (PW x NNB
-// accumulator tiles) stays within 64 registers; WPH waves cover a head and the block holds
-// HPW = 4 / WPH heads of one B/C group, which share the B and C tiles and G = B C^T.
+// accumulator tiles) stays within kStateTiles tiles (64 registers at 16: a whole 64x64 head per
+// wave, so the decay mask of a head is computed once); WPH waves cover a head and the
+// block holds HPW = 4 / WPH heads of one B/C group, which share the B and C tiles and G = B C^T.
 template <typename T, int Q, int P, int N>
 struct Cfg {
     using E = typename Lds<T>::E;
     static constexpr int NPB = P / 16;
     static constexpr int NNB = N / 16;
     static constexpr int NTB = Q / 16;
-    static constexpr int PW = NPB < (16 / NNB > 0 ? 16 / NNB : 1) ? NPB : (16 / NNB > 0 ? 16 / NNB : 1);
+    static constexpr int PW_CAP = kStateTiles / NNB > 0 ? kStateTiles / NNB : 1;
+    static constexpr int PW0 = NPB < PW_CAP ? NPB : PW_CAP;
+    static constexpr int PW = PW0 > NPB / 4 ? PW0 : NPB / 4;  // at most four waves per head
     static constexpr int WPH = NPB / PW;          // waves per head
     static constexpr int HPW = 4 / WPH;           // heads per block
     static_assert(WPH >= 1 && WPH <= 4 && HPW * WPH == 4, "work split");
@@ -249,6 +257,7 @@ void ssd_chunk_scan_kernel(ScanK k)
     __shared__ __attribute__((aligned(16))) float sDt[HPW * Q];
     __shared__ __attribute__((aligned(16))) float sW[HPW * Q];
     __shared__ __attribute__((aligned(16))) float sExpL[HPW * Q];
+    __shared__ __attribute__((aligned(16))) float sGs[HPW * Q];  // e^(Lam_e(s) - Lam_s) dt_s, e(s) = last token of s's 16-block
     __shared__ float sEnd[HPW];
 
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, li = lane & 15;
@@ -295,6 +304,7 @@ void ssd_chunk_scan_kernel(ScanK k)
     float* const dth = sDt + hw * Q;
     float* const wh = sW + hw * Q;
     float* const elh = sExpL + hw * Q;
+    float* const gsh = sGs + hw * Q;
 
     // state tiles in accumulator layout: accS[pw][nb][j] = S[p = (pblk0+pw)*16 + li][n = nb*16 + 4q + j]
     f32x4 accS[PW][Cf::NNB];
@@ -375,12 +385,15 @@ void ssd_chunk_scan_kernel(ScanK k)
         const float dtv = lane < valid ? dt_of(to_f32(pre_dt), bias_h, k.dt_min, k.dt_max) : 0.0f;
         const float lam = wave_prefix_sum(dtv * A_h);
         const float lam_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), Q - 1));
+        // log-decay at the last token of this lane's 16-token block
+        const float lam_blk = __shfl(lam, lane | 15, 64);
         if (stats_writer) {
             if (lane < Q) {
                 lamh[lane] = lam;
                 dth[lane] = dtv;
                 wh[lane] = fast_exp(lam_end - lam) * dtv;
                 elh[lane] = fast_exp(lam);
+                gsh[lane] = fast_exp(lam_blk - lam) * dtv;
             }
             if (lane == 0) sEnd[hw] = lam_end;
         }
@@ -474,22 +487,30 @@ void ssd_chunk_scan_kernel(ScanK k)
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) {
                         const int sb = 2 * ks + cc;
-                        if (sb >= Cf::tiles_in_row(tb)) {  // no such s-block
+                        if (sb >= Cf::tiles_in_row(tb) || sb > tb) {  // above the diagonal (or absent): zero
                             mh.set(cc, 0.f, 0.f, 0.f, 0.f);
                             ml.set(cc, 0.f, 0.f, 0.f, 0.f);
                             continue;
                         }
                         const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + (Cf::row_base(tb) + sb) * 256 + lane * 4);
                         const int s0 = sb * 16 + 4 * q;
-                        const float4 ls = *reinterpret_cast<const float4*>(lamh + s0);
-                        const float4 ds = *reinterpret_cast<const float4*>(dth + s0);
-                        const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
                         float m[4];
+                        if (sb < tb) {
+                            // below the diagonal: e^(Lam_t - Lam_s) = e^(Lam_t - Lam_e) e^(Lam_e - Lam_s), both
+                            // factors <= 1 (e = last token of block sb), the second precomputed per token
+                            const float f = fast_exp(lt - lamh[sb * 16 + 15]);
+                            const float4 gs = *reinterpret_cast<const float4*>(gsh + s0);
+                            m[0] = gv[0] * f * gs.x; m[1] = gv[1] * f * gs.y;
+                            m[2] = gv[2] * f * gs.z; m[3] = gv[3] * f * gs.w;
+                        } else {
+                            const float4 ls = *reinterpret_cast<const float4*>(lamh + s0);
+                            const float4 ds = *reinterpret_cast<const float4*>(dth + s0);
+                            const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float v = gv[j] * fast_exp(lt - lsv[j]) * dsv[j];
-                            if (sb < tb) m[j] = v;
-                            else m[j] = (s0 + j <= t ? v : 0.0f) + (s0 + j == t ? D_h : 0.0f);
+                            for (int j = 0; j < 4; ++j) {
+                                const float v = gv[j] * fast_exp(lt - lsv[j]) * dsv[j];
+                                m[j] = (s0 + j <= t ? v : 0.0f) + (s0 + j == t ? D_h : 0.0f);
+                            }
                         }
                         if constexpr (kSplitM) {
                             float hi[4];
@@ -566,20 +587,33 @@ void ssd_chunk_scan_kernel(ScanK k)
 }
 
 // Chain the segments: S_in[seg+1] = exp(lam[seg]) * S_in[seg] + S_end_local[seg], written over
-// S_end_local[seg] (so that segment seg+1 finds its initial state at index seg).
+// S_end_local[seg] (so that segment seg+1 finds its initial state at index seg).  Only the
+// combine is sequential: the loads of a batch of segments are issued together.
 __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(const float* __restrict__ state_in,
                                                                 float* __restrict__ ws_state,
                                                                 const float* __restrict__ ws_lam, int BH, int nseg,
                                                                 int PN)
 {
+    constexpr int kBatch = 16;
     const int bh = blockIdx.y;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= PN) return;
     float s = state_in ? state_in[(int64_t)bh * PN + i] : 0.0f;
-    for (int seg = 0; seg + 1 < nseg; ++seg) {
-        float* slot = ws_state + ((int64_t)seg * BH + bh) * PN + i;
-        s = fast_exp(ws_lam[(int64_t)seg * BH + bh]) * s + *slot;
-        *slot = s;
+    for (int seg0 = 0; seg0 + 1 < nseg; seg0 += kBatch) {
+        float loc[kBatch], dec[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int seg = seg0 + j < nseg - 1 ? seg0 + j : nseg - 2;
+            loc[j] = ws_state[((int64_t)seg * BH + bh) * PN + i];
+            dec[j] = ws_lam[(int64_t)seg * BH + bh];
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (seg0 + j < nseg - 1) {
+                s = fast_exp(dec[j]) * s + loc[j];
+                ws_state[((int64_t)(seg0 + j) * BH + bh) * PN + i] = s;
+            }
+        }
     }
 }
 
@@ -594,8 +628,9 @@ struct Plan {
 // Heads per block for the (P, N) work split (see Cfg).
 static int heads_per_block(int P, int N) {
     const int npb = P / 16, nnb = N / 16;
-    const int cap = 16 / nnb > 0 ? 16 / nnb : 1;
-    const int pw = npb < cap ? npb : cap;
+    const int cap = kStateTiles / nnb > 0 ? kStateTiles / nnb : 1;
+    int pw = npb < cap ? npb : cap;
+    pw = pw > npb / 4 ? pw : npb / 4;
     return 4 / (npb / pw);
 }
 
