@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -56,34 +58,67 @@ def step_bytes(B, H, P, N, G, W, Cd):
 
 
 def time_events(torch, fns, steps, warmup):
-    """Run the callables in order `steps` times after `warmup` passes; per-callable mean ms from
-    event pairs on the current stream, plus the wall ms of the whole timed region."""
+    """Per-callable mean ms, each from `steps` back-to-back calls between one event pair on the current
+    stream (the queue stays ahead of the GPU, so host launch gaps are not counted), then the mean ms of
+    one pass of all callables in order, again over `steps` passes, plus the wall ms of that last region."""
     for _ in range(warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
-           for _ in range(steps)]
+    per = []
+    for f in fns:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / steps)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for s in range(steps):
-        for i, f in enumerate(fns):
-            evs[s][i][0].record()
+    for _ in range(steps):
+        for f in fns:
             f()
-            evs[s][i][1].record()
     end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    per = [sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps for i in range(len(fns))]
     return per, start.elapsed_time(end), wall
 
 
-def roofline(bytes_per_launch, ms):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"ssd_scan": "ssd_scan.hip", "conv1d": "conv1d.hip", "ssd_step": "ssd_step.hip"}
+
+
+def source_digest(kernel):
+    """sha256 of the kernel's source file and the shared device header (counters go stale when either changes)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "m2_device.h"):
+        with open(os.path.join(ROOT, "selective_state_space_mixer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, scaled by the
+    plain-copy calibration; None if absent or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+        e = t["kernels"][kernel]
+        if e.get("source_sha256") != source_digest(kernel):
+            return None
+        return int(e["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def roofline(bytes_per_launch, ms, kernel=None):
     gbs = bytes_per_launch / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel) if kernel else None}
 
 
 def bench_prefill(torch, m2, workloads, args):
@@ -117,8 +152,8 @@ def bench_prefill(torch, m2, workloads, args):
     tok = B * L
     return {
         "tokens_per_s": tok / (step_ms * 1e-3), "ms_per_step": step_ms, "wall_ms": wall_ms,
-        "kernels": {"conv1d": {"ms": t_conv, "bytes": conv_b, "roofline": roofline(conv_b, t_conv)},
-                    "ssd_scan": {"ms": t_scan, "bytes": scan_b, "roofline": roofline(scan_b, t_scan)}},
+        "kernels": {"conv1d": {"ms": t_conv, "bytes": conv_b, "roofline": roofline(conv_b, t_conv, "conv1d")},
+                    "ssd_scan": {"ms": t_scan, "bytes": scan_b, "roofline": roofline(scan_b, t_scan, "ssd_scan")}},
         "path_roofline_frac": round((conv_b + scan_b) / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "config": {"workload": "zamba2-2.7b mixer prefill, batch 1 x 32768 tokens (conv1d+SiLU -> SSD scan)",
                    "batch": B, "seqlen": L, "d_model": d.d_model, "expand": d.expand, "nheads": H,
@@ -155,7 +190,7 @@ def bench_decode(torch, m2, workloads, args):
     step_ms = total_ms / steps
     return {
         "tokens_per_s": B / (step_ms * 1e-3), "ms_per_step": step_ms, "kernel_ms": t_step, "wall_ms": wall_ms,
-        "steps": steps, "roofline": roofline(sb, t_step), "bytes_per_launch": sb,
+        "steps": steps, "roofline": roofline(sb, t_step, "ssd_step"), "bytes_per_launch": sb,
         "config": {"workload": "zamba2-2.7b mixer decode, 256 sequences x %d chained tokens" % steps,
                    "batch": B, "nheads": H, "headdim": P, "d_state": N, "d_conv": W,
                    "state": "fp32 80x64x64 per sequence, N(0,0.1)", "ring": "bf16 4 x 5248, N(0,0.1)"},
@@ -194,6 +229,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe_mib:
+        # a plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+        return
     import selective_state_space_mixer_amd as m2
     import workloads
 
