@@ -23,7 +23,7 @@ template <> struct Vec<bf16_t, 8> {
         return __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
     }
     __device__ __forceinline__ void set2(int i, float lo, float hi) {
-        (&raw.x)[i >> 1] = (uint32_t)f32_to_bits(lo) | ((uint32_t)f32_to_bits(hi) << 16);
+        (&raw.x)[i >> 1] = pack_bf16x2(lo, hi);
     }
 };
 template <> struct Vec<float, 4> {

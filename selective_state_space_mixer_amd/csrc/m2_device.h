@@ -28,6 +28,19 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 __device__ __forceinline__ float bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f32_to_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one dword, low half first: a single
+// v_cvt_pk_bf16_f32 on gfx950
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// the two bf16 of a packed dword as floats
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // e^v through the hardware base-2 exponential

@@ -63,8 +63,8 @@ template <typename T> struct Frag;
 template <> struct Frag<bf16_t> {
     uint32_t w[4];
     __device__ __forceinline__ void set(int c, float a0, float a1, float a2, float a3) {
-        w[2 * c] = (uint32_t)f32_to_bits(a0) | ((uint32_t)f32_to_bits(a1) << 16);
-        w[2 * c + 1] = (uint32_t)f32_to_bits(a2) | ((uint32_t)f32_to_bits(a3) << 16);
+        w[2 * c] = pack_bf16x2(a0, a1);
+        w[2 * c + 1] = pack_bf16x2(a2, a3);
     }
     __device__ __forceinline__ float get(int c, int e) const {
         const uint32_t v = w[2 * c + (e >> 1)];
@@ -149,8 +149,8 @@ __device__ __forceinline__ void row4(const float* p, float (&o)[4]) {
 }
 __device__ __forceinline__ void put4(uint16_t* p, float a0, float a1, float a2, float a3) {
     uint2 v;
-    v.x = (uint32_t)f32_to_bits(a0) | ((uint32_t)f32_to_bits(a1) << 16);
-    v.y = (uint32_t)f32_to_bits(a2) | ((uint32_t)f32_to_bits(a3) << 16);
+    v.x = pack_bf16x2(a0, a1);
+    v.y = pack_bf16x2(a2, a3);
     *reinterpret_cast<uint2*>(p) = v;
 }
 __device__ __forceinline__ void put4(float* p, float a0, float a1, float a2, float a3) {
@@ -513,11 +513,11 @@ void ssd_chunk_scan_kernel(ScanK k)
                             }
                         }
                         if constexpr (kSplitM) {
-                            float hi[4];
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) hi[j] = bits_to_f32(f32_to_bits(m[j]));
-                            mh.set(cc, hi[0], hi[1], hi[2], hi[3]);
-                            ml.set(cc, m[0] - hi[0], m[1] - hi[1], m[2] - hi[2], m[3] - hi[3]);
+                            const uint32_t h01 = pack_bf16x2(m[0], m[1]), h23 = pack_bf16x2(m[2], m[3]);
+                            mh.w[2 * cc] = h01;
+                            mh.w[2 * cc + 1] = h23;
+                            ml.w[2 * cc] = pack_bf16x2(m[0] - lo_bf16(h01), m[1] - hi_bf16(h01));
+                            ml.w[2 * cc + 1] = pack_bf16x2(m[2] - lo_bf16(h23), m[3] - hi_bf16(h23));
                         } else {
                             mh.set(cc, m[0], m[1], m[2], m[3]);
                         }
