@@ -13,21 +13,23 @@
 // which is the token recurrence S_t = exp(dt_t A) S_{t-1} + dt_t x_t B_t^T, y_t = S_t C_t + D x_t
 // unrolled over the chunk (exactly, up to rounding).
 //
-// One workgroup walks the chunks of one (sequence, head, segment) in order and keeps
-// the fp32 state in MFMA accumulator registers for the whole walk.  Per chunk, four
-// contractions run on v_mfma_f32_16x16x32_bf16 (fp32 activations: v_mfma_f32_16x16x4f32):
-//   G^T[s][t] = sum_n B[s][n] C[t][n]            -> masked and scaled -> M[t][s] in LDS
+// One workgroup walks the chunks of a few heads of one (sequence, segment) in order; each wave
+// keeps its share of a head's fp32 state in MFMA accumulator registers for the whole walk.
+// Per chunk, four contractions run on v_mfma_f32_16x16x32_bf16 (fp32 activations:
+// v_mfma_f32_16x16x4f32):
+//   G^T[s][t] = sum_n B[s][n] C[t][n]            -> masked and scaled in registers -> M[t][s]
 //                                                   (bf16: as a hi + lo pair, see below)
-//   Y^T[p][t] = sum_n S[p][n] (e^Lam_t C[t][n])   (state part, state as the A operand)
+//   Y^T[p][t] = sum_n S[p][n] C[t][n]             (state part, state as the A operand)
 //   Y^T[p][t]+= sum_s X[s][p] M[t][s]             (intra-chunk part)
 //   S^T[n][p] = e^Lam_end S^T[n][p] + sum_s B[s][n] (w_s X[s][p]),  w_s = e^(Lam_end-Lam_s) dt_s
 // The e^Lam_t factor of the state part is applied to the output tile, w_s scales the X fragments
-// already in registers, and the D skip is folded into M's diagonal, so the per-element work
-// outside the MFMAs is one pass over M.
-// Wave w owns p-block(s) w of the state and of the output, so the state never leaves
-// its registers; only M (the same for every p-block) goes through LDS.  Operands whose
-// contraction index runs down the rows of a row-major LDS tile (X and B over tokens) are
-// read with ds_read_b64_tr_b16, which hands each lane four consecutive rows of one column.
+// already in registers, and the D skip is folded into M's diagonal.  G comes out of the MFMA in
+// exactly the register layout M needs as a B operand, so M never leaves the wave that uses it.
+//
+// The X, B and C tiles of a chunk move from HBM straight into LDS (buffer loads with the LDS
+// destination), double-buffered: chunk c+1 streams in while chunk c is computed, and one
+// barrier per chunk publishes c+1 and frees c's buffer.  Rows past the end of the sequence
+// fall outside the buffer range and read as zero.
 //
 // M carries the whole intra-chunk weight of a token on itself and its neighbours; where the
 // decay is strong those terms are large and cancel, so a single bf16 rounding of M costs
@@ -47,14 +49,15 @@ namespace m2 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // native vector: stays in registers
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // ----------------------------------------------------------------------------------------------
 // element types
 
 template <typename T> struct Lds;
-template <> struct Lds<bf16_t> { using E = uint16_t; static constexpr int PAD = 8; };
-template <> struct Lds<float> { using E = float; static constexpr int PAD = 4; };
+template <> struct Lds<bf16_t> { using E = uint16_t; };
+template <> struct Lds<float> { using E = float; };
 
 // Eight k-values of one lane for a K=32 MFMA step: chunk 0 holds k = kbase+4q+{0..3},
 // chunk 1 holds k = kbase+16+4q+{0..3} (q = lane/16).  Both operands of a product use the
@@ -88,24 +91,36 @@ __device__ __forceinline__ void mfma(f32x4& acc, const Frag<float>& a, const Fra
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
-// chunk c of a fragment from a row-major LDS tile whose k index runs along the row
-__device__ __forceinline__ void chunk_row(Frag<bf16_t>& f, int c, const uint16_t* p) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+// ----------------------------------------------------------------------------------------------
+// LDS tiles: rows of U 16-byte units followed by one unit of padding, so that the 16 rows a
+// fragment read touches at one column start in different banks.
+
+// element offset of (row, col) in a tile of E elements with U units per row
+template <typename E, int U>
+__device__ __forceinline__ int tidx(int r, int c) {
+    constexpr int EPU = 16 / (int)sizeof(E);
+    return r * ((U + 1) * EPU) + c;
+}
+
+// chunk c of a fragment from a tile whose k index runs along the row (lane: `row`, k = k0..k0+3)
+template <int U>
+__device__ __forceinline__ void chunk_row(Frag<bf16_t>& f, int c, const uint16_t* tile, int row, int k0) {
+    const uint2 v = *reinterpret_cast<const uint2*>(tile + tidx<uint16_t, U>(row, k0));
     f.w[2 * c] = v.x;
     f.w[2 * c + 1] = v.y;
 }
-__device__ __forceinline__ void chunk_row(Frag<float>& f, int c, const float* p) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
+template <int U>
+__device__ __forceinline__ void chunk_row(Frag<float>& f, int c, const float* tile, int row, int k0) {
+    const float4 v = *reinterpret_cast<const float4*>(tile + tidx<float, U>(row, k0));
     f.set(c, v.x, v.y, v.z, v.w);
 }
 
 // Fragment with k along a row: the lane supplies `row`, k = kbase + 4q (+16); kext = k extent.
-template <typename T>
-__device__ __forceinline__ Frag<T> frag_row(const typename Lds<T>::E* tile, int stride, int row, int kbase,
-                                            int kext, int q) {
+template <typename T, int U>
+__device__ __forceinline__ Frag<T> frag_row(const typename Lds<T>::E* tile, int row, int kbase, int kext, int q) {
     Frag<T> f;
-    chunk_row(f, 0, tile + row * stride + kbase + 4 * q);
-    if (kbase + 16 < kext) chunk_row(f, 1, tile + row * stride + kbase + 16 + 4 * q);
+    chunk_row<U>(f, 0, tile, row, kbase + 4 * q);
+    if (kbase + 16 < kext) chunk_row<U>(f, 1, tile, row, kbase + 16 + 4 * q);
     else f.set(1, 0.f, 0.f, 0.f, 0.f);
     return f;
 }
@@ -113,53 +128,88 @@ __device__ __forceinline__ Frag<T> frag_row(const typename Lds<T>::E* tile, int 
 // Chunk c of a fragment whose k index runs down the rows: lane (q, i) gets rows r0+4q..r0+4q+3
 // of column col0+i.  bf16: one ds_read_b64_tr_b16 (lane i addresses row i/4, columns 4(i%4)..+3
 // of its 16-lane group's 4x16 block and receives column i of the block).
-__device__ __forceinline__ void chunk_col(Frag<bf16_t>& f, int c, const uint16_t* tile, int stride, int r0, int col0,
-                                          int q, int i) {
-    const uint16_t* p = tile + (r0 + 4 * q + (i >> 2)) * stride + col0 + 4 * (i & 3);
+template <int U>
+__device__ __forceinline__ void chunk_col(Frag<bf16_t>& f, int c, const uint16_t* tile, int r0, int col0, int q,
+                                          int i) {
+    const uint16_t* p = tile + tidx<uint16_t, U>(r0 + 4 * q + (i >> 2), col0 + 4 * (i & 3));
     const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((M2_LDS i16x4_t*)(p));
     const uint2 u = __builtin_bit_cast(uint2, v);
     f.w[2 * c] = u.x;
     f.w[2 * c + 1] = u.y;
 }
-__device__ __forceinline__ void chunk_col(Frag<float>& f, int c, const float* tile, int stride, int r0, int col0,
-                                          int q, int i) {
-    const float* p = tile + (r0 + 4 * q) * stride + col0 + i;
-    f.set(c, p[0], p[stride], p[2 * stride], p[3 * stride]);
+template <int U>
+__device__ __forceinline__ void chunk_col(Frag<float>& f, int c, const float* tile, int r0, int col0, int q, int i) {
+    const int r = r0 + 4 * q, col = col0 + i;
+    f.set(c, tile[tidx<float, U>(r, col)], tile[tidx<float, U>(r + 1, col)], tile[tidx<float, U>(r + 2, col)],
+          tile[tidx<float, U>(r + 3, col)]);
 }
 
-template <typename T>
-__device__ __forceinline__ Frag<T> frag_col(const typename Lds<T>::E* tile, int stride, int kbase, int kext,
-                                            int col0, int q, int i) {
+template <typename T, int U>
+__device__ __forceinline__ Frag<T> frag_col(const typename Lds<T>::E* tile, int kbase, int kext, int col0, int q,
+                                            int i) {
     Frag<T> f;
-    chunk_col(f, 0, tile, stride, kbase, col0, q, i);
-    if (kbase + 16 < kext) chunk_col(f, 1, tile, stride, kbase + 16, col0, q, i);
+    chunk_col<U>(f, 0, tile, kbase, col0, q, i);
+    if (kbase + 16 < kext) chunk_col<U>(f, 1, tile, kbase + 16, col0, q, i);
     else f.set(1, 0.f, 0.f, 0.f, 0.f);
     return f;
 }
 
-// four consecutive elements of a row as fp32, and back
-__device__ __forceinline__ void row4(const uint16_t* p, float (&o)[4]) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
-    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+// ----------------------------------------------------------------------------------------------
+// buffer resources: a base address and a byte range; loads outside the range return zero and
+// stores outside it are dropped
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit dword access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
-__device__ __forceinline__ void row4(const float* p, float (&o)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+
+// The same resource as four dwords, for the LDS-destination load below.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_desc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
 }
-__device__ __forceinline__ void put4(uint16_t* p, float a0, float a1, float a2, float a3) {
-    uint2 v;
-    v.x = pack_bf16x2(a0, a1);
-    v.y = pack_bf16x2(a2, a3);
-    *reinterpret_cast<uint2*>(p) = v;
+
+// 64 lanes x 16 bytes from the buffer into 1 KB of LDS at `dst` (lane l -> dst + 16 l).
+// Written out (M0 = LDS address, one wait state after M0 is set) rather than through
+// the builtin: the compiler cannot tell which LDS bytes the builtin's load writes, and so holds
+// every later LDS read until all such loads are done, which would serialise the prefetch.  The
+// caller orders these loads with s_waitcnt and barriers; the load has no register result.
+__device__ __forceinline__ void load_lds16(const i32x4_t& desc, void* dst, uint32_t voff) {
+    const uint32_t m = (uint32_t)(uintptr_t)(M2_LDS void*)dst;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(desc), "{m0}"(m)
+                 : "memory");
 }
-__device__ __forceinline__ void put4(float* p, float a0, float a1, float a2, float a3) {
-    *reinterpret_cast<float4*>(p) = make_float4(a0, a1, a2, a3);
+
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, bf16_t*, const f32x4& a) {
+    const u32x2_t v = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, 0, 0);
 }
-__device__ __forceinline__ void put4g(bf16_t* p, float a0, float a1, float a2, float a3) {
-    put4(reinterpret_cast<uint16_t*>(p), a0, a1, a2, a3);
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, float*, const f32x4& a) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, a), r, (int)voff, 0, 0);
 }
-__device__ __forceinline__ void put4g(float* p, float a0, float a1, float a2, float a3) { put4(p, a0, a1, a2, a3); }
+
+// one element as raw bits, converted only where it is used (so nothing waits on the load early)
+__device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, bf16_t*) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, float*) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ float raw_to_f32(uint32_t v, bf16_t*) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float raw_to_f32(uint32_t v, float*) { return __uint_as_float(v); }
+
+// wait until at most N of this wave's vector memory operations are outstanding (gfx9 s_waitcnt:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).  Operations complete in
+// issue order, so this waits for everything issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
 
 // ----------------------------------------------------------------------------------------------
 // kernel parameters
@@ -176,6 +226,7 @@ struct ScanK {
     int64_t L;
     int batch, H, G;
     int nseg, cps;     // segments per sequence, chunks per segment
+    int win;           // chunks per buffer-resource window (byte offsets inside one stay below 2^31)
     int nblocks;       // blocks in this launch
 };
 
@@ -189,76 +240,84 @@ __device__ __forceinline__ int logical_block(int nblocks) {
     return x * per + (x < extra ? x : extra) + i / 8;
 }
 
-constexpr int kScanThreads = 256;  // four waves
-#ifndef M2_SCAN_STATE_TILES
-#define M2_SCAN_STATE_TILES 16
+// Work split.  A wave owns PW p-blocks of one head, so its share of the state is at most
+// kMaxStateTiles 16x16 accumulator tiles (32 registers); WPH waves cover a head.  A block holds
+// HPW heads of one B/C group, which share the B and C tiles in LDS, and WAVES = HPW * WPH waves
+// (eight where the LDS budget allows: two such blocks fill a compute unit at four waves per SIMD).
+// Every wave forms the decay-masked matrix M of its own head from G = C B^T tiles it computes
+// itself, so the only data exchanged between waves are the tiles and the chunk statistics.
+constexpr int kMaxStateTiles = 8;
+#ifndef M2_SCAN_WAVES
+#define M2_SCAN_WAVES 8
 #endif
-constexpr int kStateTiles = M2_SCAN_STATE_TILES;  // 16x16 state tiles per wave (PW * NNB)
+constexpr int kScanWaves = M2_SCAN_WAVES;  // waves per block, when the heads allow
 
-// Work split: each wave owns PW p-blocks of one head, so its share of the state (PW x NNB
-// accumulator tiles) stays within kStateTiles tiles (64 registers at 16: a whole 64x64 head per
-// wave, so the decay mask of a head is computed once); WPH waves cover a head and the
-// block holds HPW = 4 / WPH heads of one B/C group, which share the B and C tiles and G = B C^T.
 template <typename T, int Q, int P, int N>
 struct Cfg {
     using E = typename Lds<T>::E;
     static constexpr int NPB = P / 16;
     static constexpr int NNB = N / 16;
     static constexpr int NTB = Q / 16;
-    static constexpr int PW_CAP = kStateTiles / NNB > 0 ? kStateTiles / NNB : 1;
-    static constexpr int PW0 = NPB < PW_CAP ? NPB : PW_CAP;
-    static constexpr int PW = PW0 > NPB / 4 ? PW0 : NPB / 4;  // at most four waves per head
+    static constexpr int PW0 = kMaxStateTiles / NNB > 0 ? kMaxStateTiles / NNB : 1;
+    static constexpr int PW = NPB < PW0 ? NPB : PW0;
     static constexpr int WPH = NPB / PW;          // waves per head
-    static constexpr int HPW = 4 / WPH;           // heads per block
-    static_assert(WPH >= 1 && WPH <= 4 && HPW * WPH == 4, "work split");
-    static constexpr int XST = P + Lds<T>::PAD;   // LDS row strides (elements)
-    static constexpr int BST = N + Lds<T>::PAD;
     static constexpr int EPU = 16 / (int)sizeof(E);  // elements per 16-byte unit
-    static constexpr int XU = P / EPU, BU = N / EPU;
+    static constexpr int UX = P / EPU, UB = N / EPU;  // units per X row and per B/C row
     static constexpr int KS_N = (N + 31) / 32;    // K=32 steps over d_state
     static constexpr int KS_Q = (Q + 31) / 32;    // K=32 steps over tokens
-    // s-blocks that t-block tb's K=32 steps over tokens read: sb < 2*(tb/2)+2 (and < NTB)
-    static constexpr int tiles_in_row(int tb) { return 2 * (tb / 2) + 2 < NTB ? 2 * (tb / 2) + 2 : NTB; }
-    static constexpr int row_base(int tb) {
-        int n = 0;
-        for (int r = 0; r < tb; ++r) n += tiles_in_row(r);
-        return n;
+    static constexpr int kStats = 5;              // per-token chunk statistics (see the kernel)
+    static constexpr int round_kb(int units) { return (units + 63) / 64 * 64; }  // whole 1 KB pieces
+    // LDS units (16 bytes) of one buffer: X tiles of hpw heads, then B and C (rows padded by a unit)
+    static constexpr int x_units(int hpw) { return round_kb(hpw * Q * (UX + 1)); }
+    static constexpr int b_units() { return round_kb(Q * (UB + 1)); }
+    static constexpr int lds_bytes(int hpw) {
+        return 2 * (16 * (x_units(hpw) + 2 * b_units()) + (kStats * Q + 1) * hpw * 4);
     }
-    static constexpr int NTILES = row_base(NTB);
-};
-
-// Loads of a tile in 16-byte units: U units per row, RPP rows per pass, NP passes over R rows.
-template <int U, int R>
-struct TilePlan {
-    static constexpr int RPP = kScanThreads / U;
-    static constexpr int NP = (R + RPP - 1) / RPP;
-    static constexpr bool kGuard = (R % RPP) != 0;  // some passes run past the last row
+    static constexpr int kLdsBudget = sizeof(E) == 2 ? 72 * 1024 : 150 * 1024;
+    static constexpr int hpw_fit() {
+        int hpw = kScanWaves / WPH > 0 ? kScanWaves / WPH : 1;
+        while (hpw > 1 && lds_bytes(hpw) > kLdsBudget) hpw /= 2;
+        return hpw;
+    }
+    static constexpr int HPW = hpw_fit();         // heads per block
+    static constexpr int WAVES = HPW * WPH;
+    static constexpr int THREADS = 64 * WAVES;
+    // blocks resident on one compute unit (the occupancy the register budget is set for): up to
+    // four waves per SIMD, as far as the 160 KB of LDS allow
+    static constexpr int BPC_LDS = 160 * 1024 / lds_bytes(HPW);
+    static constexpr int BPC = 16 / WAVES < BPC_LDS ? 16 / WAVES : BPC_LDS;
+    static constexpr int WPE = BPC * WAVES / 4 > 0 ? BPC * WAVES / 4 : 1;  // waves per SIMD
+    static_assert(NPB % PW == 0 && WAVES <= 16, "work split");
 };
 
 // ----------------------------------------------------------------------------------------------
 // chunk walk.  kStateOnly: segment end state from a zero start (no C, no output).
 
 template <typename T, int Q, int P, int N, bool kStateOnly>
-__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void ssd_chunk_scan_kernel(ScanK k)
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, Cfg<T, Q, P, N>::THREADS),
+                               amdgpu_waves_per_eu(Cfg<T, Q, P, N>::WPE)))
+ssd_chunk_scan_kernel(ScanK k)
 {
     using Cf = Cfg<T, Q, P, N>;
     using E = typename Cf::E;
-    constexpr int XST = Cf::XST, BST = Cf::BST, EPU = Cf::EPU, HPW = Cf::HPW, PW = Cf::PW;
-    using PX = TilePlan<Cf::XU * HPW, Q>;  // the block's heads are adjacent in a token row
-    using PB = TilePlan<Cf::BU, Q>;
+    constexpr int HPW = Cf::HPW, PW = Cf::PW, UX = Cf::UX, UB = Cf::UB, EPU = Cf::EPU;
+    constexpr int XUN = Cf::x_units(HPW), BUN = Cf::b_units();
+    constexpr int NXP = XUN / 64, NBP = BUN / 64;        // 1 KB pieces of the X tiles and of B (C)
+    constexpr int NPIECE = NXP + (kStateOnly ? 1 : 2) * NBP;
+    constexpr int PPW = (NPIECE + Cf::WAVES - 1) / Cf::WAVES;  // pieces per wave (at most)
     constexpr bool kSplitM = sizeof(E) == 2;  // bf16 operands: M as hi + lo
+    constexpr int QS = HPW * Q;               // one statistic of every head of the block
+    constexpr uint32_t SZ = sizeof(T);
 
-    __shared__ __attribute__((aligned(16))) E Xs[HPW * Q * XST];
-    __shared__ __attribute__((aligned(16))) E Bs[Q * BST];
-    __shared__ __attribute__((aligned(16))) E Cs[kStateOnly ? 8 : Q * BST];
-    __shared__ __attribute__((aligned(16))) float Gs[kStateOnly ? 4 : Cf::NTILES * 256];
-    __shared__ __attribute__((aligned(16))) float sLam[HPW * Q];
-    __shared__ __attribute__((aligned(16))) float sDt[HPW * Q];
-    __shared__ __attribute__((aligned(16))) float sW[HPW * Q];
-    __shared__ __attribute__((aligned(16))) float sExpL[HPW * Q];
-    __shared__ __attribute__((aligned(16))) float sGs[HPW * Q];  // e^(Lam_e(s) - Lam_s) dt_s, e(s) = last token of s's 16-block
-    __shared__ float sEnd[HPW];
+    // one buffer: X tiles [HPW][Q rows][UX units], B [Q][UB], C [Q][UB] (each rounded to 1 KB)
+    __shared__ __attribute__((aligned(1024))) E tiles[2][(XUN + 2 * BUN) * EPU];
+    // per head and token, in order: Lam*log2(e), dt, w = e^(Lam_end - Lam) dt, e^Lam, and
+    // gs = e^(Lam_e - Lam) dt with e the last token of the token's 16-block
+    __shared__ __attribute__((aligned(16))) float sSt[2][Cf::kStats * QS];
+    __shared__ float sDec[2][HPW];    // factor applied to the stored state after the chunk's output
+    __shared__ float sLamEnd[2][HPW]; // summed log-decay of the chunk
+    __shared__ float sSig[HPW];       // log-scale of the stored state at the end of the walk
+    __shared__ uint64_t sBase[Cf::WAVES][5];  // x, B, C, dt, y addresses at the segment's first row
 
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -284,27 +343,32 @@ void ssd_chunk_scan_kernel(ScanK k)
     const int BH = k.batch * k.H;
     const int64_t nchunks = (k.L + Q - 1) / Q;
     const int64_t c_begin = (int64_t)seg * k.cps;
-    const int64_t c_end = c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks;
+    const int nc = (int)((c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks) - c_begin);  // chunks here
+    const int64_t row_begin = c_begin * Q;                       // first token of the segment
+    const int64_t row_end = k.L < row_begin + (int64_t)nc * Q ? k.L : row_begin + (int64_t)nc * Q;
     const float bias_h = k.dt_bias[h], A_h = k.A[h];
     const float D_h = k.D ? k.D[h] : 0.0f;
 
-    // per-thread tile coordinates and global base pointers
-    const int xr0 = tid / (Cf::XU * HPW), xu = tid % (Cf::XU * HPW);
-    int xh = xu / Cf::XU;                                  // head slot of this thread's X unit
-    xh = xh < hcount ? xh : hcount - 1;
-    const int xc = (xu % Cf::XU) * EPU;
-    const int br0 = tid / Cf::BU, bc = (tid % Cf::BU) * EPU;
-    const T* xg = reinterpret_cast<const T*>(k.x) + b * k.L * k.xs + (int64_t)(h0 + xh) * P + xc;
-    const T* bgp = reinterpret_cast<const T*>(k.B) + b * k.L * k.bcs + (int64_t)g * N + bc;
-    const T* cgp = reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N + bc;
-    const T* dtg = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
-    E* const xdst = Xs + (xu / Cf::XU) * Q * XST + xc;      // this thread's X column in its head's tile
-    const E* const Xh = Xs + hw * Q * XST;                  // this wave's head tile
-    float* const lamh = sLam + hw * Q;
-    float* const dth = sDt + hw * Q;
-    float* const wh = sW + hw * Q;
-    float* const elh = sExpL + hw * Q;
-    float* const gsh = sGs + hw * Q;
+    // Byte offset, within a chunk's rows, of the 16-byte unit this lane brings into each of its
+    // wave's LDS pieces (piece i = wave + WAVES * j), and which tile the piece belongs to.
+    uint32_t voff[PPW];
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+        const int piece = wave + Cf::WAVES * j;
+        const int u = piece * 64 + lane;  // unit index in the buffer
+        uint32_t o = 0;
+        // row padding and the rounding past the last row point outside every range (ranges stay
+        // below 2^31 and so do chunk offsets): zero-filled
+        if (piece < NXP) {
+            const int hh = u / (Q * (UX + 1)), rem = u % (Q * (UX + 1)), r = rem / (UX + 1), pos = rem % (UX + 1);
+            o = (u < HPW * Q * (UX + 1) && pos < UX) ? (uint32_t)(r * k.xs + hh * P + pos * EPU) * SZ : 0x80000000u;
+        } else {
+            const int ub = (u - XUN) % BUN;
+            const int r = ub / (UB + 1), pos = ub % (UB + 1);
+            o = (ub < Q * (UB + 1) && pos < UB) ? (uint32_t)(r * k.bcs + pos * EPU) * SZ : 0x80000000u;
+        }
+        voff[j] = o;
+    }
 
     // state tiles in accumulator layout: accS[pw][nb][j] = S[p = (pblk0+pw)*16 + li][n = nb*16 + 4q + j]
     f32x4 accS[PW][Cf::NNB];
@@ -329,156 +393,196 @@ void ssd_chunk_scan_kernel(ScanK k)
         }
     }
 
-    // Register prefetch of one chunk (+ raw dt, one token per lane of every wave).  Loads are
-    // issued without divergent branches (rows clamped into the sequence on the last chunk) and
-    // stay raw until commit(), so nothing waits on them before the next chunk starts.  Both
-    // helpers are forced inline: a prefetch array left in scratch would make every load synchronous.
-    u32x4_t px[PX::NP], pbv[PB::NP], pcv[kStateOnly ? 1 : PB::NP];
-    T pre_dt;
-    auto prefetch = [&](int64_t c) __attribute__((always_inline)) {
-        const int64_t t0 = c * Q;
-        const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
-        const bool full = valid == Q;
-#pragma unroll
-        for (int i = 0; i < PX::NP; ++i) {
-            int r = xr0 + i * PX::RPP;
-            if (PX::kGuard && r >= Q) r = Q - 1;
-            if (!full) r = r < valid ? r : valid - 1;
-            px[i] = *reinterpret_cast<const u32x4_t*>(xg + (t0 + r) * k.xs);
-        }
-#pragma unroll
-        for (int i = 0; i < PB::NP; ++i) {
-            int r = br0 + i * PB::RPP;
-            if (PB::kGuard && r >= Q) r = Q - 1;
-            if (!full) r = r < valid ? r : valid - 1;
-            pbv[i] = *reinterpret_cast<const u32x4_t*>(bgp + (t0 + r) * k.bcs);
-            if constexpr (!kStateOnly) pcv[i] = *reinterpret_cast<const u32x4_t*>(cgp + (t0 + r) * k.bcs);
-        }
-        pre_dt = dtg[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
+    // Buffer resources over a window of the segment's rows, starting at local chunk wbase; each
+    // range ends with the last row of the window (the sequence, unless the window is cut short
+    // to keep offsets below 2^31, and then only rows the window never serves are cut).  The
+    // window bases are kept in LDS rather than in scalar registers: a rebase is rare.
+    const int xs = (int)k.xs, bcs = (int)k.bcs, dts = (int)k.dts, ys = (int)k.ys;  // < 2^31 / (3 Q SZ)
+    const int nrows = (int)(row_end - row_begin);
+    if (lane == 0) {
+        const int64_t base = b * k.L + row_begin;
+        sBase[wave][0] = (uint64_t)(reinterpret_cast<const T*>(k.x) + base * k.xs + (int64_t)h0 * P);
+        sBase[wave][1] = (uint64_t)(reinterpret_cast<const T*>(k.B) + base * k.bcs + (int64_t)g * N);
+        sBase[wave][2] = (uint64_t)(reinterpret_cast<const T*>(k.C) + base * k.bcs + (int64_t)g * N);
+        sBase[wave][3] = (uint64_t)(reinterpret_cast<const T*>(k.dt) + base * k.dts + h);
+        sBase[wave][4] = (uint64_t)(reinterpret_cast<T*>(k.y) + base * k.ys + (int64_t)h * P);
+    }
+    i32x4_t rx, rb, rc;
+    __amdgpu_buffer_rsrc_t rd, ry;
+    int wbase = 0;
+    auto rebase = [&](int i0) __attribute__((always_inline)) {
+        wbase = i0;
+        const int r0 = i0 * Q;
+        const int left = nrows - r0;
+        const int rows = (left < (k.win + 2) * Q ? left : (k.win + 2) * Q) - 1;
+        auto at = [&](int j, int stride) __attribute__((always_inline)) {
+            const uint64_t v = sBase[wave][j];
+            const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+            return reinterpret_cast<const T*>(u) + (int64_t)r0 * stride;
+        };
+        rx = make_desc(at(0, xs), (uint32_t)(rows * xs + hcount * P) * SZ);
+        const uint32_t bc_bytes = (uint32_t)(rows * bcs + N) * SZ;
+        rb = make_desc(at(1, bcs), bc_bytes);
+        rc = make_desc(at(2, bcs), bc_bytes);
+        rd = make_rsrc(at(3, dts), (uint32_t)(rows * dts + 1) * SZ);
+        ry = make_rsrc(at(4, ys), hvalid && !kStateOnly ? (uint32_t)(rows * ys + P) * SZ : 0u);
     };
-    auto commit = [&](int64_t c) __attribute__((always_inline)) {
-        const int valid = (int)(k.L - c * Q < Q ? k.L - c * Q : Q);
-        const u32x4_t zero = {0u, 0u, 0u, 0u};
-        if (valid < Q) {  // the last chunk of the sequence: zero the rows past its end
+    auto valid_of = [&](int i) __attribute__((always_inline)) {
+        const int left = nrows - i * Q;
+        return left < Q ? left : Q;
+    };
+    // Stream local chunk i's tiles into LDS buffer `buf`: each wave issues its pieces.
+    auto stream = [&](int i, int buf) __attribute__((always_inline)) {
+        const uint32_t rel = (uint32_t)((i - wbase) * Q);
+        const uint32_t dx = rel * (uint32_t)xs * SZ, db = rel * (uint32_t)bcs * SZ;
 #pragma unroll
-            for (int i = 0; i < PX::NP; ++i) px[i] = xr0 + i * PX::RPP < valid ? px[i] : zero;
-#pragma unroll
-            for (int i = 0; i < PB::NP; ++i) {
-                pbv[i] = br0 + i * PB::RPP < valid ? pbv[i] : zero;
-                if constexpr (!kStateOnly) pcv[i] = br0 + i * PB::RPP < valid ? pcv[i] : zero;
-            }
+        for (int j = 0; j < PPW; ++j) {
+            const int piece = wave + Cf::WAVES * j;
+            if (piece >= NPIECE) break;
+            E* dst = &tiles[buf][piece * 64 * EPU];
+            if (piece < NXP) load_lds16(rx, dst, voff[j] + dx);
+            else if (piece < NXP + NBP) load_lds16(rb, dst, voff[j] + db);
+            else load_lds16(rc, dst, voff[j] + db);
         }
-#pragma unroll
-        for (int i = 0; i < PX::NP; ++i) {
-            const int r = xr0 + i * PX::RPP;
-            if (!PX::kGuard || r < Q) *reinterpret_cast<u32x4_t*>(xdst + r * XST) = px[i];
-        }
-#pragma unroll
-        for (int i = 0; i < PB::NP; ++i) {
-            const int r = br0 + i * PB::RPP;
-            if (!PB::kGuard || r < Q) {
-                *reinterpret_cast<u32x4_t*>(Bs + r * BST + bc) = pbv[i];
-                if constexpr (!kStateOnly) *reinterpret_cast<u32x4_t*>(Cs + r * BST + bc) = pcv[i];
-            }
-        }
-        // dt and the cumulative log-decay of this wave's head over the chunk
-        const float dtv = lane < valid ? dt_of(to_f32(pre_dt), bias_h, k.dt_min, k.dt_max) : 0.0f;
+    };
+    // raw dt of this wave's head, one token per lane (zero past the sequence)
+    auto load_dt = [&](int i) __attribute__((always_inline)) {
+        const uint32_t row = (uint32_t)((i - wbase) * Q + lane);
+        return load_raw(rd, row * (uint32_t)dts * SZ, (T*)nullptr);
+    };
+    // The state is kept as S = e^sig * S_hat: a chunk whose decay keeps sig above -kRescale only
+    // adds to S_hat (its token weights carry e^-sig, at most e^kRescale), and the stored state is
+    // multiplied out only when sig would drop below that.  The statistics writer of each head
+    // tracks sig (and the segment's summed log-decay) as it prepares the chunks in order.
+    constexpr float kRescale = 40.0f;
+    float sig = 0.0f, lam_seg = 0.0f;
+    // dt and the cumulative log-decay of this wave's head over chunk i, into statistics buffer buf
+    auto stats = [&](int i, int buf, uint32_t raw) __attribute__((always_inline)) {
+        if (!stats_writer) return;
+        const int valid = valid_of(i);
+        const float dtv = lane < valid ? dt_of(raw_to_f32(raw, (T*)nullptr), bias_h, k.dt_min, k.dt_max) : 0.0f;
         const float lam = wave_prefix_sum(dtv * A_h);
         const float lam_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), Q - 1));
-        // log-decay at the last token of this lane's 16-token block
-        const float lam_blk = __shfl(lam, lane | 15, 64);
-        if (stats_writer) {
-            if (lane < Q) {
-                lamh[lane] = lam;
-                dth[lane] = dtv;
-                wh[lane] = fast_exp(lam_end - lam) * dtv;
-                elh[lane] = fast_exp(lam);
-                gsh[lane] = fast_exp(lam_blk - lam) * dtv;
-            }
-            if (lane == 0) sEnd[hw] = lam_end;
+        const float lam_blk = __shfl(lam, lane | 15, 64);  // at the last token of this lane's 16-block
+        const float sig_prev = sig;
+        const bool rescale = sig_prev + lam_end < -kRescale;
+        // token weight e^(Lam_end - Lam_s) dt_s / e^sig_new, sig_new = 0 (rescale) or sig_prev + Lam_end
+        const float wexp = rescale ? lam_end - lam : -(sig_prev + lam);
+        sig = rescale ? 0.0f : sig_prev + lam_end;
+        lam_seg += lam_end;
+        if (lane < Q) {
+            float* st = &sSt[buf][hw * Q + lane];
+            st[0 * QS] = lam * kLog2e;
+            st[1 * QS] = dtv;
+            st[2 * QS] = fast_exp(wexp) * dtv;
+            st[3 * QS] = fast_exp(lam + sig_prev);
+            st[4 * QS] = fast_exp(lam_blk - lam) * dtv;
+        }
+        if (lane == 0) {
+            sDec[buf][hw] = rescale ? fast_exp(sig_prev + lam_end) : 1.0f;
+            sLamEnd[buf][hw] = lam_end;
         }
     };
 
-    float lam_seg = 0.0f;  // summed log-decay of the segment (state-only pass)
-    if (c_begin < c_end) prefetch(c_begin);
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        commit(c);
-        __syncthreads();  // tiles and chunk statistics in LDS
-        if (c + 1 < c_end) prefetch(c + 1);
-        const int64_t t0 = c * Q;
-        const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
-        const float lam_end = sEnd[hw];
-        lam_seg += lam_end;
-
-        if constexpr (!kStateOnly) {
-            // ---- G^T[s][t] = sum_n B[s][n] C[t][n] for the tiles the K=32 token steps read, shared by
-            // the block's heads; stored in accumulator layout (lane l owns 4 consecutive floats).
-            constexpr int TPW = (Cf::NTILES + 3) / 4;
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                int id = wave + 4 * i;
-                id = id < Cf::NTILES ? id : Cf::NTILES - 1;
-                int tb = 0;
-#pragma unroll
-                for (int tt = 1; tt < Cf::NTB; ++tt) tb += id >= Cf::row_base(tt) ? 1 : 0;
-                int base = 0;
-#pragma unroll
-                for (int tt = 1; tt < Cf::NTB; ++tt) base = id >= Cf::row_base(tt) ? Cf::row_base(tt) : base;
-                const int sb = id - base;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < Cf::KS_N; ++ks) {
-                    const Frag<T> fa = frag_row<T>(Bs, BST, sb * 16 + li, 32 * ks, N, q);
-                    const Frag<T> fb = frag_row<T>(Cs, BST, tb * 16 + li, 32 * ks, N, q);
-                    mfma(acc, fa, fb);
-                }
-                *reinterpret_cast<f32x4*>(Gs + id * 256 + lane * 4) = acc;
-            }
+    uint32_t dt_next = 0;  // raw dt of the chunk after the one being computed
+    if (nc > 0) {
+        rebase(0);
+        const uint32_t dt0 = load_dt(0);
+        if (1 < nc) dt_next = load_dt(1);
+        stream(0, 0);
+        stats(0, 0, dt0);
+    }
+    wait_vmem<0>();
+    __syncthreads();
+    // y stores issued per chunk: the end-of-chunk wait lets them drain in the background
+    constexpr int kStores = kStateOnly ? 0 : Cf::NTB * PW;
+    for (int i = 0; i < nc; ++i) {
+        const int buf = i & 1;
+        if (i - wbase == k.win) rebase(i);  // chunks i .. i+2 are addressed from here on
+        if (i + 1 < nc) {
+            const uint32_t raw = dt_next;
+            if (i + 2 < nc) dt_next = load_dt(i + 2);
+            stream(i + 1, buf ^ 1);
+            stats(i + 1, buf ^ 1, raw);
         }
+        // wave-uniform chunk values: the stored state's factor, and whether every intra-chunk decay
+        // factor e^(Lam_t - Lam_s) splits into two that stay finite
+        const float dec = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sDec[buf][hw])));
+        const bool split_diag =
+            __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sLamEnd[buf][hw]))) > -60.0f;
+        const E* const Xh = &tiles[buf][hw * Q * (UX + 1) * EPU];  // this wave's head tile
+        const E* const Bs = &tiles[buf][XUN * EPU];
+        const float* const lamh = &sSt[buf][0 * QS + hw * Q];
+        const float* const dth = &sSt[buf][1 * QS + hw * Q];
+        const float* const wh = &sSt[buf][2 * QS + hw * Q];
+        const float* const elh = &sSt[buf][3 * QS + hw * Q];
+        const float* const gsh = &sSt[buf][4 * QS + hw * Q];
 
         // X fragments of this wave's head (k = token s, column p): A operand of the intra part
         Frag<T> xf[PW][Cf::KS_Q];
 #pragma unroll
         for (int pw = 0; pw < PW; ++pw)
 #pragma unroll
-            for (int ks = 0; ks < Cf::KS_Q; ++ks)
-                xf[pw][ks] = frag_col<T>(Xh, XST, 32 * ks, Q, (pblk0 + pw) * 16, q, li);
+            for (int ks = 0; ks < Cf::KS_Q; ++ks) xf[pw][ks] = frag_col<T, UX>(Xh, 32 * ks, Q, (pblk0 + pw) * 16, q, li);
 
         if constexpr (!kStateOnly) {
-            __syncthreads();  // G complete
-            // state as the A operand of the state part: sa[pw][ks] covers n = 32ks .. 32ks+31
-            Frag<T> sa[PW][Cf::KS_N];
+            const E* const Cs = Bs + BUN * EPU;
+            // state part for every t-block first, so the bf16 copy of the state is dead before the
+            // intra part: Y^T[p][t] = sum_n S[p][n] C[t][n] (the e^Lam_t factor comes later)
+            f32x4 accY[Cf::NTB][PW];
+            {
+                // state as the A operand: sa[pw][ks] covers n = 32ks .. 32ks+31
+                Frag<T> sa[PW][Cf::KS_N];
 #pragma unroll
-            for (int pw = 0; pw < PW; ++pw)
+                for (int pw = 0; pw < PW; ++pw)
 #pragma unroll
-                for (int ks = 0; ks < Cf::KS_N; ++ks) {
-                    const f32x4 s0v = accS[pw][2 * ks];
-                    sa[pw][ks].set(0, s0v[0], s0v[1], s0v[2], s0v[3]);
-                    if (2 * ks + 1 < Cf::NNB) {
-                        const f32x4 s1v = accS[pw][2 * ks + 1];
-                        sa[pw][ks].set(1, s1v[0], s1v[1], s1v[2], s1v[3]);
-                    } else {
-                        sa[pw][ks].set(1, 0.f, 0.f, 0.f, 0.f);
+                    for (int ks = 0; ks < Cf::KS_N; ++ks) {
+                        const f32x4 s0v = accS[pw][2 * ks];
+                        sa[pw][ks].set(0, s0v[0], s0v[1], s0v[2], s0v[3]);
+                        if (2 * ks + 1 < Cf::NNB) {
+                            const f32x4 s1v = accS[pw][2 * ks + 1];
+                            sa[pw][ks].set(1, s1v[0], s1v[1], s1v[2], s1v[3]);
+                        } else {
+                            sa[pw][ks].set(1, 0.f, 0.f, 0.f, 0.f);
+                        }
+                    }
+#pragma unroll
+                for (int tb = 0; tb < Cf::NTB; ++tb) {
+#pragma unroll
+                    for (int pw = 0; pw < PW; ++pw) accY[tb][pw] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < Cf::KS_N; ++ks) {
+                        const Frag<T> cf = frag_row<T, UB>(Cs, tb * 16 + li, 32 * ks, N, q);
+#pragma unroll
+                        for (int pw = 0; pw < PW; ++pw) mfma(accY[tb][pw], sa[pw][ks], cf);
                     }
                 }
-            T* yb = reinterpret_cast<T*>(k.y) + (b * k.L + t0) * k.ys + (int64_t)h * P;
+            }
+            // output rows of this chunk and head; rows past the sequence (and waves without a
+            // head) fall outside the range of ry and are not written
+            const uint32_t yrow = (uint32_t)((i - wbase) * Q);
 #pragma unroll
             for (int tb = 0; tb < Cf::NTB; ++tb) {
                 const int t = tb * 16 + li;
-                f32x4 accY[PW];
+                // C rows of this t-block: B operand of the G tiles
+                Frag<T> cf[Cf::KS_N];
 #pragma unroll
-                for (int pw = 0; pw < PW; ++pw) accY[pw] = f32x4{0.f, 0.f, 0.f, 0.f};
-                // state part: Y^T[p][t] = e^Lam_t * sum_n S[p][n] C[t][n]
+                for (int ks = 0; ks < Cf::KS_N; ++ks) cf[ks] = frag_row<T, UB>(Cs, t, 32 * ks, N, q);
+                // G^T[s][t] = sum_n B[s][n] C[t][n] for the s-blocks at or below the diagonal, in
+                // accumulator layout: gacc[sb][j] = G[t][s = sb*16 + 4q + j]
+                f32x4 gacc[Cf::NTB];
 #pragma unroll
-                for (int ks = 0; ks < Cf::KS_N; ++ks) {
-                    const Frag<T> cf = frag_row<T>(Cs, BST, t, 32 * ks, N, q);
+                for (int sb = 0; sb <= tb; ++sb) {
+                    gacc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int pw = 0; pw < PW; ++pw) mfma(accY[pw], sa[pw][ks], cf);
+                    for (int ks = 0; ks < Cf::KS_N; ++ks)
+                        mfma(gacc[sb], frag_row<T, UB>(Bs, sb * 16 + li, 32 * ks, N, q), cf[ks]);
                 }
                 const float lt = lamh[t];
                 const float el = elh[t];
 #pragma unroll
-                for (int pw = 0; pw < PW; ++pw) accY[pw] *= el;
+                for (int pw = 0; pw < PW; ++pw) accY[tb][pw] *= el;
                 // intra part: M[t][s] = G[t][s] e^(Lam_t - Lam_s) dt_s for s <= t, + D on the diagonal
 #pragma unroll
                 for (int ks = 0; ks < Cf::KS_Q; ++ks) {
@@ -487,29 +591,35 @@ void ssd_chunk_scan_kernel(ScanK k)
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) {
                         const int sb = 2 * ks + cc;
-                        if (sb >= Cf::tiles_in_row(tb) || sb > tb) {  // above the diagonal (or absent): zero
+                        if (sb > tb) {  // above the diagonal: zero
                             mh.set(cc, 0.f, 0.f, 0.f, 0.f);
                             ml.set(cc, 0.f, 0.f, 0.f, 0.f);
                             continue;
                         }
-                        const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + (Cf::row_base(tb) + sb) * 256 + lane * 4);
+                        const f32x4 gv = gacc[sb];
                         const int s0 = sb * 16 + 4 * q;
                         float m[4];
-                        if (sb < tb) {
-                            // below the diagonal: e^(Lam_t - Lam_s) = e^(Lam_t - Lam_e) e^(Lam_e - Lam_s), both
-                            // factors <= 1 (e = last token of block sb), the second precomputed per token
-                            const float f = fast_exp(lt - lamh[sb * 16 + 15]);
+                        if (sb < tb || split_diag) {
+                            // e^(Lam_t - Lam_s) = e^(Lam_t - Lam_e) e^(Lam_e - Lam_s), e = last token of
+                            // block sb, the second factor precomputed per token.  Below the diagonal
+                            // both are <= 1; on it the first is at most e^60.
+                            const float f = __builtin_amdgcn_exp2f(lt - lamh[sb * 16 + 15]);
                             const float4 gs = *reinterpret_cast<const float4*>(gsh + s0);
                             m[0] = gv[0] * f * gs.x; m[1] = gv[1] * f * gs.y;
                             m[2] = gv[2] * f * gs.z; m[3] = gv[3] * f * gs.w;
                         } else {
                             const float4 ls = *reinterpret_cast<const float4*>(lamh + s0);
                             const float4 ds = *reinterpret_cast<const float4*>(dth + s0);
-                            const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+                            m[0] = gv[0] * __builtin_amdgcn_exp2f(lt - ls.x) * ds.x;
+                            m[1] = gv[1] * __builtin_amdgcn_exp2f(lt - ls.y) * ds.y;
+                            m[2] = gv[2] * __builtin_amdgcn_exp2f(lt - ls.z) * ds.z;
+                            m[3] = gv[3] * __builtin_amdgcn_exp2f(lt - ls.w) * ds.w;
+                        }
+                        if (sb == tb) {  // diagonal tile: causal mask (s <= t), D on the diagonal
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
-                                const float v = gv[j] * fast_exp(lt - lsv[j]) * dsv[j];
-                                m[j] = (s0 + j <= t ? v : 0.0f) + (s0 + j == t ? D_h : 0.0f);
+                                const float v = 4 * q + j == li ? m[j] + D_h : m[j];
+                                m[j] = 4 * q + j <= li ? v : 0.0f;
                             }
                         }
                         if constexpr (kSplitM) {
@@ -524,50 +634,62 @@ void ssd_chunk_scan_kernel(ScanK k)
                     }
 #pragma unroll
                     for (int pw = 0; pw < PW; ++pw) {
-                        mfma(accY[pw], xf[pw][ks], mh);
-                        if constexpr (kSplitM) mfma(accY[pw], xf[pw][ks], ml);
+                        mfma(accY[tb][pw], xf[pw][ks], mh);
+                        if constexpr (kSplitM) mfma(accY[tb][pw], xf[pw][ks], ml);
                     }
                 }
                 // store: the lane holds y[t][p = (pblk0+pw)*16 + 4q .. +3]
-                if (hvalid && t < valid) {
 #pragma unroll
-                    for (int pw = 0; pw < PW; ++pw) {
-                        const f32x4 a = accY[pw];
-                        put4g(yb + t * k.ys + (pblk0 + pw) * 16 + 4 * q, a[0], a[1], a[2], a[3]);
-                    }
-                }
+                for (int pw = 0; pw < PW; ++pw)
+                    store4(ry, ((yrow + t) * (uint32_t)ys + (pblk0 + pw) * 16 + 4 * q) * SZ, (T*)nullptr,
+                           accY[tb][pw]);
             }
         }
 
-        // ---- state update: S^T[n][p] = e^Lam_end S^T[n][p] + sum_s B[s][n] (w_s X[s][p])
-        const float decay = fast_exp(lam_end);
+        // ---- state update: S_hat^T[n][p] = dec S_hat^T[n][p] + sum_s B[s][n] (w_s X[s][p])
+        if (dec != 1.0f) {
 #pragma unroll
-        for (int pw = 0; pw < PW; ++pw)
+            for (int pw = 0; pw < PW; ++pw)
 #pragma unroll
-            for (int nb = 0; nb < Cf::NNB; ++nb) accS[pw][nb] *= decay;
+                for (int nb = 0; nb < Cf::NNB; ++nb) accS[pw][nb] *= dec;
+        }
 #pragma unroll
         for (int ks = 0; ks < Cf::KS_Q; ++ks) {
-            Frag<T> xw[PW];
+            // w_s X[s][p]: bf16 operands carry it as hi = rn(v) and lo = rn(v - hi) (two products),
+            // so the state does not take a 2^-9 rounding of every token's contribution
+            Frag<T> xw[PW], xl[PW];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int s0 = 32 * ks + 16 * cc + 4 * q;
                 const float4 wv = s0 < Q ? *reinterpret_cast<const float4*>(wh + s0) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int pw = 0; pw < PW; ++pw)
-                    xw[pw].set(cc, xf[pw][ks].get(cc, 0) * wv.x, xf[pw][ks].get(cc, 1) * wv.y,
-                               xf[pw][ks].get(cc, 2) * wv.z, xf[pw][ks].get(cc, 3) * wv.w);
+                for (int pw = 0; pw < PW; ++pw) {
+                    const float v0 = xf[pw][ks].get(cc, 0) * wv.x, v1 = xf[pw][ks].get(cc, 1) * wv.y;
+                    const float v2 = xf[pw][ks].get(cc, 2) * wv.z, v3 = xf[pw][ks].get(cc, 3) * wv.w;
+                    xw[pw].set(cc, v0, v1, v2, v3);
+                    if constexpr (kSplitM)
+                        xl[pw].set(cc, v0 - xw[pw].get(cc, 0), v1 - xw[pw].get(cc, 1), v2 - xw[pw].get(cc, 2),
+                                   v3 - xw[pw].get(cc, 3));
+                }
             }
 #pragma unroll
             for (int nb = 0; nb < Cf::NNB; ++nb) {
-                const Frag<T> bf = frag_col<T>(Bs, BST, 32 * ks, Q, nb * 16, q, li);
+                const Frag<T> bf = frag_col<T, UB>(Bs, 32 * ks, Q, nb * 16, q, li);
 #pragma unroll
-                for (int pw = 0; pw < PW; ++pw) mfma(accS[pw][nb], bf, xw[pw]);
+                for (int pw = 0; pw < PW; ++pw) {
+                    mfma(accS[pw][nb], bf, xw[pw]);
+                    if constexpr (kSplitM) mfma(accS[pw][nb], bf, xl[pw]);
+                }
             }
         }
-        __syncthreads();  // LDS tiles free for the next chunk
+        wait_vmem<kStores>();  // this wave's pieces of chunk i+1 are in LDS (the y stores may still drain)
+        __syncthreads();       // chunk i+1 published, chunk i's buffer free
     }
 
-    // ---- write the state: S[p][n..n+3] per lane
+    // ---- write the state S = e^sig S_hat: S[p][n..n+3] per lane
+    if (stats_writer && lane == 0) sSig[hw] = sig;
+    __syncthreads();
+    const float escale = fast_exp(sSig[hw]);
     float* dst = nullptr;
     if (kStateOnly) dst = k.ws_state + ((int64_t)seg * BH + bh) * P * N;
     else if (seg == k.nseg - 1) dst = k.state_out ? k.state_out + (int64_t)bh * P * N : nullptr;
@@ -577,7 +699,7 @@ void ssd_chunk_scan_kernel(ScanK k)
             const int p = (pblk0 + pw) * 16 + li;
 #pragma unroll
             for (int nb = 0; nb < Cf::NNB; ++nb) {
-                const f32x4 v = accS[pw][nb];
+                const f32x4 v = accS[pw][nb] * escale;
                 *reinterpret_cast<float4*>(dst + (int64_t)p * N + nb * 16 + 4 * q) =
                     make_float4(v[0], v[1], v[2], v[3]);
             }
@@ -625,24 +747,14 @@ struct Plan {
     size_t ws_bytes;
 };
 
-// Heads per block for the (P, N) work split (see Cfg).
-static int heads_per_block(int P, int N) {
-    const int npb = P / 16, nnb = N / 16;
-    const int cap = kStateTiles / nnb > 0 ? kStateTiles / nnb : 1;
-    int pw = npb < cap ? npb : cap;
-    pw = pw > npb / 4 ? pw : npb / 4;
-    return 4 / (npb / pw);
-}
-
-static Plan plan_for(int64_t batch, int64_t L, int H, int G, int P, int N, int Q) {
+// Segments: enough (sequence, head group, segment) units for one round of resident blocks.
+static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, int hpw, int bpc) {
     Plan pl;
     const int64_t nchunks = (L + Q - 1) / Q;
-    const int hpw = heads_per_block(P, N);
     const int hpg = H / G;
     pl.nhu = G * ((hpg + hpw - 1) / hpw);
     const int64_t units = batch * pl.nhu;
-    // one round of resident blocks: two per compute unit on 256 CUs
-    const int64_t target = 512;
+    const int64_t target = 256 * (int64_t)bpc;  // 256 compute units
     int64_t nseg = units > 0 ? target / units : 1;
     if (nseg > nchunks) nseg = nchunks;
     if (nseg < 1) nseg = 1;
@@ -650,13 +762,20 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int G, int P, int N, int Q
     nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
     pl.nseg = (int)nseg;
     pl.cps = (int)cps;
-    pl.ws_bytes = nseg > 1 ? (size_t)(nseg * batch * H) * ((size_t)P * N + 1) * sizeof(float) + 256 : 0;
+    pl.ws_bytes = nseg > 1 ? (size_t)(nseg * batch * H) * ((size_t)N_P_N + 1) * sizeof(float) + 256 : 0;
     return pl;
 }
 
 template <typename T, int Q, int P, int N>
+static Plan plan_of(int64_t batch, int64_t L, int H, int G) {
+    using Cf = Cfg<T, Q, P, N>;
+    return plan_for(batch, L, H, G, P * N, Q, Cf::HPW, Cf::BPC);
+}
+
+template <typename T, int Q, int P, int N>
 static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
-    const Plan pl = plan_for(a.batch, a.L, a.H, a.G, a.P, a.N, Q);
+    using Cf = Cfg<T, Q, P, N>;
+    const Plan pl = plan_of<T, Q, P, N>(a.batch, a.L, a.H, a.G);
     ScanK k;
     k.x = a.x; k.B = a.B; k.C = a.C; k.dt = a.dt;
     k.xs = a.xs; k.bcs = a.bcs; k.dts = a.dts; k.ys = a.ys;
@@ -664,6 +783,13 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     k.state_in = a.state_in; k.state_out = a.state_out; k.y = a.y;
     k.L = a.L; k.batch = (int)a.batch; k.H = a.H; k.G = a.G;
     k.nseg = pl.nseg; k.cps = pl.cps;
+    // buffer-resource windows: every byte offset inside one must stay below 2^31
+    int64_t row_bytes = a.xs > a.bcs ? a.xs : a.bcs;
+    row_bytes = row_bytes > a.dts ? row_bytes : a.dts;
+    row_bytes = (row_bytes > a.ys ? row_bytes : a.ys) * (int64_t)sizeof(T);
+    const int64_t win = (((int64_t)1 << 31) - 1) / ((int64_t)Q * row_bytes) - 3;
+    if (win < 1) return hipErrorInvalidValue;
+    k.win = (int)(win < pl.cps ? win : pl.cps);
     const int BH = (int)(a.batch * a.H);
     k.ws_state = nullptr;
     k.ws_lam = nullptr;
@@ -675,7 +801,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     const int per_seg = (int)a.batch * pl.nhu;
     if (pl.nseg > 1) {
         k.nblocks = (pl.nseg - 1) * per_seg;
-        e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, true>, dim3(k.nblocks), dim3(kScanThreads), 0, s, k);
+        e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, true>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
         if (e != hipSuccess) return e;
         dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH);
         e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, a.state_in, k.ws_state,
@@ -683,7 +809,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     k.nblocks = pl.nseg * per_seg;
-    return launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(kScanThreads), 0, s, k);
+    return launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
 }
 
 template <typename T, int Q>
@@ -708,8 +834,30 @@ bool ssd_scan_supported(int P, int N, int Q, bool bf16) {
 
 int ssd_scan_default_chunk(int, int, bool) { return 32; }
 
-size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool) {
-    return plan_for(batch, L, H, G, P, N, Q).ws_bytes;
+template <typename T, int Q>
+static size_t workspace_pn(int64_t batch, int64_t L, int H, int P, int N, int G) {
+#define M2_PN(PP, NN) if (P == PP && N == NN) return plan_of<T, Q, PP, NN>(batch, L, H, G).ws_bytes;
+    M2_PN(16, 16) M2_PN(16, 32) M2_PN(16, 64) M2_PN(32, 16) M2_PN(32, 32) M2_PN(32, 64)
+    M2_PN(64, 16) M2_PN(64, 32) M2_PN(64, 64) M2_PN(64, 128)
+    if constexpr (sizeof(T) == 2) {
+        M2_PN(128, 64) M2_PN(128, 128)
+    }
+#undef M2_PN
+    return 0;
+}
+
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16) {
+    if (bf16) {
+        switch (Q) {
+            case 16: return workspace_pn<bf16_t, 16>(batch, L, H, P, N, G);
+            case 32: return workspace_pn<bf16_t, 32>(batch, L, H, P, N, G);
+            default: return workspace_pn<bf16_t, 64>(batch, L, H, P, N, G);
+        }
+    }
+    switch (Q) {
+        case 16: return workspace_pn<float, 16>(batch, L, H, P, N, G);
+        default: return workspace_pn<float, 32>(batch, L, H, P, N, G);
+    }
 }
 
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s) {
