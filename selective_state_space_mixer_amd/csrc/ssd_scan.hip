@@ -270,10 +270,12 @@ struct Cfg {
     // LDS units (16 bytes) of one buffer: X tiles of hpw heads, then B and C (rows padded by a unit)
     static constexpr int x_units(int hpw) { return round_kb(hpw * Q * (UX + 1)); }
     static constexpr int b_units() { return round_kb(Q * (UB + 1)); }
+    // a wave's y tile on its way out: Q rows of PW*16 elements
+    static constexpr int YRB = PW * 16 * (int)sizeof(E);  // bytes per row
     static constexpr int lds_bytes(int hpw) {
-        return 2 * (16 * (x_units(hpw) + 2 * b_units()) + (kStats * Q + 1) * hpw * 4);
+        return 2 * (16 * (x_units(hpw) + 2 * b_units()) + (kStats * Q + 1) * hpw * 4) + hpw * WPH * Q * YRB;
     }
-    static constexpr int kLdsBudget = sizeof(E) == 2 ? 72 * 1024 : 150 * 1024;
+    static constexpr int kLdsBudget = sizeof(E) == 2 ? 80 * 1024 : 150 * 1024;
     static constexpr int hpw_fit() {
         int hpw = kScanWaves / WPH > 0 ? kScanWaves / WPH : 1;
         while (hpw > 1 && lds_bytes(hpw) > kLdsBudget) hpw /= 2;
@@ -318,12 +320,21 @@ ssd_chunk_scan_kernel(ScanK k)
     __shared__ float sLamEnd[2][HPW]; // summed log-decay of the chunk
     __shared__ float sSig[HPW];       // log-scale of the stored state at the end of the walk
     __shared__ uint64_t sBase[Cf::WAVES][5];  // x, B, C, dt, y addresses at the segment's first row
+    // Each wave's y tile is staged here so that it leaves in 16-byte pieces, consecutive lanes
+    // covering consecutive bytes of a row (the accumulator layout gives each lane 4 elements of
+    // one row, with the lanes of a row 16 apart).  16-byte unit u of row r sits at u ^ (r % YU).
+    constexpr int YRB = Cf::YRB, YU = YRB / 16;         // bytes and 16-byte units per staged row
+    constexpr int YRPS = 64 / YU;                       // rows per store instruction
+    constexpr int NYS = kStateOnly ? 0 : (Q + YRPS - 1) / YRPS;  // store instructions per chunk
+    __shared__ __attribute__((aligned(16))) uint8_t sY[kStateOnly ? 16 : Cf::WAVES * Q * YRB];
 
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hw = wave / Cf::WPH;                  // head slot of this wave
-    const int pblk0 = (wave % Cf::WPH) * PW;        // first p-block of this wave
-    const bool stats_writer = (wave % Cf::WPH) == 0;
+    // Waves w, w + HPW, w + 2 HPW, ... share head slot w % HPW, so the heads' statistics writers
+    // (waves 0 .. HPW-1) sit on different SIMDs.
+    const int hw = wave % HPW;                      // head slot of this wave
+    const int pblk0 = (wave / HPW) * PW;            // first p-block of this wave
+    const bool stats_writer = wave < HPW;
 
     // logical unit -> (segment, sequence, head group)
     const int unit = logical_block(k.nblocks);
@@ -464,7 +475,12 @@ ssd_chunk_scan_kernel(ScanK k)
         const float dtv = lane < valid ? dt_of(raw_to_f32(raw, (T*)nullptr), bias_h, k.dt_min, k.dt_max) : 0.0f;
         const float lam = wave_prefix_sum(dtv * A_h);
         const float lam_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), Q - 1));
-        const float lam_blk = __shfl(lam, lane | 15, 64);  // at the last token of this lane's 16-block
+        // log-decay at the last token of this lane's 16-block
+        const float l15 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), 15));
+        const float l31 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), 31));
+        const float l47 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), 47));
+        const float l63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), 63));
+        const float lam_blk = lane < 16 ? l15 : lane < 32 ? l31 : lane < 48 ? l47 : l63;
         const float sig_prev = sig;
         const bool rescale = sig_prev + lam_end < -kRescale;
         // token weight e^(Lam_end - Lam_s) dt_s / e^sig_new, sig_new = 0 (rescale) or sig_prev + Lam_end
@@ -496,7 +512,7 @@ ssd_chunk_scan_kernel(ScanK k)
     wait_vmem<0>();
     __syncthreads();
     // y stores issued per chunk: the end-of-chunk wait lets them drain in the background
-    constexpr int kStores = kStateOnly ? 0 : Cf::NTB * PW;
+    constexpr int kStores = NYS;
     for (int i = 0; i < nc; ++i) {
         const int buf = i & 1;
         if (i - wbase == k.win) rebase(i);  // chunks i .. i+2 are addressed from here on
@@ -562,6 +578,7 @@ ssd_chunk_scan_kernel(ScanK k)
             // output rows of this chunk and head; rows past the sequence (and waves without a
             // head) fall outside the range of ry and are not written
             const uint32_t yrow = (uint32_t)((i - wbase) * Q);
+            uint8_t* const ystage = &sY[wave * Q * YRB];
 #pragma unroll
             for (int tb = 0; tb < Cf::NTB; ++tb) {
                 const int t = tb * 16 + li;
@@ -638,11 +655,25 @@ ssd_chunk_scan_kernel(ScanK k)
                         if constexpr (kSplitM) mfma(accY[tb][pw], xf[pw][ks], ml);
                     }
                 }
-                // store: the lane holds y[t][p = (pblk0+pw)*16 + 4q .. +3]
+                // stage: the lane holds y[t][p = (pblk0+pw)*16 + 4q .. +3]
 #pragma unroll
-                for (int pw = 0; pw < PW; ++pw)
-                    store4(ry, ((yrow + t) * (uint32_t)ys + (pblk0 + pw) * 16 + 4 * q) * SZ, (T*)nullptr,
-                           accY[tb][pw]);
+                for (int pw = 0; pw < PW; ++pw) {
+                    const int b = (pw * 16 + 4 * q) * (int)SZ;  // byte offset in this wave's row share
+                    uint8_t* const dst = ystage + t * YRB + ((b >> 4) ^ (t % YU)) * 16 + (b & 15);
+                    const f32x4 a = accY[tb][pw];
+                    if constexpr (sizeof(E) == 2)
+                        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                    else
+                        *reinterpret_cast<f32x4*>(dst) = a;
+                }
+            }
+            // out to HBM: lane L takes 16-byte unit L % YU of row j*YRPS + L / YU
+#pragma unroll
+            for (int j = 0; j < NYS; ++j) {
+                const int r = j * YRPS + lane / YU, u = lane % YU;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ystage + (r < Q ? r : 0) * YRB + (u ^ (r % YU)) * 16);
+                const uint32_t off = r < Q ? ((yrow + r) * (uint32_t)ys + pblk0 * 16) * SZ + u * 16 : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)off, 0, 0);
             }
         }
 
@@ -705,7 +736,7 @@ ssd_chunk_scan_kernel(ScanK k)
             }
         }
     }
-    if (kStateOnly && hvalid && (wave % Cf::WPH) == 0 && lane == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+    if (kStateOnly && hvalid && stats_writer && lane == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
 }
 
 // Chain the segments: S_in[seg+1] = exp(lam[seg]) * S_in[seg] + S_end_local[seg], written over
