@@ -50,6 +50,8 @@ def _load():
         lib.oracle_ssd_step.restype = None
         lib.oracle_softplus.argtypes = [f64]
         lib.oracle_softplus.restype = f64
+        lib.oracle_gated_rmsnorm.argtypes = [i64, i64, i64, dp, dp, dp, f64, i64, dp]
+        lib.oracle_gated_rmsnorm.restype = None
         _lib = lib
     return _lib
 
@@ -69,6 +71,21 @@ def _p(a):
 
 def softplus(v: float) -> float:
     return _load().oracle_softplus(float(v))
+
+
+def gated_rmsnorm(y, z, w, group_size: int, eps: float = 1e-5, norm_before_gate: bool = False):
+    """Gated group RMSNorm (m2_oracle.c, "norm").  y, z [..., D], w [D] -> out [..., D]."""
+    y = _f64(y)
+    lead, D = y.shape[:-1], y.shape[-1]
+    if D % group_size:
+        raise ValueError("oracle: D %d is not a multiple of group_size %d" % (D, group_size))
+    z = _f64(z, y.shape)
+    w = _f64(w, (D,))
+    T = int(np.prod(lead)) if lead else 1
+    out = np.empty_like(y)
+    _load().oracle_gated_rmsnorm(T, D, group_size, _p(y), _p(z), _p(w), float(eps), int(bool(norm_before_gate)),
+                                 _p(out))
+    return out
 
 
 def conv1d(x, w, bias=None, ring_in=None, ring_in_step: int = 0, want_ring: bool = True):

@@ -19,6 +19,11 @@
  *           y_t = S_t . C_t + D_h * x_t
  *   step    the same for one token, with the conv window taken from a ring of the
  *           last W tokens (the cache of conv state + recurrent state, §三)
+ *   norm    the gated group RMSNorm after the scan (§三 "门控归一化": group RMSNorm times
+ *           SiLU of the gate z, over intermediate_size in groups; eps from §五 rms_norm_eps):
+ *             gate first (norm_before_gate = 0):  g = y * SiLU(z),
+ *                                                 out = g / sqrt(mean_group(g^2) + eps) * w
+ *             norm first (norm_before_gate = 1):  out = y / sqrt(mean_group(y^2) + eps) * w * SiLU(z)
  *
  * Everything is evaluated in double precision, sequentially in t, straight
  * from the definitions: no chunking, no blocking, no reordering.  OpenMP only
@@ -193,3 +198,28 @@ void oracle_ssd_step(int64_t Bn, int64_t H, int64_t P, int64_t N, int64_t G, int
 
 /* Softplus as the oracle evaluates it, exported so its pin can call it directly. */
 double oracle_softplus(double v) { return softplus(v); }
+
+/* Gated group RMSNorm over rows of D channels, in groups of GS consecutive channels.
+ * y, z, out [T, D]; w [D]. */
+void oracle_gated_rmsnorm(int64_t T, int64_t D, int64_t GS, const double* y, const double* z, const double* w,
+                          double eps, int64_t norm_before_gate, double* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t g0 = 0; g0 < D; g0 += GS) {
+            const double* yr = y + t * D + g0;
+            const double* zr = z + t * D + g0;
+            double ss = 0.0;
+            for (int64_t c = 0; c < GS; ++c) {
+                const double v = norm_before_gate ? yr[c] : yr[c] * silu(zr[c]);
+                ss += v * v;
+            }
+            const double r = 1.0 / sqrt(ss / (double)GS + eps);
+            for (int64_t c = 0; c < GS; ++c) {
+                const double v = norm_before_gate ? yr[c] * r * w[g0 + c] * silu(zr[c])
+                                                  : yr[c] * silu(zr[c]) * r * w[g0 + c];
+                out[t * D + g0 + c] = v;
+            }
+        }
+    }
+}

@@ -399,3 +399,57 @@ def test_max_rel_err_metric():
     rms = np.sqrt(np.mean(ref ** 2))
     got = ref + np.array([0.01, 0.0, 0.02, 0.0])
     assert oracle.max_rel_err(got, ref) == pytest.approx(max(0.01 / 1.0, 0.02 / rms))
+
+
+# ----------------------------------------------------------------------------- gated group RMSNorm
+# Zamba2 article §三 (group RMSNorm times SiLU of the gate after the scan), §五 (rms_norm_eps 1e-5).
+
+def test_gated_rmsnorm_by_hand():
+    # two groups of two; z = ln 3 gives sigmoid(z) = 3/4, so SiLU(z) = 0.75 ln 3 exactly
+    y = np.array([[3.0, 4.0, 1.0, -2.0]])
+    z = np.full((1, 4), np.log(3.0))
+    w = np.array([1.0, 2.0, -1.0, 0.5])
+    s = 0.75 * np.log(3.0)
+    nb = oracle.gated_rmsnorm(y, z, w, 2, eps=0.0, norm_before_gate=True)
+    want = np.array([3 / np.sqrt(12.5), 2 * 4 / np.sqrt(12.5), -1 / np.sqrt(2.5), 0.5 * -2 / np.sqrt(2.5)]) * s
+    np.testing.assert_allclose(nb[0], want, rtol=1e-14)
+    # gate first with a common gate: SiLU(z) cancels inside each group's normalisation
+    gf = oracle.gated_rmsnorm(y, z, w, 2, eps=0.0, norm_before_gate=False)
+    np.testing.assert_allclose(gf[0], want / s, rtol=1e-14)
+
+
+def test_gated_rmsnorm_eps_placement():
+    # y = (1, 1), gate first with SiLU = 1 is impossible exactly, so take norm first with z -> large:
+    # out = y / sqrt(mean(y^2) + eps) * SiLU(z); mean(y^2) = 1, eps = 1 -> 1/sqrt(2) * SiLU(z)
+    y = np.ones((1, 2))
+    z = np.full((1, 2), 40.0)
+    out = oracle.gated_rmsnorm(y, z, np.ones(2), 2, eps=1.0, norm_before_gate=True)
+    np.testing.assert_allclose(out[0], 40.0 / (1.0 + np.exp(-40.0)) / np.sqrt(2.0), rtol=1e-14)
+
+
+def test_gated_rmsnorm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(7)
+    y, z = rng.standard_normal((5, 48)), rng.standard_normal((5, 48))
+    out = oracle.gated_rmsnorm(y, z, np.ones(48), 16, eps=0.0)
+    # every group of the gate-first output has unit mean square
+    np.testing.assert_allclose((out.reshape(5, 3, 16) ** 2).mean(-1), 1.0, rtol=1e-12)
+    # and the output does not change when y is scaled by a positive factor
+    np.testing.assert_allclose(oracle.gated_rmsnorm(3.5 * y, z, np.ones(48), 16, eps=0.0), out, rtol=1e-12)
+    # norm first: scaling y leaves it unchanged too, and the gate multiplies elementwise
+    nb = oracle.gated_rmsnorm(y, z, np.ones(48), 16, eps=0.0, norm_before_gate=True)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(0.25 * y, z, np.ones(48), 16, eps=0.0, norm_before_gate=True),
+                               nb, rtol=1e-12)
+
+
+def test_gated_rmsnorm_groups_are_independent_and_zero_gate():
+    rng = np.random.default_rng(8)
+    y, z, w = rng.standard_normal((2, 32)), rng.standard_normal((2, 32)), rng.standard_normal(32)
+    a = oracle.gated_rmsnorm(y, z, w, 8)
+    y2 = y.copy()
+    y2[:, 8:16] *= 100.0
+    b = oracle.gated_rmsnorm(y2, z, w, 8)
+    np.testing.assert_array_equal(np.delete(a, np.s_[8:16], 1), np.delete(b, np.s_[8:16], 1))
+    # SiLU(0) = 0: a zero gate zeroes the output in both orders (eps keeps it finite)
+    zero = np.zeros_like(z)
+    assert not np.any(oracle.gated_rmsnorm(y, zero, w, 8))
+    assert not np.any(oracle.gated_rmsnorm(y, zero, w, 8, norm_before_gate=True))
