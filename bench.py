@@ -88,7 +88,8 @@ def time_events(torch, fns, steps, warmup):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"ssd_scan": "ssd_scan.hip", "conv1d": "conv1d.hip", "ssd_step": "ssd_step.hip"}
+KERNEL_SOURCES = {"ssd_scan": "ssd_scan.hip", "conv1d": "conv1d.hip", "ssd_step": "ssd_step.hip",
+                  "gated_rmsnorm": "gated_norm.hip"}
 
 
 def source_digest(kernel):
@@ -160,6 +161,26 @@ def bench_prefill(torch, m2, workloads, args):
                    "headdim": P, "d_state": N, "n_groups": G, "d_conv": W,
                    "chunk_size": d.chunk_size or "library default", "state": "fp32, zero initial, final returned"},
     }
+
+
+def bench_norm(torch, m2, workloads, args):
+    """Gated group RMSNorm on the 32k prefill output (2.7B shape: 32768 rows of d_inner 5120, one group)."""
+    T, D = 32768, 5120
+    y, z, w = workloads.norm_inputs(T, D, 3200, "bf16")
+    bf = torch.bfloat16
+    yt, zt = torch.from_numpy(y).to("cuda", bf), torch.from_numpy(z).to("cuda", bf)
+    wt = torch.from_numpy(w).cuda()
+    ot = torch.empty_like(yt)
+    del y, z
+
+    def norm():
+        m2.m2_gated_rmsnorm(yt, zt, wt, ot, D, eps=1e-5)
+
+    (t,), _, _ = time_events(torch, [norm], args.steps, args.warmup)
+    nbytes = 3 * T * D * 2 + D * 4
+    return {"us": round(t * 1e3, 2), "bytes": nbytes, "roofline": roofline(nbytes, t, "gated_rmsnorm"),
+            "config": {"workload": "gated group RMSNorm of the 32k prefill output (gate first)", "rows": T,
+                       "d_inner": D, "group_size": D, "eps": 1e-5}}
 
 
 def bench_decode(torch, m2, workloads, args):
@@ -292,6 +313,11 @@ def main():
                                       "frac": v["roofline"]["frac"], "achieved_GBs": v["roofline"]["achieved"]}
                                   for n, v in k.items()}
         out["prefill_path_roofline_frac"] = pre["path_roofline_frac"]
+    if args.only in ("all", "prefill"):
+        nrm = bench_norm(torch, m2, workloads, args)
+        print("gated rmsnorm: %.1f us (%.0f GB/s)" % (nrm["us"], nrm["roofline"]["achieved"]), file=sys.stderr,
+              flush=True)
+        out["epilogue"] = {"gated_rmsnorm": nrm}
     if args.only in ("all", "decode"):
         dec = bench_decode(torch, m2, workloads, args)
         print("decode: %.1f us/step, %.3e tok/s" % (dec["ms_per_step"] * 1e3, dec["tokens_per_s"]),

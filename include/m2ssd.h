@@ -1,9 +1,9 @@
 /*
  * m2ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 mixer hot path.
  *
- * The three compute entry points are the steps that the Zamba2 article
- * ("Transformers 中 Zamba2 混合架构模型解析", §三 "Mamba2 Mixer") places between the
- * mixer's input projection and its gated norm:
+ * The compute entry points are the steps that the Zamba2 article ("Transformers 中 Zamba2
+ * 混合架构模型解析", §三 "Mamba2 Mixer") places between the mixer's input projection and
+ * its output projection:
  *
  *   m2_conv1d_fwd    causal depthwise conv1d of width mamba_d_conv, then SiLU,
  *                    over a prompt (groups = conv_dim; §五: use_conv_bias)
@@ -13,6 +13,7 @@
  *                    exists and the new sequence length is 1 (§三); it also
  *                    advances the cached conv state (§三: the cache holds each
  *                    layer's conv state and recurrent state)
+ *   m2_gated_rmsnorm the gated group RMSNorm applied to the scan's output (§三)
  *
  * The recurrence, per batch element b and head h, for t = 0..L-1:
  *     dt_t = softplus(dt_raw_t + dt_bias[h])        (then clamped to [dt_min, dt_max])
@@ -146,6 +147,27 @@ m2_status m2_ssd_step(const m2_dims* dims,
                       void* ring, int64_t step,
                       float* state, void* y,
                       void* stream);
+
+/* Gated group RMSNorm after the scan (article §三: group RMSNorm times SiLU of the gate z
+ * over intermediate_size, in groups; §五: eps = rms_norm_eps, 1e-5 in Zamba2):
+ *   norm_before_gate = 0:  g = y * SiLU(z),  out = g / sqrt(mean_group(g^2) + eps) * w
+ *   norm_before_gate = 1:  out = y / sqrt(mean_group(y^2) + eps) * w * SiLU(z)
+ * Each row holds d_inner channels, normalised in groups of group_size consecutive channels
+ * (Zamba2's norm uses d_inner / n_groups).
+ * ntok     rows: batch * seqlen after a prompt scan, batch after a decode step (0: no-op)
+ * y, z     [ntok, d_inner] io, row strides y_tok_stride, z_tok_stride (>= d_inner)
+ * w        [d_inner] fp32
+ * out      [ntok, d_inner] io, row stride out_tok_stride; may be y itself (same stride), but
+ *          must not otherwise overlap y, and must not overlap z
+ * group_size must divide d_inner and be a multiple of 16 bytes / element size, at most
+ * 8192 (bf16) or 4096 (fp32) channels; y, z, out, w and all strides 16-byte aligned
+ * (else M2_ERR_UNSUPPORTED). */
+m2_status m2_gated_rmsnorm(int64_t ntok, int32_t d_inner, int32_t group_size, int32_t io,
+                           const void* y, int64_t y_tok_stride,
+                           const void* z, int64_t z_tok_stride,
+                           const float* w, float eps, int32_t norm_before_gate,
+                           void* out, int64_t out_tok_stride,
+                           void* stream);
 
 /* Static text for a status code. */
 const char* m2_status_str(m2_status status);

@@ -26,7 +26,7 @@ M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, 
 M2_F32, M2_BF16 = 0, 1
 ABI_VERSION = 1
 
-EXPORTS = ("m2_conv1d_fwd", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd", "m2_ssd_step",
+EXPORTS = ("m2_conv1d_fwd", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd", "m2_ssd_step", "m2_gated_rmsnorm",
            "m2_status_str", "m2_abi_version", "m2_last_hip_error")
 
 
@@ -78,6 +78,9 @@ def _load() -> ctypes.CDLL:
     lib.m2_ssd_scan_fwd.restype = ctypes.c_int
     lib.m2_ssd_step.argtypes = [dp, vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, f32, vp, i64, vp, vp, vp]
     lib.m2_ssd_step.restype = ctypes.c_int
+    lib.m2_gated_rmsnorm.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp, i64, vp, f32,
+                                     ctypes.c_int32, vp, i64, vp]
+    lib.m2_gated_rmsnorm.restype = ctypes.c_int
     lib.m2_status_str.argtypes = [ctypes.c_int]
     lib.m2_status_str.restype = ctypes.c_char_p
     lib.m2_abi_version.argtypes = []
@@ -289,3 +292,53 @@ def m2_ssd_step(dims: M2Dims, xbc_tok, dt_tok, w, bias, dt_bias, A, D, ring, ste
     _call("m2_ssd_step", ctypes.byref(dims), _ptr(xbc_tok), xbs, _ptr(dt_tok), dts, _ptr(w), _ptr(bias),
           _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min), float(dt_max), _ptr(ring), int(step), _ptr(state),
           _ptr(y), _stream(stream))
+
+
+def _rows(t, name):
+    """(rows, row stride) of a [..., D] tensor whose leading dims form one evenly strided run of rows."""
+    if t.dim() < 1:
+        raise ValueError("%s: expected at least one dim" % name)
+    D = t.shape[-1]
+    rows = 1
+    for n in t.shape[:-1]:
+        rows *= n
+    if rows == 0 or D == 0:
+        return 0, max(D, 1)  # empty: strides carry no meaning
+    if t.stride(-1) != 1 and D > 1:
+        raise ValueError("%s: the last dim must be contiguous" % name)
+    if t.dim() == 1 or rows <= 1:
+        return rows, D
+    stride = t.stride(-2)
+    expect = stride
+    for i in range(t.dim() - 2, -1, -1):
+        if t.shape[i] > 1 and t.stride(i) != expect:
+            raise ValueError("%s: leading dims must be one evenly strided run of rows" % name)
+        expect *= t.shape[i]
+    return rows, stride
+
+
+def m2_gated_rmsnorm(y, z, w, out, group_size: int, eps: float = 1e-5, norm_before_gate: bool = False,
+                     stream=None) -> None:
+    """Gated group RMSNorm after the scan; see include/m2ssd.h.
+
+    y, z, out [..., d_inner] (bf16 or f32, same dtype; rows evenly strided, last dim contiguous);
+    w [d_inner] f32.  out may be y itself."""
+    torch = _torch()
+    io = y.dtype
+    if io not in (torch.bfloat16, torch.float32):
+        raise TypeError("y: expected bfloat16 or float32, got %s" % io)
+    for n, t in (("z", z), ("out", out)):
+        _check(t, n, io)
+    _check(y, "y", io)
+    _check(w, "w", torch.float32)
+    D = y.shape[-1]
+    if tuple(z.shape) != tuple(y.shape) or tuple(out.shape) != tuple(y.shape):
+        raise ValueError("y, z and out must have the same shape")
+    if not w.is_contiguous() or w.numel() != D:
+        raise ValueError("w must be contiguous [d_inner]")
+    ntok, ys = _rows(y, "y")
+    _, zs = _rows(z, "z")
+    _, os_ = _rows(out, "out")
+    _call("m2_gated_rmsnorm", int(ntok), int(D), int(group_size), M2_BF16 if io == torch.bfloat16 else M2_F32,
+          _ptr(y), ys, _ptr(z), zs, _ptr(w), float(eps), int(bool(norm_before_gate)), _ptr(out), os_,
+          _stream(stream))

@@ -201,4 +201,32 @@ m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stri
     return launched(m2::launch_ssd_step(a, (hipStream_t)stream));
 }
 
+m2_status m2_gated_rmsnorm(int64_t ntok, int32_t d_inner, int32_t group_size, int32_t io, const void* y,
+                           int64_t y_tok_stride, const void* z, int64_t z_tok_stride, const float* w, float eps,
+                           int32_t norm_before_gate, void* out, int64_t out_tok_stride, void* stream) {
+    if (io != M2_F32 && io != M2_BF16) return M2_ERR_DTYPE;
+    if (ntok < 0 || d_inner < 1 || group_size < 1 || d_inner % group_size) return M2_ERR_SHAPE;
+    if (!w) return M2_ERR_NULL;
+    if (std::isnan(eps) || eps < 0.0f) return M2_ERR_SHAPE;
+    const bool bf16 = io == M2_BF16;
+    const int esize = bf16 ? 2 : 4, epv = 16 / esize;
+    if (group_size % epv || group_size > m2::gated_rmsnorm_max_group(bf16)) return M2_ERR_UNSUPPORTED;
+    if (ntok == 0) return M2_OK;
+    if (!y || !z || !out) return M2_ERR_NULL;
+    if (y_tok_stride < d_inner || z_tok_stride < d_inner || out_tok_stride < d_inner) return M2_ERR_SHAPE;
+    const Range ry = span(y, ntok, y_tok_stride, d_inner, esize);
+    const Range rz = span(z, ntok, z_tok_stride, d_inner, esize);
+    const Range ro = span(out, ntok, out_tok_stride, d_inner, esize);
+    const bool in_place = out == y && out_tok_stride == y_tok_stride;
+    if (overlap(ro, rz) || (!in_place && overlap(ro, ry))) return M2_ERR_ALIAS;
+    if (!aligned16(y) || !aligned16(z) || !aligned16(out) || !aligned16(w) || (y_tok_stride * esize) % 16 ||
+        (z_tok_stride * esize) % 16 || (out_tok_stride * esize) % 16)
+        return M2_ERR_UNSUPPORTED;
+    m2::NormArgs a;
+    a.ntok = ntok; a.d_inner = d_inner; a.gs = group_size;
+    a.y = y; a.ys = y_tok_stride; a.z = z; a.zs = z_tok_stride; a.w = w; a.eps = eps;
+    a.norm_before_gate = norm_before_gate != 0; a.out = out; a.os = out_tok_stride; a.bf16 = bf16;
+    return launched(m2::launch_gated_rmsnorm(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

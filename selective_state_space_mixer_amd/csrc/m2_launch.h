@@ -45,6 +45,18 @@ struct StepArgs {
     bool bf16;
 };
 
+struct NormArgs {
+    int64_t ntok;
+    int d_inner, gs;
+    const void* y; int64_t ys;
+    const void* z; int64_t zs;
+    const float* w;
+    float eps;
+    bool norm_before_gate;
+    void* out; int64_t os;
+    bool bf16;
+};
+
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s);
 size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16);
@@ -52,6 +64,8 @@ bool ssd_scan_supported(int P, int N, int Q, bool bf16);
 int ssd_scan_default_chunk(int P, int N, bool bf16);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
 bool ssd_step_supported(int P, int N);
+hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
+int gated_rmsnorm_max_group(bool bf16);
 
 }  // namespace m2
 

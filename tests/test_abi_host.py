@@ -135,3 +135,25 @@ def test_step_validation():
     assert step(dims(d_state=24, d_model=2560)) == m2.M2_ERR_UNSUPPORTED
     assert step(dims(), y=FAKE + 0x4000000 + 64) == m2.M2_ERR_ALIAS           # y overlaps ring
     assert step(dims(), state=FAKE + 0x1_0000_0008) == m2.M2_ERR_UNSUPPORTED  # misaligned state
+
+
+def norm(ntok=4, D=5120, gs=5120, io=m2.M2_BF16, y=FAKE, ys=None, z=FAKE + 0x1000_0000, zs=None,
+         w=FAKE + 0x2000_0000, eps=1e-5, nbg=0, out=FAKE + 0x3000_0000, os_=None):
+    return m2.lib().m2_gated_rmsnorm(ntok, D, gs, io, y, ys or D, z, zs or D, w, eps, nbg, out, os_ or D, None)
+
+
+def test_gated_rmsnorm_validation():
+    assert norm(io=5) == m2.M2_ERR_DTYPE
+    assert norm(ntok=-1) == m2.M2_ERR_SHAPE
+    assert norm(gs=3000) == m2.M2_ERR_SHAPE                     # does not divide d_inner
+    assert norm(eps=-1.0) == m2.M2_ERR_SHAPE
+    assert norm(eps=float("nan")) == m2.M2_ERR_SHAPE
+    assert norm(w=None) == m2.M2_ERR_NULL
+    assert norm(y=None) == m2.M2_ERR_NULL
+    assert norm(ntok=0, y=None, z=None, out=None) == m2.M2_OK    # nothing to do
+    assert norm(ys=5000) == m2.M2_ERR_SHAPE
+    assert norm(D=5124, gs=1281) == m2.M2_ERR_UNSUPPORTED        # not a whole number of 16-byte pieces
+    assert norm(D=16384, gs=16384) == m2.M2_ERR_UNSUPPORTED      # group longer than the kernel holds
+    assert norm(out=FAKE + 0x1000_0000 + 256) == m2.M2_ERR_ALIAS  # out overlaps z
+    assert norm(out=FAKE + 64) == m2.M2_ERR_ALIAS                # out overlaps y without being y
+    assert norm(y=FAKE + 8) == m2.M2_ERR_UNSUPPORTED             # misaligned

@@ -364,3 +364,51 @@ def test_full_size_decode_b256_sampled():
             assert oracle.max_rel_err(ys[t, b:b + 1], yr) <= 2e-2
         assert oracle.max_rel_err(state[b:b + 1], r_state) <= 2e-2
         np.testing.assert_array_equal(ring[b:b + 1], r_ring)
+
+
+# ----------------------------------------------------------------------------- gated group RMSNorm
+
+NORM_CASES = [
+    # (io, rows, d_inner, group_size, norm_before_gate, mode)
+    ("bf16", 64, 5120, 5120, False, "plain"),     # Zamba2-2.7B: one group over d_inner
+    ("bf16", 64, 5120, 5120, True, "plain"),
+    ("bf16", 37, 1536, 1536, False, "strided"),   # 130m-like d_inner, rows inside a wider buffer
+    ("bf16", 9, 5120, 1280, True, "in_place"),    # four groups, out written over y
+    ("f32", 33, 256, 64, False, "plain"),         # groups smaller than a wave's row
+    ("f32", 5, 96, 24, True, "strided"),          # six pieces per group
+    ("bf16", 0, 5120, 5120, False, "plain"),      # no rows
+]
+
+
+@pytest.mark.parametrize("case", NORM_CASES, ids=lambda c: "%s-%dx%d-g%d-nbg%d-%s" % c)
+def test_gated_rmsnorm_parity(case):
+    _need_gpu()
+    io, T, D, gs, nbg, mode = case
+    y, z, w = workloads.norm_inputs(T, D, 3000 + D + T, io)
+    if mode == "strided":
+        # y and z as column slices of one [T, 2D + 16] buffer (the gate and the scan output side by side)
+        buf = dev(np.concatenate([z, y, np.zeros((T, 16), np.float32)], 1), io)
+        zg, yg = buf[:, :D], buf[:, D:2 * D]
+    else:
+        yg, zg = dev(y, io), dev(z, io)
+    out = yg if mode == "in_place" else nan_like((T, D), io)
+    m2.m2_gated_rmsnorm(yg, zg, dev32(w), out, gs, eps=1e-5, norm_before_gate=nbg)
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(y, z, w, gs, 1e-5, nbg)
+    if T > 0:
+        assert oracle.max_rel_err(host(out), ref) <= tol_for(io)
+
+
+def test_full_size_gated_rmsnorm_32k_sampled():
+    """The whole 32k-token prefill output at the 2.7B shape; sampled rows against the oracle."""
+    _need_gpu()
+    T, D = 32768, 5120
+    y, z, w = workloads.norm_inputs(T, D, 3100, "bf16")
+    out = nan_like((T, D), "bf16")
+    m2.m2_gated_rmsnorm(dev(y, "bf16"), dev(z, "bf16"), dev32(w), out, D)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4095, 17000, 32767])
+    got = host(out[torch.from_numpy(rows).cuda()])
+    ref = oracle.gated_rmsnorm(y[rows], z[rows], w, D)
+    assert oracle.max_rel_err(got, ref) <= 2e-2
+    assert not torch.isnan(out.float()).any().item()

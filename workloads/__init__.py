@@ -174,3 +174,13 @@ def config_inputs(index: int, dims: Optional[Dims] = None) -> Inputs:
 def bf16_storage(a: np.ndarray) -> np.ndarray:
     """uint16 bf16 storage of an array whose values are bf16-representable."""
     return bf16_bits(a)
+
+
+def norm_inputs(ntok: int, d_inner: int, seed: int, io: str):
+    """Inputs of the gated group RMSNorm: y shaped like a scan output, z like the gate half of the
+    input projection (both ~N(0,1)), and a weight near one (1 + 0.1 N(0,1), fp32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    y = rng.standard_normal((ntok, d_inner), dtype=np.float32)
+    z = rng.standard_normal((ntok, d_inner), dtype=np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(d_inner, dtype=np.float32)).astype(np.float32)
+    return round_to(y, io), round_to(z, io), w
