@@ -223,6 +223,7 @@ struct ScanK {
     void* y;
     float* ws_state;   // [nseg][batch*H][P*N]: segment end states, then segment initial states
     float* ws_lam;     // [nseg][batch*H]: summed log-decay of each segment
+    float* ws_lamc;    // [nchunks][batch*H]: summed log-decay of the chunk's segment before the chunk
     int64_t L;
     int batch, H, G;
     int nseg, cps;     // segments per sequence, chunks per segment
@@ -384,11 +385,10 @@ ssd_chunk_scan_kernel(ScanK k)
     // state tiles in accumulator layout: accS[pw][nb][j] = S[p = (pblk0+pw)*16 + li][n = nb*16 + 4q + j]
     f32x4 accS[PW][Cf::NNB];
     {
+        // the first segment starts from the caller's state; later ones from zero (their true
+        // initial state is added to their output afterwards, see ssd_segment_fix_kernel)
         const float* src = nullptr;
-        if (!kStateOnly) {
-            if (seg == 0) src = k.state_in ? k.state_in + (int64_t)bh * P * N : nullptr;
-            else src = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
-        }
+        if (!kStateOnly && seg == 0) src = k.state_in ? k.state_in + (int64_t)bh * P * N : nullptr;
 #pragma unroll
         for (int pw = 0; pw < PW; ++pw) {
             const int p = (pblk0 + pw) * 16 + li;
@@ -486,6 +486,7 @@ ssd_chunk_scan_kernel(ScanK k)
         // token weight e^(Lam_end - Lam_s) dt_s / e^sig_new, sig_new = 0 (rescale) or sig_prev + Lam_end
         const float wexp = rescale ? lam_end - lam : -(sig_prev + lam);
         sig = rescale ? 0.0f : sig_prev + lam_end;
+        const float lam_before = lam_seg;  // summed log-decay of the segment before chunk i
         lam_seg += lam_end;
         if (lane < Q) {
             float* st = &sSt[buf][hw * Q + lane];
@@ -498,6 +499,7 @@ ssd_chunk_scan_kernel(ScanK k)
         if (lane == 0) {
             sDec[buf][hw] = rescale ? fast_exp(sig_prev + lam_end) : 1.0f;
             sLamEnd[buf][hw] = lam_end;
+            if (k.ws_lamc && hvalid) k.ws_lamc[(c_begin + i) * BH + bh] = lam_before;
         }
     };
 
@@ -721,9 +723,10 @@ ssd_chunk_scan_kernel(ScanK k)
     if (stats_writer && lane == 0) sSig[hw] = sig;
     __syncthreads();
     const float escale = fast_exp(sSig[hw]);
+    // one segment: the final state; several: this segment's end state from its own start, for the chain
     float* dst = nullptr;
-    if (kStateOnly) dst = k.ws_state + ((int64_t)seg * BH + bh) * P * N;
-    else if (seg == k.nseg - 1) dst = k.state_out ? k.state_out + (int64_t)bh * P * N : nullptr;
+    if (k.nseg > 1) dst = k.ws_state + ((int64_t)seg * BH + bh) * P * N;
+    else dst = k.state_out ? k.state_out + (int64_t)bh * P * N : nullptr;
     if (dst && hvalid) {
 #pragma unroll
         for (int pw = 0; pw < PW; ++pw) {
@@ -736,35 +739,173 @@ ssd_chunk_scan_kernel(ScanK k)
             }
         }
     }
-    if (kStateOnly && hvalid && stats_writer && lane == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+    if (k.nseg > 1 && hvalid && stats_writer && lane == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
 }
 
-// Chain the segments: S_in[seg+1] = exp(lam[seg]) * S_in[seg] + S_end_local[seg], written over
-// S_end_local[seg] (so that segment seg+1 finds its initial state at index seg).  Only the
-// combine is sequential: the loads of a batch of segments are issued together.
-__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(const float* __restrict__ state_in,
-                                                                float* __restrict__ ws_state,
-                                                                const float* __restrict__ ws_lam, int BH, int nseg,
+// Chain the segments.  E[seg] is segment seg's end state from its own start (segment 0 starts from
+// the caller's state), lam[seg] its summed log-decay.  The true end states follow
+//   T[0] = E[0],  T[seg] = e^lam[seg] T[seg-1] + E[seg];
+// T[seg] (the initial state of segment seg+1) is written over E[seg], and T[nseg-1] is the final
+// state.  Only the combine is sequential: the loads of a batch of segments are issued together.
+__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restrict__ ws_state,
+                                                                const float* __restrict__ ws_lam,
+                                                                float* __restrict__ state_out, int BH, int nseg,
                                                                 int PN)
 {
     constexpr int kBatch = 16;
     const int bh = blockIdx.y;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= PN) return;
-    float s = state_in ? state_in[(int64_t)bh * PN + i] : 0.0f;
-    for (int seg0 = 0; seg0 + 1 < nseg; seg0 += kBatch) {
+    float s = 0.0f;
+    for (int seg0 = 0; seg0 < nseg; seg0 += kBatch) {
         float loc[kBatch], dec[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int seg = seg0 + j < nseg - 1 ? seg0 + j : nseg - 2;
+            const int seg = seg0 + j < nseg ? seg0 + j : nseg - 1;
             loc[j] = ws_state[((int64_t)seg * BH + bh) * PN + i];
             dec[j] = ws_lam[(int64_t)seg * BH + bh];
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            if (seg0 + j < nseg - 1) {
-                s = fast_exp(dec[j]) * s + loc[j];
-                ws_state[((int64_t)(seg0 + j) * BH + bh) * PN + i] = s;
+            const int seg = seg0 + j;
+            if (seg < nseg) {
+                s = (seg == 0 ? loc[j] : fast_exp(dec[j]) * s + loc[j]);
+                if (seg < nseg - 1) ws_state[((int64_t)seg * BH + bh) * PN + i] = s;
+                else if (state_out) state_out[(int64_t)bh * PN + i] = s;
+            }
+        }
+    }
+}
+
+// Add the part of each later segment's output that comes from its true initial state S_in (the
+// main pass ran it from zero):  y[t] += e^Lam_t (S_in . C_t),  Lam_t = the summed log-decay from the
+// segment's first token through t.  The factor only falls along the segment, so only a prefix of its
+// chunks needs the term: those whose starting factor is at least e^kFixCut (about 1e-9); past them
+// the term is below 1e-9 of |S_in . C_t|, far under the output's rounding.  One block per (run of
+// kFixWaves chunks, segment, head), runs first so that the leading chunks, which nearly always need
+// it, come first.  A block whose first chunk is past the prefix leaves at once (the starting
+// log-decays are left by the main pass); otherwise it brings S_in into LDS as bf16 once, and each
+// wave corrects one chunk of the run.
+constexpr float kFixCut = -20.8f;
+constexpr int kFixWaves = 4;  // waves per block (independent tasks)
+
+template <typename T, int Q, int P, int N>
+__global__ __launch_bounds__(64 * kFixWaves) void ssd_segment_fix_kernel(ScanK k)
+{
+    constexpr int NPB = P / 16, KS_N = (N + 31) / 32, NTB = Q / 16;
+    constexpr int EB = (int)sizeof(T);
+    using E = typename Lds<T>::E;
+    constexpr int SST = N + 16 / EB;  // LDS row stride of S_in (elements of the operand type)
+    __shared__ __attribute__((aligned(16))) E Ss[P * SST];
+    const int BH = k.batch * k.H;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t per_run = (int64_t)(k.nseg - 1) * BH;
+    const int run = (int)(blockIdx.x / per_run);
+    const int seg = 1 + (int)((blockIdx.x % per_run) / BH);
+    const int bh = (int)(blockIdx.x % BH);
+    const int64_t nchunks = (k.L + Q - 1) / Q;
+    const int64_t seg_end = (int64_t)(seg + 1) * k.cps < nchunks ? (int64_t)(seg + 1) * k.cps : nchunks;
+    const int64_t c_run = (int64_t)seg * k.cps + (int64_t)run * kFixWaves;  // first chunk of the run
+    if (c_run >= seg_end || !(k.ws_lamc[c_run * BH + bh] >= kFixCut)) return;  // whole block
+
+    // S_in -> rows [p][n] in LDS, in the operand type
+    const float* S = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
+    for (int e = threadIdx.x * 4; e < P * N; e += 64 * kFixWaves * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(S + e);
+        const int p = e / N, n = e % N;
+        if constexpr (EB == 2)
+            *reinterpret_cast<uint2*>(&Ss[p * SST + n]) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        else
+            *reinterpret_cast<float4*>(&Ss[p * SST + n]) = v;
+    }
+    __syncthreads();
+    const int64_t c = c_run + wave;
+    if (c >= seg_end) return;
+    const float lam0 = k.ws_lamc[c * BH + bh];  // the same address in every lane
+    if (!(lam0 >= kFixCut)) return;
+
+    const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
+    const int64_t b = bh / k.H;
+    const int h = bh % k.H, g = h / (k.H / k.G);
+    // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n]: rows p, k = n (chunks 4q.., 16+4q..)
+    Frag<T> sa[NPB][KS_N];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+        for (int ks = 0; ks < KS_N; ++ks)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int n0 = 32 * ks + 16 * cc + 4 * q;
+                if (n0 < N) {
+                    const E* src = &Ss[(pb * 16 + li) * SST + n0];
+                    if constexpr (EB == 2) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(src);
+                        sa[pb][ks].set(cc, __uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+                    } else {
+                        const float4 v = *reinterpret_cast<const float4*>(src);
+                        sa[pb][ks].set(cc, v.x, v.y, v.z, v.w);
+                    }
+                } else {
+                    sa[pb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
+                }
+            }
+    const float bias_h = k.dt_bias[h], A_h = k.A[h];
+    const int64_t t0 = c * Q;
+    const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+    const T* dtp = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
+    const uint8_t* cp = reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N);
+    uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P);
+
+    // log-decay through each token of the chunk
+    const float raw = to_f32(dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts]);
+    const float dtv = lane < valid ? dt_of(raw, bias_h, k.dt_min, k.dt_max) : 0.0f;
+    const float lam = lam0 + wave_prefix_sum(dtv * A_h);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        const int t = tb * 16 + li;
+        const bool ok = t < valid;
+        const int tr = ok ? t : valid - 1;  // rows past the sequence: loads clamped, stores skipped
+        const float el = fast_exp(__shfl(lam, t, 64));
+        Frag<T> cf[KS_N];
+#pragma unroll
+        for (int ks = 0; ks < KS_N; ++ks)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int n0 = 32 * ks + 16 * cc + 4 * q;
+                if (n0 < N) {
+                    const uint8_t* src = cp + ((t0 + tr) * k.bcs + n0) * EB;
+                    if constexpr (EB == 2) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(src);
+                        cf[ks].set(cc, __uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                                   __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+                    } else {
+                        const float4 v = *reinterpret_cast<const float4*>(src);
+                        cf[ks].set(cc, v.x, v.y, v.z, v.w);
+                    }
+                } else {
+                    cf[ks].set(cc, 0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[ks]);
+            // the lane holds y[t][p = pb*16 + 4q .. +3]
+            uint8_t* dst = yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB;
+            if constexpr (EB == 2) {
+                const uint2 v = *reinterpret_cast<const uint2*>(dst);
+                const float o0 = __uint_as_float(v.x << 16) + el * acc[0];
+                const float o1 = __uint_as_float(v.x & 0xffff0000u) + el * acc[1];
+                const float o2 = __uint_as_float(v.y << 16) + el * acc[2];
+                const float o3 = __uint_as_float(v.y & 0xffff0000u) + el * acc[3];
+                if (ok) *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+            } else {
+                const float4 v = *reinterpret_cast<const float4*>(dst);
+                if (ok)
+                    *reinterpret_cast<float4*>(dst) =
+                        make_float4(v.x + el * acc[0], v.y + el * acc[1], v.z + el * acc[2], v.w + el * acc[3]);
             }
         }
     }
@@ -793,7 +934,9 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, i
     nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
     pl.nseg = (int)nseg;
     pl.cps = (int)cps;
-    pl.ws_bytes = nseg > 1 ? (size_t)(nseg * batch * H) * ((size_t)N_P_N + 1) * sizeof(float) + 256 : 0;
+    pl.ws_bytes = nseg > 1 ? ((size_t)(nseg * batch * H) * ((size_t)N_P_N + 1) + (size_t)(nchunks * batch * H)) *
+                                 sizeof(float) + 256
+                           : 0;
     return pl;
 }
 
@@ -824,23 +967,24 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     const int BH = (int)(a.batch * a.H);
     k.ws_state = nullptr;
     k.ws_lam = nullptr;
+    k.ws_lamc = nullptr;
     if (pl.nseg > 1) {
         k.ws_state = reinterpret_cast<float*>(a.ws);
         k.ws_lam = k.ws_state + (size_t)pl.nseg * BH * P * N;
+        k.ws_lamc = k.ws_lam + (size_t)pl.nseg * BH;
     }
-    hipError_t e;
-    const int per_seg = (int)a.batch * pl.nhu;
-    if (pl.nseg > 1) {
-        k.nblocks = (pl.nseg - 1) * per_seg;
-        e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, true>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
-        if (e != hipSuccess) return e;
-        dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH);
-        e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, a.state_in, k.ws_state,
-                          (const float*)k.ws_lam, BH, pl.nseg, P * N);
-        if (e != hipSuccess) return e;
-    }
-    k.nblocks = pl.nseg * per_seg;
-    return launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
+    // every segment at once (later ones from a zero state), then, with several segments, the chain
+    // of their end states and the fix-up of the later segments' leading chunks
+    k.nblocks = pl.nseg * (int)a.batch * pl.nhu;
+    hipError_t e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
+    if (e != hipSuccess || pl.nseg == 1) return e;
+    dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH);
+    e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k.ws_state, (const float*)k.ws_lam, a.state_out,
+                      BH, pl.nseg, P * N);
+    if (e != hipSuccess) return e;
+    const int64_t runs = (pl.cps + kFixWaves - 1) / kFixWaves;
+    return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3((unsigned)(runs * (pl.nseg - 1) * BH)),
+                         dim3(64 * kFixWaves), 0, s, k);
 }
 
 template <typename T, int Q>
