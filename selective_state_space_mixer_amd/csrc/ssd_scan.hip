@@ -780,132 +780,131 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
 // Add the part of each later segment's output that comes from its true initial state S_in (the
 // main pass ran it from zero):  y[t] += e^Lam_t (S_in . C_t),  Lam_t = the summed log-decay from the
 // segment's first token through t.  The factor only falls along the segment, so only a prefix of its
-// chunks needs the term: those whose starting factor is at least e^kFixCut (about 1e-9); past them
-// the term is below 1e-9 of |S_in . C_t|, far under the output's rounding.  One block per (run of
-// kFixWaves chunks, segment, head), runs first so that the leading chunks, which nearly always need
-// it, come first.  A block whose first chunk is past the prefix leaves at once (the starting
-// log-decays are left by the main pass); otherwise it brings S_in into LDS as bf16 once, and each
-// wave corrects one chunk of the run.
-constexpr float kFixCut = -20.8f;
-constexpr int kFixWaves = 4;  // waves per block (independent tasks)
+// chunks needs the term: those whose starting factor is at least e^cut.  The cut keeps the dropped
+// term far under the output's rounding: e^-12 (6e-6 of |S_in . C_t|, against bf16's 2^-9) for bf16
+// outputs, e^-20.8 (1e-9) for fp32.
+//
+// Work items are chunks of (segment, sequence, head), numbered chunk-major so the leading chunks,
+// which nearly always need the term, spread over all waves.  A wave takes items w + i * waves; one
+// lane per item reads the chunk's starting log-decay (left by the main pass), so the wave learns at
+// once which items need work.  For each, every load it needs (S_in, dt, C, y) is independent and
+// issued together.
+template <typename T> constexpr float fix_cut() { return sizeof(T) == 2 ? -12.0f : -20.8f; }
+constexpr int kFixThreads = 256;
+constexpr int kFixBlocks = 2048;
 
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__(64 * kFixWaves) void ssd_segment_fix_kernel(ScanK k)
+__global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
 {
     constexpr int NPB = P / 16, KS_N = (N + 31) / 32, NTB = Q / 16;
     constexpr int EB = (int)sizeof(T);
-    using E = typename Lds<T>::E;
-    constexpr int SST = N + 16 / EB;  // LDS row stride of S_in (elements of the operand type)
-    __shared__ __attribute__((aligned(16))) E Ss[P * SST];
-    const int BH = k.batch * k.H;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t per_run = (int64_t)(k.nseg - 1) * BH;
-    const int run = (int)(blockIdx.x / per_run);
-    const int seg = 1 + (int)((blockIdx.x % per_run) / BH);
-    const int bh = (int)(blockIdx.x % BH);
-    const int64_t nchunks = (k.L + Q - 1) / Q;
-    const int64_t seg_end = (int64_t)(seg + 1) * k.cps < nchunks ? (int64_t)(seg + 1) * k.cps : nchunks;
-    const int64_t c_run = (int64_t)seg * k.cps + (int64_t)run * kFixWaves;  // first chunk of the run
-    if (c_run >= seg_end || !(k.ws_lamc[c_run * BH + bh] >= kFixCut)) return;  // whole block
-
-    // S_in -> rows [p][n] in LDS, in the operand type
-    const float* S = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
-    for (int e = threadIdx.x * 4; e < P * N; e += 64 * kFixWaves * 4) {
-        const float4 v = *reinterpret_cast<const float4*>(S + e);
-        const int p = e / N, n = e % N;
-        if constexpr (EB == 2)
-            *reinterpret_cast<uint2*>(&Ss[p * SST + n]) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-        else
-            *reinterpret_cast<float4*>(&Ss[p * SST + n]) = v;
-    }
-    __syncthreads();
-    const int64_t c = c_run + wave;
-    if (c >= seg_end) return;
-    const float lam0 = k.ws_lamc[c * BH + bh];  // the same address in every lane
-    if (!(lam0 >= kFixCut)) return;
-
+    constexpr float kCut = fix_cut<T>();
     const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
-    const int64_t b = bh / k.H;
-    const int h = bh % k.H, g = h / (k.H / k.G);
-    // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n]: rows p, k = n (chunks 4q.., 16+4q..)
-    Frag<T> sa[NPB][KS_N];
-#pragma unroll
-    for (int pb = 0; pb < NPB; ++pb)
-#pragma unroll
-        for (int ks = 0; ks < KS_N; ++ks)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int n0 = 32 * ks + 16 * cc + 4 * q;
-                if (n0 < N) {
-                    const E* src = &Ss[(pb * 16 + li) * SST + n0];
-                    if constexpr (EB == 2) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(src);
-                        sa[pb][ks].set(cc, __uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-                    } else {
-                        const float4 v = *reinterpret_cast<const float4*>(src);
-                        sa[pb][ks].set(cc, v.x, v.y, v.z, v.w);
-                    }
-                } else {
-                    sa[pb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
-                }
-            }
-    const float bias_h = k.dt_bias[h], A_h = k.A[h];
-    const int64_t t0 = c * Q;
-    const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
-    const T* dtp = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
-    const uint8_t* cp = reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N);
-    uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P);
+    const int64_t gw = (int64_t)blockIdx.x * (kFixThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * (kFixThreads / 64);
+    const int BH = k.batch * k.H;
+    const int64_t per_j = (int64_t)(k.nseg - 1) * BH;
+    const int64_t items = (int64_t)k.cps * per_j;
+    const int64_t nchunks = (k.L + Q - 1) / Q;
 
-    // log-decay through each token of the chunk
-    const float raw = to_f32(dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts]);
-    const float dtv = lane < valid ? dt_of(raw, bias_h, k.dt_min, k.dt_max) : 0.0f;
-    const float lam = lam0 + wave_prefix_sum(dtv * A_h);
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
-        const int t = tb * 16 + li;
-        const bool ok = t < valid;
-        const int tr = ok ? t : valid - 1;  // rows past the sequence: loads clamped, stores skipped
-        const float el = fast_exp(__shfl(lam, t, 64));
-        Frag<T> cf[KS_N];
-#pragma unroll
-        for (int ks = 0; ks < KS_N; ++ks)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int n0 = 32 * ks + 16 * cc + 4 * q;
-                if (n0 < N) {
-                    const uint8_t* src = cp + ((t0 + tr) * k.bcs + n0) * EB;
-                    if constexpr (EB == 2) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(src);
-                        cf[ks].set(cc, __uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                                   __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-                    } else {
-                        const float4 v = *reinterpret_cast<const float4*>(src);
-                        cf[ks].set(cc, v.x, v.y, v.z, v.w);
-                    }
-                } else {
-                    cf[ks].set(cc, 0.f, 0.f, 0.f, 0.f);
-                }
+    for (int64_t base = gw; base < items; base += nwaves * 64) {
+        // item -> chunk; which of this wave's 64 items need the term
+        bool need = false;
+        {
+            const int64_t item = base + (int64_t)lane * nwaves;
+            if (item < items) {
+                const int j = (int)(item / per_j);
+                const int seg = 1 + (int)((item % per_j) / BH), bh = (int)(item % BH);
+                const int64_t c = (int64_t)seg * k.cps + j;
+                need = c < nchunks && k.ws_lamc[c * BH + bh] >= kCut;
             }
+        }
+        uint64_t mask = __builtin_amdgcn_ballot_w64(need);
+        while (mask) {
+            const int i = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int64_t item = base + (int64_t)i * nwaves;
+            const int j = (int)(item / per_j);
+            const int seg = 1 + (int)((item % per_j) / BH), bh = (int)(item % BH);
+            const int64_t c = (int64_t)seg * k.cps + j;
+            const int64_t b = bh / k.H;
+            const int h = bh % k.H, g = h / (k.H / k.G);
+            const int64_t t0 = c * Q;
+            const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+            const float lam0 = k.ws_lamc[c * BH + bh];  // the same address in every lane
+            // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n]: rows p, k = n (chunks 4q.., 16+4q..)
+            const float* S = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
+            Frag<T> sa[NPB][KS_N];
 #pragma unroll
-        for (int pb = 0; pb < NPB; ++pb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-            for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[ks]);
-            // the lane holds y[t][p = pb*16 + 4q .. +3]
-            uint8_t* dst = yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB;
-            if constexpr (EB == 2) {
-                const uint2 v = *reinterpret_cast<const uint2*>(dst);
-                const float o0 = __uint_as_float(v.x << 16) + el * acc[0];
-                const float o1 = __uint_as_float(v.x & 0xffff0000u) + el * acc[1];
-                const float o2 = __uint_as_float(v.y << 16) + el * acc[2];
-                const float o3 = __uint_as_float(v.y & 0xffff0000u) + el * acc[3];
-                if (ok) *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-            } else {
-                const float4 v = *reinterpret_cast<const float4*>(dst);
-                if (ok)
-                    *reinterpret_cast<float4*>(dst) =
-                        make_float4(v.x + el * acc[0], v.y + el * acc[1], v.z + el * acc[2], v.w + el * acc[3]);
+                for (int ks = 0; ks < KS_N; ++ks)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const int n0 = 32 * ks + 16 * cc + 4 * q;
+                        if (n0 < N) {
+                            const float4 v = *reinterpret_cast<const float4*>(S + (int64_t)(pb * 16 + li) * N + n0);
+                            sa[pb][ks].set(cc, v.x, v.y, v.z, v.w);
+                        } else {
+                            sa[pb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
+                        }
+                    }
+            const float bias_h = k.dt_bias[h], A_h = k.A[h];
+            const T* dtp = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
+            const uint8_t* cp =
+                reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N);
+            uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P);
+            // log-decay through each token of the chunk
+            const float raw = to_f32(dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts]);
+            const float dtv = lane < valid ? dt_of(raw, bias_h, k.dt_min, k.dt_max) : 0.0f;
+            const float lam = lam0 + wave_prefix_sum(dtv * A_h);
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) {
+                const int t = tb * 16 + li;
+                const bool ok = t < valid;
+                const int tr = ok ? t : valid - 1;  // rows past the sequence: loads clamped, stores skipped
+                const float el = fast_exp(__shfl(lam, t, 64));
+                Frag<T> cf[KS_N];
+#pragma unroll
+                for (int ks = 0; ks < KS_N; ++ks)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const int n0 = 32 * ks + 16 * cc + 4 * q;
+                        if (n0 < N) {
+                            const uint8_t* src = cp + ((t0 + tr) * k.bcs + n0) * EB;
+                            if constexpr (EB == 2) {
+                                const uint2 v = *reinterpret_cast<const uint2*>(src);
+                                cf[ks].set(cc, __uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+                            } else {
+                                const float4 v = *reinterpret_cast<const float4*>(src);
+                                cf[ks].set(cc, v.x, v.y, v.z, v.w);
+                            }
+                        } else {
+                            cf[ks].set(cc, 0.f, 0.f, 0.f, 0.f);
+                        }
+                    }
+#pragma unroll
+                for (int pb = 0; pb < NPB; ++pb) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[ks]);
+                    // the lane holds y[t][p = pb*16 + 4q .. +3]
+                    uint8_t* dst = yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB;
+                    if constexpr (EB == 2) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(dst);
+                        const float o0 = __uint_as_float(v.x << 16) + el * acc[0];
+                        const float o1 = __uint_as_float(v.x & 0xffff0000u) + el * acc[1];
+                        const float o2 = __uint_as_float(v.y << 16) + el * acc[2];
+                        const float o3 = __uint_as_float(v.y & 0xffff0000u) + el * acc[3];
+                        if (ok) *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+                    } else {
+                        const float4 v = *reinterpret_cast<const float4*>(dst);
+                        if (ok)
+                            *reinterpret_cast<float4*>(dst) = make_float4(v.x + el * acc[0], v.y + el * acc[1],
+                                                                          v.z + el * acc[2], v.w + el * acc[3]);
+                    }
+                }
             }
         }
     }
@@ -982,9 +981,10 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k.ws_state, (const float*)k.ws_lam, a.state_out,
                       BH, pl.nseg, P * N);
     if (e != hipSuccess) return e;
-    const int64_t runs = (pl.cps + kFixWaves - 1) / kFixWaves;
-    return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3((unsigned)(runs * (pl.nseg - 1) * BH)),
-                         dim3(64 * kFixWaves), 0, s, k);
+    const int64_t items = (int64_t)pl.cps * (pl.nseg - 1) * BH;
+    const int64_t blocks = (items + 63) / 64;
+    return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3((unsigned)(blocks < kFixBlocks ? blocks : kFixBlocks)),
+                         dim3(kFixThreads), 0, s, k);
 }
 
 template <typename T, int Q>
