@@ -42,9 +42,9 @@ def _load():
         dp = ctypes.c_void_p
         i64 = ctypes.c_int64
         f64 = ctypes.c_double
-        lib.oracle_conv1d.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, i64, dp, dp]
+        lib.oracle_conv1d.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, i64, dp, dp, dp]
         lib.oracle_conv1d.restype = None
-        lib.oracle_ssd_scan.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64, dp, dp, dp]
+        lib.oracle_ssd_scan.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64, dp, dp, dp, dp]
         lib.oracle_ssd_scan.restype = None
         lib.oracle_ssd_step.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64, dp, i64, dp, dp]
         lib.oracle_ssd_step.restype = None
@@ -88,8 +88,20 @@ def gated_rmsnorm(y, z, w, group_size: int, eps: float = 1e-5, norm_before_gate:
     return out
 
 
-def conv1d(x, w, bias=None, ring_in=None, ring_in_step: int = 0, want_ring: bool = True):
-    """Causal depthwise conv1d + SiLU.  x [B,L,Cd], w [Cd,W] -> (out [B,L,Cd], ring_out [B,W,Cd])."""
+def _lens(seq_lens, Bn, L):
+    if seq_lens is None:
+        return None
+    a = np.ascontiguousarray(seq_lens, dtype=np.int64)
+    if a.shape != (Bn,) or a.min(initial=0) < 0 or a.max(initial=0) > L:
+        raise ValueError("oracle: seq_lens must be [batch] values in [0, seqlen]")
+    return a
+
+
+def conv1d(x, w, bias=None, ring_in=None, ring_in_step: int = 0, want_ring: bool = True, seq_lens=None):
+    """Causal depthwise conv1d + SiLU.  x [B,L,Cd], w [Cd,W] -> (out [B,L,Cd], ring_out [B,W,Cd]).
+
+    seq_lens [B] (optional): sequence b holds only its first seq_lens[b] tokens; outputs past them
+    are NaN here, and ring_out holds the W tokens before seq_lens[b]."""
     x = _f64(x)
     Bn, L, Cd = x.shape
     w = _f64(w)
@@ -97,18 +109,21 @@ def conv1d(x, w, bias=None, ring_in=None, ring_in_step: int = 0, want_ring: bool
     w = _f64(w, (Cd, W))
     bias = _f64(bias, (Cd,))
     ring_in = _f64(ring_in, (Bn, W, Cd))
-    out = np.empty_like(x)
+    lens = _lens(seq_lens, Bn, L)
+    out = np.full_like(x, np.nan)
     ring_out = np.empty((Bn, W, Cd)) if want_ring else None
     _load().oracle_conv1d(Bn, L, Cd, W, _p(x), _p(w), _p(bias), _p(ring_in), int(ring_in_step),
-                          _p(ring_out), _p(out))
+                          _p(ring_out), _p(out), _p(lens))
     return out, ring_out
 
 
 def ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None,
-             dt_min: float = 0.0, dt_max: float = float("inf")):
+             dt_min: float = 0.0, dt_max: float = float("inf"), seq_lens=None):
     """Sequential selective-SSM recurrence.
 
-    x [B,L,H,P], Bm/Cm [B,L,G,N], dt_raw [B,L,H] -> (y [B,L,H,P], state_out [B,H,P,N])."""
+    x [B,L,H,P], Bm/Cm [B,L,G,N], dt_raw [B,L,H] -> (y [B,L,H,P], state_out [B,H,P,N]).
+    seq_lens [B] (optional): sequence b consumes only its first seq_lens[b] tokens; y past them is
+    NaN here, and state_out is the state after its last token."""
     x = _f64(x)
     Bn, L, H, P = x.shape
     Bm = _f64(Bm)
@@ -122,10 +137,11 @@ def ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None,
     state_in = _f64(state_in, (Bn, H, P, N))
     if H % G:
         raise ValueError("oracle: nheads must be a multiple of n_groups")
-    y = np.empty_like(x)
+    lens = _lens(seq_lens, Bn, L)
+    y = np.full_like(x, np.nan)
     state_out = np.empty((Bn, H, P, N))
     _load().oracle_ssd_scan(Bn, L, H, P, N, G, _p(x), _p(Bm), _p(Cm), _p(dt_raw), _p(dt_bias), _p(A),
-                            _p(D), float(dt_min), float(dt_max), _p(state_in), _p(y), _p(state_out))
+                            _p(D), float(dt_min), float(dt_max), _p(state_in), _p(y), _p(state_out), _p(lens))
     return y, state_out
 
 

@@ -62,17 +62,20 @@ static double step_size(double raw, double bias, double dt_min, double dt_max) {
 /* Causal depthwise conv1d + SiLU over a prompt (article §三: groups = conv_dim,
  * kernel width mamba_d_conv, SiLU on the output; §五: use_conv_bias).
  * ring_in (nullable) supplies the W-1 tokens before t = 0 at phase ring_in_step;
- * ring_out (nullable) receives the last W tokens at phase 0. */
+ * ring_out (nullable) receives the last W tokens at phase 0.
+ * lens (nullable): sequence b holds only its first lens[b] tokens (the rest is padding): outputs
+ * past them are not written and ring_out holds the W tokens before lens[b]. */
 void oracle_conv1d(int64_t Bn, int64_t L, int64_t Cd, int64_t W,
                    const double* x, const double* w, const double* bias,
                    const double* ring_in, int64_t ring_in_step,
-                   double* ring_out, double* out)
+                   double* ring_out, double* out, const int64_t* lens)
 {
     #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t b = 0; b < Bn; ++b) {
         for (int64_t c = 0; c < Cd; ++c) {
             const double* xb = x + b * L * Cd;
-            for (int64_t t = 0; t < L; ++t) {
+            const int64_t Lb = lens ? lens[b] : L;
+            for (int64_t t = 0; t < Lb; ++t) {
                 double v = bias ? bias[c] : 0.0;
                 for (int64_t k = 0; k < W; ++k) {
                     int64_t tau = t - (W - 1) + k;  /* token index feeding tap k */
@@ -86,7 +89,7 @@ void oracle_conv1d(int64_t Bn, int64_t L, int64_t Cd, int64_t W,
             }
             if (ring_out) {
                 for (int64_t j = 0; j < W; ++j) {
-                    int64_t tau = L - W + j;  /* slot j at phase 0 */
+                    int64_t tau = Lb - W + j;  /* slot j at phase 0 */
                     double xv;
                     if (tau >= 0) xv = xb[tau * Cd + c];
                     else if (ring_in) xv = ring_in[(b * W + pmod(ring_in_step + tau, W)) * Cd + c];
@@ -100,12 +103,14 @@ void oracle_conv1d(int64_t Bn, int64_t L, int64_t Cd, int64_t W,
 
 /* Selective state-space recurrence over a prompt, one token at a time
  * (the chunked scan of article §三 computes exactly this sum; here it is
- * evaluated sequentially).  state_in / D nullable (zero). */
+ * evaluated sequentially).  state_in / D nullable (zero).
+ * lens (nullable): sequence b consumes only its first lens[b] tokens; y past them is not written
+ * and state_out is the state after token lens[b] - 1. */
 void oracle_ssd_scan(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                      const double* x, const double* Bm, const double* Cm,
                      const double* dt_raw, const double* dt_bias, const double* A, const double* D,
                      double dt_min, double dt_max,
-                     const double* state_in, double* y, double* state_out)
+                     const double* state_in, double* y, double* state_out, const int64_t* lens)
 {
     const int64_t hpg = H / G;
     #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -116,7 +121,8 @@ void oracle_ssd_scan(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t N, int
             for (int64_t i = 0; i < P * N; ++i)
                 S[i] = state_in ? state_in[((b * H + h) * P) * N + i] : 0.0;
             const double Dh = D ? D[h] : 0.0;
-            for (int64_t t = 0; t < L; ++t) {
+            const int64_t Lb = lens ? lens[b] : L;
+            for (int64_t t = 0; t < Lb; ++t) {
                 const int64_t bt = b * L + t;
                 const double dt = step_size(dt_raw[bt * H + h], dt_bias[h], dt_min, dt_max);
                 const double decay = exp(dt * A[h]);

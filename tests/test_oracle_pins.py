@@ -453,3 +453,56 @@ def test_gated_rmsnorm_groups_are_independent_and_zero_gate():
     zero = np.zeros_like(z)
     assert not np.any(oracle.gated_rmsnorm(y, zero, w, 8))
     assert not np.any(oracle.gated_rmsnorm(y, zero, w, 8, norm_before_gate=True))
+
+
+# ----------------------------------------------------------------- right-padded batches
+
+def test_conv_padded_batch_equals_each_sequence_alone():
+    # sequence b of a right-padded batch: outputs and ring equal those of its first lens[b] tokens run
+    # on their own; positions past lens[b] stay unwritten (NaN); the ring holds the last W real tokens
+    rng = np.random.default_rng(40)
+    Bn, L, Cd, W = 5, 13, 4, 4
+    x = rng.standard_normal((Bn, L, Cd))
+    w = rng.uniform(-0.5, 0.5, (Cd, W))
+    bias = rng.uniform(-0.5, 0.5, Cd)
+    ring = rng.standard_normal((Bn, W, Cd))
+    lens = np.array([13, 0, 2, 7, 4])
+    for phase in (0, 3):
+        out, ring_out = oracle.conv1d(x, w, bias, ring, phase, seq_lens=lens)
+        for b, n in enumerate(lens):
+            ob, rb = oracle.conv1d(x[b:b + 1, :n], w, bias, ring[b:b + 1], phase)
+            np.testing.assert_allclose(out[b, :n], ob[0], rtol=1e-14, atol=1e-300)
+            assert np.isnan(out[b, n:]).all()
+            np.testing.assert_array_equal(ring_out[b], rb[0])
+            hist = np.stack([ring[b, (phase - j) % W] for j in range(W, 0, -1)])   # tokens -W..-1
+            np.testing.assert_array_equal(ring_out[b], np.concatenate([hist, x[b, :n]])[-W:])
+
+
+def test_scan_padded_batch_equals_each_sequence_alone():
+    rng = np.random.default_rng(41)
+    Bn, L, H, P, N, G = 4, 19, 4, 3, 5, 2
+    x, Bm, Cm, dt_raw, dt_bias, A, D, S0 = _rand_scan(rng, Bn, L, H, P, N, G)
+    lens = np.array([19, 0, 1, 11])
+    y, s = oracle.ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D, S0, seq_lens=lens)
+    for b, n in enumerate(lens):
+        sl = slice(b, b + 1)
+        yb, sb = _bruteforce(x[sl, :n], Bm[sl, :n], Cm[sl, :n], dt_raw[sl, :n], dt_bias, A, D, S0[sl])
+        assert rel(y[b, :n], yb[0]) < RTOL if n else True
+        assert np.isnan(y[b, n:]).all()
+        assert rel(s[b], sb[0]) < RTOL
+    np.testing.assert_array_equal(s[1], S0[1])     # an empty sequence hands its state back unchanged
+
+
+def test_scan_padding_content_is_ignored():
+    # whatever sits in the padded positions must not reach any output
+    rng = np.random.default_rng(42)
+    x, Bm, Cm, dt_raw, dt_bias, A, D, S0 = _rand_scan(rng, 3, 16, 2, 3, 4, 1)
+    lens = np.array([16, 5, 9])
+    y, s = oracle.ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D, S0, seq_lens=lens)
+    junk = [a.copy() for a in (x, Bm, Cm, dt_raw)]
+    for a in junk:
+        for b, n in enumerate(lens):
+            a[b, n:] = 1e3 * rng.standard_normal(a[b, n:].shape)
+    y2, s2 = oracle.ssd_scan(*junk, dt_bias, A, D, S0, seq_lens=lens)
+    np.testing.assert_array_equal(np.nan_to_num(y, nan=7.0), np.nan_to_num(y2, nan=7.0))
+    np.testing.assert_array_equal(s, s2)
