@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define M2SSD_ABI_VERSION 1
+#define M2SSD_ABI_VERSION 2
 
 typedef enum {
     M2_OK = 0,
@@ -91,6 +91,11 @@ typedef struct {
  *          phase 0 (slot j = token seqlen-W+j, taken from ring_in when negative);
  *          must not overlap ring_in or xbc
  * out      [batch, seqlen, conv_dim] io, token stride out_tok_stride; must not overlap xbc
+ * seq_lens [batch] int32 on the device, or NULL (every sequence is seqlen tokens long): a
+ *          right-padded batch, in which sequence b holds only its first seq_lens[b] tokens
+ *          (the recurrent mask of the Zamba2 page, §2.3, for padding at the end).  Values
+ *          are clamped to [0, seqlen].  out at later positions is left as it was, and
+ *          ring_out holds the W tokens before seq_lens[b].  Must not overlap an output.
  * seqlen may be 0 (then only ring_out is written, as a copy of the history). */
 m2_status m2_conv1d_fwd(const m2_dims* dims,
                         const void* xbc, int64_t xbc_tok_stride,
@@ -98,6 +103,7 @@ m2_status m2_conv1d_fwd(const m2_dims* dims,
                         const void* ring_in, int64_t ring_in_step,
                         void* ring_out,
                         void* out, int64_t out_tok_stride,
+                        const int32_t* seq_lens,
                         void* stream);
 
 /* Workspace bytes m2_ssd_scan_fwd needs for these dims (0 if none). */
@@ -115,6 +121,11 @@ size_t m2_ssd_scan_workspace(const m2_dims* dims);
  *          x, B, C or dt
  * workspace device scratch of at least m2_ssd_scan_workspace(dims) bytes (NULL if 0);
  *          its contents on entry do not matter.
+ * seq_lens [batch] int32 on the device, or NULL (every sequence is seqlen tokens long): a
+ *          right-padded batch as in m2_conv1d_fwd.  Sequence b consumes only its first
+ *          seq_lens[b] tokens (clamped to [0, seqlen]): y at later positions is left as it
+ *          was, and state_out is the state after its last token (state_in, or zero, for an
+ *          empty one).  Must not overlap an output or the workspace.
  * x/B/C may be strided views into one conv1d output (token stride conv_dim). */
 m2_status m2_ssd_scan_fwd(const m2_dims* dims,
                           const void* x, int64_t x_tok_stride,
@@ -125,6 +136,7 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims,
                           const float* state_in, float* state_out,
                           void* y, int64_t y_tok_stride,
                           void* workspace, size_t workspace_bytes,
+                          const int32_t* seq_lens,
                           void* stream);
 
 /* One decode token for every sequence, fused: conv window (W-1 cached tokens + the new

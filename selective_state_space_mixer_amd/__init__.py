@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libm2ssd.so")
 M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, M2_ERR_UNSUPPORTED, \
     M2_ERR_LAUNCH = range(8)
 M2_F32, M2_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTS = ("m2_conv1d_fwd", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd", "m2_ssd_step", "m2_gated_rmsnorm",
            "m2_status_str", "m2_abi_version", "m2_last_hip_error")
@@ -69,12 +69,12 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     dp = ctypes.POINTER(M2Dims)
-    lib.m2_conv1d_fwd.argtypes = [dp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp]
+    lib.m2_conv1d_fwd.argtypes = [dp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp]
     lib.m2_conv1d_fwd.restype = ctypes.c_int
     lib.m2_ssd_scan_workspace.argtypes = [dp]
     lib.m2_ssd_scan_workspace.restype = sz
     lib.m2_ssd_scan_fwd.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp, i64,
-                                    vp, sz, vp]
+                                    vp, sz, vp, vp]
     lib.m2_ssd_scan_fwd.restype = ctypes.c_int
     lib.m2_ssd_step.argtypes = [dp, vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, f32, vp, i64, vp, vp, vp]
     lib.m2_ssd_step.restype = ctypes.c_int
@@ -185,6 +185,16 @@ def _tok_stride(t, name, dims: M2Dims, row: int) -> int:
     return ts
 
 
+def _lens_ptr(seq_lens, dims: M2Dims):
+    """Device pointer of an int32 [batch] lengths tensor (None: no padding)."""
+    if seq_lens is None:
+        return None
+    _check(seq_lens, "seq_lens", _torch().int32)
+    if not seq_lens.is_contiguous() or tuple(seq_lens.shape) != (dims.batch,):
+        raise ValueError("seq_lens must be a contiguous int32 [batch] tensor")
+    return _ptr(seq_lens)
+
+
 def _call(fn, *args):
     st = getattr(_lib, fn)(*args)
     if st != M2_OK:
@@ -192,11 +202,12 @@ def _call(fn, *args):
 
 
 def m2_conv1d_fwd(dims: M2Dims, xbc, w, bias, out, ring_in=None, ring_in_step: int = 0, ring_out=None,
-                  stream=None) -> None:
+                  stream=None, seq_lens=None) -> None:
     """out[b,t,c] = SiLU(bias[c] + sum_k w[c,k] x[b,t-(W-1)+k,c]); see include/m2ssd.h.
 
     xbc, out [B, L, conv_dim] (io dtype, token-strided views allowed); w [conv_dim, W] f32;
-    bias [conv_dim] f32 or None; ring_in / ring_out [B, W, conv_dim] io or None."""
+    bias [conv_dim] f32 or None; ring_in / ring_out [B, W, conv_dim] io or None;
+    seq_lens: int32 [B] GPU tensor of each right-padded sequence's length, or None."""
     torch = _torch()
     io = _io_dtype(dims)
     Cd = dims.conv_dim
@@ -214,7 +225,7 @@ def m2_conv1d_fwd(dims: M2Dims, xbc, w, bias, out, ring_in=None, ring_in_step: i
     xs = _tok_stride(xbc, "xbc", dims, Cd)
     os_ = _tok_stride(out, "out", dims, Cd)
     _call("m2_conv1d_fwd", ctypes.byref(dims), _ptr(xbc), xs, _ptr(w), _ptr(bias), _ptr(ring_in),
-          int(ring_in_step), _ptr(ring_out), _ptr(out), os_, _stream(stream))
+          int(ring_in_step), _ptr(ring_out), _ptr(out), os_, _lens_ptr(seq_lens, dims), _stream(stream))
 
 
 def m2_ssd_scan_workspace(dims: M2Dims) -> int:
@@ -222,13 +233,15 @@ def m2_ssd_scan_workspace(dims: M2Dims) -> int:
 
 
 def m2_ssd_scan_fwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, state_out=None,
-                    dt_min: float = 0.0, dt_max: float = float("inf"), workspace=None, stream=None) -> None:
+                    dt_min: float = 0.0, dt_max: float = float("inf"), workspace=None, stream=None,
+                    seq_lens=None) -> None:
     """Chunked selective-SSM scan; see include/m2ssd.h.
 
     x [B, L, H, P] (or [B, L, H*P]), B/C [B, L, G, N] (or [B, L, G*N]), dt [B, L, H], y like x,
     all io dtype, token-strided views allowed (B and C must share one token stride);
     dt_bias, A, D [H] f32 (D may be None); state_in / state_out [B, H, P, N] f32 or None;
-    workspace: a uint8 GPU tensor of at least m2_ssd_scan_workspace(dims) bytes, or None."""
+    workspace: a uint8 GPU tensor of at least m2_ssd_scan_workspace(dims) bytes, or None;
+    seq_lens: int32 [B] GPU tensor of each right-padded sequence's length, or None."""
     torch = _torch()
     io = _io_dtype(dims)
     H, P, N, G = dims.nheads, dims.headdim, dims.d_state, dims.n_groups
@@ -257,7 +270,7 @@ def m2_ssd_scan_fwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, 
         raise ValueError("m2_ssd_scan_fwd needs a workspace of %d bytes" % need)
     _call("m2_ssd_scan_fwd", ctypes.byref(dims), _ptr(x), xs, _ptr(B), _ptr(C), bs, _ptr(dt), dts,
           _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min), float(dt_max), _ptr(state_in), _ptr(state_out),
-          _ptr(y), ys, ws_ptr, ws_bytes, _stream(stream))
+          _ptr(y), ys, ws_ptr, ws_bytes, _lens_ptr(seq_lens, dims), _stream(stream))
 
 
 def m2_ssd_step(dims: M2Dims, xbc_tok, dt_tok, w, bias, dt_bias, A, D, ring, step: int, state, y,

@@ -94,7 +94,7 @@ const char* m2_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); 
 
 m2_status m2_conv1d_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_stride, const float* w,
                         const float* bias, const void* ring_in, int64_t ring_in_step, void* ring_out, void* out,
-                        int64_t out_tok_stride, void* stream) {
+                        int64_t out_tok_stride, const int32_t* seq_lens, void* stream) {
     Derived d;
     m2_status st = derive(dims, d);
     if (st != M2_OK) return st;
@@ -107,13 +107,16 @@ m2_status m2_conv1d_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_st
     const Range ro = span(out, rows, out_tok_stride, d.Cd, d.esize);
     const Range rri = span(ring_in, d.batch * d.W, d.Cd, d.Cd, d.esize);
     const Range rro = span(ring_out, d.batch * d.W, d.Cd, d.Cd, d.esize);
-    if (overlap(rx, ro) || overlap(rri, rro) || overlap(rro, rx) || overlap(rro, ro) || overlap(ro, rri))
+    const Range rl = span(seq_lens, d.batch, 1, 1, 4);
+    if (overlap(rx, ro) || overlap(rri, rro) || overlap(rro, rx) || overlap(rro, ro) || overlap(ro, rri) ||
+        overlap(rl, ro) || overlap(rl, rro))
         return M2_ERR_ALIAS;
+    if ((uintptr_t)seq_lens & 3u) return M2_ERR_UNSUPPORTED;
     m2::ConvArgs a;
     a.xbc = xbc; a.xs = xbc_tok_stride; a.L = d.L; a.Cd = d.Cd; a.W = d.W; a.batch = d.batch;
     a.w = w; a.bias = bias; a.ring_in = ring_in;
     a.ring_phase = (int)(((ring_in_step % d.W) + d.W) % d.W);
-    a.ring_out = ring_out; a.out = out; a.os = out_tok_stride; a.bf16 = d.bf16;
+    a.ring_out = ring_out; a.out = out; a.os = out_tok_stride; a.lens = seq_lens; a.bf16 = d.bf16;
     const int vec = d.bf16 ? 8 : 4;
     a.vec = (d.Cd % vec == 0) && (rows == 0 || (xbc_tok_stride % vec == 0 && out_tok_stride % vec == 0 &&
                                                  aligned16(xbc) && aligned16(out))) &&
@@ -133,7 +136,7 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
                           int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
                           const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
                           float* state_out, void* y, int64_t y_tok_stride, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
     Derived d;
     m2_status st = derive(dims, d);
     if (st != M2_OK) return st;
@@ -158,15 +161,18 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
         overlap(ry, span(dt, rows, dt_tok_stride, d.H, d.esize)) || overlap(rs_in, rs_out) ||
         overlap(rs_out, ry))
         return M2_ERR_ALIAS;
-    if (!aligned16(state_in) || !aligned16(state_out)) return M2_ERR_UNSUPPORTED;
+    if (!aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)seq_lens & 3u)) return M2_ERR_UNSUPPORTED;
     const size_t need = m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
     if (need > 0 && (!workspace || workspace_bytes < need)) return M2_ERR_WORKSPACE;
+    const Range rl = span(seq_lens, d.batch, 1, 1, 4);
+    if (overlap(rl, ry) || overlap(rl, rs_out) || overlap(rl, span(workspace, 1, 0, (int64_t)need, 1)))
+        return M2_ERR_ALIAS;
     m2::ScanArgs a;
     a.batch = d.batch; a.L = d.L; a.H = d.H; a.P = d.P; a.N = d.N; a.G = d.G; a.Q = Q;
     a.x = x; a.xs = x_tok_stride; a.B = B; a.C = C; a.bcs = bc_tok_stride; a.dt = dt; a.dts = dt_tok_stride;
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.dt_min = dt_min; a.dt_max = dt_max;
     a.state_in = state_in; a.state_out = state_out; a.y = y; a.ys = y_tok_stride;
-    a.ws = workspace; a.ws_bytes = workspace_bytes; a.bf16 = d.bf16;
+    a.ws = workspace; a.ws_bytes = workspace_bytes; a.lens = seq_lens; a.bf16 = d.bf16;
     return launched(m2::launch_ssd_scan(a, (hipStream_t)stream));
 }
 

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     const T* __restrict__ xbc, int64_t xs, int64_t L, int Cd,
     const float* __restrict__ w, const float* __restrict__ bias,
     const T* __restrict__ ring_in, int ring_phase,
-    T* __restrict__ ring_out, T* __restrict__ out, int64_t os)
+    T* __restrict__ ring_out, T* __restrict__ out, int64_t os, const int32_t* __restrict__ lens)
 {
     using R = typename Raw<T, VEC>::type;
     const int CG = Cd / VEC;
@@ -105,6 +105,14 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     const int c0 = (int)(item % CG) * VEC;
     const int64_t t0 = (item / CG) * kConvTileTokens;
     const int64_t b = blockIdx.y;
+    // a right-padded sequence ends at its own length; the tile that starts at token 0 always
+    // runs, so that an empty sequence still writes its ring
+    int64_t Lb = L;
+    if (lens) {
+        const int64_t v = lens[b];
+        Lb = v < 0 ? 0 : (v > L ? L : v);
+    }
+    if (t0 > 0 && t0 >= Lb) return;
     const T* xb = xbc + b * L * xs + c0;
     T* ob = out + b * L * os + c0;
 
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
         }
     }
 
-    const int64_t t_end = t0 + kConvTileTokens < L ? t0 + kConvTileTokens : L;
+    const int64_t t_end = t0 + kConvTileTokens < Lb ? t0 + kConvTileTokens : Lb;
     const int n = (int)(t_end - t0);
     R cur[kConvGroup], nxt[kConvGroup];
     auto load_group = [&](R (&dst)[kConvGroup], int base) __attribute__((always_inline)) {
@@ -168,8 +176,8 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
         for (int u = 0; u < kConvGroup; ++u) cur[u] = nxt[u];
     }
 
-    // the tile holding the last token writes the ring (phase 0: slot j = token L-W+j)
-    if (ring_out && t_end == L) {
+    // the tile holding the last token writes the ring (phase 0: slot j = token Lb-W+j)
+    if (ring_out && t_end == Lb) {
 #pragma unroll
         for (int kk = 0; kk < W; ++kk) store_vals<T, VEC>(ring_out + (b * W + kk) * (int64_t)Cd + c0, win[kk]);
     }
@@ -182,7 +190,7 @@ static hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
     dim3 grid((unsigned)((items + kConvThreads - 1) / kConvThreads), (unsigned)a.batch);
     return launch_kernel(conv1d_silu_kernel<T, VEC, W>, grid, dim3(kConvThreads), 0, s,
                          (const T*)a.xbc, a.xs, a.L, a.Cd, a.w, a.bias, (const T*)a.ring_in, a.ring_phase,
-                         (T*)a.ring_out, (T*)a.out, a.os);
+                         (T*)a.ring_out, (T*)a.out, a.os, a.lens);
 }
 
 template <typename T, int VEC>

@@ -14,6 +14,7 @@ struct ConvArgs {
     const void* ring_in; int ring_phase;
     void* ring_out;
     void* out; int64_t os;
+    const int32_t* lens;  // [batch] valid tokens per sequence (device), or null
     bool bf16;  // storage type of activations
     bool vec;   // 16-byte vector path (alignment checked by the caller)
 };
@@ -29,6 +30,7 @@ struct ScanArgs {
     const float* state_in; float* state_out;
     void* y; int64_t ys;
     void* ws; size_t ws_bytes;
+    const int32_t* lens;  // [batch] valid tokens per sequence (device), or null
     bool bf16;
 };
 

@@ -224,12 +224,20 @@ struct ScanK {
     float* ws_state;   // [nseg][batch*H][P*N]: segment end states, then segment initial states
     float* ws_lam;     // [nseg][batch*H]: summed log-decay of each segment
     float* ws_lamc;    // [nchunks][batch*H]: summed log-decay of the chunk's segment before the chunk
+    const int32_t* lens;  // [batch] tokens of each right-padded sequence, or null (all L)
     int64_t L;
     int batch, H, G;
     int nseg, cps;     // segments per sequence, chunks per segment
     int win;           // chunks per buffer-resource window (byte offsets inside one stay below 2^31)
     int nblocks;       // blocks in this launch
 };
+
+// Tokens of sequence b: its length, clamped to [0, L], in a right-padded batch; else L.
+__device__ __forceinline__ int64_t seq_len(const ScanK& k, int64_t b) {
+    if (!k.lens) return k.L;
+    const int64_t v = k.lens[b];
+    return v < 0 ? 0 : (v > k.L ? k.L : v);
+}
 
 // Block -> logical unit.  Consecutive blocks are dealt round-robin to the 8 XCDs; the remap
 // gives each XCD a contiguous run of logical units (the head groups of one sequence and
@@ -353,11 +361,15 @@ ssd_chunk_scan_kernel(ScanK k)
     const bool hvalid = hw < hcount;
     const int bh = (int)b * k.H + h;
     const int BH = k.batch * k.H;
-    const int64_t nchunks = (k.L + Q - 1) / Q;
+    // a right-padded sequence ends at its own length: chunks past it are not run, a segment that
+    // starts past it runs none (end state = start state, log-decay 0)
+    const int64_t Lb = seq_len(k, b);
+    const int64_t nchunks = (Lb + Q - 1) / Q;
     const int64_t c_begin = (int64_t)seg * k.cps;
-    const int nc = (int)((c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks) - c_begin);  // chunks here
+    const int64_t c_stop = c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks;
+    const int nc = c_stop > c_begin ? (int)(c_stop - c_begin) : 0;  // chunks here
     const int64_t row_begin = c_begin * Q;                       // first token of the segment
-    const int64_t row_end = k.L < row_begin + (int64_t)nc * Q ? k.L : row_begin + (int64_t)nc * Q;
+    const int64_t row_end = Lb < row_begin + (int64_t)nc * Q ? Lb : row_begin + (int64_t)nc * Q;
     const float bias_h = k.dt_bias[h], A_h = k.A[h];
     const float D_h = k.D ? k.D[h] : 0.0f;
 
@@ -409,7 +421,7 @@ ssd_chunk_scan_kernel(ScanK k)
     // to keep offsets below 2^31, and then only rows the window never serves are cut).  The
     // window bases are kept in LDS rather than in scalar registers: a rebase is rare.
     const int xs = (int)k.xs, bcs = (int)k.bcs, dts = (int)k.dts, ys = (int)k.ys;  // < 2^31 / (3 Q SZ)
-    const int nrows = (int)(row_end - row_begin);
+    const int nrows = nc > 0 ? (int)(row_end - row_begin) : 0;
     if (lane == 0) {
         const int64_t base = b * k.L + row_begin;
         sBase[wave][0] = (uint64_t)(reinterpret_cast<const T*>(k.x) + base * k.xs + (int64_t)h0 * P);
@@ -805,7 +817,6 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
     const int BH = k.batch * k.H;
     const int64_t per_j = (int64_t)(k.nseg - 1) * BH;
     const int64_t items = (int64_t)k.cps * per_j;
-    const int64_t nchunks = (k.L + Q - 1) / Q;
 
     for (int64_t base = gw; base < items; base += nwaves * 64) {
         // item -> chunk; which of this wave's 64 items need the term
@@ -816,7 +827,7 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
                 const int j = (int)(item / per_j);
                 const int seg = 1 + (int)((item % per_j) / BH), bh = (int)(item % BH);
                 const int64_t c = (int64_t)seg * k.cps + j;
-                need = c < nchunks && k.ws_lamc[c * BH + bh] >= kCut;
+                need = c * Q < seq_len(k, bh / k.H) && k.ws_lamc[c * BH + bh] >= kCut;
             }
         }
         uint64_t mask = __builtin_amdgcn_ballot_w64(need);
@@ -830,7 +841,8 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
             const int64_t b = bh / k.H;
             const int h = bh % k.H, g = h / (k.H / k.G);
             const int64_t t0 = c * Q;
-            const int valid = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+            const int64_t Lb = seq_len(k, b);
+            const int valid = (int)(Lb - t0 < Q ? Lb - t0 : Q);
             const float lam0 = k.ws_lamc[c * BH + bh];  // the same address in every lane
             // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n]: rows p, k = n (chunks 4q.., 16+4q..)
             const float* S = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
@@ -954,7 +966,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     k.xs = a.xs; k.bcs = a.bcs; k.dts = a.dts; k.ys = a.ys;
     k.dt_bias = a.dt_bias; k.A = a.A; k.D = a.D; k.dt_min = a.dt_min; k.dt_max = a.dt_max;
     k.state_in = a.state_in; k.state_out = a.state_out; k.y = a.y;
-    k.L = a.L; k.batch = (int)a.batch; k.H = a.H; k.G = a.G;
+    k.L = a.L; k.batch = (int)a.batch; k.H = a.H; k.G = a.G; k.lens = a.lens;
     k.nseg = pl.nseg; k.cps = pl.cps;
     // buffer-resource windows: every byte offset inside one must stay below 2^31
     int64_t row_bytes = a.xs > a.bcs ? a.xs : a.bcs;

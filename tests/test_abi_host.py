@@ -50,21 +50,21 @@ def dims(**kw):
 
 
 def conv(d, xbc=FAKE, xs=None, w=FAKE + 0x100000, bias=None, ring_in=None, step=0, ring_out=None,
-         out=FAKE + 0x4000_0000, os_=None):
+         out=FAKE + 0x4000_0000, os_=None, lens=None):
     lib = m2.lib()
     cd = d.conv_dim if d.expand > 0 else 1
     return lib.m2_conv1d_fwd(ctypes.byref(d) if d is not None else None, xbc, xs or cd, w, bias, ring_in, step,
-                             ring_out, out, os_ or cd, None)
+                             ring_out, out, os_ or cd, lens, None)
 
 
 def scan(d, x=FAKE, xs=None, B=FAKE + 0x10000000, C=FAKE + 0x10000100, bcs=None, dt=FAKE + 0x20000000, dts=None,
          dt_bias=FAKE + 0x30000000, A=FAKE + 0x30001000, D=None, dt_min=0.0, dt_max=float("inf"),
-         s_in=None, s_out=None, y=FAKE + 0x4000_0000_00, ys=None, ws=None, ws_bytes=0):
+         s_in=None, s_out=None, y=FAKE + 0x4000_0000_00, ys=None, ws=None, ws_bytes=0, lens=None):
     lib = m2.lib()
     di = d.expand * d.d_model
     return lib.m2_ssd_scan_fwd(ctypes.byref(d), x, xs or di, B, C, bcs or d.n_groups * d.d_state, dt,
                                dts or max(di // max(d.headdim, 1), 1), dt_bias, A, D, dt_min, dt_max, s_in, s_out,
-                               y, ys or di, ws, ws_bytes, None)
+                               y, ys or di, ws, ws_bytes, lens, None)
 
 
 def step(d, xbc=FAKE, xs=None, dt=FAKE + 0x1000000, dts=None, w=FAKE + 0x2000000, bias=None,
@@ -76,7 +76,7 @@ def step(d, xbc=FAKE, xs=None, dt=FAKE + 0x1000000, dts=None, w=FAKE + 0x2000000
 
 
 def test_null_dims():
-    assert m2.lib().m2_conv1d_fwd(None, FAKE, 1, FAKE, None, None, 0, None, FAKE, 1, None) == m2.M2_ERR_NULL
+    assert m2.lib().m2_conv1d_fwd(None, FAKE, 1, FAKE, None, None, 0, None, FAKE, 1, None, None) == m2.M2_ERR_NULL
     assert m2.lib().m2_ssd_scan_workspace(None) == 0
 
 
@@ -95,6 +95,21 @@ def test_conv_validation():
     assert conv(d, os_=d.conv_dim - 8) == m2.M2_ERR_SHAPE
     assert conv(d, out=FAKE + 64) == m2.M2_ERR_ALIAS             # out overlaps xbc
     assert conv(d, ring_in=FAKE + 0x2000_0000_0, ring_out=FAKE + 0x2000_0000_0 + 16) == m2.M2_ERR_ALIAS
+
+
+def test_seq_lens_validation():
+    d = dims()
+    assert conv(d, lens=FAKE + 0x6_0000_0002) == m2.M2_ERR_UNSUPPORTED          # misaligned lengths
+    assert conv(d, lens=FAKE + 0x4000_0000 + 4) == m2.M2_ERR_ALIAS              # lengths inside out
+    assert conv(d, ring_out=FAKE + 0x7_0000_0000, lens=FAKE + 0x7_0000_0000) == m2.M2_ERR_ALIAS
+    ws = dict(ws=FAKE + 0x9_0000_0000, ws_bytes=m2.m2_ssd_scan_workspace(d))
+    assert scan(d, lens=FAKE + 0x6_0000_0002, **ws) == m2.M2_ERR_UNSUPPORTED
+    assert scan(d, lens=FAKE + 0x4000_0000_00 + 8, **ws) == m2.M2_ERR_ALIAS       # lengths inside y
+    assert scan(d, s_out=FAKE + 0x5_0000_0000, lens=FAKE + 0x5_0000_0000 + 64, **ws) == m2.M2_ERR_ALIAS
+    big = dims(batch=1, seqlen=32768)
+    need = m2.m2_ssd_scan_workspace(big)
+    if need:
+        assert scan(big, ws=FAKE + 0x8_0000_0000, ws_bytes=need, lens=FAKE + 0x8_0000_0000 + 256) == m2.M2_ERR_ALIAS
 
 
 def test_empty_batch_is_a_no_op():

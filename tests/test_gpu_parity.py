@@ -96,7 +96,7 @@ def _scan_inputs(d, seed, cached):
     return (inp, x.reshape(lead + (H, P)), b.reshape(lead + (G, N)), c.reshape(lead + (G, N)))
 
 
-def _run_scan(d, inp, x, b, c, state_in, strided=False):
+def _run_scan(d, inp, x, b, c, state_in, strided=False, seq_lens=None):
     io = d.io
     H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
     Bn, L = d.batch, d.seqlen
@@ -116,9 +116,13 @@ def _run_scan(d, inp, x, b, c, state_in, strided=False):
     y = nan_like((Bn, L, H * P), io)
     s_out = torch.full((Bn, H, P, N), float("nan"), device="cuda")
     m2.m2_ssd_scan_fwd(dims, xg, bg, cg, dtg, dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y,
-                       dev32(state_in), s_out, workspace=workspace(dims))
+                       dev32(state_in), s_out, workspace=workspace(dims), seq_lens=_lens_dev(seq_lens))
     torch.cuda.synchronize()
     return host(y).reshape(Bn, L, H, P), host(s_out)
+
+
+def _lens_dev(lens):
+    return None if lens is None else torch.as_tensor(np.asarray(lens, np.int32), device="cuda")
 
 
 SCAN_CASES = [
@@ -190,6 +194,126 @@ def test_ssd_scan_deterministic():
     y2, s2 = _run_scan(d, inp, x, b, c, inp.state0)
     np.testing.assert_array_equal(y1, y2)
     np.testing.assert_array_equal(s1, s2)
+
+
+# ----------------------------------------------------------------------------- right-padded batches
+# Sequence b of a batch holds its first seq_lens[b] tokens; the rest is padding.  Lengths outside
+# [0, seqlen] are clamped by the library, so the oracle gets the clamped values.
+
+PAD_CONV_CASES = [
+    # (config index, dims overrides, lengths, ring history, ring phase)
+    (2, dict(batch=6, seqlen=200), [200, 0, 1, 64, 131, 3], True, 2),
+    (0, dict(batch=3, seqlen=70), [70, 5, 0], False, 0),
+    (2, dict(batch=2, seqlen=96), [-3, 1000], True, 1),
+]
+
+
+@pytest.mark.parametrize("case", PAD_CONV_CASES, ids=lambda c: "cfg%d-%s-%s" % (c[0], c[1], c[2]))
+def test_conv1d_padded_batch_parity(case):
+    _need_gpu()
+    idx, over, lens, use_ring, phase = case
+    d = workloads.CONFIGS[idx].dims.replace(**over)
+    inp = workloads.generate(d, 1100 + idx, use_ring)
+    io = d.io
+    Bn, L, Cd, W = d.batch, d.seqlen, d.conv_dim, d.d_conv
+    eff = np.clip(lens, 0, L)
+    ring_in = inp.ring0 if use_ring else None
+    ref, ref_ring = oracle.conv1d(inp.xbc, inp.conv_w, inp.conv_b, ring_in, phase, seq_lens=eff)
+    out = nan_like((Bn, L, Cd), io)
+    ring_out = nan_like((Bn, W, Cd), io)
+    m2.m2_conv1d_fwd(dims_of(d), dev(inp.xbc, io), dev32(inp.conv_w), dev32(inp.conv_b), out,
+                     dev(ring_in, io), phase, ring_out, seq_lens=_lens_dev(lens))
+    torch.cuda.synchronize()
+    got = host(out)
+    for b, n in enumerate(eff):
+        if n:
+            assert oracle.max_rel_err(got[b, :n], ref[b, :n]) <= tol_for(io), b
+        assert np.isnan(got[b, n:]).all(), "padding of sequence %d written" % b
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
+
+
+PAD_SCAN_CASES = [
+    # (config index, dims overrides, lengths, cached initial state)
+    (2, dict(batch=4, seqlen=300), [300, 0, 37, 129], True),
+    (0, dict(batch=3, seqlen=100), [100, 17, 0], True),
+    (2, dict(batch=2, seqlen=96), [-3, 1000], False),
+    (2, dict(batch=1, seqlen=130, chunk_size=16), [113], True),
+]
+
+
+@pytest.mark.parametrize("case", PAD_SCAN_CASES, ids=lambda c: "cfg%d-%s-%s" % (c[0], c[1], c[2]))
+def test_ssd_scan_padded_batch_parity(case):
+    _need_gpu()
+    idx, over, lens, cached = case
+    d = workloads.CONFIGS[idx].dims.replace(**over)
+    inp, x, b, c = _scan_inputs(d, 2100 + idx, cached)
+    eff = np.clip(lens, 0, d.seqlen)
+    y, s = _run_scan(d, inp, x, b, c, inp.state0, seq_lens=lens)
+    yr, sr = oracle.ssd_scan(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, seq_lens=eff)
+    tol = tol_for(d.io)
+    for bb, n in enumerate(eff):
+        if n:
+            assert oracle.max_rel_err(y[bb, :n], yr[bb, :n]) <= tol, bb
+        assert np.isnan(y[bb, n:]).all(), "padding of sequence %d written" % bb
+    assert oracle.max_rel_err(s, sr) <= tol
+
+
+def test_ssd_scan_padded_batch_several_segments():
+    """Long sequences run as several segments per sequence (chain of end states, fix-up of the later
+    segments' outputs); a sequence that ends early leaves whole segments empty."""
+    _need_gpu()
+    d = workloads.CONFIGS[2].dims.replace(batch=3, seqlen=4096)
+    assert m2.m2_ssd_scan_workspace(dims_of(d)) > 0, "expected a multi-segment plan at this size"
+    lens = [4096, 1500, 0]
+    inp, x, b, c = _scan_inputs(d, 2150, True)
+    y, s = _run_scan(d, inp, x, b, c, inp.state0, seq_lens=lens)
+    yr, sr = oracle.ssd_scan(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, seq_lens=lens)
+    for bb, n in enumerate(lens):
+        if n:
+            assert oracle.max_rel_err(y[bb, :n], yr[bb, :n]) <= 2e-2, bb
+        assert np.isnan(y[bb, n:]).all(), "padding of sequence %d written" % bb
+    assert oracle.max_rel_err(s, sr) <= 2e-2
+
+
+def test_padded_prefill_then_decode():
+    """A right-padded prefill hands each sequence's own ring and state to the decode step."""
+    _need_gpu()
+    L, steps = 150, 4
+    lens = [150, 40, 2]
+    d = workloads.CONFIGS[2].dims.replace(batch=3, seqlen=L)
+    inp = workloads.generate(d, 43, True)
+    tok = workloads.generate(d.replace(seqlen=1), 44, False, steps)
+    io = d.io
+    Bn, H, P, N, G, W, Cd = d.batch, d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    lg = _lens_dev(lens)
+    act = nan_like((Bn, L, Cd), io)
+    ring = nan_like((Bn, W, Cd), io)
+    m2.m2_conv1d_fwd(dims, dev(inp.xbc, io), dev32(inp.conv_w), dev32(inp.conv_b), act, dev(inp.ring0, io), 0,
+                     ring, seq_lens=lg)
+    y = nan_like((Bn, L, H * P), io)
+    state = torch.empty((Bn, H, P, N), device="cuda")
+    m2.m2_ssd_scan_fwd(dims, act[:, :, :H * P], act[:, :, H * P:H * P + G * N], act[:, :, H * P + G * N:],
+                       dev(inp.dt_raw, io), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(inp.state0),
+                       state, workspace=workspace(dims), seq_lens=lg)
+    ys = []
+    xt, dtt = dev(tok.xbc, io), dev(tok.dt_raw, io)
+    w, cb, dtb, A, D = (dev32(a) for a in (inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D))
+    for t in range(steps):
+        yt = nan_like((Bn, H * P), io)
+        m2.m2_ssd_step(dims, xt[t], dtt[t], w, cb, dtb, A, D, ring, t, state, yt)
+        ys.append(host(yt))
+    torch.cuda.synchronize()
+    # oracle: the same padded prefill, then the same steps
+    ref_act, r_ring = oracle.conv1d(inp.xbc, inp.conv_w, inp.conv_b, inp.ring0, 0, seq_lens=lens)
+    rx, rb, rc = oracle.split_act(np.nan_to_num(ref_act), H, P, N, G)
+    _, r_state = oracle.ssd_scan(rx, rb, rc, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, seq_lens=lens)
+    for t in range(steps):
+        yr, r_ring, r_state = oracle.ssd_step(tok.xbc[t], tok.dt_raw[t], inp.conv_w, inp.conv_b, inp.dt_bias,
+                                              inp.A, inp.D, r_ring, t, r_state, H, P, N, G)
+        assert oracle.max_rel_err(ys[t], yr) <= 2e-2, "step %d" % t
+    assert oracle.max_rel_err(host(state), r_state) <= 2e-2
+    np.testing.assert_array_equal(host(ring), r_ring)
 
 
 # ----------------------------------------------------------------------------- decode step
