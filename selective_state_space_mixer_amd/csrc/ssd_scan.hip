@@ -224,6 +224,10 @@ struct ScanK {
     float* ws_state;   // [nseg][batch*H][P*N]: segment end states, then segment initial states
     float* ws_lam;     // [nseg][batch*H]: summed log-decay of each segment
     float* ws_lamc;    // [nchunks][batch*H]: summed log-decay of the chunk's segment before the chunk
+    int* ws_nfix;      // [nseg-1][batch*H]: leading chunks of each later segment that need the fix-up
+    uint2* fix_items;  // the fix-up's work list: (later segment - 1) * batch*H + sequence*H + head, chunk
+    int* fix_count;    // its length
+    uint16_t* ws_tin;  // bf16 outputs: [nseg-1][batch*H][P*N] bf16 initial states of segments 1.. (else null)
     const int32_t* lens;  // [batch] tokens of each right-padded sequence, or null (all L)
     int64_t L;
     int batch, H, G;
@@ -238,6 +242,12 @@ __device__ __forceinline__ int64_t seq_len(const ScanK& k, int64_t b) {
     const int64_t v = k.lens[b];
     return v < 0 ? 0 : (v > k.L ? k.L : v);
 }
+
+// A later segment starts from zero in the main pass; the part of its output that comes from its true
+// initial state decays with the segment's summed log-decay and is added afterwards only where that
+// factor is at least e^cut (the term dropped beyond it is far under the output's rounding: e^-12 is
+// 6e-6 of |S_in . C_t| against bf16's 2^-9; e^-20.8 is 1e-9 for fp32 outputs).
+template <typename T> constexpr float fix_cut() { return sizeof(T) == 2 ? -12.0f : -20.8f; }
 
 // Block -> logical unit.  Consecutive blocks are dealt round-robin to the 8 XCDs; the remap
 // gives each XCD a contiguous run of logical units (the head groups of one sequence and
@@ -480,6 +490,7 @@ ssd_chunk_scan_kernel(ScanK k)
     // tracks sig (and the segment's summed log-decay) as it prepares the chunks in order.
     constexpr float kRescale = 40.0f;
     float sig = 0.0f, lam_seg = 0.0f;
+    int nfix = 0;  // chunks of this segment whose starting decay factor is at least e^cut
     // dt and the cumulative log-decay of this wave's head over chunk i, into statistics buffer buf
     auto stats = [&](int i, int buf, uint32_t raw) __attribute__((always_inline)) {
         if (!stats_writer) return;
@@ -500,6 +511,7 @@ ssd_chunk_scan_kernel(ScanK k)
         sig = rescale ? 0.0f : sig_prev + lam_end;
         const float lam_before = lam_seg;  // summed log-decay of the segment before chunk i
         lam_seg += lam_end;
+        nfix += lam_before >= fix_cut<T>() ? 1 : 0;
         if (lane < Q) {
             float* st = &sSt[buf][hw * Q + lane];
             st[0 * QS] = lam * kLog2e;
@@ -751,21 +763,66 @@ ssd_chunk_scan_kernel(ScanK k)
             }
         }
     }
-    if (k.nseg > 1 && hvalid && stats_writer && lane == 0) k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+    if (k.nseg > 1 && hvalid && stats_writer && lane == 0) {
+        k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+        if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
+    }
+}
+
+// The fix-up's work list: one entry per (later segment, sequence-head, chunk) with chunk < nfix of
+// its pair.  One block of 256 threads: thread t owns pairs t, t + 256, ..., counts their chunks,
+// takes its place in the list from a block-wide prefix sum and writes its entries.
+__device__ void list_fix_items(const int* __restrict__ nfix, uint2* __restrict__ items, int* __restrict__ count,
+                               int npairs)
+{
+    constexpr int kUnroll = 8;
+    __shared__ int sTot[4];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int mine = 0;
+    for (int p0 = t; p0 < npairs; p0 += 256 * kUnroll) {
+        int v[kUnroll];
+#pragma unroll
+        for (int e = 0; e < kUnroll; ++e) v[e] = p0 + e * 256 < npairs ? nfix[p0 + e * 256] : 0;
+#pragma unroll
+        for (int e = 0; e < kUnroll; ++e) mine += v[e];
+    }
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) sTot[w] = incl;
+    __syncthreads();
+    int off = incl - mine;
+    for (int i = 0; i < w; ++i) off += sTot[i];
+    for (int p = t; p < npairs; p += 256) {
+        const int n = nfix[p];
+        for (int j = 0; j < n; ++j) items[off++] = make_uint2((uint32_t)p, (uint32_t)j);
+    }
+    if (t == 255) *count = off;
 }
 
 // Chain the segments.  E[seg] is segment seg's end state from its own start (segment 0 starts from
 // the caller's state), lam[seg] its summed log-decay.  The true end states follow
 //   T[0] = E[0],  T[seg] = e^lam[seg] T[seg-1] + E[seg];
-// T[seg] (the initial state of segment seg+1) is written over E[seg], and T[nseg-1] is the final
+// T[seg] (the initial state of segment seg+1) is written over E[seg] (or, for bf16 outputs, to a
+// bf16 copy), and T[nseg-1] is the final
 // state.  Only the combine is sequential: the loads of a batch of segments are issued together.
+// The block row past the last sequence-head writes the fix-up's work list instead.
 __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restrict__ ws_state,
                                                                 const float* __restrict__ ws_lam,
                                                                 float* __restrict__ state_out, int BH, int nseg,
-                                                                int PN)
+                                                                int PN, const int* __restrict__ nfix,
+                                                                uint2* __restrict__ items, int* __restrict__ count,
+                                                                uint16_t* __restrict__ tin)
 {
     constexpr int kBatch = 16;
     const int bh = blockIdx.y;
+    if (bh == BH) {
+        if (blockIdx.x == 0) list_fix_items(nfix, items, count, (nseg - 1) * BH);
+        return;
+    }
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= PN) return;
     float s = 0.0f;
@@ -782,7 +839,12 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
             const int seg = seg0 + j;
             if (seg < nseg) {
                 s = (seg == 0 ? loc[j] : fast_exp(dec[j]) * s + loc[j]);
-                if (seg < nseg - 1) ws_state[((int64_t)seg * BH + bh) * PN + i] = s;
+                if (seg < nseg - 1) {
+                    // the initial state of segment seg+1, for the fix-up: in bf16 when that is the
+                    // precision it enters the fix-up's product in
+                    if (tin) tin[((int64_t)seg * BH + bh) * PN + i] = f32_to_bits(s);
+                    else ws_state[((int64_t)seg * BH + bh) * PN + i] = s;
+                }
                 else if (state_out) state_out[(int64_t)bh * PN + i] = s;
             }
         }
@@ -792,130 +854,125 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
 // Add the part of each later segment's output that comes from its true initial state S_in (the
 // main pass ran it from zero):  y[t] += e^Lam_t (S_in . C_t),  Lam_t = the summed log-decay from the
 // segment's first token through t.  The factor only falls along the segment, so only a prefix of its
-// chunks needs the term: those whose starting factor is at least e^cut.  The cut keeps the dropped
-// term far under the output's rounding: e^-12 (6e-6 of |S_in . C_t|, against bf16's 2^-9) for bf16
-// outputs, e^-20.8 (1e-9) for fp32.
-//
-// Work items are chunks of (segment, sequence, head), numbered chunk-major so the leading chunks,
-// which nearly always need the term, spread over all waves.  A wave takes items w + i * waves; one
-// lane per item reads the chunk's starting log-decay (left by the main pass), so the wave learns at
-// once which items need work.  For each, every load it needs (S_in, dt, C, y) is independent and
-// issued together.
-template <typename T> constexpr float fix_cut() { return sizeof(T) == 2 ? -12.0f : -20.8f; }
+// chunks needs the term: those whose starting factor is at least e^cut (fix_cut), counted by the main
+// pass and listed by the chain kernel.  A wave takes one listed chunk at a time: S_in, dt, C and y
+// are loaded together, then the term is added and y stored.
 constexpr int kFixThreads = 256;
 constexpr int kFixBlocks = 2048;
+
+// one chunk's inputs of the fix-up, as loaded
+template <typename T> struct YRaw;
+template <> struct YRaw<bf16_t> { using type = uint2; };   // 4 bf16 outputs
+template <> struct YRaw<float> { using type = float4; };
 
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
 {
     constexpr int NPB = P / 16, KS_N = (N + 31) / 32, NTB = Q / 16;
     constexpr int EB = (int)sizeof(T);
-    constexpr float kCut = fix_cut<T>();
+    using YV = typename YRaw<T>::type;
     const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
-    const int64_t gw = (int64_t)blockIdx.x * (kFixThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * (kFixThreads / 64);
     const int BH = k.batch * k.H;
-    const int64_t per_j = (int64_t)(k.nseg - 1) * BH;
-    const int64_t items = (int64_t)k.cps * per_j;
+    const int count = *k.fix_count;
+    const int64_t nwaves = (int64_t)gridDim.x * (kFixThreads / 64);
+    for (int64_t item = (int64_t)blockIdx.x * (kFixThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         item < count; item += nwaves) {
+        const uint2 it = k.fix_items[item];  // the same address in every lane
+        const int pair = (int)it.x, j = (int)it.y;
+        const int seg = 1 + pair / BH, bh = pair % BH;
+        const int64_t b = bh / k.H;
+        const int h = bh % k.H, g = h / (k.H / k.G);
+        const int64_t c = (int64_t)seg * k.cps + j;
+        const int64_t t0 = c * Q;
+        const int64_t left = seq_len(k, b) - t0;
+        const int valid = (int)(left < Q ? left : Q);  // >= 1: listed chunks lie inside the sequence
 
-    for (int64_t base = gw; base < items; base += nwaves * 64) {
-        // item -> chunk; which of this wave's 64 items need the term
-        bool need = false;
-        {
-            const int64_t item = base + (int64_t)lane * nwaves;
-            if (item < items) {
-                const int j = (int)(item / per_j);
-                const int seg = 1 + (int)((item % per_j) / BH), bh = (int)(item % BH);
-                const int64_t c = (int64_t)seg * k.cps + j;
-                need = c * Q < seq_len(k, bh / k.H) && k.ws_lamc[c * BH + bh] >= kCut;
-            }
-        }
-        uint64_t mask = __builtin_amdgcn_ballot_w64(need);
-        while (mask) {
-            const int i = __builtin_ctzll(mask);
-            mask &= mask - 1;
-            const int64_t item = base + (int64_t)i * nwaves;
-            const int j = (int)(item / per_j);
-            const int seg = 1 + (int)((item % per_j) / BH), bh = (int)(item % BH);
-            const int64_t c = (int64_t)seg * k.cps + j;
-            const int64_t b = bh / k.H;
-            const int h = bh % k.H, g = h / (k.H / k.G);
-            const int64_t t0 = c * Q;
-            const int64_t Lb = seq_len(k, b);
-            const int valid = (int)(Lb - t0 < Q ? Lb - t0 : Q);
-            const float lam0 = k.ws_lamc[c * BH + bh];  // the same address in every lane
-            // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n]: rows p, k = n (chunks 4q.., 16+4q..)
-            const float* S = k.ws_state + ((int64_t)(seg - 1) * BH + bh) * P * N;
-            Frag<T> sa[NPB][KS_N];
+        // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n]: rows p, k = n (chunks 4q.., 16+4q..),
+        // from the chain's bf16 copy for bf16 outputs, else from its fp32 states
+        Frag<T> sa[NPB][KS_N];
+        const int64_t soff = ((int64_t)(seg - 1) * BH + bh) * P * N;
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+            for (int ks = 0; ks < KS_N; ++ks)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int n0 = 32 * ks + 16 * cc + 4 * q;
+                    const int64_t e = soff + (int64_t)(pb * 16 + li) * N + n0;
+                    if (n0 >= N) {
+                        sa[pb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
+                    } else if constexpr (EB == 2) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(k.ws_tin + e);
+                        sa[pb][ks].w[2 * cc] = v.x;
+                        sa[pb][ks].w[2 * cc + 1] = v.y;
+                    } else {
+                        const float4 v = *reinterpret_cast<const float4*>(k.ws_state + e);
+                        sa[pb][ks].set(cc, v.x, v.y, v.z, v.w);
+                    }
+                }
+        // the chunk: starting log-decay, dt of token `lane`, C rows and y (rows past the sequence
+        // clamped to its last token, their stores skipped)
+        const float lam0 = k.ws_lamc[c * BH + bh];
+        const T* dtp = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
+        const T dtr = dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
+        const uint8_t* cp =
+            reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N);
+        uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P);
+        Frag<T> cf[NTB][KS_N];
+        YV yv[NTB][NPB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const int t = tb * 16 + li;
+            const int tr = t < valid ? t : valid - 1;
+#pragma unroll
+            for (int ks = 0; ks < KS_N; ++ks)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int n0 = 32 * ks + 16 * cc + 4 * q;
+                    if (n0 < N) {
+                        const uint8_t* src = cp + ((t0 + tr) * k.bcs + n0) * EB;
+                        if constexpr (EB == 2) {
+                            const uint2 v = *reinterpret_cast<const uint2*>(src);
+                            cf[tb][ks].w[2 * cc] = v.x;
+                            cf[tb][ks].w[2 * cc + 1] = v.y;
+                        } else {
+                            const float4 v = *reinterpret_cast<const float4*>(src);
+                            cf[tb][ks].set(cc, v.x, v.y, v.z, v.w);
+                        }
+                    } else {
+                        cf[tb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
+                    }
+                }
 #pragma unroll
             for (int pb = 0; pb < NPB; ++pb)
+                yv[tb][pb] = *reinterpret_cast<const YV*>(yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB);
+        }
+        const float dtv = lane < valid ? dt_of(to_f32(dtr), k.dt_bias[h], k.dt_min, k.dt_max) : 0.0f;
+        const float lam = lam0 + wave_prefix_sum(dtv * k.A[h]);
 #pragma unroll
-                for (int ks = 0; ks < KS_N; ++ks)
+        for (int tb = 0; tb < NTB; ++tb) {
+            const int t = tb * 16 + li;
+            const bool ok = t < valid;
+            const int tr = ok ? t : valid - 1;
+            const float el = fast_exp(__shfl(lam, t, 64));
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        const int n0 = 32 * ks + 16 * cc + 4 * q;
-                        if (n0 < N) {
-                            const float4 v = *reinterpret_cast<const float4*>(S + (int64_t)(pb * 16 + li) * N + n0);
-                            sa[pb][ks].set(cc, v.x, v.y, v.z, v.w);
-                        } else {
-                            sa[pb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
-                        }
-                    }
-            const float bias_h = k.dt_bias[h], A_h = k.A[h];
-            const T* dtp = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
-            const uint8_t* cp =
-                reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N);
-            uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P);
-            // log-decay through each token of the chunk
-            const float raw = to_f32(dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts]);
-            const float dtv = lane < valid ? dt_of(raw, bias_h, k.dt_min, k.dt_max) : 0.0f;
-            const float lam = lam0 + wave_prefix_sum(dtv * A_h);
+            for (int pb = 0; pb < NPB; ++pb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) {
-                const int t = tb * 16 + li;
-                const bool ok = t < valid;
-                const int tr = ok ? t : valid - 1;  // rows past the sequence: loads clamped, stores skipped
-                const float el = fast_exp(__shfl(lam, t, 64));
-                Frag<T> cf[KS_N];
-#pragma unroll
-                for (int ks = 0; ks < KS_N; ++ks)
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        const int n0 = 32 * ks + 16 * cc + 4 * q;
-                        if (n0 < N) {
-                            const uint8_t* src = cp + ((t0 + tr) * k.bcs + n0) * EB;
-                            if constexpr (EB == 2) {
-                                const uint2 v = *reinterpret_cast<const uint2*>(src);
-                                cf[ks].set(cc, __uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-                            } else {
-                                const float4 v = *reinterpret_cast<const float4*>(src);
-                                cf[ks].set(cc, v.x, v.y, v.z, v.w);
-                            }
-                        } else {
-                            cf[ks].set(cc, 0.f, 0.f, 0.f, 0.f);
-                        }
-                    }
-#pragma unroll
-                for (int pb = 0; pb < NPB; ++pb) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[ks]);
-                    // the lane holds y[t][p = pb*16 + 4q .. +3]
-                    uint8_t* dst = yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB;
-                    if constexpr (EB == 2) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(dst);
-                        const float o0 = __uint_as_float(v.x << 16) + el * acc[0];
-                        const float o1 = __uint_as_float(v.x & 0xffff0000u) + el * acc[1];
-                        const float o2 = __uint_as_float(v.y << 16) + el * acc[2];
-                        const float o3 = __uint_as_float(v.y & 0xffff0000u) + el * acc[3];
-                        if (ok) *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-                    } else {
-                        const float4 v = *reinterpret_cast<const float4*>(dst);
-                        if (ok)
-                            *reinterpret_cast<float4*>(dst) = make_float4(v.x + el * acc[0], v.y + el * acc[1],
-                                                                          v.z + el * acc[2], v.w + el * acc[3]);
-                    }
+                for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[tb][ks]);
+                // the lane holds y[t][p = pb*16 + 4q .. +3]
+                uint8_t* dst = yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB;
+                const YV v = yv[tb][pb];
+                if constexpr (EB == 2) {
+                    const float o0 = __uint_as_float(v.x << 16) + el * acc[0];
+                    const float o1 = __uint_as_float(v.x & 0xffff0000u) + el * acc[1];
+                    const float o2 = __uint_as_float(v.y << 16) + el * acc[2];
+                    const float o3 = __uint_as_float(v.y & 0xffff0000u) + el * acc[3];
+                    if (ok) *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+                } else {
+                    if (ok)
+                        *reinterpret_cast<float4*>(dst) = make_float4(v.x + el * acc[0], v.y + el * acc[1],
+                                                                      v.z + el * acc[2], v.w + el * acc[3]);
                 }
             }
         }
@@ -930,8 +987,29 @@ struct Plan {
     size_t ws_bytes;
 };
 
+// Byte offsets of the workspace parts, from a 256-byte aligned base (the caller's pointer rounded up):
+// segment states [nseg][B*H][P*N] f32, segment log-decays [nseg][B*H] f32, per-chunk starting
+// log-decays [nchunks][B*H] f32, fix-up counts [nseg-1][B*H] i32, the work list's length, the work
+// list [(nseg-1)*B*H*cps] (pair, chunk), and for bf16 outputs the segments' initial states in bf16
+// [nseg-1][B*H][P*N].
+struct WsLayout {
+    size_t lam, lamc, nfix, count, items, tin, total;
+};
+static WsLayout ws_layout(int64_t nseg, int64_t BH, int64_t PN, int64_t nchunks, int64_t cps, bool bf16) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    WsLayout w;
+    w.lam = up((size_t)(nseg * BH * PN) * sizeof(float));
+    w.lamc = up(w.lam + (size_t)(nseg * BH) * sizeof(float));
+    w.nfix = up(w.lamc + (size_t)(nchunks * BH) * sizeof(float));
+    w.count = up(w.nfix + (size_t)((nseg - 1) * BH) * sizeof(int));
+    w.items = up(w.count + sizeof(int));
+    w.tin = up(w.items + (size_t)((nseg - 1) * BH * cps) * sizeof(uint2));
+    w.total = w.tin + (bf16 ? (size_t)((nseg - 1) * BH * PN) * sizeof(uint16_t) : 0);
+    return w;
+}
+
 // Segments: enough (sequence, head group, segment) units for one round of resident blocks.
-static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, int hpw, int bpc) {
+static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, int hpw, int bpc, bool bf16) {
     Plan pl;
     const int64_t nchunks = (L + Q - 1) / Q;
     const int hpg = H / G;
@@ -945,16 +1023,14 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, i
     nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
     pl.nseg = (int)nseg;
     pl.cps = (int)cps;
-    pl.ws_bytes = nseg > 1 ? ((size_t)(nseg * batch * H) * ((size_t)N_P_N + 1) + (size_t)(nchunks * batch * H)) *
-                                 sizeof(float) + 256
-                           : 0;
+    pl.ws_bytes = nseg > 1 ? ws_layout(nseg, batch * H, N_P_N, nchunks, cps, bf16).total + 256 : 0;
     return pl;
 }
 
 template <typename T, int Q, int P, int N>
 static Plan plan_of(int64_t batch, int64_t L, int H, int G) {
     using Cf = Cfg<T, Q, P, N>;
-    return plan_for(batch, L, H, G, P * N, Q, Cf::HPW, Cf::BPC);
+    return plan_for(batch, L, H, G, P * N, Q, Cf::HPW, Cf::BPC, sizeof(T) == 2);
 }
 
 template <typename T, int Q, int P, int N>
@@ -979,24 +1055,32 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     k.ws_state = nullptr;
     k.ws_lam = nullptr;
     k.ws_lamc = nullptr;
+    k.ws_nfix = nullptr;
+    k.fix_items = nullptr;
+    k.fix_count = nullptr;
+    k.ws_tin = nullptr;
     if (pl.nseg > 1) {
-        k.ws_state = reinterpret_cast<float*>(a.ws);
-        k.ws_lam = k.ws_state + (size_t)pl.nseg * BH * P * N;
-        k.ws_lamc = k.ws_lam + (size_t)pl.nseg * BH;
+        const WsLayout w = ws_layout(pl.nseg, BH, P * N, (a.L + Q - 1) / Q, pl.cps, sizeof(T) == 2);
+        uint8_t* base = reinterpret_cast<uint8_t*>(((uintptr_t)a.ws + 255) & ~(uintptr_t)255);
+        k.ws_state = reinterpret_cast<float*>(base);
+        k.ws_lam = reinterpret_cast<float*>(base + w.lam);
+        k.ws_lamc = reinterpret_cast<float*>(base + w.lamc);
+        k.ws_nfix = reinterpret_cast<int*>(base + w.nfix);
+        k.fix_count = reinterpret_cast<int*>(base + w.count);
+        k.fix_items = reinterpret_cast<uint2*>(base + w.items);
+        if (sizeof(T) == 2) k.ws_tin = reinterpret_cast<uint16_t*>(base + w.tin);
     }
     // every segment at once (later ones from a zero state), then, with several segments, the chain
     // of their end states and the fix-up of the later segments' leading chunks
     k.nblocks = pl.nseg * (int)a.batch * pl.nhu;
     hipError_t e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
     if (e != hipSuccess || pl.nseg == 1) return e;
-    dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH);
+    // one extra block row lists the fix-up's work
+    dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH + 1);
     e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k.ws_state, (const float*)k.ws_lam, a.state_out,
-                      BH, pl.nseg, P * N);
+                      BH, pl.nseg, P * N, (const int*)k.ws_nfix, k.fix_items, k.fix_count, k.ws_tin);
     if (e != hipSuccess) return e;
-    const int64_t items = (int64_t)pl.cps * (pl.nseg - 1) * BH;
-    const int64_t blocks = (items + 63) / 64;
-    return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3((unsigned)(blocks < kFixBlocks ? blocks : kFixBlocks)),
-                         dim3(kFixThreads), 0, s, k);
+    return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3(kFixBlocks), dim3(kFixThreads), 0, s, k);
 }
 
 template <typename T, int Q>
