@@ -823,29 +823,34 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
         if (blockIdx.x == 0) list_fix_items(nfix, items, count, (nseg - 1) * BH);
         return;
     }
-    const int i = blockIdx.x * 256 + threadIdx.x;
+    // four consecutive state entries per thread (PN is a multiple of 16)
+    const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= PN) return;
-    float s = 0.0f;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int seg0 = 0; seg0 < nseg; seg0 += kBatch) {
-        float loc[kBatch], dec[kBatch];
+        float4 loc[kBatch];
+        float dec[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int seg = seg0 + j < nseg ? seg0 + j : nseg - 1;
-            loc[j] = ws_state[((int64_t)seg * BH + bh) * PN + i];
+            loc[j] = *reinterpret_cast<const float4*>(ws_state + ((int64_t)seg * BH + bh) * PN + i);
             dec[j] = ws_lam[(int64_t)seg * BH + bh];
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int seg = seg0 + j;
             if (seg < nseg) {
-                s = (seg == 0 ? loc[j] : fast_exp(dec[j]) * s + loc[j]);
+                const float d = seg == 0 ? 0.0f : fast_exp(dec[j]);
+                s = make_float4(d * s.x + loc[j].x, d * s.y + loc[j].y, d * s.z + loc[j].z, d * s.w + loc[j].w);
+                const int64_t o = ((int64_t)seg * BH + bh) * PN + i;
                 if (seg < nseg - 1) {
                     // the initial state of segment seg+1, for the fix-up: in bf16 when that is the
                     // precision it enters the fix-up's product in
-                    if (tin) tin[((int64_t)seg * BH + bh) * PN + i] = f32_to_bits(s);
-                    else ws_state[((int64_t)seg * BH + bh) * PN + i] = s;
+                    if (tin) *reinterpret_cast<uint2*>(tin + o) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+                    else *reinterpret_cast<float4*>(ws_state + o) = s;
+                } else if (state_out) {
+                    *reinterpret_cast<float4*>(state_out + (int64_t)bh * PN + i) = s;
                 }
-                else if (state_out) state_out[(int64_t)bh * PN + i] = s;
             }
         }
     }
@@ -1076,7 +1081,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     hipError_t e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
     if (e != hipSuccess || pl.nseg == 1) return e;
     // one extra block row lists the fix-up's work
-    dim3 g2((unsigned)((P * N + 255) / 256), (unsigned)BH + 1);
+    dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH + 1);
     e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k.ws_state, (const float*)k.ws_lam, a.state_out,
                       BH, pl.nseg, P * N, (const int*)k.ws_nfix, k.fix_items, k.fix_count, k.ws_tin);
     if (e != hipSuccess) return e;
