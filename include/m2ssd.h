@@ -126,7 +126,9 @@ size_t m2_ssd_scan_workspace(const m2_dims* dims);
  *          seq_lens[b] tokens (clamped to [0, seqlen]): y at later positions is left as it
  *          was, and state_out is the state after its last token (state_in, or zero, for an
  *          empty one).  Must not overlap an output or the workspace.
- * x/B/C may be strided views into one conv1d output (token stride conv_dim). */
+ * x/B/C may be strided views into one conv1d output (token stride conv_dim).
+ * x, B, C and y must start on 16-byte boundaries and their token strides be multiples of 16
+ * bytes (else M2_ERR_UNSUPPORTED); dt has no alignment requirement. */
 m2_status m2_ssd_scan_fwd(const m2_dims* dims,
                           const void* x, int64_t x_tok_stride,
                           const void* B, const void* C, int64_t bc_tok_stride,

@@ -162,6 +162,10 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
         overlap(rs_out, ry))
         return M2_ERR_ALIAS;
     if (!aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)seq_lens & 3u)) return M2_ERR_UNSUPPORTED;
+    // x, B, C and y move in 16-byte pieces of rows
+    if (rows > 0 && (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+                     (x_tok_stride * d.esize) % 16 || (bc_tok_stride * d.esize) % 16 || (y_tok_stride * d.esize) % 16))
+        return M2_ERR_UNSUPPORTED;
     const size_t need = m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
     if (need > 0 && (!workspace || workspace_bytes < need)) return M2_ERR_WORKSPACE;
     const Range rl = span(seq_lens, d.batch, 1, 1, 4);

@@ -865,18 +865,41 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
 constexpr int kFixThreads = 256;
 constexpr int kFixBlocks = 2048;
 
-// one chunk's inputs of the fix-up, as loaded
-template <typename T> struct YRaw;
-template <> struct YRaw<bf16_t> { using type = uint2; };   // 4 bf16 outputs
-template <> struct YRaw<float> { using type = float4; };
+// Eight consecutive k-values of one lane, k = kbase + 8q .. +7, for a K = 32 MFMA step.  The fix-up
+// gives both operands this assignment (any assignment the two operands share gives the same sum),
+// so each lane reads 16 (bf16) or 32 (fp32) contiguous bytes of a row.
+__device__ __forceinline__ void load8(Frag<bf16_t>& f, const void* src) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    f.w[0] = v.x; f.w[1] = v.y; f.w[2] = v.z; f.w[3] = v.w;
+}
+__device__ __forceinline__ void load8(Frag<float>& f, const void* src) {
+    const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+template <typename T> __device__ __forceinline__ void zero8(Frag<T>& f) {
+    f.set(0, 0.f, 0.f, 0.f, 0.f);
+    f.set(1, 0.f, 0.f, 0.f, 0.f);
+}
 
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
 {
     constexpr int NPB = P / 16, KS_N = (N + 31) / 32, NTB = Q / 16;
     constexpr int EB = (int)sizeof(T);
-    using YV = typename YRaw<T>::type;
+    // The term comes out of the MFMA as 4 consecutive p of one row per lane; it goes through LDS
+    // (fp32, 16 rows at a time) so that y is read and written as 16 contiguous bytes per lane, whole
+    // rows of the head per group of lanes.
+    constexpr int EPL = 16 / EB;                  // y elements per lane and row piece
+    constexpr int LPR = P / EPL;                  // lanes per row
+    constexpr int RPP = 64 / LPR;                 // rows per pass
+    constexpr int NPASS = (16 + RPP - 1) / RPP;   // passes per 16 rows
+    constexpr int RS = P + 4;                     // LDS row stride in floats
+    static_assert(64 % LPR == 0 && LPR >= 1, "y row pieces must tile a wave");
+    __shared__ __attribute__((aligned(16))) float sAcc[kFixThreads / 64][16 * RS];
     const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
+    float* acc_lds = sAcc[threadIdx.x >> 6];
+    const int prow = lane / LPR, pcol = (lane % LPR) * EPL;  // this lane's row in a pass, first column
     const int BH = k.batch * k.H;
     const int count = *k.fix_count;
     const int64_t nwaves = (int64_t)gridDim.x * (kFixThreads / 64);
@@ -892,31 +915,21 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
         const int64_t left = seq_len(k, b) - t0;
         const int valid = (int)(left < Q ? left : Q);  // >= 1: listed chunks lie inside the sequence
 
-        // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n]: rows p, k = n (chunks 4q.., 16+4q..),
-        // from the chain's bf16 copy for bf16 outputs, else from its fp32 states
+        // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n] (rows p), from the chain's bf16
+        // copy for bf16 outputs, else from its fp32 states
         Frag<T> sa[NPB][KS_N];
         const int64_t soff = ((int64_t)(seg - 1) * BH + bh) * P * N;
+        const void* sbase = EB == 2 ? (const void*)(k.ws_tin + soff) : (const void*)(k.ws_state + soff);
 #pragma unroll
         for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-            for (int ks = 0; ks < KS_N; ++ks)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int n0 = 32 * ks + 16 * cc + 4 * q;
-                    const int64_t e = soff + (int64_t)(pb * 16 + li) * N + n0;
-                    if (n0 >= N) {
-                        sa[pb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
-                    } else if constexpr (EB == 2) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(k.ws_tin + e);
-                        sa[pb][ks].w[2 * cc] = v.x;
-                        sa[pb][ks].w[2 * cc + 1] = v.y;
-                    } else {
-                        const float4 v = *reinterpret_cast<const float4*>(k.ws_state + e);
-                        sa[pb][ks].set(cc, v.x, v.y, v.z, v.w);
-                    }
-                }
-        // the chunk: starting log-decay, dt of token `lane`, C rows and y (rows past the sequence
-        // clamped to its last token, their stores skipped)
+            for (int ks = 0; ks < KS_N; ++ks) {
+                const int n0 = 32 * ks + 8 * q;
+                if (n0 < N) load8(sa[pb][ks], (const uint8_t*)sbase + ((int64_t)(pb * 16 + li) * N + n0) * EB);
+                else zero8(sa[pb][ks]);
+            }
+        // the chunk: starting log-decay, dt of token `lane`, C rows (B operand, rows t) and y (rows
+        // past the sequence clamped to its last token; their stores are skipped)
         const float lam0 = k.ws_lamc[c * BH + bh];
         const T* dtp = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
         const T dtr = dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
@@ -924,60 +937,60 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
             reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N);
         uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P);
         Frag<T> cf[NTB][KS_N];
-        YV yv[NTB][NPB];
+        uint4 yv[NTB][NPASS];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             const int t = tb * 16 + li;
             const int tr = t < valid ? t : valid - 1;
 #pragma unroll
-            for (int ks = 0; ks < KS_N; ++ks)
+            for (int ks = 0; ks < KS_N; ++ks) {
+                const int n0 = 32 * ks + 8 * q;
+                if (n0 < N) load8(cf[tb][ks], cp + ((t0 + tr) * k.bcs + n0) * EB);
+                else zero8(cf[tb][ks]);
+            }
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const int n0 = 32 * ks + 16 * cc + 4 * q;
-                    if (n0 < N) {
-                        const uint8_t* src = cp + ((t0 + tr) * k.bcs + n0) * EB;
-                        if constexpr (EB == 2) {
-                            const uint2 v = *reinterpret_cast<const uint2*>(src);
-                            cf[tb][ks].w[2 * cc] = v.x;
-                            cf[tb][ks].w[2 * cc + 1] = v.y;
-                        } else {
-                            const float4 v = *reinterpret_cast<const float4*>(src);
-                            cf[tb][ks].set(cc, v.x, v.y, v.z, v.w);
-                        }
-                    } else {
-                        cf[tb][ks].set(cc, 0.f, 0.f, 0.f, 0.f);
-                    }
-                }
-#pragma unroll
-            for (int pb = 0; pb < NPB; ++pb)
-                yv[tb][pb] = *reinterpret_cast<const YV*>(yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB);
+            for (int ps = 0; ps < NPASS; ++ps) {
+                const int row = tb * 16 + ps * RPP + prow;
+                const int rr = row < valid ? row : valid - 1;
+                yv[tb][ps] = *reinterpret_cast<const uint4*>(yp + ((t0 + rr) * k.ys + pcol) * EB);
+            }
         }
         const float dtv = lane < valid ? dt_of(to_f32(dtr), k.dt_bias[h], k.dt_min, k.dt_max) : 0.0f;
         const float lam = lam0 + wave_prefix_sum(dtv * k.A[h]);
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-            const int t = tb * 16 + li;
-            const bool ok = t < valid;
-            const int tr = ok ? t : valid - 1;
-            const float el = fast_exp(__shfl(lam, t, 64));
+            // e^Lam_t (S_in . C_t) for the 16 rows t = tb*16 + li, into LDS as [row][p]
+            const float el = fast_exp(__shfl(lam, tb * 16 + li, 64));
 #pragma unroll
             for (int pb = 0; pb < NPB; ++pb) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[tb][ks]);
-                // the lane holds y[t][p = pb*16 + 4q .. +3]
-                uint8_t* dst = yp + ((t0 + tr) * k.ys + pb * 16 + 4 * q) * EB;
-                const YV v = yv[tb][pb];
-                if constexpr (EB == 2) {
-                    const float o0 = __uint_as_float(v.x << 16) + el * acc[0];
-                    const float o1 = __uint_as_float(v.x & 0xffff0000u) + el * acc[1];
-                    const float o2 = __uint_as_float(v.y << 16) + el * acc[2];
-                    const float o3 = __uint_as_float(v.y & 0xffff0000u) + el * acc[3];
-                    if (ok) *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-                } else {
-                    if (ok)
-                        *reinterpret_cast<float4*>(dst) = make_float4(v.x + el * acc[0], v.y + el * acc[1],
-                                                                      v.z + el * acc[2], v.w + el * acc[3]);
+                *reinterpret_cast<float4*>(acc_lds + li * RS + pb * 16 + 4 * q) =
+                    make_float4(el * acc[0], el * acc[1], el * acc[2], el * acc[3]);
+            }
+            // back in row pieces (LDS operations of one wave complete in order): y += term
+#pragma unroll
+            for (int ps = 0; ps < NPASS; ++ps) {
+                const int rloc = ps * RPP + prow;
+                const int row = tb * 16 + rloc;
+                if (rloc < 16 && row < valid) {
+                    const float* src = acc_lds + rloc * RS + pcol;
+                    uint8_t* dst = yp + ((t0 + row) * k.ys + pcol) * EB;
+                    const uint4 v = yv[tb][ps];
+                    if constexpr (EB == 2) {
+                        const float4 a = reinterpret_cast<const float4*>(src)[0];
+                        const float4 e = reinterpret_cast<const float4*>(src)[1];
+                        *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(lo_bf16(v.x) + a.x, hi_bf16(v.x) + a.y),
+                                                                    pack_bf16x2(lo_bf16(v.y) + a.z, hi_bf16(v.y) + a.w),
+                                                                    pack_bf16x2(lo_bf16(v.z) + e.x, hi_bf16(v.z) + e.y),
+                                                                    pack_bf16x2(lo_bf16(v.w) + e.z, hi_bf16(v.w) + e.w));
+                    } else {
+                        const float4 a = *reinterpret_cast<const float4*>(src);
+                        *reinterpret_cast<float4*>(dst) =
+                            make_float4(__uint_as_float(v.x) + a.x, __uint_as_float(v.y) + a.y,
+                                        __uint_as_float(v.z) + a.z, __uint_as_float(v.w) + a.w);
+                    }
                 }
             }
         }

@@ -131,6 +131,10 @@ def test_scan_validation():
     assert scan(dims(), y=FAKE + 128) == m2.M2_ERR_ALIAS                       # y overlaps x
     assert scan(dims(), s_in=FAKE + 0x5_0000_0000, s_out=FAKE + 0x5_0000_0000) == m2.M2_ERR_ALIAS
     assert scan(dims(), s_in=FAKE + 0x5_0000_0004) == m2.M2_ERR_UNSUPPORTED    # misaligned state
+    assert scan(dims(), x=FAKE + 8) == m2.M2_ERR_UNSUPPORTED                    # misaligned x
+    assert scan(dims(), C=FAKE + 0x10000100 + 2) == m2.M2_ERR_UNSUPPORTED       # misaligned C
+    assert scan(dims(), bcs=5252) == m2.M2_ERR_UNSUPPORTED                      # B/C rows not 16-byte multiples
+    assert scan(dims(), ys=5124) == m2.M2_ERR_UNSUPPORTED                       # y rows not 16-byte multiples
 
 
 def test_scan_workspace_required_when_reported():
