@@ -37,9 +37,10 @@
 // intra contraction runs twice, which leaves M's error near 2^-17.
 //
 // Long sequences with few (sequence, head) pairs are split into segments that run in
-// parallel: a first pass computes each segment's end state from a zero start, a small
-// pass chains those into each segment's true initial state, and the main pass then
-// walks every segment from its initial state.
+// parallel: the main pass walks every segment at once (the first from the caller's state,
+// the others from zero), a small pass chains the segments' end states into each segment's
+// true initial state and the final state, and a fix-up adds the initial state's share of
+// the later segments' outputs where it has not yet decayed away.
 #include "m2_device.h"
 #include "m2_launch.h"
 
@@ -221,7 +222,7 @@ struct ScanK {
     float dt_min, dt_max;
     const float* state_in; float* state_out;
     void* y;
-    float* ws_state;   // [nseg][batch*H][P*N]: segment end states, then segment initial states
+    float* ws_state;   // [nseg][batch*H][P*N]: segment end states (fp32 outputs: then initial states)
     float* ws_lam;     // [nseg][batch*H]: summed log-decay of each segment
     float* ws_lamc;    // [nchunks][batch*H]: summed log-decay of the chunk's segment before the chunk
     int* ws_nfix;      // [nseg-1][batch*H]: leading chunks of each later segment that need the fix-up
@@ -312,9 +313,9 @@ struct Cfg {
 };
 
 // ----------------------------------------------------------------------------------------------
-// chunk walk.  kStateOnly: segment end state from a zero start (no C, no output).
+// chunk walk
 
-template <typename T, int Q, int P, int N, bool kStateOnly>
+template <typename T, int Q, int P, int N>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, Cfg<T, Q, P, N>::THREADS),
                                amdgpu_waves_per_eu(Cfg<T, Q, P, N>::WPE)))
 ssd_chunk_scan_kernel(ScanK k)
@@ -324,7 +325,7 @@ ssd_chunk_scan_kernel(ScanK k)
     constexpr int HPW = Cf::HPW, PW = Cf::PW, UX = Cf::UX, UB = Cf::UB, EPU = Cf::EPU;
     constexpr int XUN = Cf::x_units(HPW), BUN = Cf::b_units();
     constexpr int NXP = XUN / 64, NBP = BUN / 64;        // 1 KB pieces of the X tiles and of B (C)
-    constexpr int NPIECE = NXP + (kStateOnly ? 1 : 2) * NBP;
+    constexpr int NPIECE = NXP + 2 * NBP;
     constexpr int PPW = (NPIECE + Cf::WAVES - 1) / Cf::WAVES;  // pieces per wave (at most)
     constexpr bool kSplitM = sizeof(E) == 2;  // bf16 operands: M as hi + lo
     constexpr int QS = HPW * Q;               // one statistic of every head of the block
@@ -344,8 +345,8 @@ ssd_chunk_scan_kernel(ScanK k)
     // one row, with the lanes of a row 16 apart).  16-byte unit u of row r sits at u ^ (r % YU).
     constexpr int YRB = Cf::YRB, YU = YRB / 16;         // bytes and 16-byte units per staged row
     constexpr int YRPS = 64 / YU;                       // rows per store instruction
-    constexpr int NYS = kStateOnly ? 0 : (Q + YRPS - 1) / YRPS;  // store instructions per chunk
-    __shared__ __attribute__((aligned(16))) uint8_t sY[kStateOnly ? 16 : Cf::WAVES * Q * YRB];
+    constexpr int NYS = (Q + YRPS - 1) / YRPS;  // store instructions per chunk
+    __shared__ __attribute__((aligned(16))) uint8_t sY[Cf::WAVES * Q * YRB];
 
     const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, li = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -410,7 +411,7 @@ ssd_chunk_scan_kernel(ScanK k)
         // the first segment starts from the caller's state; later ones from zero (their true
         // initial state is added to their output afterwards, see ssd_segment_fix_kernel)
         const float* src = nullptr;
-        if (!kStateOnly && seg == 0) src = k.state_in ? k.state_in + (int64_t)bh * P * N : nullptr;
+        if (seg == 0) src = k.state_in ? k.state_in + (int64_t)bh * P * N : nullptr;
 #pragma unroll
         for (int pw = 0; pw < PW; ++pw) {
             const int p = (pblk0 + pw) * 16 + li;
@@ -459,7 +460,7 @@ ssd_chunk_scan_kernel(ScanK k)
         rb = make_desc(at(1, bcs), bc_bytes);
         rc = make_desc(at(2, bcs), bc_bytes);
         rd = make_rsrc(at(3, dts), (uint32_t)(rows * dts + 1) * SZ);
-        ry = make_rsrc(at(4, ys), hvalid && !kStateOnly ? (uint32_t)(rows * ys + P) * SZ : 0u);
+        ry = make_rsrc(at(4, ys), hvalid ? (uint32_t)(rows * ys + P) * SZ : 0u);
     };
     auto valid_of = [&](int i) __attribute__((always_inline)) {
         const int left = nrows - i * Q;
@@ -568,7 +569,7 @@ ssd_chunk_scan_kernel(ScanK k)
 #pragma unroll
             for (int ks = 0; ks < Cf::KS_Q; ++ks) xf[pw][ks] = frag_col<T, UX>(Xh, 32 * ks, Q, (pblk0 + pw) * 16, q, li);
 
-        if constexpr (!kStateOnly) {
+        {
             const E* const Cs = Bs + BUN * EPU;
             // state part for every t-block first, so the bf16 copy of the state is dead before the
             // intra part: Y^T[p][t] = sum_n S[p][n] C[t][n] (the e^Lam_t factor comes later)
@@ -1091,7 +1092,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     // every segment at once (later ones from a zero state), then, with several segments, the chain
     // of their end states and the fix-up of the later segments' leading chunks
     k.nblocks = pl.nseg * (int)a.batch * pl.nhu;
-    hipError_t e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N, false>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
+    hipError_t e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
     if (e != hipSuccess || pl.nseg == 1) return e;
     // one extra block row lists the fix-up's work
     dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH + 1);
