@@ -145,6 +145,53 @@ def ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None,
     return y, state_out
 
 
+def _cu(cu_seqlens, T):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("oracle: cu_seqlens must rise from 0 to the token count")
+    return cu
+
+
+def conv1d_packed(x, cu_seqlens, w, bias=None, ring_in=None, ring_in_step: int = 0):
+    """Packed batch: x [T, Cd] holds sequence b at rows cu_seqlens[b] .. cu_seqlens[b+1]-1.
+
+    Each sequence is convolved on its own (its history from ring_in[b], or zero), exactly as conv1d
+    does for one sequence.  Returns (out [T, Cd], ring_out [nseq, W, Cd])."""
+    x = _f64(x)
+    T, Cd = x.shape
+    cu = _cu(cu_seqlens, T)
+    W = np.asarray(w).shape[1]
+    out = np.empty_like(x)
+    rings = []
+    for b in range(cu.size - 1):
+        r = None if ring_in is None else np.asarray(ring_in)[b:b + 1]
+        o, ro = conv1d(x[None, cu[b]:cu[b + 1]], w, bias, r, ring_in_step)
+        out[cu[b]:cu[b + 1]] = o[0]
+        rings.append(ro[0])
+    return out, (np.stack(rings) if rings else np.empty((0, W, Cd)))
+
+
+def ssd_scan_packed(x, Bm, Cm, dt_raw, cu_seqlens, dt_bias, A, D=None, state_in=None,
+                    dt_min: float = 0.0, dt_max: float = float("inf")):
+    """Packed batch: x [T, H, P], Bm/Cm [T, G, N], dt_raw [T, H]; sequence b at rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1, starting from state_in[b] (or zero), scanned on its own.
+    Returns (y [T, H, P], state_out [nseq, H, P, N])."""
+    x = _f64(x)
+    T, H, P = x.shape
+    N = np.asarray(Bm).shape[2]
+    cu = _cu(cu_seqlens, T)
+    y = np.empty_like(x)
+    states = []
+    for b in range(cu.size - 1):
+        sl = slice(cu[b], cu[b + 1])
+        s0 = None if state_in is None else np.asarray(state_in)[b:b + 1]
+        yb, sb = ssd_scan(x[None, sl], np.asarray(Bm)[None, sl], np.asarray(Cm)[None, sl],
+                          np.asarray(dt_raw)[None, sl], dt_bias, A, D, s0, dt_min, dt_max)
+        y[sl] = yb[0]
+        states.append(sb[0])
+    return y, (np.stack(states) if states else np.empty((0, H, P, N)))
+
+
 def ssd_step(xbc_tok, dt_tok, w, bias, dt_bias, A, D, ring, step: int, state,
              H: int, P: int, N: int, G: int = 1,
              dt_min: float = 0.0, dt_max: float = float("inf")):

@@ -506,3 +506,46 @@ def test_scan_padding_content_is_ignored():
     y2, s2 = oracle.ssd_scan(*junk, dt_bias, A, D, S0, seq_lens=lens)
     np.testing.assert_array_equal(np.nan_to_num(y, nan=7.0), np.nan_to_num(y2, nan=7.0))
     np.testing.assert_array_equal(s, s2)
+
+
+# ----------------------------------------------------------------- packed batches
+
+def test_packed_equals_padded_batch():
+    # the packed form (sequences back to back, sliced apart) against the right-padded form (one
+    # row per sequence, lengths given to the C oracle): two different routes to the same sums
+    rng = np.random.default_rng(50)
+    lens = np.array([7, 0, 19, 1, 12])
+    Bn, L, H, P, N, G, W = len(lens), int(lens.max()), 4, 3, 5, 2, 4
+    Cd = H * P + 2 * G * N
+    x, Bm, Cm, dt_raw, dt_bias, A, D, S0 = _rand_scan(rng, Bn, L, H, P, N, G)
+    xbc = rng.standard_normal((Bn, L, Cd))
+    w = rng.uniform(-0.5, 0.5, (Cd, W))
+    ring = rng.standard_normal((Bn, W, Cd))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    pack = lambda a: np.concatenate([a[b, :n] for b, n in enumerate(lens)], 0)
+    yp, sp = oracle.ssd_scan_packed(pack(x), pack(Bm), pack(Cm), pack(dt_raw), cu, dt_bias, A, D, S0)
+    yq, sq = oracle.ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D, S0, seq_lens=lens)
+    np.testing.assert_allclose(yp, pack(yq), rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(sp, sq, rtol=1e-13, atol=1e-300)
+    op, rp = oracle.conv1d_packed(pack(xbc), cu, w, None, ring, 2)
+    oq, rq = oracle.conv1d(xbc, w, None, ring, 2, seq_lens=lens)
+    np.testing.assert_allclose(op, pack(oq), rtol=1e-14, atol=1e-300)
+    np.testing.assert_array_equal(rp, rq)
+
+
+def test_packed_sequences_do_not_interact():
+    # changing one sequence's tokens changes no other sequence's outputs or state
+    rng = np.random.default_rng(51)
+    lens = [9, 14, 5]
+    T, H, P, N, G = sum(lens), 2, 3, 4, 1
+    x, Bm, Cm, dt_raw, dt_bias, A, D, _ = _rand_scan(rng, 1, T, H, P, N, G)
+    x, Bm, Cm, dt_raw = x[0], Bm[0], Cm[0], dt_raw[0]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    y1, s1 = oracle.ssd_scan_packed(x, Bm, Cm, dt_raw, cu, dt_bias, A, D)
+    x2 = x.copy()
+    x2[cu[1]:cu[2]] += 1.0
+    y2, s2 = oracle.ssd_scan_packed(x2, Bm, Cm, dt_raw, cu, dt_bias, A, D)
+    for b in (0, 2):
+        np.testing.assert_array_equal(y1[cu[b]:cu[b + 1]], y2[cu[b]:cu[b + 1]])
+        np.testing.assert_array_equal(s1[b], s2[b])
+    assert not np.allclose(y1[cu[1]:cu[2]], y2[cu[1]:cu[2]])
