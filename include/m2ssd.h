@@ -15,6 +15,10 @@
  *                    layer's conv state and recurrent state)
  *   m2_gated_rmsnorm the gated group RMSNorm applied to the scan's output (§三)
  *
+ * A batch of prompts of different lengths (the recurrent mask of §2.3) is given either
+ * right-padded (seq_lens on m2_conv1d_fwd / m2_ssd_scan_fwd) or packed back to back
+ * (m2_conv1d_fwd_packed / m2_ssd_scan_fwd_packed with cu_seqlens offsets).
+ *
  * The recurrence, per batch element b and head h, for t = 0..L-1:
  *     dt_t = softplus(dt_raw_t + dt_bias[h])        (then clamped to [dt_min, dt_max])
  *     S_t  = exp(dt_t * A[h]) * S_{t-1} + dt_t * x_t (outer) B_t     S is headdim x d_state, fp32
@@ -48,7 +52,7 @@
 extern "C" {
 #endif
 
-#define M2SSD_ABI_VERSION 2
+#define M2SSD_ABI_VERSION 3
 
 typedef enum {
     M2_OK = 0,
@@ -106,7 +110,25 @@ m2_status m2_conv1d_fwd(const m2_dims* dims,
                         const int32_t* seq_lens,
                         void* stream);
 
-/* Workspace bytes m2_ssd_scan_fwd needs for these dims (0 if none). */
+/* Packed batch (sequences back to back, no padding): the same as m2_conv1d_fwd for dims.batch
+ * sequences that lie one after another in one token-major array of total_tokens rows.
+ * cu_seqlens [batch+1] int32 on the device: sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1
+ *          (cu_seqlens[0] = 0, non-decreasing, cu_seqlens[batch] = total_tokens).  On the device
+ *          the offsets are clamped to [0, total_tokens] and a sequence is cut at dims.seqlen tokens,
+ *          so dims.seqlen is the longest sequence (rows past the cut are left as they were).
+ *          Must not overlap an output.
+ * xbc, out [total_tokens, conv_dim] io with token strides as in m2_conv1d_fwd;
+ * ring_in, ring_out [batch, W, conv_dim] io or NULL, one ring per sequence, as in m2_conv1d_fwd. */
+m2_status m2_conv1d_fwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                               const void* xbc, int64_t xbc_tok_stride,
+                               const float* w, const float* bias,
+                               const void* ring_in, int64_t ring_in_step,
+                               void* ring_out,
+                               void* out, int64_t out_tok_stride,
+                               void* stream);
+
+/* Workspace bytes m2_ssd_scan_fwd (and m2_ssd_scan_fwd_packed, with dims.seqlen the longest
+ * sequence) needs for these dims (0 if none). */
 size_t m2_ssd_scan_workspace(const m2_dims* dims);
 
 /* Chunked selective state-space scan over a prompt (the recurrence above for t = 0..seqlen-1).
@@ -140,6 +162,23 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims,
                           void* workspace, size_t workspace_bytes,
                           const int32_t* seq_lens,
                           void* stream);
+
+/* Packed batch: the same as m2_ssd_scan_fwd for dims.batch sequences back to back in arrays of
+ * total_tokens rows (x [total_tokens, nheads, headdim], B/C [total_tokens, n_groups, d_state],
+ * dt [total_tokens, nheads], y [total_tokens, nheads*headdim], with token strides and alignment as
+ * in m2_ssd_scan_fwd).  cu_seqlens as in m2_conv1d_fwd_packed; dims.seqlen is the longest
+ * sequence.  Each sequence starts from its own state_in[b] (or zero) and returns state_out[b], the
+ * state after its last token.  Sequences never see one another's tokens. */
+m2_status m2_ssd_scan_fwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                                 const void* x, int64_t x_tok_stride,
+                                 const void* B, const void* C, int64_t bc_tok_stride,
+                                 const void* dt, int64_t dt_tok_stride,
+                                 const float* dt_bias, const float* A, const float* D,
+                                 float dt_min, float dt_max,
+                                 const float* state_in, float* state_out,
+                                 void* y, int64_t y_tok_stride,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* One decode token for every sequence, fused: conv window (W-1 cached tokens + the new
  * one) -> SiLU -> split x | B | C -> dt -> state update -> output.

@@ -8,8 +8,9 @@ computation runs in the library's kernels.  There is no CPU fallback: if the
 library is missing, importing this package raises.
 
 Names and semantics follow the C ABI:
-    m2_conv1d_fwd, m2_ssd_scan_workspace, m2_ssd_scan_fwd, m2_ssd_step,
-    m2_status_str, m2_abi_version
+    m2_conv1d_fwd, m2_conv1d_fwd_packed, m2_ssd_scan_workspace, m2_ssd_scan_fwd,
+    m2_ssd_scan_fwd_packed, m2_ssd_step, m2_gated_rmsnorm, m2_status_str, m2_abi_version,
+    m2_last_hip_error
 """
 from __future__ import annotations
 
@@ -24,10 +25,11 @@ LIB_PATH = os.path.join(_PKG, "libm2ssd.so")
 M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, M2_ERR_UNSUPPORTED, \
     M2_ERR_LAUNCH = range(8)
 M2_F32, M2_BF16 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
-EXPORTS = ("m2_conv1d_fwd", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd", "m2_ssd_step", "m2_gated_rmsnorm",
-           "m2_status_str", "m2_abi_version", "m2_last_hip_error")
+EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
+           "m2_ssd_scan_fwd_packed", "m2_ssd_step", "m2_gated_rmsnorm", "m2_status_str", "m2_abi_version",
+           "m2_last_hip_error")
 
 
 class M2Dims(ctypes.Structure):
@@ -71,11 +73,16 @@ def _load() -> ctypes.CDLL:
     dp = ctypes.POINTER(M2Dims)
     lib.m2_conv1d_fwd.argtypes = [dp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp]
     lib.m2_conv1d_fwd.restype = ctypes.c_int
+    lib.m2_conv1d_fwd_packed.argtypes = [dp, i64, vp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp]
+    lib.m2_conv1d_fwd_packed.restype = ctypes.c_int
     lib.m2_ssd_scan_workspace.argtypes = [dp]
     lib.m2_ssd_scan_workspace.restype = sz
     lib.m2_ssd_scan_fwd.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp, i64,
                                     vp, sz, vp, vp]
     lib.m2_ssd_scan_fwd.restype = ctypes.c_int
+    lib.m2_ssd_scan_fwd_packed.argtypes = [dp, i64, vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp,
+                                           vp, i64, vp, sz, vp]
+    lib.m2_ssd_scan_fwd_packed.restype = ctypes.c_int
     lib.m2_ssd_step.argtypes = [dp, vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, f32, vp, i64, vp, vp, vp]
     lib.m2_ssd_step.restype = ctypes.c_int
     lib.m2_gated_rmsnorm.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp, i64, vp, f32,
@@ -271,6 +278,92 @@ def m2_ssd_scan_fwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, 
     _call("m2_ssd_scan_fwd", ctypes.byref(dims), _ptr(x), xs, _ptr(B), _ptr(C), bs, _ptr(dt), dts,
           _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min), float(dt_max), _ptr(state_in), _ptr(state_out),
           _ptr(y), ys, ws_ptr, ws_bytes, _lens_ptr(seq_lens, dims), _stream(stream))
+
+
+def _packed_stride(t, name, T, row: int) -> int:
+    """Token stride of a packed [T, ...] tensor whose trailing dims pack `row` contiguous elements."""
+    shape = tuple(t.shape)
+    if t.dim() < 2 or shape[0] != T or math.prod(shape[1:]) != row:
+        raise ValueError("%s: expected [%d, ...] with %d elements per token, got %s" % (name, T, row, shape))
+    if T == 0:
+        return row
+    exp = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if shape[d] != 1 and t.stride(d) != exp:
+            raise ValueError("%s: trailing dims must be contiguous" % name)
+        exp *= shape[d]
+    return t.stride(0) if T > 1 else row
+
+
+def _cu_ptr(cu_seqlens, dims: M2Dims):
+    _check(cu_seqlens, "cu_seqlens", _torch().int32)
+    if not cu_seqlens.is_contiguous() or tuple(cu_seqlens.shape) != (dims.batch + 1,):
+        raise ValueError("cu_seqlens must be a contiguous int32 [batch + 1] tensor")
+    return _ptr(cu_seqlens)
+
+
+def m2_conv1d_fwd_packed(dims: M2Dims, cu_seqlens, xbc, w, bias, out, ring_in=None, ring_in_step: int = 0,
+                         ring_out=None, stream=None) -> None:
+    """Packed batch conv; see include/m2ssd.h.  dims.batch sequences, dims.seqlen the longest;
+    xbc, out [T, conv_dim] (io dtype, token-strided views allowed); cu_seqlens int32 [batch + 1] on
+    the GPU; ring_in / ring_out [batch, W, conv_dim] or None."""
+    torch = _torch()
+    io = _io_dtype(dims)
+    Cd = dims.conv_dim
+    for n, t in (("xbc", xbc), ("out", out), ("ring_in", ring_in), ("ring_out", ring_out)):
+        _check(t, n, io)
+    for n, t in (("w", w), ("bias", bias)):
+        _check(t, n, torch.float32)
+    if not w.is_contiguous() or tuple(w.shape) != (Cd, dims.d_conv):
+        raise ValueError("w must be contiguous [conv_dim, d_conv]")
+    if bias is not None and (not bias.is_contiguous() or bias.numel() != Cd):
+        raise ValueError("bias must be contiguous [conv_dim]")
+    for n, t in (("ring_in", ring_in), ("ring_out", ring_out)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, dims.d_conv, Cd)):
+            raise ValueError("%s must be contiguous [batch, d_conv, conv_dim]" % n)
+    T = int(xbc.shape[0])
+    xs = _packed_stride(xbc, "xbc", T, Cd)
+    os_ = _packed_stride(out, "out", T, Cd)
+    _call("m2_conv1d_fwd_packed", ctypes.byref(dims), T, _cu_ptr(cu_seqlens, dims), _ptr(xbc), xs, _ptr(w),
+          _ptr(bias), _ptr(ring_in), int(ring_in_step), _ptr(ring_out), _ptr(out), os_, _stream(stream))
+
+
+def m2_ssd_scan_fwd_packed(dims: M2Dims, cu_seqlens, x, B, C, dt, dt_bias, A, D, y, state_in=None, state_out=None,
+                           dt_min: float = 0.0, dt_max: float = float("inf"), workspace=None, stream=None) -> None:
+    """Packed batch scan; see include/m2ssd.h.  dims.batch sequences, dims.seqlen the longest;
+    x [T, H, P] (or [T, H*P]), B/C [T, G, N], dt [T, H], y like x (token-strided views allowed, B and C
+    sharing one stride); cu_seqlens int32 [batch + 1] on the GPU; state_in / state_out
+    [batch, H, P, N] f32 or None; workspace as for m2_ssd_scan_fwd."""
+    torch = _torch()
+    io = _io_dtype(dims)
+    H, P, N, G = dims.nheads, dims.headdim, dims.d_state, dims.n_groups
+    for n, t in (("x", x), ("B", B), ("C", C), ("dt", dt), ("y", y)):
+        _check(t, n, io)
+    for n, t in (("dt_bias", dt_bias), ("A", A), ("D", D), ("state_in", state_in), ("state_out", state_out)):
+        _check(t, n, torch.float32)
+    for n, t in (("dt_bias", dt_bias), ("A", A), ("D", D)):
+        if t is not None and (not t.is_contiguous() or t.numel() != H):
+            raise ValueError("%s must be contiguous [nheads]" % n)
+    for n, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, H, P, N)):
+            raise ValueError("%s must be contiguous [batch, nheads, headdim, d_state]" % n)
+    T = int(x.shape[0])
+    xs = _packed_stride(x, "x", T, H * P)
+    bs = _packed_stride(B, "B", T, G * N)
+    cs = _packed_stride(C, "C", T, G * N)
+    if bs != cs:
+        raise ValueError("B and C must have the same token stride")
+    dts = _packed_stride(dt, "dt", T, H)
+    ys = _packed_stride(y, "y", T, H * P)
+    need = m2_ssd_scan_workspace(dims)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    elif need > 0:
+        raise ValueError("m2_ssd_scan_fwd_packed needs a workspace of %d bytes" % need)
+    _call("m2_ssd_scan_fwd_packed", ctypes.byref(dims), T, _cu_ptr(cu_seqlens, dims), _ptr(x), xs, _ptr(B), _ptr(C),
+          bs, _ptr(dt), dts, _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min), float(dt_max), _ptr(state_in),
+          _ptr(state_out), _ptr(y), ys, ws_ptr, ws_bytes, _stream(stream))
 
 
 def m2_ssd_step(dims: M2Dims, xbc_tok, dt_tok, w, bias, dt_bias, A, D, ring, step: int, state, y,

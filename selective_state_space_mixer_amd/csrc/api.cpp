@@ -92,13 +92,15 @@ int m2_abi_version(void) { return M2SSD_ABI_VERSION; }
 
 const char* m2_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
 
-m2_status m2_conv1d_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_stride, const float* w,
-                        const float* bias, const void* ring_in, int64_t ring_in_step, void* ring_out, void* out,
-                        int64_t out_tok_stride, const int32_t* seq_lens, void* stream) {
-    Derived d;
-    m2_status st = derive(dims, d);
-    if (st != M2_OK) return st;
-    const int64_t rows = d.batch * d.L;
+}  // extern "C"
+
+namespace {
+
+// Shared by the padded and the packed conv entry points: rows = rows of xbc/out; a packed batch
+// passes its row offsets cu (batch+1 entries) and rows = total tokens.
+m2_status conv_run(const Derived& d, int64_t rows, const int32_t* cu, const void* xbc, int64_t xbc_tok_stride,
+                   const float* w, const float* bias, const void* ring_in, int64_t ring_in_step, void* ring_out,
+                   void* out, int64_t out_tok_stride, const int32_t* seq_lens, void* stream) {
     if (!w) return M2_ERR_NULL;
     if (rows > 0 && (!xbc || !out)) return M2_ERR_NULL;
     if (rows > 0 && (xbc_tok_stride < d.Cd || out_tok_stride < d.Cd)) return M2_ERR_SHAPE;
@@ -107,22 +109,50 @@ m2_status m2_conv1d_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_st
     const Range ro = span(out, rows, out_tok_stride, d.Cd, d.esize);
     const Range rri = span(ring_in, d.batch * d.W, d.Cd, d.Cd, d.esize);
     const Range rro = span(ring_out, d.batch * d.W, d.Cd, d.Cd, d.esize);
-    const Range rl = span(seq_lens, d.batch, 1, 1, 4);
+    const Range rl = cu ? span(cu, d.batch + 1, 1, 1, 4) : span(seq_lens, d.batch, 1, 1, 4);
     if (overlap(rx, ro) || overlap(rri, rro) || overlap(rro, rx) || overlap(rro, ro) || overlap(ro, rri) ||
         overlap(rl, ro) || overlap(rl, rro))
         return M2_ERR_ALIAS;
-    if ((uintptr_t)seq_lens & 3u) return M2_ERR_UNSUPPORTED;
+    if (((uintptr_t)seq_lens & 3u) || ((uintptr_t)cu & 3u)) return M2_ERR_UNSUPPORTED;
     m2::ConvArgs a;
     a.xbc = xbc; a.xs = xbc_tok_stride; a.L = d.L; a.Cd = d.Cd; a.W = d.W; a.batch = d.batch;
     a.w = w; a.bias = bias; a.ring_in = ring_in;
     a.ring_phase = (int)(((ring_in_step % d.W) + d.W) % d.W);
     a.ring_out = ring_out; a.out = out; a.os = out_tok_stride; a.lens = seq_lens; a.bf16 = d.bf16;
+    a.cu = cu; a.total = cu ? rows : 0;
     const int vec = d.bf16 ? 8 : 4;
     a.vec = (d.Cd % vec == 0) && (rows == 0 || (xbc_tok_stride % vec == 0 && out_tok_stride % vec == 0 &&
                                                  aligned16(xbc) && aligned16(out))) &&
             aligned16(ring_in) && aligned16(ring_out);
-    if (d.L == 0) { a.xbc = nullptr; a.out = nullptr; }
+    if (d.L == 0 || rows == 0) { a.xbc = nullptr; a.out = nullptr; }
     return launched(m2::launch_conv1d(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+m2_status m2_conv1d_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_stride, const float* w,
+                        const float* bias, const void* ring_in, int64_t ring_in_step, void* ring_out, void* out,
+                        int64_t out_tok_stride, const int32_t* seq_lens, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    return conv_run(d, d.batch * d.L, nullptr, xbc, xbc_tok_stride, w, bias, ring_in, ring_in_step, ring_out, out,
+                    out_tok_stride, seq_lens, stream);
+}
+
+m2_status m2_conv1d_fwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                               const void* xbc, int64_t xbc_tok_stride, const float* w, const float* bias,
+                               const void* ring_in, int64_t ring_in_step, void* ring_out, void* out,
+                               int64_t out_tok_stride, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    if (total_tokens < 0) return M2_ERR_SHAPE;
+    if (d.batch > 0 && !cu_seqlens) return M2_ERR_NULL;
+    return conv_run(d, total_tokens, cu_seqlens, xbc, xbc_tok_stride, w, bias, ring_in, ring_in_step, ring_out, out,
+                    out_tok_stride, nullptr, stream);
 }
 
 size_t m2_ssd_scan_workspace(const m2_dims* dims) {
@@ -132,15 +162,16 @@ size_t m2_ssd_scan_workspace(const m2_dims* dims) {
     return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
 }
 
-m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B, const void* C,
-                          int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
-                          const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
-                          float* state_out, void* y, int64_t y_tok_stride, void* workspace,
-                          size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
-    Derived d;
-    m2_status st = derive(dims, d);
-    if (st != M2_OK) return st;
-    const int64_t rows = d.batch * d.L;
+}  // extern "C"
+
+namespace {
+
+// Shared by the padded and the packed scan entry points (rows and cu as for conv_run).
+m2_status scan_run(const Derived& d, int64_t rows, const int32_t* cu, const void* x, int64_t x_tok_stride,
+                   const void* B, const void* C, int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride,
+                   const float* dt_bias, const float* A, const float* D, float dt_min, float dt_max,
+                   const float* state_in, float* state_out, void* y, int64_t y_tok_stride, void* workspace,
+                   size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
     if (!dt_bias || !A) return M2_ERR_NULL;
     if (rows > 0 && (!x || !B || !C || !dt || !y)) return M2_ERR_NULL;
     const int GN = d.G * d.N;
@@ -161,14 +192,15 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
         overlap(ry, span(dt, rows, dt_tok_stride, d.H, d.esize)) || overlap(rs_in, rs_out) ||
         overlap(rs_out, ry))
         return M2_ERR_ALIAS;
-    if (!aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)seq_lens & 3u)) return M2_ERR_UNSUPPORTED;
+    if (!aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)cu & 3u))
+        return M2_ERR_UNSUPPORTED;
     // x, B, C and y move in 16-byte pieces of rows
     if (rows > 0 && (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
                      (x_tok_stride * d.esize) % 16 || (bc_tok_stride * d.esize) % 16 || (y_tok_stride * d.esize) % 16))
         return M2_ERR_UNSUPPORTED;
     const size_t need = m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
     if (need > 0 && (!workspace || workspace_bytes < need)) return M2_ERR_WORKSPACE;
-    const Range rl = span(seq_lens, d.batch, 1, 1, 4);
+    const Range rl = cu ? span(cu, d.batch + 1, 1, 1, 4) : span(seq_lens, d.batch, 1, 1, 4);
     if (overlap(rl, ry) || overlap(rl, rs_out) || overlap(rl, span(workspace, 1, 0, (int64_t)need, 1)))
         return M2_ERR_ALIAS;
     m2::ScanArgs a;
@@ -177,7 +209,41 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.dt_min = dt_min; a.dt_max = dt_max;
     a.state_in = state_in; a.state_out = state_out; a.y = y; a.ys = y_tok_stride;
     a.ws = workspace; a.ws_bytes = workspace_bytes; a.lens = seq_lens; a.bf16 = d.bf16;
+    a.cu = cu; a.total = cu ? rows : 0;
     return launched(m2::launch_ssd_scan(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+m2_status m2_ssd_scan_fwd(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B, const void* C,
+                          int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
+                          const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
+                          float* state_out, void* y, int64_t y_tok_stride, void* workspace,
+                          size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    return scan_run(d, d.batch * d.L, nullptr, x, x_tok_stride, B, C, bc_tok_stride, dt, dt_tok_stride, dt_bias, A,
+                    D, dt_min, dt_max, state_in, state_out, y, y_tok_stride, workspace, workspace_bytes, seq_lens,
+                    stream);
+}
+
+m2_status m2_ssd_scan_fwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                                 const void* x, int64_t x_tok_stride, const void* B, const void* C,
+                                 int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
+                                 const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
+                                 float* state_out, void* y, int64_t y_tok_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    if (total_tokens < 0) return M2_ERR_SHAPE;
+    if (d.batch > 0 && !cu_seqlens) return M2_ERR_NULL;
+    return scan_run(d, total_tokens, cu_seqlens, x, x_tok_stride, B, C, bc_tok_stride, dt, dt_tok_stride, dt_bias,
+                    A, D, dt_min, dt_max, state_in, state_out, y, y_tok_stride, workspace, workspace_bytes, nullptr,
+                    stream);
 }
 
 m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stride, const void* dt_tok,

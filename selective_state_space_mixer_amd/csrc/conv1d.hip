@@ -95,7 +95,8 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     const T* __restrict__ xbc, int64_t xs, int64_t L, int Cd,
     const float* __restrict__ w, const float* __restrict__ bias,
     const T* __restrict__ ring_in, int ring_phase,
-    T* __restrict__ ring_out, T* __restrict__ out, int64_t os, const int32_t* __restrict__ lens)
+    T* __restrict__ ring_out, T* __restrict__ out, int64_t os, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ cu, int64_t total)
 {
     using R = typename Raw<T, VEC>::type;
     const int CG = Cd / VEC;
@@ -105,16 +106,22 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     const int c0 = (int)(item % CG) * VEC;
     const int64_t t0 = (item / CG) * kConvTileTokens;
     const int64_t b = blockIdx.y;
-    // a right-padded sequence ends at its own length; the tile that starts at token 0 always
-    // runs, so that an empty sequence still writes its ring
-    int64_t Lb = L;
-    if (lens) {
+    // Sequence b starts at row b*L, or at cu[b] in a packed batch, and ends at its own length
+    // (clamped to the rows that exist and to L).  The tile that starts at token 0 always runs, so
+    // that an empty sequence still writes its ring.
+    int64_t row0 = b * L, Lb = L;
+    if (cu) {
+        const int64_t r0 = cu[b], r1 = cu[b + 1];
+        row0 = r0 < 0 ? 0 : (r0 > total ? total : r0);
+        const int64_t end = r1 < row0 ? row0 : (r1 > total ? total : r1);
+        Lb = end - row0 < L ? end - row0 : L;
+    } else if (lens) {
         const int64_t v = lens[b];
         Lb = v < 0 ? 0 : (v > L ? L : v);
     }
     if (t0 > 0 && t0 >= Lb) return;
-    const T* xb = xbc + b * L * xs + c0;
-    T* ob = out + b * L * os + c0;
+    const T* xb = xbc + row0 * xs + c0;
+    T* ob = out + row0 * os + c0;
 
     float wr[VEC][W], br[VEC];
 #pragma unroll
@@ -190,7 +197,7 @@ static hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
     dim3 grid((unsigned)((items + kConvThreads - 1) / kConvThreads), (unsigned)a.batch);
     return launch_kernel(conv1d_silu_kernel<T, VEC, W>, grid, dim3(kConvThreads), 0, s,
                          (const T*)a.xbc, a.xs, a.L, a.Cd, a.w, a.bias, (const T*)a.ring_in, a.ring_phase,
-                         (T*)a.ring_out, (T*)a.out, a.os, a.lens);
+                         (T*)a.ring_out, (T*)a.out, a.os, a.lens, a.cu, a.total);
 }
 
 template <typename T, int VEC>

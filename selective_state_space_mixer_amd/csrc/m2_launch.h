@@ -15,6 +15,8 @@ struct ConvArgs {
     void* ring_out;
     void* out; int64_t os;
     const int32_t* lens;  // [batch] valid tokens per sequence (device), or null
+    const int32_t* cu;    // packed batch: [batch+1] first row of each sequence (device), or null
+    int64_t total;        // packed batch: rows of the packed arrays
     bool bf16;  // storage type of activations
     bool vec;   // 16-byte vector path (alignment checked by the caller)
 };
@@ -31,6 +33,8 @@ struct ScanArgs {
     void* y; int64_t ys;
     void* ws; size_t ws_bytes;
     const int32_t* lens;  // [batch] valid tokens per sequence (device), or null
+    const int32_t* cu;    // packed batch: [batch+1] first row of each sequence (device), or null
+    int64_t total;        // packed batch: rows of the packed arrays
     bool bf16;
 };
 

@@ -230,6 +230,8 @@ struct ScanK {
     int* fix_count;    // its length
     uint16_t* ws_tin;  // bf16 outputs: [nseg-1][batch*H][P*N] bf16 initial states of segments 1.. (else null)
     const int32_t* lens;  // [batch] tokens of each right-padded sequence, or null (all L)
+    const int32_t* cu;    // packed batch: [batch+1] first row of each sequence, or null
+    int64_t total;        // packed batch: rows of the packed arrays
     int64_t L;
     int batch, H, G;
     int nseg, cps;     // segments per sequence, chunks per segment
@@ -237,8 +239,20 @@ struct ScanK {
     int nblocks;       // blocks in this launch
 };
 
-// Tokens of sequence b: its length, clamped to [0, L], in a right-padded batch; else L.
+// First row of sequence b: b*L, or cu[b] (clamped to the rows that exist) in a packed batch.
+__device__ __forceinline__ int64_t seq_row0(const ScanK& k, int64_t b) {
+    if (!k.cu) return b * k.L;
+    const int64_t r0 = k.cu[b];
+    return r0 < 0 ? 0 : (r0 > k.total ? k.total : r0);
+}
+// Tokens of sequence b: L; its length clamped to [0, L] in a right-padded batch; in a packed
+// batch cu[b+1] - cu[b], clamped to the rows that exist and to L.
 __device__ __forceinline__ int64_t seq_len(const ScanK& k, int64_t b) {
+    if (k.cu) {
+        const int64_t r0 = seq_row0(k, b), r1 = k.cu[b + 1];
+        const int64_t end = r1 < r0 ? r0 : (r1 > k.total ? k.total : r1);
+        return end - r0 < k.L ? end - r0 : k.L;
+    }
     if (!k.lens) return k.L;
     const int64_t v = k.lens[b];
     return v < 0 ? 0 : (v > k.L ? k.L : v);
@@ -434,7 +448,7 @@ ssd_chunk_scan_kernel(ScanK k)
     const int xs = (int)k.xs, bcs = (int)k.bcs, dts = (int)k.dts, ys = (int)k.ys;  // < 2^31 / (3 Q SZ)
     const int nrows = nc > 0 ? (int)(row_end - row_begin) : 0;
     if (lane == 0) {
-        const int64_t base = b * k.L + row_begin;
+        const int64_t base = seq_row0(k, b) + row_begin;
         sBase[wave][0] = (uint64_t)(reinterpret_cast<const T*>(k.x) + base * k.xs + (int64_t)h0 * P);
         sBase[wave][1] = (uint64_t)(reinterpret_cast<const T*>(k.B) + base * k.bcs + (int64_t)g * N);
         sBase[wave][2] = (uint64_t)(reinterpret_cast<const T*>(k.C) + base * k.bcs + (int64_t)g * N);
@@ -932,11 +946,12 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
         // the chunk: starting log-decay, dt of token `lane`, C rows (B operand, rows t) and y (rows
         // past the sequence clamped to its last token; their stores are skipped)
         const float lam0 = k.ws_lamc[c * BH + bh];
-        const T* dtp = reinterpret_cast<const T*>(k.dt) + b * k.L * k.dts + h;
+        const int64_t row0 = seq_row0(k, b);
+        const T* dtp = reinterpret_cast<const T*>(k.dt) + row0 * k.dts + h;
         const T dtr = dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
         const uint8_t* cp =
-            reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + b * k.L * k.bcs + (int64_t)g * N);
-        uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + b * k.L * k.ys + (int64_t)h * P);
+            reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + row0 * k.bcs + (int64_t)g * N);
+        uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + row0 * k.ys + (int64_t)h * P);
         Frag<T> cf[NTB][KS_N];
         uint4 yv[NTB][NPASS];
 #pragma unroll
@@ -1061,7 +1076,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     k.xs = a.xs; k.bcs = a.bcs; k.dts = a.dts; k.ys = a.ys;
     k.dt_bias = a.dt_bias; k.A = a.A; k.D = a.D; k.dt_min = a.dt_min; k.dt_max = a.dt_max;
     k.state_in = a.state_in; k.state_out = a.state_out; k.y = a.y;
-    k.L = a.L; k.batch = (int)a.batch; k.H = a.H; k.G = a.G; k.lens = a.lens;
+    k.L = a.L; k.batch = (int)a.batch; k.H = a.H; k.G = a.G; k.lens = a.lens; k.cu = a.cu; k.total = a.total;
     k.nseg = pl.nseg; k.cps = pl.cps;
     // buffer-resource windows: every byte offset inside one must stay below 2^31
     int64_t row_bytes = a.xs > a.bcs ? a.xs : a.bcs;

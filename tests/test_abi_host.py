@@ -112,6 +112,29 @@ def test_seq_lens_validation():
         assert scan(big, ws=FAKE + 0x8_0000_0000, ws_bytes=need, lens=FAKE + 0x8_0000_0000 + 256) == m2.M2_ERR_ALIAS
 
 
+def test_packed_validation():
+    lib = m2.lib()
+    d = dims()
+    cd, di = d.conv_dim, d.expand * d.d_model
+    out = FAKE + 0x4000_0000
+    conv_p = lambda T, cu, o=out: lib.m2_conv1d_fwd_packed(ctypes.byref(d), T, cu, FAKE, cd, FAKE + 0x100000, None,
+                                                           None, 0, None, o, cd, None)
+    assert conv_p(256, None) == m2.M2_ERR_NULL
+    assert conv_p(-1, FAKE + 0x6_0000_0000) == m2.M2_ERR_SHAPE
+    assert conv_p(256, FAKE + 0x6_0000_0002) == m2.M2_ERR_UNSUPPORTED             # misaligned offsets
+    assert conv_p(256, out + 64) == m2.M2_ERR_ALIAS                               # offsets inside out
+    ws = m2.m2_ssd_scan_workspace(d)
+    scan_p = lambda T, cu: lib.m2_ssd_scan_fwd_packed(ctypes.byref(d), T, cu, FAKE, di, FAKE + 0x10000000,
+                                                      FAKE + 0x10000100, 128, FAKE + 0x20000000, 80,
+                                                      FAKE + 0x30000000, FAKE + 0x30001000, None, 0.0,
+                                                      float("inf"), None, None, FAKE + 0x4000_0000_00, di,
+                                                      FAKE + 0x9_0000_0000, ws, None)
+    assert scan_p(256, None) == m2.M2_ERR_NULL
+    assert scan_p(-5, FAKE + 0x6_0000_0000) == m2.M2_ERR_SHAPE
+    assert scan_p(256, FAKE + 0x6_0000_0001) == m2.M2_ERR_UNSUPPORTED
+    assert scan_p(256, FAKE + 0x4000_0000_00 + 32) == m2.M2_ERR_ALIAS             # offsets inside y
+
+
 def test_empty_batch_is_a_no_op():
     assert conv(dims(batch=0), xbc=None, out=None) == m2.M2_OK
     assert scan(dims(batch=0), x=None, B=None, C=None, dt=None, y=None) == m2.M2_OK

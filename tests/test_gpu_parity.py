@@ -316,6 +316,121 @@ def test_padded_prefill_then_decode():
     np.testing.assert_array_equal(host(ring), r_ring)
 
 
+# ----------------------------------------------------------------------------- packed batches
+# Sequences back to back in one token-major array, row offsets cu_seqlens (int32 [batch + 1]);
+# dims.batch is the number of sequences and dims.seqlen the longest one.
+
+def _pack(a, lens):
+    return np.concatenate([a[b, :n] for b, n in enumerate(lens)], 0)
+
+
+def _cu_dev(lens):
+    return torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+
+
+PACK_CASES = [
+    # (config index, lengths, cached initial state / ring history)
+    (2, [200, 0, 1, 64, 131, 3], True),
+    (0, [64, 5, 0, 33], True),
+    (1, [300, 17], False),
+]
+
+
+@pytest.mark.parametrize("case", PACK_CASES, ids=lambda c: "cfg%d-%s" % (c[0], c[1]))
+def test_conv1d_packed_parity(case):
+    _need_gpu()
+    idx, lens, use_ring = case
+    d = workloads.CONFIGS[idx].dims.replace(batch=len(lens), seqlen=max(lens))
+    inp = workloads.generate(d, 1200 + idx, use_ring)
+    io = d.io
+    Cd, W = d.conv_dim, d.d_conv
+    xp = _pack(inp.xbc, lens)
+    ring_in = inp.ring0 if use_ring else None
+    ref, ref_ring = oracle.conv1d_packed(xp, np.concatenate([[0], np.cumsum(lens)]), inp.conv_w, inp.conv_b,
+                                         ring_in, 3)
+    out = nan_like((len(xp), Cd), io)
+    ring_out = nan_like((len(lens), W, Cd), io)
+    m2.m2_conv1d_fwd_packed(dims_of(d), _cu_dev(lens), dev(xp, io), dev32(inp.conv_w), dev32(inp.conv_b), out,
+                            dev(ring_in, io), 3, ring_out)
+    torch.cuda.synchronize()
+    assert oracle.max_rel_err(host(out), ref) <= tol_for(io)
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
+
+
+PACK_SCAN_CASES = PACK_CASES + [
+    (2, [4096, 1500, 0, 2500], True),   # several segments per sequence; empty segments; an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", PACK_SCAN_CASES, ids=lambda c: "cfg%d-%s" % (c[0], c[1]))
+def test_ssd_scan_packed_parity(case):
+    _need_gpu()
+    idx, lens, cached = case
+    d = workloads.CONFIGS[idx].dims.replace(batch=len(lens), seqlen=max(lens))
+    inp, x, b, c = _scan_inputs(d, 2200 + idx, cached)
+    io = d.io
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    xp, bp, cp, dtp = _pack(x, lens), _pack(b, lens), _pack(c, lens), _pack(inp.dt_raw, lens)
+    T = len(xp)
+    yr, sr = oracle.ssd_scan_packed(xp, bp, cp, dtp, np.concatenate([[0], np.cumsum(lens)]), inp.dt_bias, inp.A,
+                                    inp.D, inp.state0)
+    dims = dims_of(d)
+    y = nan_like((T, H * P), io)
+    s_out = torch.full((len(lens), H, P, N), float("nan"), device="cuda")
+    m2.m2_ssd_scan_fwd_packed(dims, _cu_dev(lens), dev(xp, io), dev(bp, io), dev(cp, io), dev(dtp, io),
+                              dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(inp.state0), s_out,
+                              workspace=workspace(dims))
+    torch.cuda.synchronize()
+    tol = tol_for(io)
+    assert oracle.max_rel_err(host(y).reshape(T, H, P), yr) <= tol
+    assert oracle.max_rel_err(host(s_out), sr) <= tol
+
+
+def test_packed_prefill_then_decode():
+    """A packed prefill (conv -> scan through the conv output's strided views) hands each sequence its
+    own ring and state; decode steps continue every sequence from there."""
+    _need_gpu()
+    lens, steps = [150, 40, 2, 77], 3
+    d = workloads.CONFIGS[2].dims.replace(batch=len(lens), seqlen=max(lens))
+    inp = workloads.generate(d, 45, True)
+    tok = workloads.generate(d.replace(seqlen=1), 46, False, steps)
+    io = d.io
+    Bn, H, P, N, G, W, Cd = d.batch, d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    cu = _cu_dev(lens)
+    xp, dtp = _pack(inp.xbc, lens), _pack(inp.dt_raw, lens)
+    T = len(xp)
+    act = nan_like((T, Cd), io)
+    ring = nan_like((Bn, W, Cd), io)
+    m2.m2_conv1d_fwd_packed(dims, cu, dev(xp, io), dev32(inp.conv_w), dev32(inp.conv_b), act, dev(inp.ring0, io),
+                            0, ring)
+    y = nan_like((T, H * P), io)
+    state = torch.empty((Bn, H, P, N), device="cuda")
+    m2.m2_ssd_scan_fwd_packed(dims, cu, act[:, :H * P], act[:, H * P:H * P + G * N], act[:, H * P + G * N:],
+                              dev(dtp, io), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(inp.state0),
+                              state, workspace=workspace(dims))
+    ys = []
+    xt, dtt = dev(tok.xbc, io), dev(tok.dt_raw, io)
+    w, cb, dtb, A, D = (dev32(a) for a in (inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D))
+    for t in range(steps):
+        yt = nan_like((Bn, H * P), io)
+        m2.m2_ssd_step(dims, xt[t], dtt[t], w, cb, dtb, A, D, ring, t, state, yt)
+        ys.append(host(yt))
+    torch.cuda.synchronize()
+    cu_np = np.concatenate([[0], np.cumsum(lens)])
+    ref_act, r_ring = oracle.conv1d_packed(xp, cu_np, inp.conv_w, inp.conv_b, inp.ring0, 0)
+    assert oracle.max_rel_err(host(act), ref_act) <= 2e-2
+    rx, rb, rc = oracle.split_act(ref_act, H, P, N, G)
+    ry, r_state = oracle.ssd_scan_packed(rx, rb, rc, dtp, cu_np, inp.dt_bias, inp.A, inp.D, inp.state0)
+    assert oracle.max_rel_err(host(y).reshape(T, H, P), ry) <= 2e-2
+    for t in range(steps):
+        yr, r_ring, r_state = oracle.ssd_step(tok.xbc[t], tok.dt_raw[t], inp.conv_w, inp.conv_b, inp.dt_bias,
+                                              inp.A, inp.D, r_ring, t, r_state, H, P, N, G)
+        assert oracle.max_rel_err(ys[t], yr) <= 2e-2, "step %d" % t
+    assert oracle.max_rel_err(host(state), r_state) <= 2e-2
+    np.testing.assert_array_equal(host(ring), r_ring)
+
+
 # ----------------------------------------------------------------------------- decode step
 
 def _gpu_chain(d, inp, steps, ring0, state0, first_step=0):
