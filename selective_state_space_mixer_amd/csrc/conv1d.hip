@@ -154,7 +154,9 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
 #pragma unroll
         for (int u = 0; u < kConvGroup; ++u) {
             const int tt = base + u < n ? base + u : n - 1;  // clamped: rows past the end are never used
-            dst[u] = *reinterpret_cast<const R*>(xb + (t0 + tt) * xs);
+            // read once: streaming loads leave the cache to the output, which the scan reads next
+            if constexpr (VEC > 1) dst[u] = __builtin_nontemporal_load(reinterpret_cast<const R*>(xb + (t0 + tt) * xs));
+            else dst[u] = *reinterpret_cast<const R*>(xb + (t0 + tt) * xs);
         }
     };
     if (n > 0) load_group(cur, 0);
