@@ -19,7 +19,7 @@
  *           y_t = S_t . C_t + D_h * x_t
  *   step    the same for one token, with the conv window taken from a ring of the
  *           last W tokens (the cache of conv state + recurrent state, §三)
- *   norm    the gated group RMSNorm after the scan (§三 "门控归一化": group RMSNorm times
+ *   norm    the gated group RMSNorm after the scan (§三, the gated normalisation: group RMSNorm times
  *           SiLU of the gate z, over intermediate_size in groups; eps from §五 rms_norm_eps):
  *             gate first (norm_before_gate = 0):  g = y * SiLU(z),
  *                                                 out = g / sqrt(mean_group(g^2) + eps) * w
