@@ -359,14 +359,17 @@ def test_conv1d_packed_parity(case):
 
 PACK_SCAN_CASES = PACK_CASES + [
     (2, [4096, 1500, 0, 2500], True),   # several segments per sequence; empty segments; an empty sequence
+    (0, [50, 13, 0, 64], True, dict(d_model=64, headdim=16, d_state=32, n_groups=4)),
+    (0, [70, 1, 33], True, dict(d_model=64, headdim=32, d_state=16, n_groups=2, io="bf16", chunk_size=32)),
 ]
 
 
-@pytest.mark.parametrize("case", PACK_SCAN_CASES, ids=lambda c: "cfg%d-%s" % (c[0], c[1]))
+@pytest.mark.parametrize("case", PACK_SCAN_CASES, ids=lambda c: "cfg%d-%s%s" % (c[0], c[1], c[3] if len(c) > 3 else ""))
 def test_ssd_scan_packed_parity(case):
     _need_gpu()
-    idx, lens, cached = case
-    d = workloads.CONFIGS[idx].dims.replace(batch=len(lens), seqlen=max(lens))
+    idx, lens, cached = case[:3]
+    over = case[3] if len(case) > 3 else {}
+    d = workloads.CONFIGS[idx].dims.replace(batch=len(lens), seqlen=max(lens), **over)
     inp, x, b, c = _scan_inputs(d, 2200 + idx, cached)
     io = d.io
     H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
