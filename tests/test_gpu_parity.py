@@ -154,6 +154,33 @@ def test_ssd_scan_parity(case):
     assert oracle.max_rel_err(s, sr) <= tol
 
 
+def test_ssd_scan_buffer_windows_move():
+    """A token stride so wide that a 2^31-byte buffer window holds only a few chunks: the kernel must
+    move its windows along the sequence (here after every chunk) and still match the oracle."""
+    _need_gpu()
+    Q = 64
+    d = workloads.CONFIGS[2].dims.replace(batch=4, seqlen=3 * Q, chunk_size=Q)
+    dims = dims_of(d)
+    assert m2.m2_ssd_scan_workspace(dims) == 0, "expected one segment per sequence (the whole walk in one block)"
+    Bn, L, H, P, N, G = d.batch, d.seqlen, d.nheads, d.headdim, d.d_state, d.n_groups
+    xs = 3_600_000                                   # elements: 7.2 MB per token row of x
+    win = (2 ** 31 - 1) // (Q * xs * 2) - 3          # chunks per window, as the library sizes them
+    assert 1 <= win < L // Q, "the stride must force at least one window move"
+    inp, x, b, c = _scan_inputs(d, 2300, True)
+    xbig = torch.empty((Bn, L, xs), device="cuda", dtype=torch.bfloat16)   # 5.5 GB, only the head filled
+    xv = xbig[:, :, :H * P]
+    xv.copy_(dev(x.reshape(Bn, L, H * P), "bf16"))
+    y = nan_like((Bn, L, H * P), "bf16")
+    s_out = torch.full((Bn, H, P, N), float("nan"), device="cuda")
+    m2.m2_ssd_scan_fwd(dims, xv, dev(b, "bf16"), dev(c, "bf16"), dev(inp.dt_raw, "bf16"), dev32(inp.dt_bias),
+                       dev32(inp.A), dev32(inp.D), y, dev32(inp.state0), s_out, workspace=None)
+    torch.cuda.synchronize()
+    del xbig, xv
+    yr, sr = oracle.ssd_scan(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0)
+    assert oracle.max_rel_err(host(y).reshape(Bn, L, H, P), yr) <= 2e-2
+    assert oracle.max_rel_err(host(s_out), sr) <= 2e-2
+
+
 def test_ssd_scan_chunk_size_invariance():
     """Results do not depend on the chunk length (up to rounding)."""
     _need_gpu()
