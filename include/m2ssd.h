@@ -141,8 +141,9 @@ size_t m2_ssd_scan_workspace(const m2_dims* dims);
  * state_out [batch, nheads, headdim, d_state] fp32 or NULL; must not overlap state_in
  * y        [batch, seqlen, nheads*headdim] io, token stride y_tok_stride; must not overlap
  *          x, B, C or dt
- * workspace device scratch of at least m2_ssd_scan_workspace(dims) bytes (NULL if 0);
- *          its contents on entry do not matter.
+ * workspace device scratch of at least m2_ssd_scan_workspace(dims) bytes (NULL if 0), any
+ *          alignment; its contents on entry do not matter.  Calls that may run at the same
+ *          time (other streams) need separate workspaces.
  * seq_lens [batch] int32 on the device, or NULL (every sequence is seqlen tokens long): a
  *          right-padded batch as in m2_conv1d_fwd.  Sequence b consumes only its first
  *          seq_lens[b] tokens (clamped to [0, seqlen]): y at later positions is left as it
