@@ -16,6 +16,7 @@ cores (`cpu_baseline`).
 from __future__ import annotations
 
 import argparse
+import itertools
 import json
 import os
 import sys
@@ -161,6 +162,50 @@ def bench_prefill(torch, m2, workloads, args):
                    "headdim": P, "d_state": N, "n_groups": G, "d_conv": W,
                    "chunk_size": d.chunk_size or "library default", "state": "fp32, zero initial, final returned"},
     }
+
+
+VARLEN_LENS = (8192, 6144, 5120, 4096, 3584, 2560, 2048, 1024)  # 32768 tokens in 8 prompts
+
+
+def bench_varlen(torch, m2, workloads, args):
+    """The same 32768 tokens as eight prompts of different lengths, packed back to back
+    (m2_conv1d_fwd_packed then m2_ssd_scan_fwd_packed, each prompt from a zero state)."""
+    d1 = workloads.CONFIGS[3].dims
+    lens = VARLEN_LENS
+    T = sum(lens)
+    inp = workloads.generate(d1.replace(seqlen=T), 1003, False)   # one row of T tokens, cut into prompts
+    Bn, H, P, N, G, W, Cd = len(lens), d1.nheads, d1.headdim, d1.d_state, d1.n_groups, d1.d_conv, d1.conv_dim
+    dims = m2.make_dims(Bn, max(lens), d1.d_model, d1.expand, P, N, G, W, d1.chunk_size, d1.io)
+    bf = torch.bfloat16
+    cu = torch.as_tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device="cuda")
+    xbc = torch.from_numpy(inp.xbc[0]).to("cuda", bf)
+    dt = torch.from_numpy(inp.dt_raw[0]).to("cuda", bf)
+    cw, cb, dtb, A, D = (torch.from_numpy(a).cuda() for a in (inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D))
+    act = torch.empty((T, Cd), device="cuda", dtype=bf)
+    ring_out = torch.empty((Bn, W, Cd), device="cuda", dtype=bf)
+    y = torch.empty((T, H * P), device="cuda", dtype=bf)
+    s_out = torch.empty((Bn, H, P, N), device="cuda")
+    nws = m2.m2_ssd_scan_workspace_packed(dims, T)
+    ws = torch.empty(max(nws, 1), device="cuda", dtype=torch.uint8) if nws else None
+    del inp
+
+    def conv():
+        m2.m2_conv1d_fwd_packed(dims, cu, xbc, cw, cb, act, None, 0, ring_out)
+
+    def scan():
+        m2.m2_ssd_scan_fwd_packed(dims, cu, act[:, :H * P], act[:, H * P:H * P + G * N], act[:, H * P + G * N:], dt,
+                                  dtb, A, D, y, None, s_out, workspace=ws)
+
+    (t_conv, t_scan), total_ms, _ = time_events(torch, [conv, scan], args.steps, args.warmup)
+    conv_b, scan_b = prefill_bytes(1, T, H, P, N, G, W, Cd, False, True)
+    conv_b += (Bn - 1) * W * Cd * 2           # one ring per prompt
+    scan_b += (Bn - 1) * H * P * N * 4        # one final state per prompt
+    step_ms = total_ms / args.steps
+    return {"value": round(T / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
+            "kernels": {"conv1d_packed": {"us": round(t_conv * 1e3, 2), "roofline": roofline(conv_b, t_conv)},
+                        "ssd_scan_packed": {"us": round(t_scan * 1e3, 2), "roofline": roofline(scan_b, t_scan)}},
+            "config": {"workload": "zamba2-2.7b mixer prefill, 8 prompts packed back to back (cu_seqlens)",
+                       "lengths": list(lens), "tokens": T, "state": "fp32, zero initial, final returned per prompt"}}
 
 
 def bench_norm(torch, m2, workloads, args):
@@ -314,6 +359,10 @@ def main():
                                   for n, v in k.items()}
         out["prefill_path_roofline_frac"] = pre["path_roofline_frac"]
     if args.only in ("all", "prefill"):
+        vl = bench_varlen(torch, m2, workloads, args)
+        print("packed prompts: %.3f ms/step, %.3e tok/s" % (vl["ms_per_step"], vl["value"]), file=sys.stderr,
+              flush=True)
+        out["varlen"] = vl
         nrm = bench_norm(torch, m2, workloads, args)
         print("gated rmsnorm: %.1f us (%.0f GB/s)" % (nrm["us"], nrm["roofline"]["achieved"]), file=sys.stderr,
               flush=True)

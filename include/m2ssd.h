@@ -60,7 +60,7 @@ typedef enum {
     M2_ERR_SHAPE = 2,        /* non-positive or inconsistent sizes, stride below row width */
     M2_ERR_DTYPE = 3,        /* dims.io is not a supported storage type */
     M2_ERR_ALIAS = 4,        /* an output overlaps an input it must not overlap */
-    M2_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than m2_ssd_scan_workspace() */
+    M2_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the size its query reports */
     M2_ERR_UNSUPPORTED = 6,  /* valid but not built: headdim/d_state/alignment outside the kernels' set */
     M2_ERR_LAUNCH = 7        /* the HIP runtime reported an error at launch */
 } m2_status;
@@ -127,8 +127,7 @@ m2_status m2_conv1d_fwd_packed(const m2_dims* dims, int64_t total_tokens, const 
                                void* out, int64_t out_tok_stride,
                                void* stream);
 
-/* Workspace bytes m2_ssd_scan_fwd (and m2_ssd_scan_fwd_packed, with dims.seqlen the longest
- * sequence) needs for these dims (0 if none). */
+/* Workspace bytes m2_ssd_scan_fwd needs for these dims (0 if none). */
 size_t m2_ssd_scan_workspace(const m2_dims* dims);
 
 /* Chunked selective state-space scan over a prompt (the recurrence above for t = 0..seqlen-1).
@@ -164,11 +163,17 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims,
                           const int32_t* seq_lens,
                           void* stream);
 
+/* Workspace bytes m2_ssd_scan_fwd_packed needs for dims (dims.seqlen the longest sequence) and
+ * total_tokens rows (0 if none, or if the arguments are invalid).  The packed scan sizes its
+ * segments from the total, so this can differ from m2_ssd_scan_workspace(dims). */
+size_t m2_ssd_scan_workspace_packed(const m2_dims* dims, int64_t total_tokens);
+
 /* Packed batch: the same as m2_ssd_scan_fwd for dims.batch sequences back to back in arrays of
  * total_tokens rows (x [total_tokens, nheads, headdim], B/C [total_tokens, n_groups, d_state],
  * dt [total_tokens, nheads], y [total_tokens, nheads*headdim], with token strides and alignment as
  * in m2_ssd_scan_fwd).  cu_seqlens as in m2_conv1d_fwd_packed; dims.seqlen is the longest
- * sequence.  Each sequence starts from its own state_in[b] (or zero) and returns state_out[b], the
+ * sequence; workspace holds at least m2_ssd_scan_workspace_packed(dims, total_tokens) bytes.
+ * Each sequence starts from its own state_in[b] (or zero) and returns state_out[b], the
  * state after its last token.  Sequences never see one another's tokens. */
 m2_status m2_ssd_scan_fwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
                                  const void* x, int64_t x_tok_stride,

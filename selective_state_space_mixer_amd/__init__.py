@@ -9,7 +9,7 @@ library is missing, importing this package raises.
 
 Names and semantics follow the C ABI:
     m2_conv1d_fwd, m2_conv1d_fwd_packed, m2_ssd_scan_workspace, m2_ssd_scan_fwd,
-    m2_ssd_scan_fwd_packed, m2_ssd_step, m2_gated_rmsnorm, m2_status_str, m2_abi_version,
+    m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_step, m2_gated_rmsnorm, m2_status_str, m2_abi_version,
     m2_last_hip_error
 """
 from __future__ import annotations
@@ -28,7 +28,7 @@ M2_F32, M2_BF16 = 0, 1
 ABI_VERSION = 3
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
-           "m2_ssd_scan_fwd_packed", "m2_ssd_step", "m2_gated_rmsnorm", "m2_status_str", "m2_abi_version",
+           "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_step", "m2_gated_rmsnorm", "m2_status_str", "m2_abi_version",
            "m2_last_hip_error")
 
 
@@ -77,6 +77,8 @@ def _load() -> ctypes.CDLL:
     lib.m2_conv1d_fwd_packed.restype = ctypes.c_int
     lib.m2_ssd_scan_workspace.argtypes = [dp]
     lib.m2_ssd_scan_workspace.restype = sz
+    lib.m2_ssd_scan_workspace_packed.argtypes = [dp, i64]
+    lib.m2_ssd_scan_workspace_packed.restype = sz
     lib.m2_ssd_scan_fwd.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp, i64,
                                     vp, sz, vp, vp]
     lib.m2_ssd_scan_fwd.restype = ctypes.c_int
@@ -239,6 +241,10 @@ def m2_ssd_scan_workspace(dims: M2Dims) -> int:
     return int(_lib.m2_ssd_scan_workspace(ctypes.byref(dims)))
 
 
+def m2_ssd_scan_workspace_packed(dims: M2Dims, total_tokens: int) -> int:
+    return int(_lib.m2_ssd_scan_workspace_packed(ctypes.byref(dims), int(total_tokens)))
+
+
 def m2_ssd_scan_fwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, state_out=None,
                     dt_min: float = 0.0, dt_max: float = float("inf"), workspace=None, stream=None,
                     seq_lens=None) -> None:
@@ -333,7 +339,8 @@ def m2_ssd_scan_fwd_packed(dims: M2Dims, cu_seqlens, x, B, C, dt, dt_bias, A, D,
     """Packed batch scan; see include/m2ssd.h.  dims.batch sequences, dims.seqlen the longest;
     x [T, H, P] (or [T, H*P]), B/C [T, G, N], dt [T, H], y like x (token-strided views allowed, B and C
     sharing one stride); cu_seqlens int32 [batch + 1] on the GPU; state_in / state_out
-    [batch, H, P, N] f32 or None; workspace as for m2_ssd_scan_fwd."""
+    [batch, H, P, N] f32 or None; workspace: a uint8 GPU tensor of at least
+    m2_ssd_scan_workspace_packed(dims, T) bytes, or None."""
     torch = _torch()
     io = _io_dtype(dims)
     H, P, N, G = dims.nheads, dims.headdim, dims.d_state, dims.n_groups
@@ -355,7 +362,7 @@ def m2_ssd_scan_fwd_packed(dims: M2Dims, cu_seqlens, x, B, C, dt, dt_bias, A, D,
         raise ValueError("B and C must have the same token stride")
     dts = _packed_stride(dt, "dt", T, H)
     ys = _packed_stride(y, "y", T, H * P)
-    need = m2_ssd_scan_workspace(dims)
+    need = m2_ssd_scan_workspace_packed(dims, T)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()

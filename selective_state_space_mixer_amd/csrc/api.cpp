@@ -159,7 +159,14 @@ size_t m2_ssd_scan_workspace(const m2_dims* dims) {
     Derived d;
     if (derive(dims, d) != M2_OK) return 0;
     const int Q = d.Q ? d.Q : m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
-    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
+    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16, -1);
+}
+
+size_t m2_ssd_scan_workspace_packed(const m2_dims* dims, int64_t total_tokens) {
+    Derived d;
+    if (derive(dims, d) != M2_OK || total_tokens < 0) return 0;
+    const int Q = d.Q ? d.Q : m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
+    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16, total_tokens);
 }
 
 }  // extern "C"
@@ -198,7 +205,7 @@ m2_status scan_run(const Derived& d, int64_t rows, const int32_t* cu, const void
     if (rows > 0 && (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
                      (x_tok_stride * d.esize) % 16 || (bc_tok_stride * d.esize) % 16 || (y_tok_stride * d.esize) % 16))
         return M2_ERR_UNSUPPORTED;
-    const size_t need = m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16);
+    const size_t need = m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16, cu ? rows : -1);
     if (need > 0 && (!workspace || workspace_bytes < need)) return M2_ERR_WORKSPACE;
     const Range rl = cu ? span(cu, d.batch + 1, 1, 1, 4) : span(seq_lens, d.batch, 1, 1, 4);
     if (overlap(rl, ry) || overlap(rl, rs_out) || overlap(rl, span(workspace, 1, 0, (int64_t)need, 1)))

@@ -65,7 +65,9 @@ struct NormArgs {
 
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s);
-size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16);
+// total: tokens of a packed batch (L its longest sequence), or -1 for a padded one
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16,
+                                int64_t total);
 bool ssd_scan_supported(int P, int N, int Q, bool bf16);
 int ssd_scan_default_chunk(int P, int N, bool bf16);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);

@@ -371,7 +371,11 @@ ssd_chunk_scan_kernel(ScanK k)
     const bool stats_writer = wave < HPW;
 
     // logical unit -> (segment, sequence, head group)
-    const int unit = logical_block(k.nblocks);
+    // Uniform sequences: each XCD takes a contiguous run of units (head groups sharing B/C rows in
+    // one L2).  Variable lengths: which units have work is known only here, and the units of the
+    // first segments (nearly all busy) come first; dealt round-robin as launched, they spread
+    // evenly over the XCDs, where contiguous runs would pile them onto the first few.
+    const int unit = (k.lens || k.cu) ? (int)blockIdx.x : logical_block(k.nblocks);
     const int hpg = k.H / k.G;
     const int upg = (hpg + HPW - 1) / HPW;          // head units per group
     const int nhu = k.G * upg;
@@ -1043,18 +1047,31 @@ static WsLayout ws_layout(int64_t nseg, int64_t BH, int64_t PN, int64_t nchunks,
 }
 
 // Segments: enough (sequence, head group, segment) units for one round of resident blocks.
-static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, int hpw, int bpc, bool bf16) {
+// A packed batch (total >= 0 tokens, L the longest sequence) sizes its segments from the total:
+// every (sequence, segment) pair with work should fit in one round of resident blocks, and
+// sum_b ceil(c_b / cps) <= (total chunks + batch) / cps + batch bounds their number.
+static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, int hpw, int bpc, bool bf16,
+                     int64_t total) {
     Plan pl;
     const int64_t nchunks = (L + Q - 1) / Q;
     const int hpg = H / G;
     pl.nhu = G * ((hpg + hpw - 1) / hpw);
     const int64_t units = batch * pl.nhu;
     const int64_t target = 256 * (int64_t)bpc;  // 256 compute units
-    int64_t nseg = units > 0 ? target / units : 1;
-    if (nseg > nchunks) nseg = nchunks;
-    if (nseg < 1) nseg = 1;
-    const int64_t cps = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 1;
-    nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
+    int64_t cps;
+    if (total >= 0) {
+        const int64_t pairs = target / pl.nhu;                  // (sequence, segment) pairs per round
+        const int64_t tchunks = (total + Q - 1) / Q + batch;
+        cps = pairs > batch ? (tchunks + (pairs - batch) - 1) / (pairs - batch) : nchunks;
+    } else {
+        int64_t nseg = units > 0 ? target / units : 1;
+        if (nseg > nchunks) nseg = nchunks;
+        if (nseg < 1) nseg = 1;
+        cps = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 1;
+    }
+    if (cps > nchunks) cps = nchunks;
+    if (cps < 1) cps = 1;
+    const int64_t nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
     pl.nseg = (int)nseg;
     pl.cps = (int)cps;
     pl.ws_bytes = nseg > 1 ? ws_layout(nseg, batch * H, N_P_N, nchunks, cps, bf16).total + 256 : 0;
@@ -1062,15 +1079,15 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, i
 }
 
 template <typename T, int Q, int P, int N>
-static Plan plan_of(int64_t batch, int64_t L, int H, int G) {
+static Plan plan_of(int64_t batch, int64_t L, int H, int G, int64_t total) {
     using Cf = Cfg<T, Q, P, N>;
-    return plan_for(batch, L, H, G, P * N, Q, Cf::HPW, Cf::BPC, sizeof(T) == 2);
+    return plan_for(batch, L, H, G, P * N, Q, Cf::HPW, Cf::BPC, sizeof(T) == 2, total);
 }
 
 template <typename T, int Q, int P, int N>
 static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
     using Cf = Cfg<T, Q, P, N>;
-    const Plan pl = plan_of<T, Q, P, N>(a.batch, a.L, a.H, a.G);
+    const Plan pl = plan_of<T, Q, P, N>(a.batch, a.L, a.H, a.G, a.cu ? a.total : -1);
     ScanK k;
     k.x = a.x; k.B = a.B; k.C = a.C; k.dt = a.dt;
     k.xs = a.xs; k.bcs = a.bcs; k.dts = a.dts; k.ys = a.ys;
@@ -1140,8 +1157,8 @@ bool ssd_scan_supported(int P, int N, int Q, bool bf16) {
 int ssd_scan_default_chunk(int, int, bool) { return 32; }
 
 template <typename T, int Q>
-static size_t workspace_pn(int64_t batch, int64_t L, int H, int P, int N, int G) {
-#define M2_PN(PP, NN) if (P == PP && N == NN) return plan_of<T, Q, PP, NN>(batch, L, H, G).ws_bytes;
+static size_t workspace_pn(int64_t batch, int64_t L, int H, int P, int N, int G, int64_t total) {
+#define M2_PN(PP, NN) if (P == PP && N == NN) return plan_of<T, Q, PP, NN>(batch, L, H, G, total).ws_bytes;
     M2_PN(16, 16) M2_PN(16, 32) M2_PN(16, 64) M2_PN(32, 16) M2_PN(32, 32) M2_PN(32, 64)
     M2_PN(64, 16) M2_PN(64, 32) M2_PN(64, 64) M2_PN(64, 128)
     if constexpr (sizeof(T) == 2) {
@@ -1151,17 +1168,18 @@ static size_t workspace_pn(int64_t batch, int64_t L, int H, int P, int N, int G)
     return 0;
 }
 
-size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16) {
+size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16,
+                                int64_t total) {
     if (bf16) {
         switch (Q) {
-            case 16: return workspace_pn<bf16_t, 16>(batch, L, H, P, N, G);
-            case 32: return workspace_pn<bf16_t, 32>(batch, L, H, P, N, G);
-            default: return workspace_pn<bf16_t, 64>(batch, L, H, P, N, G);
+            case 16: return workspace_pn<bf16_t, 16>(batch, L, H, P, N, G, total);
+            case 32: return workspace_pn<bf16_t, 32>(batch, L, H, P, N, G, total);
+            default: return workspace_pn<bf16_t, 64>(batch, L, H, P, N, G, total);
         }
     }
     switch (Q) {
-        case 16: return workspace_pn<float, 16>(batch, L, H, P, N, G);
-        default: return workspace_pn<float, 32>(batch, L, H, P, N, G);
+        case 16: return workspace_pn<float, 16>(batch, L, H, P, N, G, total);
+        default: return workspace_pn<float, 32>(batch, L, H, P, N, G, total);
     }
 }
 

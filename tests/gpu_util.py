@@ -46,6 +46,7 @@ def nan_like(shape, io: str):
     return torch.full(shape, float("nan"), device="cuda", dtype=torch_io(io))
 
 
-def workspace(dims):
-    n = m2.m2_ssd_scan_workspace(dims)
+def workspace(dims, packed_tokens=None):
+    """Scan workspace for dims (a packed batch: pass its token count)."""
+    n = m2.m2_ssd_scan_workspace(dims) if packed_tokens is None else m2.m2_ssd_scan_workspace_packed(dims, packed_tokens)
     return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda") if n > 0 else None

@@ -123,7 +123,7 @@ def test_packed_validation():
     assert conv_p(-1, FAKE + 0x6_0000_0000) == m2.M2_ERR_SHAPE
     assert conv_p(256, FAKE + 0x6_0000_0002) == m2.M2_ERR_UNSUPPORTED             # misaligned offsets
     assert conv_p(256, out + 64) == m2.M2_ERR_ALIAS                               # offsets inside out
-    ws = m2.m2_ssd_scan_workspace(d)
+    ws = max(m2.m2_ssd_scan_workspace_packed(d, 256), m2.m2_ssd_scan_workspace(d))
     scan_p = lambda T, cu: lib.m2_ssd_scan_fwd_packed(ctypes.byref(d), T, cu, FAKE, di, FAKE + 0x10000000,
                                                       FAKE + 0x10000100, 128, FAKE + 0x20000000, 80,
                                                       FAKE + 0x30000000, FAKE + 0x30001000, None, 0.0,
@@ -133,6 +133,23 @@ def test_packed_validation():
     assert scan_p(-5, FAKE + 0x6_0000_0000) == m2.M2_ERR_SHAPE
     assert scan_p(256, FAKE + 0x6_0000_0001) == m2.M2_ERR_UNSUPPORTED
     assert scan_p(256, FAKE + 0x4000_0000_00 + 32) == m2.M2_ERR_ALIAS             # offsets inside y
+
+
+def test_packed_workspace_follows_the_total():
+    # eight prompts of 32768 tokens in all, the longest 8192: the packed plan sizes segments from the
+    # total, the padded plan from batch x longest; both report sizes for their own plans
+    d = dims(batch=8, seqlen=8192)
+    assert m2.m2_ssd_scan_workspace_packed(d, 32768) > 0
+    assert m2.m2_ssd_scan_workspace_packed(d, -1) == 0
+    assert m2.m2_ssd_scan_workspace_packed(dims(io=7), 100) == 0
+    needed = m2.m2_ssd_scan_workspace_packed(d, 32768)
+    lib = m2.lib()
+    di = d.expand * d.d_model
+    st = lib.m2_ssd_scan_fwd_packed(ctypes.byref(d), 32768, FAKE + 0x6_0000_0000, FAKE, di, FAKE + 0x10000000,
+                                    FAKE + 0x10000100, 128, FAKE + 0x20000000, 80, FAKE + 0x30000000,
+                                    FAKE + 0x30001000, None, 0.0, float("inf"), None, None, FAKE + 0x4000_0000_00,
+                                    di, FAKE + 0x9_0000_0000, needed - 1, None)
+    assert st == m2.M2_ERR_WORKSPACE
 
 
 def test_empty_batch_is_a_no_op():

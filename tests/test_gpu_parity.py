@@ -409,7 +409,7 @@ def test_ssd_scan_packed_parity(case):
     s_out = torch.full((len(lens), H, P, N), float("nan"), device="cuda")
     m2.m2_ssd_scan_fwd_packed(dims, _cu_dev(lens), dev(xp, io), dev(bp, io), dev(cp, io), dev(dtp, io),
                               dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(inp.state0), s_out,
-                              workspace=workspace(dims))
+                              workspace=workspace(dims, T))
     torch.cuda.synchronize()
     tol = tol_for(io)
     assert oracle.max_rel_err(host(y).reshape(T, H, P), yr) <= tol
@@ -438,7 +438,7 @@ def test_packed_prefill_then_decode():
     state = torch.empty((Bn, H, P, N), device="cuda")
     m2.m2_ssd_scan_fwd_packed(dims, cu, act[:, :H * P], act[:, H * P:H * P + G * N], act[:, H * P + G * N:],
                               dev(dtp, io), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(inp.state0),
-                              state, workspace=workspace(dims))
+                              state, workspace=workspace(dims, T))
     ys = []
     xt, dtt = dev(tok.xbc, io), dev(tok.dt_raw, io)
     w, cb, dtb, A, D = (dev32(a) for a in (inp.conv_w, inp.conv_b, inp.dt_bias, inp.A, inp.D))
