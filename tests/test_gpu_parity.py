@@ -614,6 +614,50 @@ def test_full_size_prefill_130m_sampled():
     _sampled_scan_check(1, heads=[0, 23], batches=[0, 3])
 
 
+def test_full_size_packed_prompts_sampled():
+    """Eight prompts of 8192 .. 1024 tokens (32768 in all) packed back to back at the Zamba2-2.7B shape,
+    as the benchmark runs them: sampled prompts and heads of the scan, fed the GPU's own conv output."""
+    _need_gpu()
+    lens = [8192, 6144, 5120, 4096, 3584, 2560, 2048, 1024]
+    d1 = workloads.CONFIGS[3].dims
+    T = sum(lens)
+    inp = workloads.generate(d1.replace(seqlen=T), 1003, False)
+    H, P, N, G, W, Cd = d1.nheads, d1.headdim, d1.d_state, d1.n_groups, d1.d_conv, d1.conv_dim
+    d = d1.replace(batch=len(lens), seqlen=max(lens))
+    dims = dims_of(d)
+    cu = _cu_dev(lens)
+    cu_np = np.concatenate([[0], np.cumsum(lens)])
+    act = torch.empty((T, Cd), device="cuda", dtype=torch.bfloat16)
+    ring_out = torch.empty((len(lens), W, Cd), device="cuda", dtype=torch.bfloat16)
+    m2.m2_conv1d_fwd_packed(dims, cu, dev(inp.xbc[0], "bf16"), dev32(inp.conv_w), dev32(inp.conv_b), act, None, 0,
+                            ring_out)
+    y = torch.empty((T, H * P), device="cuda", dtype=torch.bfloat16)
+    s_out = torch.empty((len(lens), H, P, N), device="cuda")
+    m2.m2_ssd_scan_fwd_packed(dims, cu, act[:, :H * P], act[:, H * P:H * P + G * N], act[:, H * P + G * N:],
+                              dev(inp.dt_raw[0], "bf16"), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, None,
+                              s_out, workspace=workspace(dims, T))
+    torch.cuda.synchronize()
+    a_all = host(act)
+    for b in (0, 3, 7):
+        r0, r1 = cu_np[b], cu_np[b + 1]
+        n = r1 - r0
+        # conv of sampled channels of this prompt, and its ring
+        chans = np.array([0, H * P - 1, H * P, Cd - 1])
+        ref, ref_ring = oracle.conv1d(inp.xbc[0][None, r0:r1][:, :, chans], inp.conv_w[chans], inp.conv_b[chans])
+        assert oracle.max_rel_err(a_all[None, r0:r1][:, :, chans], ref) <= 2e-2, b
+        np.testing.assert_array_equal(host(ring_out[b])[:, chans], ref_ring[0])
+        for h in (0, 41, 79):
+            g = h // (H // G)
+            xs = a_all[r0:r1, h * P:(h + 1) * P].reshape(1, n, 1, P)
+            bs = a_all[r0:r1, H * P + g * N:H * P + (g + 1) * N].reshape(1, n, 1, N)
+            cs = a_all[r0:r1, H * P + G * N + g * N:H * P + G * N + (g + 1) * N].reshape(1, n, 1, N)
+            yr, sr = oracle.ssd_scan(xs, bs, cs, inp.dt_raw[0][None, r0:r1, h:h + 1], inp.dt_bias[h:h + 1],
+                                     inp.A[h:h + 1], inp.D[h:h + 1])
+            got = host(y[r0:r1, h * P:(h + 1) * P]).reshape(1, n, 1, P)
+            assert oracle.max_rel_err(got, yr) <= 2e-2, (b, h)
+            assert oracle.max_rel_err(host(s_out[b:b + 1, h:h + 1]), sr) <= 2e-2, (b, h)
+
+
 def test_full_size_decode_b256_sampled():
     """256 sequences, a few chained steps; sampled sequences against the oracle chain."""
     _need_gpu()
