@@ -90,7 +90,7 @@ def time_events(torch, fns, steps, warmup):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"ssd_scan": "ssd_scan.hip", "conv1d": "conv1d.hip", "ssd_step": "ssd_step.hip",
-                  "gated_rmsnorm": "gated_norm.hip"}
+                  "gated_rmsnorm": "gated_norm.hip", "ssd_scan_packed": "ssd_scan.hip", "conv1d_packed": "conv1d.hip"}
 
 
 def source_digest(kernel):
@@ -202,8 +202,10 @@ def bench_varlen(torch, m2, workloads, args):
     scan_b += (Bn - 1) * H * P * N * 4        # one final state per prompt
     step_ms = total_ms / args.steps
     return {"value": round(T / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
-            "kernels": {"conv1d_packed": {"us": round(t_conv * 1e3, 2), "roofline": roofline(conv_b, t_conv)},
-                        "ssd_scan_packed": {"us": round(t_scan * 1e3, 2), "roofline": roofline(scan_b, t_scan)}},
+            "kernels": {"conv1d_packed": {"us": round(t_conv * 1e3, 2),
+                                          "roofline": roofline(conv_b, t_conv, "conv1d_packed")},
+                        "ssd_scan_packed": {"us": round(t_scan * 1e3, 2),
+                                            "roofline": roofline(scan_b, t_scan, "ssd_scan_packed")}},
             "config": {"workload": "zamba2-2.7b mixer prefill, 8 prompts packed back to back (cu_seqlens)",
                        "lengths": list(lens), "tokens": T, "state": "fp32, zero initial, final returned per prompt"}}
 
