@@ -53,6 +53,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t norm_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// cache policy of the y and z loads: streaming (non-temporal) -- each is read once, and the
+// cache is better left to the output, which the next layer reads (5% faster on the 32k output)
+constexpr int kStream = 2;
+
 template <typename T, int NV>
 __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(NormK k)
 {
@@ -73,8 +77,8 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(NormK k)
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const uint32_t off = (uint32_t)(j * 64 + lane) * 16u;
-        yv[j] = __builtin_amdgcn_raw_buffer_load_b128(ry, (int)off, 0, 0);
-        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)off, 0, 0);
+        yv[j] = __builtin_amdgcn_raw_buffer_load_b128(ry, (int)off, 0, kStream);
+        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)off, 0, kStream);
     }
     // sum of squares of the normalised operand (pieces past the group read as zero)
     float ss = 0.0f;
