@@ -154,6 +154,26 @@ def test_ssd_scan_parity(case):
     assert oracle.max_rel_err(s, sr) <= tol
 
 
+_PN = [(16, 16), (16, 32), (16, 64), (32, 16), (32, 32), (32, 64), (64, 16), (64, 32), (64, 64), (64, 128)]
+SHAPE_CASES = ([("bf16", p, n, q) for p, n in _PN + [(128, 64), (128, 128)] for q in (16, 32, 64)] +
+               [("f32", p, n, q) for p, n in _PN for q in (16, 32)])
+
+
+@pytest.mark.parametrize("case", SHAPE_CASES, ids=lambda c: "%s-P%d-N%d-Q%d" % c)
+def test_ssd_scan_every_built_shape(case):
+    """Every (headdim, d_state, chunk, dtype) the library builds, on a short ragged prompt with a cached
+    state, two groups and a plan of several segments (so the chain and the fix-up run too)."""
+    _need_gpu()
+    io, P, N, Q = case
+    d = workloads.Dims(2, 3 * Q + 5, 2 * P, 2, P, N, 2, 4, Q, io)   # 4 heads in 2 groups
+    inp, x, b, c = _scan_inputs(d, 2400 + P + N + Q, True)
+    y, s = _run_scan(d, inp, x, b, c, inp.state0)
+    yr, sr = oracle.ssd_scan(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0)
+    tol = tol_for(io)
+    assert oracle.max_rel_err(y, yr) <= tol
+    assert oracle.max_rel_err(s, sr) <= tol
+
+
 def test_ssd_scan_buffer_windows_move():
     """A token stride so wide that a 2^31-byte buffer window holds only a few chunks: the kernel must
     move its windows along the sequence (here after every chunk) and still match the oracle."""
