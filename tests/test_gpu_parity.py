@@ -519,6 +519,31 @@ def test_ssd_step_chain_parity(over, steps):
     np.testing.assert_array_equal(ring, r_ring)
 
 
+STEP_SHAPES = [("bf16", 16, 16, 4), ("f32", 24, 32, 3), ("bf16", 64, 64, 2), ("f32", 64, 128, 4),
+               ("bf16", 128, 64, 4), ("bf16", 32, 256, 3), ("f32", 80, 64, 4), ("bf16", 256, 32, 4)]
+
+
+@pytest.mark.parametrize("case", STEP_SHAPES, ids=lambda c: "%s-P%d-N%d-W%d" % c)
+def test_ssd_step_every_kind_of_shape(case):
+    """Decode steps over head sizes that use every per-thread state share the kernel has (1, 2, 4, 8
+    float4 per thread), odd head sizes, each d_state it builds, each conv width, both dtypes."""
+    _need_gpu()
+    io, P, N, W = case
+    d = workloads.Dims(3, 1, 2 * P, 2, P, N, 2, W, 0, io)   # 4 heads in 2 groups
+    steps = 3
+    inp = workloads.generate(d, 1500 + P + N, True, steps)
+    H, G = d.nheads, d.n_groups
+    ys, ring, state = _gpu_chain(d, inp, steps, inp.ring0, inp.state0, first_step=2)
+    r_ring, r_state = inp.ring0.astype(np.float64), inp.state0.astype(np.float64)
+    tol = tol_for(io)
+    for t in range(steps):
+        yr, r_ring, r_state = oracle.ssd_step(inp.xbc[t], inp.dt_raw[t], inp.conv_w, inp.conv_b, inp.dt_bias,
+                                              inp.A, inp.D, r_ring, 2 + t, r_state, H, P, N, G)
+        assert oracle.max_rel_err(ys[t], yr) <= tol, "step %d" % t
+    assert oracle.max_rel_err(state, r_state) <= tol
+    np.testing.assert_array_equal(ring, r_ring)
+
+
 def test_ssd_step_fp32_chain_parity():
     _need_gpu()
     d = workloads.CONFIGS[0].dims.replace(batch=2, seqlen=1)
