@@ -41,6 +41,10 @@
 // the others from zero), a small pass chains the segments' end states into each segment's
 // true initial state and the final state, and a fix-up adds the initial state's share of
 // the later segments' outputs where it has not yet decayed away.
+//
+// Sequence b's rows start at b*L (or, in a packed batch, at cu_seqlens[b]) and it has L tokens
+// (or its padded or packed length); chunks are counted from each sequence's own first row, so
+// a chunk never holds two sequences, and chunks past a sequence's end are not run.
 #include "m2_device.h"
 #include "m2_launch.h"
 
