@@ -830,8 +830,8 @@ __device__ void list_fix_items(const int* __restrict__ nfix, uint2* __restrict__
 // the caller's state), lam[seg] its summed log-decay.  The true end states follow
 //   T[0] = E[0],  T[seg] = e^lam[seg] T[seg-1] + E[seg];
 // T[seg] (the initial state of segment seg+1) is written over E[seg] (or, for bf16 outputs, to a
-// bf16 copy), and T[nseg-1] is the final
-// state.  Only the combine is sequential: the loads of a batch of segments are issued together.
+// bf16 copy), and T[nseg-1] is the final state.  Only the combine is sequential: the loads of a
+// batch of segments are issued together.
 // The block row past the last sequence-head writes the fix-up's work list instead.
 __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restrict__ ws_state,
                                                                 const float* __restrict__ ws_lam,
