@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "m2_launch.h"
 
@@ -70,6 +71,24 @@ m2_status launched(hipError_t e) {
 
 namespace m2 {
 void note_hip_error(hipError_t e) { g_last_hip_error = e; }
+
+DeviceShape device_shape() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static DeviceShape cache[kMaxDevices];
+    static bool known[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DeviceShape{256, 8};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev]) {
+        int cus = 0, xcds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+        if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds < 1) xcds = 8;
+        cache[dev] = DeviceShape{cus, xcds};
+        known[dev] = true;
+    }
+    return cache[dev];
+}
 }  // namespace m2
 
 extern "C" {

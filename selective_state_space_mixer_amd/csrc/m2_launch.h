@@ -63,6 +63,12 @@ struct NormArgs {
     bool bf16;
 };
 
+// Compute units and XCDs of the calling thread's current device, read once per device with
+// hipDeviceGetAttribute and cached (thread-safe).  Plans that spread work over the chip size
+// themselves from it; if the query fails, 256 compute units in 8 XCDs are assumed.
+struct DeviceShape { int cus; int xcds; };
+DeviceShape device_shape();
+
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s);
 // total: tokens of a packed batch (L its longest sequence), or -1 for a padded one
