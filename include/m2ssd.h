@@ -27,9 +27,12 @@
  *
  * Conventions
  *   - Every pointer argument except `stream` is DEVICE memory owned by the caller.
- *     The library allocates nothing, keeps no state between calls and never
- *     synchronises: each call only enqueues kernels on `stream` (a hipStream_t;
- *     NULL = the default stream) and returns.  Calls are thread-safe.
+ *     The library allocates nothing and never synchronises: each call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *     It keeps no state between calls beyond a cached record of each device's compute
+ *     units and XCDs and one static scratch array per device (m2_ssd_scan_fwd_noalloc).
+ *     Calls are thread-safe, except that calls of m2_ssd_scan_fwd_noalloc that may
+ *     overlap on one GPU share its scratch array.
  *   - Activations (xBC, x, B, C, dt, y, conv ring) are stored in dims.io (bf16 or
  *     fp32); fp32 accumulation everywhere.  Parameters (conv w/bias, dt_bias, A, D)
  *     and the SSM state are always fp32.
@@ -52,7 +55,7 @@
 extern "C" {
 #endif
 
-#define M2SSD_ABI_VERSION 3
+#define M2SSD_ABI_VERSION 4
 
 typedef enum {
     M2_OK = 0,
@@ -62,8 +65,12 @@ typedef enum {
     M2_ERR_ALIAS = 4,        /* an output overlaps an input it must not overlap */
     M2_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the size its query reports */
     M2_ERR_UNSUPPORTED = 6,  /* valid but not built: headdim/d_state/alignment outside the kernels' set */
-    M2_ERR_LAUNCH = 7        /* the HIP runtime reported an error at launch */
+    M2_ERR_LAUNCH = 7,       /* the HIP runtime reported an error at launch */
+    M2_ERR_TOO_LARGE = 8     /* the call needs more scratch than the library's static buffer holds */
 } m2_status;
+
+/* Bytes of the static device scratch buffer behind m2_ssd_scan_fwd_noalloc (one per GPU). */
+#define M2_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum { M2_F32 = 0, M2_BF16 = 1 } m2_dtype;
 
@@ -185,6 +192,27 @@ m2_status m2_ssd_scan_fwd_packed(const m2_dims* dims, int64_t total_tokens, cons
                                  void* y, int64_t y_tok_stride,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* m2_ssd_scan_fwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * workspace m2_ssd_scan_workspace(dims) reports comes from a static device array of
+ * M2_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process ends;
+ * its address is looked up once per device on the first call there.  Arguments, results and
+ * errors are those of m2_ssd_scan_fwd, plus M2_ERR_TOO_LARGE (nothing launched) when the call
+ * needs more than M2_STATIC_SCRATCH_BYTES (the Zamba2-2.7B mixer shape needs about 50 MB for one
+ * 32768-token sequence).  No call allocates or frees memory.  Every call on one GPU uses the same
+ * array: calls that may overlap on one GPU (other streams, other threads without ordering) race
+ * and must not be made; calls ordered on one stream are safe. */
+m2_status m2_ssd_scan_fwd_noalloc(const m2_dims* dims,
+                                  const void* x, int64_t x_tok_stride,
+                                  const void* B, const void* C, int64_t bc_tok_stride,
+                                  const void* dt, int64_t dt_tok_stride,
+                                  const float* dt_bias, const float* A, const float* D,
+                                  float dt_min, float dt_max,
+                                  const float* state_in, float* state_out,
+                                  void* y, int64_t y_tok_stride,
+                                  const int32_t* seq_lens,
+                                  void* stream);
 
 /* One decode token for every sequence, fused: conv window (W-1 cached tokens + the new
  * one) -> SiLU -> split x | B | C -> dt -> state update -> output.

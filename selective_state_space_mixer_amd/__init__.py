@@ -9,8 +9,8 @@ library is missing, importing this package raises.
 
 Names and semantics follow the C ABI:
     m2_conv1d_fwd, m2_conv1d_fwd_packed, m2_ssd_scan_workspace, m2_ssd_scan_fwd,
-    m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_step, m2_gated_rmsnorm, m2_status_str, m2_abi_version,
-    m2_last_hip_error
+    m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_scan_fwd_noalloc, m2_ssd_step, m2_gated_rmsnorm,
+    m2_status_str, m2_abi_version, m2_last_hip_error
 """
 from __future__ import annotations
 
@@ -23,13 +23,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libm2ssd.so")
 
 M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, M2_ERR_UNSUPPORTED, \
-    M2_ERR_LAUNCH = range(8)
+    M2_ERR_LAUNCH, M2_ERR_TOO_LARGE = range(9)
+M2_STATIC_SCRATCH_BYTES = 64 << 20
 M2_F32, M2_BF16 = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
-           "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_step", "m2_gated_rmsnorm", "m2_status_str", "m2_abi_version",
-           "m2_last_hip_error")
+           "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc", "m2_ssd_step",
+           "m2_gated_rmsnorm", "m2_status_str", "m2_abi_version", "m2_last_hip_error")
 
 
 class M2Dims(ctypes.Structure):
@@ -85,6 +86,9 @@ def _load() -> ctypes.CDLL:
     lib.m2_ssd_scan_fwd_packed.argtypes = [dp, i64, vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp,
                                            vp, i64, vp, sz, vp]
     lib.m2_ssd_scan_fwd_packed.restype = ctypes.c_int
+    lib.m2_ssd_scan_fwd_noalloc.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp, i64,
+                                            vp, vp]
+    lib.m2_ssd_scan_fwd_noalloc.restype = ctypes.c_int
     lib.m2_ssd_step.argtypes = [dp, vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, f32, vp, i64, vp, vp, vp]
     lib.m2_ssd_step.restype = ctypes.c_int
     lib.m2_gated_rmsnorm.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp, i64, vp, f32,
@@ -245,16 +249,8 @@ def m2_ssd_scan_workspace_packed(dims: M2Dims, total_tokens: int) -> int:
     return int(_lib.m2_ssd_scan_workspace_packed(ctypes.byref(dims), int(total_tokens)))
 
 
-def m2_ssd_scan_fwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, state_out=None,
-                    dt_min: float = 0.0, dt_max: float = float("inf"), workspace=None, stream=None,
-                    seq_lens=None) -> None:
-    """Chunked selective-SSM scan; see include/m2ssd.h.
-
-    x [B, L, H, P] (or [B, L, H*P]), B/C [B, L, G, N] (or [B, L, G*N]), dt [B, L, H], y like x,
-    all io dtype, token-strided views allowed (B and C must share one token stride);
-    dt_bias, A, D [H] f32 (D may be None); state_in / state_out [B, H, P, N] f32 or None;
-    workspace: a uint8 GPU tensor of at least m2_ssd_scan_workspace(dims) bytes, or None;
-    seq_lens: int32 [B] GPU tensor of each right-padded sequence's length, or None."""
+def _scan_args(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in, state_out):
+    """Checked pointers and token strides of a padded-batch scan call (shared by both scan entry points)."""
     torch = _torch()
     io = _io_dtype(dims)
     H, P, N, G = dims.nheads, dims.headdim, dims.d_state, dims.n_groups
@@ -275,15 +271,38 @@ def m2_ssd_scan_fwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, 
         raise ValueError("B and C must have the same token stride")
     dts = _tok_stride(dt, "dt", dims, H)
     ys = _tok_stride(y, "y", dims, H * P)
+    return (_ptr(x), xs, _ptr(B), _ptr(C), bs, _ptr(dt), dts, _ptr(dt_bias), _ptr(A), _ptr(D)), \
+        (_ptr(state_in), _ptr(state_out), _ptr(y), ys)
+
+
+def m2_ssd_scan_fwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, state_out=None,
+                    dt_min: float = 0.0, dt_max: float = float("inf"), workspace=None, stream=None,
+                    seq_lens=None) -> None:
+    """Chunked selective-SSM scan; see include/m2ssd.h.
+
+    x [B, L, H, P] (or [B, L, H*P]), B/C [B, L, G, N] (or [B, L, G*N]), dt [B, L, H], y like x,
+    all io dtype, token-strided views allowed (B and C must share one token stride);
+    dt_bias, A, D [H] f32 (D may be None); state_in / state_out [B, H, P, N] f32 or None;
+    workspace: a uint8 GPU tensor of at least m2_ssd_scan_workspace(dims) bytes, or None;
+    seq_lens: int32 [B] GPU tensor of each right-padded sequence's length, or None."""
+    ins, outs = _scan_args(dims, x, B, C, dt, dt_bias, A, D, y, state_in, state_out)
     need = m2_ssd_scan_workspace(dims)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     elif need > 0:
         raise ValueError("m2_ssd_scan_fwd needs a workspace of %d bytes" % need)
-    _call("m2_ssd_scan_fwd", ctypes.byref(dims), _ptr(x), xs, _ptr(B), _ptr(C), bs, _ptr(dt), dts,
-          _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min), float(dt_max), _ptr(state_in), _ptr(state_out),
-          _ptr(y), ys, ws_ptr, ws_bytes, _lens_ptr(seq_lens, dims), _stream(stream))
+    _call("m2_ssd_scan_fwd", ctypes.byref(dims), *ins, float(dt_min), float(dt_max), *outs, ws_ptr, ws_bytes,
+          _lens_ptr(seq_lens, dims), _stream(stream))
+
+
+def m2_ssd_scan_fwd_noalloc(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_in=None, state_out=None,
+                            dt_min: float = 0.0, dt_max: float = float("inf"), stream=None, seq_lens=None) -> None:
+    """m2_ssd_scan_fwd with the library's static scratch buffer as its workspace (no allocation);
+    see include/m2ssd.h.  Arguments as m2_ssd_scan_fwd without `workspace`."""
+    ins, outs = _scan_args(dims, x, B, C, dt, dt_bias, A, D, y, state_in, state_out)
+    _call("m2_ssd_scan_fwd_noalloc", ctypes.byref(dims), *ins, float(dt_min), float(dt_max), *outs,
+          _lens_ptr(seq_lens, dims), _stream(stream))
 
 
 def _packed_stride(t, name, T, row: int) -> int:

@@ -103,6 +103,7 @@ const char* m2_status_str(m2_status s) {
         case M2_ERR_WORKSPACE: return "workspace missing or too small";
         case M2_ERR_UNSUPPORTED: return "shape, width or alignment not supported by the built kernels";
         case M2_ERR_LAUNCH: return "kernel launch failed";
+        case M2_ERR_TOO_LARGE: return "the call needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }
@@ -270,6 +271,29 @@ m2_status m2_ssd_scan_fwd_packed(const m2_dims* dims, int64_t total_tokens, cons
     return scan_run(d, total_tokens, cu_seqlens, x, x_tok_stride, B, C, bc_tok_stride, dt, dt_tok_stride, dt_bias,
                     A, D, dt_min, dt_max, state_in, state_out, y, y_tok_stride, workspace, workspace_bytes, nullptr,
                     stream);
+}
+
+m2_status m2_ssd_scan_fwd_noalloc(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B,
+                                  const void* C, int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride,
+                                  const float* dt_bias, const float* A, const float* D, float dt_min, float dt_max,
+                                  const float* state_in, float* state_out, void* y, int64_t y_tok_stride,
+                                  const int32_t* seq_lens, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    // the workspace this call needs (0 if its plan has one segment); compared with the static size
+    // before the buffer's address is looked up, so an oversize call touches nothing
+    const size_t need = m2_ssd_scan_workspace(dims);
+    if (need > M2_STATIC_SCRATCH_BYTES) return M2_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need > 0) {
+        const hipError_t e = m2::static_scratch(&ws, &ws_bytes);
+        if (e != hipSuccess) return launched(e);
+        if (ws_bytes < need) return M2_ERR_TOO_LARGE;
+    }
+    return scan_run(d, d.batch * d.L, nullptr, x, x_tok_stride, B, C, bc_tok_stride, dt, dt_tok_stride, dt_bias, A,
+                    D, dt_min, dt_max, state_in, state_out, y, y_tok_stride, ws, ws_bytes, seq_lens, stream);
 }
 
 m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stride, const void* dt_tok,

@@ -75,6 +75,9 @@ hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s);
 size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16,
                                 int64_t total);
 bool ssd_scan_supported(int P, int N, int Q, bool bf16);
+// The library's static scratch buffer on the current device (address looked up once per device)
+// and its size in bytes; for the entry point that must not allocate.
+hipError_t static_scratch(void** ptr, size_t* bytes);
 int ssd_scan_default_chunk(int P, int N, bool bf16);
 hipError_t launch_ssd_step(const StepArgs& a, hipStream_t s);
 bool ssd_step_supported(int P, int N);

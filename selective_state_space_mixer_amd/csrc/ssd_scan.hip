@@ -47,7 +47,37 @@
 // a chunk never holds two sequences, and chunks past a sequence's end are not run.
 #include "ssd_common.h"
 
+#include <mutex>
+
 namespace m2 {
+
+// Workspace for callers that cannot allocate (m2_ssd_scan_fwd_noalloc): a static array each GPU the
+// library runs on holds until the process ends.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t static_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = kScratchBytes;
+    return hipSuccess;
+}
 
 // Work split.  A wave owns PW p-blocks of one head, so its share of the state is at most
 // kMaxStateTiles 16x16 accumulator tiles (32 registers); WPH waves cover a head.  A block holds

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert m2.m2_abi_version() == m2.ABI_VERSION
-    for s in range(8):
+    for s in range(9):
         assert m2.m2_status_str(s)
     assert m2.m2_status_str(99) == "unknown status"
 
@@ -216,3 +216,19 @@ def test_gated_rmsnorm_validation():
     assert norm(out=FAKE + 0x1000_0000 + 256) == m2.M2_ERR_ALIAS  # out overlaps z
     assert norm(out=FAKE + 64) == m2.M2_ERR_ALIAS                # out overlaps y without being y
     assert norm(y=FAKE + 8) == m2.M2_ERR_UNSUPPORTED             # misaligned
+
+
+def test_noalloc_scan_rejects_oversize_calls_before_any_launch():
+    """m2_ssd_scan_fwd_noalloc compares the workspace a call needs with its static buffer on the host and
+    returns M2_ERR_TOO_LARGE (nothing launched, no device touched) when it does not fit."""
+    lib = m2.lib()
+    d = dims(batch=1, seqlen=1 << 24)
+    assert m2.m2_ssd_scan_workspace(d) > m2.M2_STATIC_SCRATCH_BYTES
+    di = d.expand * d.d_model
+    st = lib.m2_ssd_scan_fwd_noalloc(ctypes.byref(d), FAKE, di, FAKE + 0x10000000, FAKE + 0x10000100, 64,
+                                     FAKE + 0x20000000, 80, FAKE + 0x30000000, FAKE + 0x30001000, None, 0.0,
+                                     float("inf"), None, None, FAKE + 0x4000_0000_00, di, None, None)
+    assert st == m2.M2_ERR_TOO_LARGE
+    # argument errors are still reported first
+    assert lib.m2_ssd_scan_fwd_noalloc(None, FAKE, di, FAKE, FAKE, 64, FAKE, 80, FAKE, FAKE, None, 0.0,
+                                       float("inf"), None, None, FAKE, di, None, None) == m2.M2_ERR_NULL
