@@ -86,7 +86,8 @@ typedef struct {
     int32_t d_state;     /* [mamba_d_state]  N */
     int32_t n_groups;    /* [mamba_ngroups]  G, must divide nheads */
     int32_t d_conv;      /* [mamba_d_conv]   W, 2..4 */
-    int32_t chunk_size;  /* [chunk_size]     0 = library choice; else 16, 32 or 64 */
+    int32_t chunk_size;  /* [chunk_size]     a hint: 16, 32 or 64 are used where built (64 not
+                          * for fp32); any other value, 0 included, means the library's choice */
     int32_t io;          /* m2_dtype of the activations */
 } m2_dims;
 

@@ -49,6 +49,14 @@ m2_status derive(const m2_dims* d, Derived& o) {
     return M2_OK;
 }
 
+// The chunk length the scan runs with: dims.chunk_size when the kernels are built for it at this
+// (headdim, d_state, dtype), else the library's choice.  Results do not depend on it beyond rounding,
+// so a model configuration's own value (Zamba2 uses 256) is taken as a hint.
+int scan_chunk(const Derived& d) {
+    if (d.Q > 0 && m2::ssd_scan_supported(d.P, d.N, d.Q, d.bf16)) return d.Q;
+    return m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
+}
+
 // Byte range of a [rows, row_elems] view with `stride` elements between rows.
 struct Range { uintptr_t lo, hi; };
 Range span(const void* p, int64_t rows, int64_t stride, int64_t row_elems, int esize) {
@@ -178,15 +186,13 @@ m2_status m2_conv1d_fwd_packed(const m2_dims* dims, int64_t total_tokens, const 
 size_t m2_ssd_scan_workspace(const m2_dims* dims) {
     Derived d;
     if (derive(dims, d) != M2_OK) return 0;
-    const int Q = d.Q ? d.Q : m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
-    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16, -1);
+    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, scan_chunk(d), d.bf16, -1);
 }
 
 size_t m2_ssd_scan_workspace_packed(const m2_dims* dims, int64_t total_tokens) {
     Derived d;
     if (derive(dims, d) != M2_OK || total_tokens < 0) return 0;
-    const int Q = d.Q ? d.Q : m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
-    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, Q, d.bf16, total_tokens);
+    return m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, scan_chunk(d), d.bf16, total_tokens);
 }
 
 }  // extern "C"
@@ -206,8 +212,7 @@ m2_status scan_run(const Derived& d, int64_t rows, const int32_t* cu, const void
                      y_tok_stride < d.d_inner))
         return M2_ERR_SHAPE;
     if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return M2_ERR_SHAPE;
-    const int Q = d.Q ? d.Q : m2::ssd_scan_default_chunk(d.P, d.N, d.bf16);
-    if (!(Q == 16 || Q == 32 || Q == 64)) return M2_ERR_UNSUPPORTED;
+    const int Q = scan_chunk(d);
     if (!m2::ssd_scan_supported(d.P, d.N, Q, d.bf16)) return M2_ERR_UNSUPPORTED;
     if (d.batch == 0) return M2_OK;
     const Range ry = span(y, rows, y_tok_stride, d.d_inner, d.esize);

@@ -166,7 +166,6 @@ def test_scan_validation():
     assert scan(dims(), dts=79) == m2.M2_ERR_SHAPE
     assert scan(dims(), dt_min=1.0, dt_max=0.5) == m2.M2_ERR_SHAPE
     assert scan(dims(), dt_min=float("nan")) == m2.M2_ERR_SHAPE
-    assert scan(dims(chunk_size=48)) == m2.M2_ERR_UNSUPPORTED
     assert scan(dims(d_state=24, d_model=2560)) == m2.M2_ERR_UNSUPPORTED
     assert scan(dims(), y=FAKE + 128) == m2.M2_ERR_ALIAS                       # y overlaps x
     assert scan(dims(), s_in=FAKE + 0x5_0000_0000, s_out=FAKE + 0x5_0000_0000) == m2.M2_ERR_ALIAS
@@ -175,6 +174,20 @@ def test_scan_validation():
     assert scan(dims(), C=FAKE + 0x10000100 + 2) == m2.M2_ERR_UNSUPPORTED       # misaligned C
     assert scan(dims(), bcs=5252) == m2.M2_ERR_UNSUPPORTED                      # B/C rows not 16-byte multiples
     assert scan(dims(), ys=5124) == m2.M2_ERR_UNSUPPORTED                       # y rows not 16-byte multiples
+
+
+def test_chunk_size_outside_the_built_set_is_a_hint():
+    """A chunk_size the kernels are not built for (Zamba2's configuration uses 256) means the library's
+    choice: the same workspace as chunk_size 0, and the call gets past the chunk check (here it stops at
+    the missing workspace, before any launch)."""
+    base = m2.m2_ssd_scan_workspace(dims(batch=1, seqlen=32768))
+    assert base > 0
+    for q in (48, 128, 256, 1 << 20):
+        assert m2.m2_ssd_scan_workspace(dims(batch=1, seqlen=32768, chunk_size=q)) == base
+        assert scan(dims(batch=1, seqlen=32768, chunk_size=q), ws=None) == m2.M2_ERR_WORKSPACE
+    # a built chunk length is honoured (a different plan, so a different workspace)
+    assert m2.m2_ssd_scan_workspace(dims(batch=1, seqlen=32768, chunk_size=64)) != base
+    assert scan(dims(chunk_size=-1)) == m2.M2_ERR_SHAPE
 
 
 def test_scan_workspace_required_when_reported():
