@@ -13,6 +13,8 @@
  *                    exists and the new sequence length is 1 (§三); it also
  *                    advances the cached conv state (§三: the cache holds each
  *                    layer's conv state and recurrent state)
+ *   m2_mixer_prefill_fwd  the conv and the scan of a prompt in one pass, without
+ *                    writing the conv output (§五: use_mem_eff_path)
  *   m2_gated_rmsnorm the gated group RMSNorm applied to the scan's output (§三)
  *
  * A batch of prompts of different lengths (the recurrent mask of §2.3) is given either
@@ -193,6 +195,39 @@ m2_status m2_ssd_scan_fwd_packed(const m2_dims* dims, int64_t total_tokens, cons
                                  void* y, int64_t y_tok_stride,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* Workspace bytes m2_mixer_prefill_fwd needs for these dims (0 when the fused path is not built for
+ * them: then it returns M2_ERR_UNSUPPORTED). */
+size_t m2_mixer_prefill_workspace(const m2_dims* dims);
+
+/* The prompt path in one pass: conv1d + SiLU of the raw conv input, then the scan, with the conv
+ * output never written to memory (article §五: use_mem_eff_path, the fused conv1d + scan path).
+ * Results are those of m2_conv1d_fwd followed by m2_ssd_scan_fwd on its x | B | C split, except that
+ * the x channels enter the state update at fp32 instead of rounded to the storage type:
+ *   y, state_out  as m2_ssd_scan_fwd;  ring_out as m2_conv1d_fwd (the last W raw tokens).
+ * xbc      [batch, seqlen, conv_dim] raw conv input (x | B | C), token stride xbc_tok_stride
+ * conv_w, conv_b, ring_in, ring_in_step, ring_out   as in m2_conv1d_fwd
+ * dt, dt_bias, A, D, dt_min, dt_max, state_in, state_out, y, seq_lens   as in m2_ssd_scan_fwd
+ * workspace device scratch of at least m2_mixer_prefill_workspace(dims) bytes, any alignment
+ *          (it holds the conv output of the B and C channels and the scan's segment records)
+ * Built for bf16 activations, headdim 64, d_state 64 (the Zamba2-2.7B mixer shape), nheads /
+ * n_groups a multiple of 4, chunk_size taken as a hint (32 tokens are used).  Other shapes, and dt
+ * views not on a 4-byte boundary or with an odd token stride, return M2_ERR_UNSUPPORTED: use the
+ * two entry points.  xbc and y as the scan's x and y (16-byte aligned rows); outputs must not
+ * overlap inputs, each other or the workspace. */
+m2_status m2_mixer_prefill_fwd(const m2_dims* dims,
+                               const void* xbc, int64_t xbc_tok_stride,
+                               const float* conv_w, const float* conv_b,
+                               const void* ring_in, int64_t ring_in_step,
+                               void* ring_out,
+                               const void* dt, int64_t dt_tok_stride,
+                               const float* dt_bias, const float* A, const float* D,
+                               float dt_min, float dt_max,
+                               const float* state_in, float* state_out,
+                               void* y, int64_t y_tok_stride,
+                               void* workspace, size_t workspace_bytes,
+                               const int32_t* seq_lens,
+                               void* stream);
 
 /* m2_ssd_scan_fwd without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The

@@ -9,8 +9,8 @@ library is missing, importing this package raises.
 
 Names and semantics follow the C ABI:
     m2_conv1d_fwd, m2_conv1d_fwd_packed, m2_ssd_scan_workspace, m2_ssd_scan_fwd,
-    m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_scan_fwd_noalloc, m2_ssd_step, m2_gated_rmsnorm,
-    m2_status_str, m2_abi_version, m2_last_hip_error
+    m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_scan_fwd_noalloc, m2_mixer_prefill_workspace,
+    m2_mixer_prefill_fwd, m2_ssd_step, m2_gated_rmsnorm, m2_status_str, m2_abi_version, m2_last_hip_error
 """
 from __future__ import annotations
 
@@ -29,8 +29,9 @@ M2_F32, M2_BF16 = 0, 1
 ABI_VERSION = 4
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
-           "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc", "m2_ssd_step",
-           "m2_gated_rmsnorm", "m2_status_str", "m2_abi_version", "m2_last_hip_error")
+           "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc",
+           "m2_mixer_prefill_workspace", "m2_mixer_prefill_fwd", "m2_ssd_step", "m2_gated_rmsnorm", "m2_status_str",
+           "m2_abi_version", "m2_last_hip_error")
 
 
 class M2Dims(ctypes.Structure):
@@ -89,6 +90,11 @@ def _load() -> ctypes.CDLL:
     lib.m2_ssd_scan_fwd_noalloc.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp, i64,
                                             vp, vp]
     lib.m2_ssd_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.m2_mixer_prefill_workspace.argtypes = [dp]
+    lib.m2_mixer_prefill_workspace.restype = sz
+    lib.m2_mixer_prefill_fwd.argtypes = [dp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp,
+                                         i64, vp, sz, vp, vp]
+    lib.m2_mixer_prefill_fwd.restype = ctypes.c_int
     lib.m2_ssd_step.argtypes = [dp, vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, f32, vp, i64, vp, vp, vp]
     lib.m2_ssd_step.restype = ctypes.c_int
     lib.m2_gated_rmsnorm.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp, i64, vp, f32,
@@ -303,6 +309,55 @@ def m2_ssd_scan_fwd_noalloc(dims: M2Dims, x, B, C, dt, dt_bias, A, D, y, state_i
     ins, outs = _scan_args(dims, x, B, C, dt, dt_bias, A, D, y, state_in, state_out)
     _call("m2_ssd_scan_fwd_noalloc", ctypes.byref(dims), *ins, float(dt_min), float(dt_max), *outs,
           _lens_ptr(seq_lens, dims), _stream(stream))
+
+
+def m2_mixer_prefill_workspace(dims: M2Dims) -> int:
+    return int(_lib.m2_mixer_prefill_workspace(ctypes.byref(dims)))
+
+
+def m2_mixer_prefill_fwd(dims: M2Dims, xbc, w, bias, dt, dt_bias, A, D, y, ring_in=None, ring_in_step: int = 0,
+                         ring_out=None, state_in=None, state_out=None, dt_min: float = 0.0,
+                         dt_max: float = float("inf"), workspace=None, stream=None, seq_lens=None) -> None:
+    """conv1d + SiLU and the scan of a prompt in one pass; see include/m2ssd.h.
+
+    xbc [B, L, conv_dim] raw conv input; w [conv_dim, W], bias [conv_dim] or None; ring_in / ring_out
+    [B, W, conv_dim] or None; dt [B, L, H]; dt_bias, A, D [H]; y [B, L, H*P]; state_in / state_out
+    [B, H, P, N] f32 or None; workspace: a uint8 GPU tensor of at least m2_mixer_prefill_workspace(dims)
+    bytes; seq_lens: int32 [B] GPU tensor or None."""
+    torch = _torch()
+    io = _io_dtype(dims)
+    H, P, N, Cd = dims.nheads, dims.headdim, dims.d_state, dims.conv_dim
+    for n, t in (("xbc", xbc), ("dt", dt), ("y", y), ("ring_in", ring_in), ("ring_out", ring_out)):
+        _check(t, n, io)
+    for n, t in (("w", w), ("bias", bias), ("dt_bias", dt_bias), ("A", A), ("D", D), ("state_in", state_in),
+                 ("state_out", state_out)):
+        _check(t, n, torch.float32)
+    if not w.is_contiguous() or tuple(w.shape) != (Cd, dims.d_conv):
+        raise ValueError("w must be contiguous [conv_dim, d_conv]")
+    if bias is not None and (not bias.is_contiguous() or bias.numel() != Cd):
+        raise ValueError("bias must be contiguous [conv_dim]")
+    for n, t in (("ring_in", ring_in), ("ring_out", ring_out)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, dims.d_conv, Cd)):
+            raise ValueError("%s must be contiguous [batch, d_conv, conv_dim]" % n)
+    for n, t in (("dt_bias", dt_bias), ("A", A), ("D", D)):
+        if t is not None and (not t.is_contiguous() or t.numel() != H):
+            raise ValueError("%s must be contiguous [nheads]" % n)
+    for n, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, H, P, N)):
+            raise ValueError("%s must be contiguous [batch, nheads, headdim, d_state]" % n)
+    xs = _tok_stride(xbc, "xbc", dims, Cd)
+    dts = _tok_stride(dt, "dt", dims, H)
+    ys = _tok_stride(y, "y", dims, H * P)
+    need = m2_mixer_prefill_workspace(dims)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    elif need > 0:
+        raise ValueError("m2_mixer_prefill_fwd needs a workspace of %d bytes" % need)
+    _call("m2_mixer_prefill_fwd", ctypes.byref(dims), _ptr(xbc), xs, _ptr(w), _ptr(bias), _ptr(ring_in),
+          int(ring_in_step), _ptr(ring_out), _ptr(dt), dts, _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min),
+          float(dt_max), _ptr(state_in), _ptr(state_out), _ptr(y), ys, ws_ptr, ws_bytes, _lens_ptr(seq_lens, dims),
+          _stream(stream))
 
 
 def _packed_stride(t, name, T, row: int) -> int:

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     const T* __restrict__ xbc, int64_t xs, int64_t L, int Cd,
     const float* __restrict__ w, const float* __restrict__ bias,
     const T* __restrict__ ring_in, int ring_phase,
-    T* __restrict__ ring_out, T* __restrict__ out, int64_t os, const int32_t* __restrict__ lens,
+    T* __restrict__ ring_out, int64_t rs, T* __restrict__ out, int64_t os, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ cu, int64_t total)
 {
     using R = typename Raw<T, VEC>::type;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
             load_vals<T, VEC>(xb + tau * xs, win[kk]);
         } else if (tau < 0 && ring_in) {
             const int slot = (int)(((ring_phase + tau) % W + W) % W);
-            load_vals<T, VEC>(ring_in + (b * W + slot) * (int64_t)Cd + c0, win[kk]);
+            load_vals<T, VEC>(ring_in + (b * W + slot) * rs + c0, win[kk]);
         } else {
 #pragma unroll
             for (int i = 0; i < VEC; ++i) win[kk][i] = 0.0f;  // no history, or never enters a sum
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     // the tile holding the last token writes the ring (phase 0: slot j = token Lb-W+j)
     if (ring_out && t_end == Lb) {
 #pragma unroll
-        for (int kk = 0; kk < W; ++kk) store_vals<T, VEC>(ring_out + (b * W + kk) * (int64_t)Cd + c0, win[kk]);
+        for (int kk = 0; kk < W; ++kk) store_vals<T, VEC>(ring_out + (b * W + kk) * rs + c0, win[kk]);
     }
 }
 
@@ -199,7 +199,7 @@ static hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
     dim3 grid((unsigned)((items + kConvThreads - 1) / kConvThreads), (unsigned)a.batch);
     return launch_kernel(conv1d_silu_kernel<T, VEC, W>, grid, dim3(kConvThreads), 0, s,
                          (const T*)a.xbc, a.xs, a.L, a.Cd, a.w, a.bias, (const T*)a.ring_in, a.ring_phase,
-                         (T*)a.ring_out, (T*)a.out, a.os, a.lens, a.cu, a.total);
+                         (T*)a.ring_out, a.rs, (T*)a.out, a.os, a.lens, a.cu, a.total);
 }
 
 template <typename T, int VEC>

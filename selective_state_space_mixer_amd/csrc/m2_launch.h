@@ -13,6 +13,7 @@ struct ConvArgs {
     const float* w; const float* bias;
     const void* ring_in; int ring_phase;
     void* ring_out;
+    int64_t rs;                       // elements between ring slots (conv_dim of the full ring)
     void* out; int64_t os;
     const int32_t* lens;  // [batch] valid tokens per sequence (device), or null
     const int32_t* cu;    // packed batch: [batch+1] first row of each sequence (device), or null
@@ -75,6 +76,16 @@ hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s);
 size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16,
                                 int64_t total);
 bool ssd_scan_supported(int P, int N, int Q, bool bf16);
+// The fused prompt path (conv1d + SiLU and the scan in one pass over the raw conv input): built for
+// bf16, headdim 64, d_state 64, head groups of a multiple of four heads, a dword-aligned dt view and
+// padded (not packed) batches.  The conv of the B and C channels runs first, into `act`
+// ([batch*seqlen, 2*G*N] bf16); the x channels are convolved inside the scan's main pass.  `c` holds
+// the conv of all channels (out unused), `a` the scan (x/B/C unused: the launcher points them).
+bool mixer_fusable(int P, int N, int H, int G, bool bf16);
+bool mixer_dt_fusable(const void* dt, int64_t dts);
+size_t mixer_act_bytes(int64_t batch, int64_t L, int G, int N);
+hipError_t launch_mixer_prefill(const ConvArgs& c, const ScanArgs& a, void* act, hipStream_t s);
+
 // The library's static scratch buffer on the current device (address looked up once per device)
 // and its size in bytes; for the entry point that must not allocate.
 hipError_t static_scratch(void** ptr, size_t* bytes);

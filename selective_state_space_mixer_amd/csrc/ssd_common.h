@@ -246,8 +246,22 @@ __device__ __forceinline__ int logical_block(int nblocks, int nx) {
     return x * per + (x < extra ? x : extra) + i / nx;
 }
 
+// The conv of the x channels when the main pass takes the raw conv input (the fused prompt path):
+// k.x then points at the raw xBC rows (x channels first), and k.B / k.C at the already convolved
+// B and C channels.
+struct WalkConv {
+    const float* w;       // [conv_dim, W] conv weights
+    const float* bias;    // [conv_dim], or null
+    const void* ring_in;  // [batch, W, rs] history (bf16) before each sequence's first token, or null
+    void* ring_out;       // [batch, W, rs]: receives the last W raw tokens of the x channels, or null
+    int64_t rs;           // elements between ring slots (conv_dim)
+    int W;                // conv width, 2..4
+    int phase;            // ring_in's phase: token -j sits in slot (phase - j) mod W
+};
+
 // The main pass at headdim 64, d_state 64, bf16, 32-token chunks (ssd_walk.hip): one wave per
-// head, four heads per block, the same workspace contract as the general main pass.
-hipError_t launch_ssd_walk(const ScanK& k, hipStream_t s);
+// head, four heads per block, the same workspace contract as the general main pass.  With a
+// WalkConv it convolves the raw x channels itself.
+hipError_t launch_ssd_walk(const ScanK& k, const WalkConv* conv, hipStream_t s);
 
 }  // namespace m2

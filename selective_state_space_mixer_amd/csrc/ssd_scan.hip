@@ -899,7 +899,7 @@ static Plan plan_of(int64_t batch, int64_t L, int H, int G, int64_t total) {
 constexpr bool kWalkKernel = M2_WALK_KERNEL != 0;
 
 template <typename T, int Q, int P, int N>
-static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
+static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* conv = nullptr) {
     using Cf = Cfg<T, Q, P, N>;
     const Plan pl = plan_of<T, Q, P, N>(a.batch, a.L, a.H, a.G, a.cu ? a.total : -1);
     ScanK k;
@@ -946,7 +946,8 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s) {
         // its blocks hold four heads of one group each, and it reads dt two heads per dword
         walk = (a.H / a.G) % 4 == 0 && ((uintptr_t)a.dt & 3u) == 0 && (a.dts & 1) == 0;
     }
-    if (walk) e = launch_ssd_walk(k, s);
+    if (conv && !walk) return hipErrorInvalidValue;  // the fused path needs the walk kernel
+    if (walk) e = launch_ssd_walk(k, conv, s);
     else e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
     if (e != hipSuccess || pl.nseg == 1) return e;
     // one extra block row lists the fix-up's work
@@ -1018,6 +1019,48 @@ hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s) {
         case 16: return dispatch_pn<float, 16>(a, s);
         default: return dispatch_pn<float, 32>(a, s);
     }
+}
+
+// ----------------------------------------------------------------------------------------------
+// the fused prompt path
+
+bool mixer_fusable(int P, int N, int H, int G, bool bf16) {
+    return kWalkKernel && bf16 && P == 64 && N == 64 && G > 0 && (H / G) % 4 == 0;
+}
+
+bool mixer_dt_fusable(const void* dt, int64_t dts) { return ((uintptr_t)dt & 3u) == 0 && (dts & 1) == 0; }
+
+size_t mixer_act_bytes(int64_t batch, int64_t L, int G, int N) {
+    return ((size_t)(batch * L * 2 * G * N) * sizeof(uint16_t) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_mixer_prefill(const ConvArgs& c, const ScanArgs& a, void* act, hipStream_t s) {
+    const int GN = a.G * a.N, Di = a.H * a.P;
+    // 1. conv + SiLU of the B and C channels into act (the scan's main pass reads them as tiles)
+    ConvArgs bc = c;
+    bc.xbc = c.xbc ? reinterpret_cast<const uint16_t*>(c.xbc) + Di : nullptr;
+    bc.Cd = 2 * GN;
+    bc.w = c.w + (int64_t)Di * c.W;
+    bc.bias = c.bias ? c.bias + Di : nullptr;
+    bc.ring_in = c.ring_in ? reinterpret_cast<const uint16_t*>(c.ring_in) + Di : nullptr;
+    bc.ring_out = c.ring_out ? reinterpret_cast<uint16_t*>(c.ring_out) + Di : nullptr;
+    bc.rs = c.Cd;
+    bc.out = c.xbc ? act : nullptr;
+    bc.os = 2 * GN;
+    bc.vec = c.vec && GN % 4 == 0 && Di % 8 == 0;
+    hipError_t e = launch_conv1d(bc, s);
+    if (e != hipSuccess) return e;
+    // 2. the scan, whose main pass convolves the x channels of the raw rows itself
+    ScanArgs sa = a;
+    sa.x = c.xbc;
+    sa.xs = c.xs;
+    sa.B = act;
+    sa.C = reinterpret_cast<uint16_t*>(act) + GN;
+    sa.bcs = 2 * GN;
+    WalkConv cv;
+    cv.w = c.w; cv.bias = c.bias; cv.ring_in = c.ring_in; cv.ring_out = c.ring_out;
+    cv.rs = c.Cd; cv.W = c.W; cv.phase = c.ring_phase;
+    return run_scan<bf16_t, 32, 64, 64>(sa, s, &cv);
 }
 
 }  // namespace m2

@@ -49,8 +49,9 @@ __device__ __forceinline__ uint2 lds_read8_tr(const uint8_t* base, int off) {
     return __builtin_bit_cast(uint2, v);
 }
 
+template <bool FUSED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, walk::THREADS), amdgpu_waves_per_eu(2)))
-ssd_walk_kernel(ScanK k)
+ssd_walk_kernel(ScanK k, WalkConv cv)
 {
     using namespace walk;
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[NBUF * BUFB];
@@ -58,6 +59,8 @@ ssd_walk_kernel(ScanK k)
     // gs = e^(Lam_e - Lam) dt with e the last token of the token's 16-block
     __shared__ __attribute__((aligned(16))) float sSt[2][HPB][NSTAT][Q];
     __shared__ uint64_t sBase[HPB][5];                                 // x, B, C, dt, y at the segment's first row
+    // fused: the last four raw x rows of the chunk before, per head, laid out as tile rows 28..31
+    __shared__ __attribute__((aligned(16))) uint8_t sHalo[FUSED ? HPB : 1][FUSED ? 4 * ROWB : 16];
 
     const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -122,6 +125,30 @@ ssd_walk_kernel(ScanK k)
     auto col_off = [&](int hf, int cb) __attribute__((always_inline)) {
         return (acol ^ (((2 * cb) ^ (4 * hf)) << 4)) + 2048 * hf;
     };
+
+    // ---- fused: this lane's conv taps and bias for its four x channels p = 16 pb + li of head h, taps
+    // right-aligned (tap 3 multiplies the current token; a narrower conv leaves the first taps zero).
+    // Transposing reads of raw rows 4g .. 4g+3 of column block cb sit at base(g) ^ (2 cb << 4); the
+    // lanes of q-group q read row groups q-1, q (tokens 4q-4 .. 4q+3) and q+3, q+4 (16+4q-4 .. 16+4q+3).
+    // Group -1 is the halo: the last raw rows of the chunk before, kept as rows 28..31 in sHalo.
+    float cw[4][4], cb4[4];
+    int offA = 0, offB = 0, offC = 0, offD = 0;
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            const int64_t c = (int64_t)h * P + 16 * pb + li;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) cw[pb][t] = t >= 4 - cv.W ? cv.w[c * cv.W + (t - (4 - cv.W))] : 0.0f;
+            cb4[pb] = cv.bias ? cv.bias[c] : 0.0f;
+        }
+        auto gbase = [&](int r) __attribute__((always_inline)) {
+            return r * ROWB + ((((li >> 1) & 1) ^ rowperm(r)) << 4) + 8 * (li & 1);
+        };
+        offA = gbase(q == 0 ? 28 + (li >> 2) : 4 * (q - 1) + (li >> 2));
+        offB = gbase(4 * q + (li >> 2));
+        offC = gbase(4 * (q + 3) + (li >> 2));
+        offD = gbase(4 * (q + 4) + (li >> 2));
+    }
 
     // ---- the state, in accumulator layout: accS[pb][nb] lane (q, li) = S[p = 16 pb + li][n = 16 nb + 4q + j]
     f32x4 accS[4][4];
@@ -220,6 +247,25 @@ ssd_walk_kernel(ScanK k)
     };
 
     float dec_n = 1.0f, lamend_n = 0.0f;
+    if constexpr (FUSED) {
+        // the raw x rows just before the segment (tokens row_begin-4 .. row_begin-1 of this head) into
+        // the halo, where chunk 0's conv looks for the chunk before; before the sequence they come from
+        // the conv history (or are zero)
+        if (nc > 0 && lane < 32) {
+            const int r = lane >> 3, u = lane & 7;
+            const int64_t tau = row_begin - 4 + r;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (tau >= 0) {
+                v = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(k.x) + (seq_row0(k, b) + tau) * k.xs +
+                                                    (int64_t)h * P + 8 * u);
+            } else if (cv.ring_in && tau >= -(int64_t)(cv.W - 1)) {
+                const int slot = (int)(((cv.phase + tau) % cv.W + cv.W) % cv.W);
+                v = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(cv.ring_in) +
+                                                    (b * cv.W + slot) * cv.rs + (int64_t)h * P + 8 * u);
+            }
+            *reinterpret_cast<uint4*>(&sHalo[w][r * ROWB + ((u ^ rowperm(28 + r)) << 4)]) = v;
+        }
+    }
     if (nc > 0) {
         rebase(0);
         stream(0, 0);
@@ -297,10 +343,56 @@ ssd_walk_kernel(ScanK k)
             }
         // X columns (k = token s): A operand of the intra part, and the source of w_s x_s
         Frag<bf16_t> xf[4];
+        Frag<bf16_t> xwh[4], xwl[4];  // w_s x_s as bf16 hi + lo (fused: from the fp32 conv output)
+        if constexpr (FUSED) {
+            // conv + SiLU of the raw x rows, straight into fragment order: lane (q, li) computes
+            // x[s][p = 16 pb + li] for s = 4q .. 4q+3 and 16+4q .. 16+4q+3
+            // group -1 reads the halo, addressed as rows 28..31
+            const uint8_t* const XA = q == 0 ? &sHalo[w][0] : Xt;
+            const int offA_ = q == 0 ? offA - 28 * ROWB : offA;
+            const float4 w0 = *reinterpret_cast<const float4*>(wh + 4 * q);
+            const float4 w1 = *reinterpret_cast<const float4*>(wh + 16 + 4 * q);
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const uint2 a = lds_read8_tr(Xt, col_off(0, pb)), c = lds_read8_tr(Xt, col_off(1, pb));
-            xf[pb].w[0] = a.x; xf[pb].w[1] = a.y; xf[pb].w[2] = c.x; xf[pb].w[3] = c.y;
+            for (int pb = 0; pb < 4; ++pb) {
+                const int m = (2 * pb) << 4;
+                const uint2 ra = lds_read8_tr(XA, offA_ ^ m), rb = lds_read8_tr(Xt, offB ^ m);
+                const uint2 rc = lds_read8_tr(Xt, offC ^ m), rd = lds_read8_tr(Xt, offD ^ m);
+                float v[2][8];  // raw rows 4g .. 4g+7 of the two halves
+                v[0][0] = lo_bf16(ra.x); v[0][1] = hi_bf16(ra.x); v[0][2] = lo_bf16(ra.y); v[0][3] = hi_bf16(ra.y);
+                v[0][4] = lo_bf16(rb.x); v[0][5] = hi_bf16(rb.x); v[0][6] = lo_bf16(rb.y); v[0][7] = hi_bf16(rb.y);
+                v[1][0] = lo_bf16(rc.x); v[1][1] = hi_bf16(rc.x); v[1][2] = lo_bf16(rc.y); v[1][3] = hi_bf16(rc.y);
+                v[1][4] = lo_bf16(rd.x); v[1][5] = hi_bf16(rd.x); v[1][6] = lo_bf16(rd.y); v[1][7] = hi_bf16(rd.y);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    float xo[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float a = cb4[pb];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) a = fmaf(cw[pb][t], v[c][j + 1 + t], a);
+                        xo[j] = silu(a);
+                    }
+                    xf[pb].set(c, xo[0], xo[1], xo[2], xo[3]);
+                    const float4 wv = c == 0 ? w0 : w1;
+                    const float p0 = xo[0] * wv.x, p1 = xo[1] * wv.y, p2 = xo[2] * wv.z, p3 = xo[3] * wv.w;
+                    xwh[pb].set(c, p0, p1, p2, p3);
+                    xwl[pb].set(c, p0 - xwh[pb].get(c, 0), p1 - xwh[pb].get(c, 1), p2 - xwh[pb].get(c, 2),
+                                p3 - xwh[pb].get(c, 3));
+                }
+            }
+            // this chunk's last four raw rows become the halo of the next (read before the output
+            // staging below overwrites this tile; LDS operations of one wave run in order)
+            if (lane < 32) {
+                const int o = (lane >> 3) * ROWB + 16 * (lane & 7);
+                const uint4 hv = *reinterpret_cast<const uint4*>(Xt + 28 * ROWB + o);
+                *reinterpret_cast<uint4*>(&sHalo[w][o]) = hv;
+            }
+        } else {
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const uint2 a = lds_read8_tr(Xt, col_off(0, pb)), c = lds_read8_tr(Xt, col_off(1, pb));
+                xf[pb].w[0] = a.x; xf[pb].w[1] = a.y; xf[pb].w[2] = c.x; xf[pb].w[3] = c.y;
+            }
         }
         // e^(Lam_t + sig) on the state part
 #pragma unroll
@@ -387,9 +479,8 @@ ssd_walk_kernel(ScanK k)
         }
         const float4 w0 = *reinterpret_cast<const float4*>(wh + 4 * q);
         const float4 w1 = *reinterpret_cast<const float4*>(wh + 16 + 4 * q);
-        Frag<bf16_t> xwh[4], xwl[4];
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
+        for (int pb = 0; pb < 4 && !FUSED; ++pb) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const float4 wv = c == 0 ? w0 : w1;
@@ -438,10 +529,30 @@ ssd_walk_kernel(ScanK k)
         k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
         if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
     }
+    if constexpr (FUSED) {
+        // the conv ring of the block's x channels: the last W raw tokens before the sequence's end,
+        // written by the block that holds its last chunk (the first segment's, for an empty sequence)
+        const bool last = nc > 0 ? c_stop == nchunks : (nchunks == 0 && seg == 0);
+        if (last && cv.ring_out) {
+            const int64_t c = (int64_t)h0 * P + threadIdx.x;  // 256 threads: the four heads' x channels
+            const bf16_t* X = reinterpret_cast<const bf16_t*>(k.x);
+            const bf16_t* R = reinterpret_cast<const bf16_t*>(cv.ring_in);
+            bf16_t* O = reinterpret_cast<bf16_t*>(cv.ring_out);
+            const int64_t row0 = seq_row0(k, b);
+            for (int j = 0; j < cv.W; ++j) {
+                const int64_t tau = Lb - cv.W + j;
+                bf16_t v{0};
+                if (tau >= 0) v = X[(row0 + tau) * k.xs + c];
+                else if (R) v = R[(b * cv.W + (((cv.phase + tau) % cv.W + cv.W) % cv.W)) * cv.rs + c];
+                O[(b * cv.W + j) * cv.rs + c] = v;
+            }
+        }
+    }
 }
 
-hipError_t launch_ssd_walk(const ScanK& k, hipStream_t s) {
-    return launch_kernel(ssd_walk_kernel, dim3(k.nblocks), dim3(walk::THREADS), 0, s, k);
+hipError_t launch_ssd_walk(const ScanK& k, const WalkConv* conv, hipStream_t s) {
+    if (conv) return launch_kernel(ssd_walk_kernel<true>, dim3(k.nblocks), dim3(walk::THREADS), 0, s, k, *conv);
+    return launch_kernel(ssd_walk_kernel<false>, dim3(k.nblocks), dim3(walk::THREADS), 0, s, k, WalkConv{});
 }
 
 }  // namespace m2

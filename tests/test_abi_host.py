@@ -245,3 +245,24 @@ def test_noalloc_scan_rejects_oversize_calls_before_any_launch():
     # argument errors are still reported first
     assert lib.m2_ssd_scan_fwd_noalloc(None, FAKE, di, FAKE, FAKE, 64, FAKE, 80, FAKE, FAKE, None, 0.0,
                                        float("inf"), None, None, FAKE, di, None, None) == m2.M2_ERR_NULL
+
+
+def test_fused_prefill_shapes_and_validation():
+    """The one-pass prompt path is built for bf16 headdim 64 / d_state 64; elsewhere it reports no
+    workspace and M2_ERR_UNSUPPORTED, before anything is launched."""
+    lib = m2.lib()
+    assert m2.m2_mixer_prefill_workspace(dims(batch=1, seqlen=32768)) > m2.m2_ssd_scan_workspace(dims(batch=1, seqlen=32768))
+    for bad in (dict(d_state=128), dict(headdim=32), dict(io=m2.M2_F32), dict(n_groups=40)):
+        assert m2.m2_mixer_prefill_workspace(dims(**bad)) == 0, bad
+
+    def call(d, xbc=FAKE, dt=FAKE + 0x2000_0000_0, y=FAKE + 0x4000_0000_00, ws=None, wsb=0, dts=None):
+        return lib.m2_mixer_prefill_fwd(ctypes.byref(d), xbc, d.conv_dim, FAKE + 0x1000_0000_0, None, None, 0, None,
+                                        dt, dts or d.expand * d.d_model // d.headdim, FAKE + 0x3000_0000_0,
+                                        FAKE + 0x3000_1000_0, None, 0.0, float("inf"), None, None, y,
+                                        d.expand * d.d_model, ws, wsb, None, None)
+    assert call(dims(d_state=128)) == m2.M2_ERR_UNSUPPORTED
+    assert call(dims(), xbc=None) == m2.M2_ERR_NULL
+    assert call(dims(), dt=FAKE + 0x2000_0000_2) == m2.M2_ERR_UNSUPPORTED     # dt not on a dword
+    assert call(dims(), dts=81) == m2.M2_ERR_UNSUPPORTED                       # odd dt token stride
+    assert call(dims(), y=FAKE + 64) == m2.M2_ERR_ALIAS                         # y overlaps xbc
+    assert call(dims(batch=1, seqlen=32768)) == m2.M2_ERR_WORKSPACE
