@@ -292,6 +292,12 @@ m2_status m2_gated_rmsnorm(int64_t ntok, int32_t d_inner, int32_t group_size, in
                            void* out, int64_t out_tok_stride,
                            void* stream);
 
+/* A plain device-to-device copy of `bytes` (a multiple of 16; dst and src 16-byte aligned and not
+ * overlapping): not part of the mixer, but the attainable read + write bandwidth of the device,
+ * measured with a streaming kernel of this library, which the benchmark reports beside the HBM
+ * peak as the reference for the kernels' bandwidth fractions. */
+m2_status m2_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* Static text for a status code. */
 const char* m2_status_str(m2_status status);
 

@@ -10,7 +10,8 @@ library is missing, importing this package raises.
 Names and semantics follow the C ABI:
     m2_conv1d_fwd, m2_conv1d_fwd_packed, m2_ssd_scan_workspace, m2_ssd_scan_fwd,
     m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_scan_fwd_noalloc, m2_mixer_prefill_workspace,
-    m2_mixer_prefill_fwd, m2_ssd_step, m2_gated_rmsnorm, m2_status_str, m2_abi_version, m2_last_hip_error
+    m2_mixer_prefill_fwd, m2_ssd_step, m2_gated_rmsnorm, m2_stream_copy, m2_status_str, m2_abi_version,
+    m2_last_hip_error
 """
 from __future__ import annotations
 
@@ -30,8 +31,8 @@ ABI_VERSION = 4
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
            "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc",
-           "m2_mixer_prefill_workspace", "m2_mixer_prefill_fwd", "m2_ssd_step", "m2_gated_rmsnorm", "m2_status_str",
-           "m2_abi_version", "m2_last_hip_error")
+           "m2_mixer_prefill_workspace", "m2_mixer_prefill_fwd", "m2_ssd_step", "m2_gated_rmsnorm", "m2_stream_copy",
+           "m2_status_str", "m2_abi_version", "m2_last_hip_error")
 
 
 class M2Dims(ctypes.Structure):
@@ -100,6 +101,8 @@ def _load() -> ctypes.CDLL:
     lib.m2_gated_rmsnorm.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp, i64, vp, f32,
                                      ctypes.c_int32, vp, i64, vp]
     lib.m2_gated_rmsnorm.restype = ctypes.c_int
+    lib.m2_stream_copy.argtypes = [vp, vp, sz, vp]
+    lib.m2_stream_copy.restype = ctypes.c_int
     lib.m2_status_str.argtypes = [ctypes.c_int]
     lib.m2_status_str.restype = ctypes.c_char_p
     lib.m2_abi_version.argtypes = []
@@ -529,3 +532,14 @@ def m2_gated_rmsnorm(y, z, w, out, group_size: int, eps: float = 1e-5, norm_befo
     _call("m2_gated_rmsnorm", int(ntok), int(D), int(group_size), M2_BF16 if io == torch.bfloat16 else M2_F32,
           _ptr(y), ys, _ptr(z), zs, _ptr(w), float(eps), int(bool(norm_before_gate)), _ptr(out), os_,
           _stream(stream))
+
+
+def m2_stream_copy(dst, src, stream=None) -> None:
+    """Copy src into dst (same byte size, 16-byte aligned GPU tensors) with the library's streaming copy
+    kernel; see include/m2ssd.h."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not dst.is_cuda or not src.is_cuda:
+        raise ValueError("dst and src must be GPU tensors of the same byte size")
+    if not dst.is_contiguous() or not src.is_contiguous():
+        raise ValueError("dst and src must be contiguous")
+    _call("m2_stream_copy", _ptr(dst), _ptr(src), n, _stream(stream))

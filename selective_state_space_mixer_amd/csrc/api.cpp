@@ -402,6 +402,15 @@ m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stri
     return launched(m2::launch_ssd_step(a, (hipStream_t)stream));
 }
 
+m2_status m2_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (bytes == 0) return M2_OK;
+    if (!dst || !src) return M2_ERR_NULL;
+    if (bytes % 16 || !aligned16(dst) || !aligned16(src)) return M2_ERR_UNSUPPORTED;
+    if (overlap(Range{(uintptr_t)dst, (uintptr_t)dst + bytes}, Range{(uintptr_t)src, (uintptr_t)src + bytes}))
+        return M2_ERR_ALIAS;
+    return launched(m2::launch_stream_copy(dst, src, bytes, (hipStream_t)stream));
+}
+
 m2_status m2_gated_rmsnorm(int64_t ntok, int32_t d_inner, int32_t group_size, int32_t io, const void* y,
                            int64_t y_tok_stride, const void* z, int64_t z_tok_stride, const float* w, float eps,
                            int32_t norm_before_gate, void* out, int64_t out_tok_stride, void* stream) {

@@ -31,6 +31,16 @@ template <> struct Vec<float, 4> {
     __device__ __forceinline__ float get(int i) const { return (&raw.x)[i]; }
     __device__ __forceinline__ void set2(int i, float lo, float hi) { (&raw.x)[i] = lo; (&raw.x)[i + 1] = hi; }
 };
+template <> struct Vec<bf16_t, 4> {
+    uint2 raw;
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t wd = (&raw.x)[i >> 1];
+        return __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
+    }
+    __device__ __forceinline__ void set2(int i, float lo, float hi) {
+        (&raw.x)[i >> 1] = pack_bf16x2(lo, hi);
+    }
+};
 template <typename T> struct Vec<T, 1> {
     T raw;
     __device__ __forceinline__ float get(int) const { return to_f32(raw); }
@@ -62,12 +72,20 @@ __device__ __forceinline__ void load_vals(const T* p, float (&o)[VEC]) {
     for (int i = 0; i < VEC; ++i) o[i] = v.get(i);
 }
 
-constexpr int kConvTileTokens = 64;  // tokens per lane
-constexpr int kConvGroup = 8;        // tokens per load group (one group in flight while the previous computes)
+#ifndef M2_CONV_TILE
+#define M2_CONV_TILE 64
+#endif
+#ifndef M2_CONV_GROUP
+#define M2_CONV_GROUP 8
+#endif
+constexpr int kConvTileTokens = M2_CONV_TILE;  // tokens per lane
+constexpr int kConvGroup = M2_CONV_GROUP;      // tokens per load group (one group in flight while the previous computes)
 constexpr int kConvThreads = 256;
 
 template <typename T, int VEC> struct Raw;
 template <> struct Raw<bf16_t, 8> { using type = u32x4; };
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+template <> struct Raw<bf16_t, 4> { using type = u32x2v; };
 template <> struct Raw<float, 4> { using type = u32x4; };
 template <typename T> struct Raw<T, 1> { using type = T; };
 
@@ -89,9 +107,13 @@ __device__ __forceinline__ void unpack(const typename Raw<T, VEC>::type& r, floa
 
 // Lane <-> (token tile, channel group): the channel group runs fastest, so a wave covers 64
 // adjacent 16-byte channel groups of one token row (a contiguous 1 KiB) and every lane has work
-// whatever conv_dim is.  Each lane walks kConvTileTokens tokens of its VEC channels.
-template <typename T, int VEC, int W>
-__global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
+// whatever conv_dim is.  Each lane walks TILE tokens of its VEC channels.
+#ifndef M2_CONV_WPE
+#define M2_CONV_WPE 1
+#endif
+template <typename T, int VEC, int W, int TILE>
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, kConvThreads), amdgpu_waves_per_eu(M2_CONV_WPE)))
+conv1d_silu_kernel(
     const T* __restrict__ xbc, int64_t xs, int64_t L, int Cd,
     const float* __restrict__ w, const float* __restrict__ bias,
     const T* __restrict__ ring_in, int ring_phase,
@@ -100,11 +122,11 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
 {
     using R = typename Raw<T, VEC>::type;
     const int CG = Cd / VEC;
-    const int64_t ntiles = L > 0 ? (L + kConvTileTokens - 1) / kConvTileTokens : 1;
+    const int64_t ntiles = L > 0 ? (L + TILE - 1) / TILE : 1;
     const int64_t item = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
     if (item >= ntiles * CG) return;
     const int c0 = (int)(item % CG) * VEC;
-    const int64_t t0 = (item / CG) * kConvTileTokens;
+    const int64_t t0 = (item / CG) * TILE;
     const int64_t b = blockIdx.y;
     // Sequence b starts at row b*L, or at cu[b] in a packed batch, and ends at its own length
     // (clamped to the rows that exist and to L).  The tile that starts at token 0 always runs, so
@@ -147,7 +169,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
         }
     }
 
-    const int64_t t_end = t0 + kConvTileTokens < Lb ? t0 + kConvTileTokens : Lb;
+    const int64_t t_end = t0 + TILE < Lb ? t0 + TILE : Lb;
     const int n = (int)(t_end - t0);
     R cur[kConvGroup], nxt[kConvGroup];
     auto load_group = [&](R (&dst)[kConvGroup], int base) __attribute__((always_inline)) {
@@ -178,7 +200,18 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
                     for (int kk = 0; kk < W; ++kk) v = fmaf(wr[i][kk], win[kk][i], v);
                     o[i] = silu(v);
                 }
+#if M2_CONV_NTSTORE
+                if constexpr (VEC == 8 || (VEC == 4 && sizeof(T) == 4)) {
+                    Vec<T, VEC> sv;
+#pragma unroll
+                    for (int i = 0; i < VEC; i += 2) sv.set2(i, o[i], o[i + 1]);
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sv.raw), reinterpret_cast<u32x4*>(ob + (t0 + base + u) * os));
+                } else {
+                    store_vals<T, VEC>(ob + (t0 + base + u) * os, o);
+                }
+#else
                 store_vals<T, VEC>(ob + (t0 + base + u) * os, o);
+#endif
             }
         }
 #pragma unroll
@@ -192,14 +225,23 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_silu_kernel(
     }
 }
 
-template <typename T, int VEC, int W>
-static hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
-    const int64_t tiles = a.L > 0 ? (a.L + kConvTileTokens - 1) / kConvTileTokens : 1;
+// Tokens per lane: kConvTileTokens, or fewer where the channels are too few for the grid to fill the
+// chip (the B and C channels alone, in the fused prompt path): about 2048 blocks at least.
+template <typename T, int VEC, int W, int TILE>
+static hipError_t launch_conv_t(const ConvArgs& a, hipStream_t s) {
+    const int64_t tiles = a.L > 0 ? (a.L + TILE - 1) / TILE : 1;
     const int64_t items = tiles * (a.Cd / VEC);
     dim3 grid((unsigned)((items + kConvThreads - 1) / kConvThreads), (unsigned)a.batch);
-    return launch_kernel(conv1d_silu_kernel<T, VEC, W>, grid, dim3(kConvThreads), 0, s,
+    return launch_kernel(conv1d_silu_kernel<T, VEC, W, TILE>, grid, dim3(kConvThreads), 0, s,
                          (const T*)a.xbc, a.xs, a.L, a.Cd, a.w, a.bias, (const T*)a.ring_in, a.ring_phase,
                          (T*)a.ring_out, a.rs, (T*)a.out, a.os, a.lens, a.cu, a.total);
+}
+
+template <typename T, int VEC, int W>
+static hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
+    const int64_t groups = (int64_t)(a.Cd / VEC) * a.batch * (a.L > 0 ? a.L : 1);  // lanes at one token per lane
+    if (groups / kConvTileTokens >= 2048 * (int64_t)kConvThreads) return launch_conv_t<T, VEC, W, kConvTileTokens>(a, s);
+    return launch_conv_t<T, VEC, W, 8>(a, s);
 }
 
 template <typename T, int VEC>
@@ -211,8 +253,11 @@ static hipError_t launch_conv_w(const ConvArgs& a, hipStream_t s) {
     }
 }
 
+#ifndef M2_CONV_VEC
+#define M2_CONV_VEC 4
+#endif
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s) {
-    if (a.bf16) return a.vec ? launch_conv_w<bf16_t, 8>(a, s) : launch_conv_w<bf16_t, 1>(a, s);
+    if (a.bf16) return a.vec ? launch_conv_w<bf16_t, M2_CONV_VEC>(a, s) : launch_conv_w<bf16_t, 1>(a, s);
     return a.vec ? launch_conv_w<float, 4>(a, s) : launch_conv_w<float, 1>(a, s);
 }
 

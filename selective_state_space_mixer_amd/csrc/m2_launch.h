@@ -86,6 +86,9 @@ bool mixer_dt_fusable(const void* dt, int64_t dts);
 size_t mixer_act_bytes(int64_t batch, int64_t L, int G, int N);
 hipError_t launch_mixer_prefill(const ConvArgs& c, const ScanArgs& a, void* act, hipStream_t s);
 
+// A plain copy of `bytes` (a multiple of 16, both pointers 16-byte aligned): the bandwidth reference.
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
 // The library's static scratch buffer on the current device (address looked up once per device)
 // and its size in bytes; for the entry point that must not allocate.
 hipError_t static_scratch(void** ptr, size_t* bytes);
