@@ -199,6 +199,8 @@ struct ScanK {
     uint2* fix_items;  // the fix-up's work list: (later segment - 1) * batch*H + sequence*H + head, chunk
     int* fix_count;    // its length
     uint16_t* ws_tin;  // bf16 outputs: [nseg-1][batch*H][P*N] bf16 initial states of segments 1.. (else null)
+    float* ws_emax;    // [nseg][batch*H]: max |E[seg]|, the segment's end state from its own start
+    unsigned* ws_tmax; // [nseg][batch*H]: max |T[seg]| (float bits, maxed atomically by the chain kernel)
     const int32_t* lens;  // [batch] tokens of each right-padded sequence, or null (all L)
     const int32_t* cu;    // packed batch: [batch+1] first row of each sequence, or null
     int64_t total;        // packed batch: rows of the packed arrays
@@ -230,10 +232,23 @@ __device__ __forceinline__ int64_t seq_len(const ScanK& k, int64_t b) {
 }
 
 // A later segment starts from zero in the main pass; the part of its output that comes from its true
-// initial state decays with the segment's summed log-decay and is added afterwards only where that
-// factor is at least e^cut (the term dropped beyond it is far under the output's rounding: e^-12 is
-// 6e-6 of |S_in . C_t| against bf16's 2^-9; e^-20.8 is 1e-9 for fp32 outputs).
+// initial state T decays with the segment's summed log-decay Lam and is added afterwards (the fix-up)
+// to each chunk j whose starting factor still matters against the segment's own state:
+//     e^Lam_before(j) * max|T|  >=  e^cut * max|E|,   E = the segment's end state from zero.
+// The term left out beyond that is below e^cut of the segment's own state scale: e^-12 (6e-6, far
+// under bf16's 2^-9) for bf16 outputs, e^-20.8 (1e-9) for fp32 outputs.  The main pass lists the
+// chunks with Lam_before >= cut - kFixMargin; the fix-up applies the exact test to each, so the test
+// holds whenever max|T| <= e^kFixMargin max|E| (beyond that, listed chunks are fixed and later
+// ones left out).
 template <typename T> constexpr float fix_cut() { return sizeof(T) == 2 ? -12.0f : -20.8f; }
+constexpr float kFixMargin = 30.0f;
+
+// max over the 64 lanes of a wave
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
 
 // Block -> logical unit.  Consecutive blocks are dealt round-robin to the device's nx XCDs; the
 // remap gives each XCD a contiguous run of logical units (the head groups of one sequence and

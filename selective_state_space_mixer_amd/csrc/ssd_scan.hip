@@ -338,7 +338,7 @@ ssd_chunk_scan_kernel(ScanK k)
         sig = rescale ? 0.0f : sig_prev + lam_end;
         const float lam_before = lam_seg;  // summed log-decay of the segment before chunk i
         lam_seg += lam_end;
-        nfix += lam_before >= fix_cut<T>() ? 1 : 0;
+        nfix += lam_before >= fix_cut<T>() - kFixMargin ? 1 : 0;
         if (lane < Q) {
             float* st = &sSt[buf][hw * Q + lane];
             st[0 * QS] = lam * kLog2e;
@@ -578,6 +578,7 @@ ssd_chunk_scan_kernel(ScanK k)
     float* dst = nullptr;
     if (k.nseg > 1) dst = k.ws_state + ((int64_t)seg * BH + bh) * P * N;
     else dst = k.state_out ? k.state_out + (int64_t)bh * P * N : nullptr;
+    float emax = 0.0f;  // max |state entry| of this wave's share
     if (dst && hvalid) {
 #pragma unroll
         for (int pw = 0; pw < PW; ++pw) {
@@ -587,12 +588,24 @@ ssd_chunk_scan_kernel(ScanK k)
                 const f32x4 v = accS[pw][nb] * escale;
                 *reinterpret_cast<float4*>(dst + (int64_t)p * N + nb * 16 + 4 * q) =
                     make_float4(v[0], v[1], v[2], v[3]);
+                emax = fmaxf(emax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
             }
         }
     }
-    if (k.nseg > 1 && hvalid && stats_writer && lane == 0) {
-        k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
-        if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
+    if (k.nseg > 1) {
+        // the segment's state scale for the fix-up test: max over the head's waves
+        __shared__ float sEmax[Cf::WAVES];
+        emax = wave_max(emax);
+        if (lane == 0) sEmax[wave] = emax;
+        __syncthreads();
+        if (hvalid && stats_writer && lane == 0) {
+            float m = 0.0f;
+            for (int j = hw; j < Cf::WAVES; j += HPW) m = fmaxf(m, sEmax[j]);
+            k.ws_emax[(int64_t)seg * BH + bh] = m;
+            k.ws_tmax[(int64_t)seg * BH + bh] = 0u;
+            k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+            if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
+        }
     }
 }
 
@@ -642,7 +655,8 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
                                                                 float* __restrict__ state_out, int BH, int nseg,
                                                                 int PN, const int* __restrict__ nfix,
                                                                 uint2* __restrict__ items, int* __restrict__ count,
-                                                                uint16_t* __restrict__ tin)
+                                                                uint16_t* __restrict__ tin,
+                                                                unsigned* __restrict__ tmax)
 {
     constexpr int kBatch = 16;
     const int bh = blockIdx.y;
@@ -651,8 +665,10 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
         return;
     }
     // four consecutive state entries per thread (PN is a multiple of 16)
+    // threads past the state's end take part in the wave maxima with zero (the waves stay whole)
     const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= PN) return;
+    const bool in = i < PN;
+    const int ic = in ? i : 0;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int seg0 = 0; seg0 < nseg; seg0 += kBatch) {
         float4 loc[kBatch];
@@ -660,7 +676,7 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int seg = seg0 + j < nseg ? seg0 + j : nseg - 1;
-            loc[j] = *reinterpret_cast<const float4*>(ws_state + ((int64_t)seg * BH + bh) * PN + i);
+            loc[j] = *reinterpret_cast<const float4*>(ws_state + ((int64_t)seg * BH + bh) * PN + ic);
             dec[j] = ws_lam[(int64_t)seg * BH + bh];
         }
 #pragma unroll
@@ -673,9 +689,15 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
                 if (seg < nseg - 1) {
                     // the initial state of segment seg+1, for the fix-up: in bf16 when that is the
                     // precision it enters the fix-up's product in
-                    if (tin) *reinterpret_cast<uint2*>(tin + o) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
-                    else *reinterpret_cast<float4*>(ws_state + o) = s;
-                } else if (state_out) {
+                    if (in) {
+                        if (tin) *reinterpret_cast<uint2*>(tin + o) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+                        else *reinterpret_cast<float4*>(ws_state + o) = s;
+                    }
+                    // and its largest entry (non-negative floats order like their bit patterns)
+                    float m = in ? fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w))) : 0.0f;
+                    m = wave_max(m);
+                    if ((threadIdx.x & 63) == 0) atomicMax(&tmax[(int64_t)seg * BH + bh], __float_as_uint(m));
+                } else if (state_out && in) {
                     *reinterpret_cast<float4*>(state_out + (int64_t)bh * PN + i) = s;
                 }
             }
@@ -738,6 +760,16 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
         const int64_t b = bh / k.H;
         const int h = bh % k.H, g = h / (k.H / k.G);
         const int64_t c = (int64_t)seg * k.cps + j;
+        // the chunk needs the term while e^Lam_before max|T| >= e^cut max|E| (logs in nats; a zero T
+        // needs nothing, a zero E needs everything, NaN keeps the chunk)
+        {
+            const float tm = __uint_as_float(k.ws_tmax[(int64_t)(seg - 1) * BH + bh]);
+            const float em = k.ws_emax[(int64_t)seg * BH + bh];
+            const float lb = k.ws_lamc[c * BH + bh];
+            constexpr float kLn2 = 0.6931471805599453f;
+            if (tm == 0.0f || lb + kLn2 * __builtin_amdgcn_logf(tm) < fix_cut<T>() + kLn2 * __builtin_amdgcn_logf(em))
+                continue;
+        }
         const int64_t t0 = c * Q;
         const int64_t left = seq_len(k, b) - t0;
         const int valid = (int)(left < Q ? left : Q);  // >= 1: listed chunks lie inside the sequence
@@ -839,13 +871,15 @@ struct Plan {
 // list [(nseg-1)*B*H*cps] (pair, chunk), and for bf16 outputs the segments' initial states in bf16
 // [nseg-1][B*H][P*N].
 struct WsLayout {
-    size_t lam, lamc, nfix, count, items, tin, total;
+    size_t lam, emax, tmax, lamc, nfix, count, items, tin, total;
 };
 static WsLayout ws_layout(int64_t nseg, int64_t BH, int64_t PN, int64_t nchunks, int64_t cps, bool bf16) {
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     WsLayout w;
     w.lam = up((size_t)(nseg * BH * PN) * sizeof(float));
-    w.lamc = up(w.lam + (size_t)(nseg * BH) * sizeof(float));
+    w.emax = up(w.lam + (size_t)(nseg * BH) * sizeof(float));
+    w.tmax = up(w.emax + (size_t)(nseg * BH) * sizeof(float));
+    w.lamc = up(w.tmax + (size_t)(nseg * BH) * sizeof(unsigned));
     w.nfix = up(w.lamc + (size_t)(nchunks * BH) * sizeof(float));
     w.count = up(w.nfix + (size_t)((nseg - 1) * BH) * sizeof(int));
     w.items = up(w.count + sizeof(int));
@@ -924,11 +958,15 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     k.fix_items = nullptr;
     k.fix_count = nullptr;
     k.ws_tin = nullptr;
+    k.ws_emax = nullptr;
+    k.ws_tmax = nullptr;
     if (pl.nseg > 1) {
         const WsLayout w = ws_layout(pl.nseg, BH, P * N, (a.L + Q - 1) / Q, pl.cps, sizeof(T) == 2);
         uint8_t* base = reinterpret_cast<uint8_t*>(((uintptr_t)a.ws + 255) & ~(uintptr_t)255);
         k.ws_state = reinterpret_cast<float*>(base);
         k.ws_lam = reinterpret_cast<float*>(base + w.lam);
+        k.ws_emax = reinterpret_cast<float*>(base + w.emax);
+        k.ws_tmax = reinterpret_cast<unsigned*>(base + w.tmax);
         k.ws_lamc = reinterpret_cast<float*>(base + w.lamc);
         k.ws_nfix = reinterpret_cast<int*>(base + w.nfix);
         k.fix_count = reinterpret_cast<int*>(base + w.count);
@@ -953,7 +991,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     // one extra block row lists the fix-up's work
     dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH + 1);
     e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k.ws_state, (const float*)k.ws_lam, a.state_out,
-                      BH, pl.nseg, P * N, (const int*)k.ws_nfix, k.fix_items, k.fix_count, k.ws_tin);
+                      BH, pl.nseg, P * N, (const int*)k.ws_nfix, k.fix_items, k.fix_count, k.ws_tin, k.ws_tmax);
     if (e != hipSuccess) return e;
     return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3(kFixBlocks), dim3(kFixThreads), 0, s, k);
 }

@@ -232,7 +232,7 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
         sig = rescale ? 0.0f : sig_prev + lam_end;
         const float lam_before = lam_seg;
         lam_seg += lam_end;
-        nfix += lam_before >= fix_cut<bf16_t>() ? 1 : 0;
+        nfix += lam_before >= fix_cut<bf16_t>() - kFixMargin ? 1 : 0;
         if (lane < Q) {
             float* st = &sSt[sbuf][w][0][lane];
             st[0 * Q] = lam * kLog2e;
@@ -515,6 +515,7 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
     float* dst = nullptr;
     if (k.nseg > 1) dst = k.ws_state + ((int64_t)seg * BH + bh) * P * N;
     else dst = k.state_out ? k.state_out + (int64_t)bh * P * N : nullptr;
+    float emax = 0.0f;  // max |state entry|: the segment's state scale for the fix-up test
     if (dst && hvalid) {
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb)
@@ -523,11 +524,17 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 const f32x4 v = accS[pb][nb] * escale;
                 *reinterpret_cast<float4*>(dst + (int64_t)(16 * pb + li) * N + 16 * nb + 4 * q) =
                     make_float4(v[0], v[1], v[2], v[3]);
+                emax = fmaxf(emax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
             }
     }
-    if (k.nseg > 1 && hvalid && lane == 0) {
-        k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
-        if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
+    if (k.nseg > 1) {
+        emax = wave_max(emax);
+        if (hvalid && lane == 0) {
+            k.ws_emax[(int64_t)seg * BH + bh] = emax;
+            k.ws_tmax[(int64_t)seg * BH + bh] = 0u;
+            k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
+            if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
+        }
     }
     if constexpr (FUSED) {
         // the conv ring of the block's x channels: the last W raw tokens before the sequence's end,
