@@ -195,12 +195,9 @@ struct ScanK {
     float* ws_state;   // [nseg][batch*H][P*N]: segment end states (fp32 outputs: then initial states)
     float* ws_lam;     // [nseg][batch*H]: summed log-decay of each segment
     float* ws_lamc;    // [nchunks][batch*H]: summed log-decay of the chunk's segment before the chunk
-    int* ws_nfix;      // [nseg-1][batch*H]: leading chunks of each later segment that need the fix-up
-    uint2* fix_items;  // the fix-up's work list: (later segment - 1) * batch*H + sequence*H + head, chunk
-    int* fix_count;    // its length
     uint16_t* ws_tin;  // bf16 outputs: [nseg-1][batch*H][P*N] bf16 initial states of segments 1.. (else null)
     float* ws_emax;    // [nseg][batch*H]: max |E[seg]|, the segment's end state from its own start
-    unsigned* ws_tmax; // [nseg][batch*H]: max |T[seg]| (float bits, maxed atomically by the chain kernel)
+    float* ws_tb;      // [nseg][batch*H]: a bound on max |T[seg]|, the true end state (chain kernel)
     const int32_t* lens;  // [batch] tokens of each right-padded sequence, or null (all L)
     const int32_t* cu;    // packed batch: [batch+1] first row of each sequence, or null
     int64_t total;        // packed batch: rows of the packed arrays
@@ -236,12 +233,11 @@ __device__ __forceinline__ int64_t seq_len(const ScanK& k, int64_t b) {
 // to each chunk j whose starting factor still matters against the segment's own state:
 //     e^Lam_before(j) * max|T|  >=  e^cut * max|E|,   E = the segment's end state from zero.
 // The term left out beyond that is below e^cut of the segment's own state scale: e^-12 (6e-6, far
-// under bf16's 2^-9) for bf16 outputs, e^-20.8 (1e-9) for fp32 outputs.  The main pass lists the
-// chunks with Lam_before >= cut - kFixMargin; the fix-up applies the exact test to each, so the test
-// holds whenever max|T| <= e^kFixMargin max|E| (beyond that, listed chunks are fixed and later
-// ones left out).
+// under bf16's 2^-9) for bf16 outputs, e^-20.8 (1e-9) for fp32 outputs.  The main pass records
+// Lam_before of every chunk and max|E| of every segment; the chain kernel bounds max|T| by the chain
+// of maxima Tb[seg] = e^lam[seg] Tb[seg-1] + max|E[seg]|, and the fix-up applies the test with Tb,
+// which keeps every chunk the rule asks for (adding the exact term to a chunk is never wrong).
 template <typename T> constexpr float fix_cut() { return sizeof(T) == 2 ? -12.0f : -20.8f; }
-constexpr float kFixMargin = 30.0f;
 
 // max over the 64 lanes of a wave
 __device__ __forceinline__ float wave_max(float v) {

@@ -317,7 +317,6 @@ ssd_chunk_scan_kernel(ScanK k)
     // tracks sig (and the segment's summed log-decay) as it prepares the chunks in order.
     constexpr float kRescale = 40.0f;
     float sig = 0.0f, lam_seg = 0.0f;
-    int nfix = 0;  // chunks of this segment whose starting decay factor is at least e^cut
     // dt and the cumulative log-decay of this wave's head over chunk i, into statistics buffer buf
     auto stats = [&](int i, int buf, uint32_t raw) __attribute__((always_inline)) {
         if (!stats_writer) return;
@@ -338,7 +337,6 @@ ssd_chunk_scan_kernel(ScanK k)
         sig = rescale ? 0.0f : sig_prev + lam_end;
         const float lam_before = lam_seg;  // summed log-decay of the segment before chunk i
         lam_seg += lam_end;
-        nfix += lam_before >= fix_cut<T>() - kFixMargin ? 1 : 0;
         if (lane < Q) {
             float* st = &sSt[buf][hw * Q + lane];
             st[0 * QS] = lam * kLog2e;
@@ -602,45 +600,9 @@ ssd_chunk_scan_kernel(ScanK k)
             float m = 0.0f;
             for (int j = hw; j < Cf::WAVES; j += HPW) m = fmaxf(m, sEmax[j]);
             k.ws_emax[(int64_t)seg * BH + bh] = m;
-            k.ws_tmax[(int64_t)seg * BH + bh] = 0u;
             k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
-            if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
         }
     }
-}
-
-// The fix-up's work list: one entry per (later segment, sequence-head, chunk) with chunk < nfix of
-// its pair.  One block of 256 threads: thread t owns pairs t, t + 256, ..., counts their chunks,
-// takes its place in the list from a block-wide prefix sum and writes its entries.
-__device__ void list_fix_items(const int* __restrict__ nfix, uint2* __restrict__ items, int* __restrict__ count,
-                               int npairs)
-{
-    constexpr int kUnroll = 8;
-    __shared__ int sTot[4];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    int mine = 0;
-    for (int p0 = t; p0 < npairs; p0 += 256 * kUnroll) {
-        int v[kUnroll];
-#pragma unroll
-        for (int e = 0; e < kUnroll; ++e) v[e] = p0 + e * 256 < npairs ? nfix[p0 + e * 256] : 0;
-#pragma unroll
-        for (int e = 0; e < kUnroll; ++e) mine += v[e];
-    }
-    int incl = mine;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
-    }
-    if (lane == 63) sTot[w] = incl;
-    __syncthreads();
-    int off = incl - mine;
-    for (int i = 0; i < w; ++i) off += sTot[i];
-    for (int p = t; p < npairs; p += 256) {
-        const int n = nfix[p];
-        for (int j = 0; j < n; ++j) items[off++] = make_uint2((uint32_t)p, (uint32_t)j);
-    }
-    if (t == 255) *count = off;
 }
 
 // Chain the segments.  E[seg] is segment seg's end state from its own start (segment 0 starts from
@@ -650,34 +612,34 @@ __device__ void list_fix_items(const int* __restrict__ nfix, uint2* __restrict__
 // bf16 copy), and T[nseg-1] is the final state.  Only the combine is sequential: the loads of a
 // batch of segments are issued together.
 // The block row past the last sequence-head writes the fix-up's work list instead.
-__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restrict__ ws_state,
-                                                                const float* __restrict__ ws_lam,
-                                                                float* __restrict__ state_out, int BH, int nseg,
-                                                                int PN, const int* __restrict__ nfix,
-                                                                uint2* __restrict__ items, int* __restrict__ count,
-                                                                uint16_t* __restrict__ tin,
-                                                                unsigned* __restrict__ tmax)
+__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(ScanK k, int BH, int PN)
 {
-    constexpr int kBatch = 16;
+#ifndef M2_CHAIN_BATCH
+#define M2_CHAIN_BATCH 32
+#endif
+    constexpr int kBatch = M2_CHAIN_BATCH;  // segments whose loads are issued together
+    const int nseg = k.nseg;
     const int bh = blockIdx.y;
-    if (bh == BH) {
-        if (blockIdx.x == 0) list_fix_items(nfix, items, count, (nseg - 1) * BH);
-        return;
-    }
+    float* __restrict__ ws_state = k.ws_state;
+    const float* __restrict__ ws_lam = k.ws_lam;
+    const float* __restrict__ ws_emax = k.ws_emax;
+    uint16_t* __restrict__ tin = k.ws_tin;
     // four consecutive state entries per thread (PN is a multiple of 16)
-    // threads past the state's end take part in the wave maxima with zero (the waves stay whole)
     const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
-    const bool in = i < PN;
-    const int ic = in ? i : 0;
+    if (i >= PN) return;
+    // the first block of each sequence-head also chains the bounds on the end states' maxima
+    const bool bound = blockIdx.x == 0 && threadIdx.x == 0;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    float tb = 0.0f;
     for (int seg0 = 0; seg0 < nseg; seg0 += kBatch) {
         float4 loc[kBatch];
-        float dec[kBatch];
+        float dec[kBatch], em[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             const int seg = seg0 + j < nseg ? seg0 + j : nseg - 1;
-            loc[j] = *reinterpret_cast<const float4*>(ws_state + ((int64_t)seg * BH + bh) * PN + ic);
+            loc[j] = *reinterpret_cast<const float4*>(ws_state + ((int64_t)seg * BH + bh) * PN + i);
             dec[j] = ws_lam[(int64_t)seg * BH + bh];
+            em[j] = ws_emax[(int64_t)seg * BH + bh];
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
@@ -685,20 +647,16 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
             if (seg < nseg) {
                 const float d = seg == 0 ? 0.0f : fast_exp(dec[j]);
                 s = make_float4(d * s.x + loc[j].x, d * s.y + loc[j].y, d * s.z + loc[j].z, d * s.w + loc[j].w);
+                tb = d * tb + em[j];
+                if (bound) k.ws_tb[(int64_t)seg * BH + bh] = tb;
                 const int64_t o = ((int64_t)seg * BH + bh) * PN + i;
                 if (seg < nseg - 1) {
                     // the initial state of segment seg+1, for the fix-up: in bf16 when that is the
                     // precision it enters the fix-up's product in
-                    if (in) {
-                        if (tin) *reinterpret_cast<uint2*>(tin + o) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
-                        else *reinterpret_cast<float4*>(ws_state + o) = s;
-                    }
-                    // and its largest entry (non-negative floats order like their bit patterns)
-                    float m = in ? fmaxf(fmaxf(fabsf(s.x), fabsf(s.y)), fmaxf(fabsf(s.z), fabsf(s.w))) : 0.0f;
-                    m = wave_max(m);
-                    if ((threadIdx.x & 63) == 0) atomicMax(&tmax[(int64_t)seg * BH + bh], __float_as_uint(m));
-                } else if (state_out && in) {
-                    *reinterpret_cast<float4*>(state_out + (int64_t)bh * PN + i) = s;
+                    if (tin) *reinterpret_cast<uint2*>(tin + o) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+                    else *reinterpret_cast<float4*>(ws_state + o) = s;
+                } else if (k.state_out) {
+                    *reinterpret_cast<float4*>(k.state_out + (int64_t)bh * PN + i) = s;
                 }
             }
         }
@@ -707,12 +665,12 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(float* __restric
 
 // Add the part of each later segment's output that comes from its true initial state S_in (the
 // main pass ran it from zero):  y[t] += e^Lam_t (S_in . C_t),  Lam_t = the summed log-decay from the
-// segment's first token through t.  The factor only falls along the segment, so only a prefix of its
-// chunks needs the term: those whose starting factor is at least e^cut (fix_cut), counted by the main
-// pass and listed by the chain kernel.  A wave takes one listed chunk at a time: S_in, dt, C and y
-// are loaded together, then the term is added and y stored.
+// segment's first token through t.  The factor only falls along the segment, so only a leading run of
+// its chunks needs the term (the test of fix_cut, on the main pass's and the chain kernel's figures).
+// A wave takes one such chunk at a time: S_in, dt, C and y are loaded together, then the term is
+// added and y stored.
 constexpr int kFixThreads = 256;
-constexpr int kFixBlocks = 2048;
+constexpr int kFixBlocksPerCU = 4;
 
 // Eight consecutive k-values of one lane, k = kbase + 8q .. +7, for a K = 32 MFMA step.  The fix-up
 // gives both operands this assignment (any assignment the two operands share gives the same sum),
@@ -750,110 +708,135 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
     float* acc_lds = sAcc[threadIdx.x >> 6];
     const int prow = lane / LPR, pcol = (lane % LPR) * EPL;  // this lane's row in a pass, first column
     const int BH = k.batch * k.H;
-    const int count = *k.fix_count;
-    const int64_t nwaves = (int64_t)gridDim.x * (kFixThreads / 64);
-    for (int64_t item = (int64_t)blockIdx.x * (kFixThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-         item < count; item += nwaves) {
-        const uint2 it = k.fix_items[item];  // the same address in every lane
-        const int pair = (int)it.x, j = (int)it.y;
-        const int seg = 1 + pair / BH, bh = pair % BH;
-        const int64_t b = bh / k.H;
-        const int h = bh % k.H, g = h / (k.H / k.G);
-        const int64_t c = (int64_t)seg * k.cps + j;
-        // the chunk needs the term while e^Lam_before max|T| >= e^cut max|E| (logs in nats; a zero T
-        // needs nothing, a zero E needs everything, NaN keeps the chunk)
+    // Candidates: chunk j of pair = (later segment - 1) * BH + bh is cand = pair * cps + j.  Block b
+    // tests b, b + nblocks, ..., a thread each, lists in LDS the ones that pass, and its waves share
+    // the list.
+    __shared__ int sItem[kFixThreads];
+    __shared__ int sCount;
+    const int npairs = (k.nseg - 1) * BH;
+    const int64_t ncand = (int64_t)npairs * k.cps;
+    const int64_t nblk = gridDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t base = blockIdx.x; base < ncand; base += nblk * kFixThreads) {
+        bool act = false;
         {
-            const float tm = __uint_as_float(k.ws_tmax[(int64_t)(seg - 1) * BH + bh]);
-            const float em = k.ws_emax[(int64_t)seg * BH + bh];
-            const float lb = k.ws_lamc[c * BH + bh];
-            constexpr float kLn2 = 0.6931471805599453f;
-            if (tm == 0.0f || lb + kLn2 * __builtin_amdgcn_logf(tm) < fix_cut<T>() + kLn2 * __builtin_amdgcn_logf(em))
-                continue;
+            const int64_t cand = base + (int64_t)threadIdx.x * nblk;
+            const int pair = (int)(cand / k.cps), j = (int)(cand % k.cps);
+            if (cand < ncand && pair < npairs) {
+                const int seg = 1 + pair / BH, bh = pair % BH;
+                const int64_t c = (int64_t)seg * k.cps + j;
+                // chunks past the sequence have no recorded log-decay and nothing to fix
+                if (c * Q < seq_len(k, bh / k.H)) {
+                    const float tb = k.ws_tb[pair], em = k.ws_emax[pair + BH], lb = k.ws_lamc[c * BH + bh];
+                    // e^lb tb >= e^cut em, in nats (a zero tb needs nothing, a zero em everything, NaN keeps it)
+                    constexpr float kLn2 = 0.6931471805599453f;
+                    act = tb != 0.0f &&
+                          !(lb + kLn2 * __builtin_amdgcn_logf(tb) < fix_cut<T>() + kLn2 * __builtin_amdgcn_logf(em));
+                }
+            }
         }
-        const int64_t t0 = c * Q;
-        const int64_t left = seq_len(k, b) - t0;
-        const int valid = (int)(left < Q ? left : Q);  // >= 1: listed chunks lie inside the sequence
+        if (threadIdx.x == 0) sCount = 0;
+        __syncthreads();
+        const uint64_t mask = __ballot(act);
+        int pos = 0;
+        if (lane == 0 && mask) pos = atomicAdd(&sCount, (int)__popcll(mask));
+        pos = __shfl(pos, 0, 64);
+        if (act) sItem[pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = threadIdx.x;
+        __syncthreads();
+        const int nitems = sCount;
+        for (int it = wave; it < nitems; it += kFixThreads / 64) {
+            const int64_t cand = base + (int64_t)sItem[it] * nblk;
+            const int pair = (int)(cand / k.cps), j = (int)(cand % k.cps);
+            const int seg = 1 + pair / BH, bh = pair % BH;
+            const int64_t b = bh / k.H;
+            const int h = bh % k.H, g = h / (k.H / k.G);
+            const int64_t c = (int64_t)seg * k.cps + j;
+            const int64_t t0 = c * Q;
+            const int64_t left = seq_len(k, b) - t0;
+            const int valid = (int)(left < Q ? left : Q);  // >= 1: listed chunks lie inside the sequence
 
-        // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n] (rows p), from the chain's bf16
-        // copy for bf16 outputs, else from its fp32 states
-        Frag<T> sa[NPB][KS_N];
-        const int64_t soff = ((int64_t)(seg - 1) * BH + bh) * P * N;
-        const void* sbase = EB == 2 ? (const void*)(k.ws_tin + soff) : (const void*)(k.ws_state + soff);
+            // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n] (rows p), from the chain's bf16
+            // copy for bf16 outputs, else from its fp32 states
+            Frag<T> sa[NPB][KS_N];
+            const int64_t soff = ((int64_t)(seg - 1) * BH + bh) * P * N;
+            const void* sbase = EB == 2 ? (const void*)(k.ws_tin + soff) : (const void*)(k.ws_state + soff);
 #pragma unroll
-        for (int pb = 0; pb < NPB; ++pb)
+            for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-            for (int ks = 0; ks < KS_N; ++ks) {
-                const int n0 = 32 * ks + 8 * q;
-                if (n0 < N) load8(sa[pb][ks], (const uint8_t*)sbase + ((int64_t)(pb * 16 + li) * N + n0) * EB);
-                else zero8(sa[pb][ks]);
+                for (int ks = 0; ks < KS_N; ++ks) {
+                    const int n0 = 32 * ks + 8 * q;
+                    if (n0 < N) load8(sa[pb][ks], (const uint8_t*)sbase + ((int64_t)(pb * 16 + li) * N + n0) * EB);
+                    else zero8(sa[pb][ks]);
+                }
+            // the chunk: starting log-decay, dt of token `lane`, C rows (B operand, rows t) and y (rows
+            // past the sequence clamped to its last token; their stores are skipped)
+            const float lam0 = k.ws_lamc[c * BH + bh];
+            const int64_t row0 = seq_row0(k, b);
+            const T* dtp = reinterpret_cast<const T*>(k.dt) + row0 * k.dts + h;
+            const T dtr = dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
+            const uint8_t* cp =
+                reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + row0 * k.bcs + (int64_t)g * N);
+            uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + row0 * k.ys + (int64_t)h * P);
+            Frag<T> cf[NTB][KS_N];
+            uint4 yv[NTB][NPASS];
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) {
+                const int t = tb * 16 + li;
+                const int tr = t < valid ? t : valid - 1;
+#pragma unroll
+                for (int ks = 0; ks < KS_N; ++ks) {
+                    const int n0 = 32 * ks + 8 * q;
+                    if (n0 < N) load8(cf[tb][ks], cp + ((t0 + tr) * k.bcs + n0) * EB);
+                    else zero8(cf[tb][ks]);
+                }
+#pragma unroll
+                for (int ps = 0; ps < NPASS; ++ps) {
+                    const int row = tb * 16 + ps * RPP + prow;
+                    const int rr = row < valid ? row : valid - 1;
+                    yv[tb][ps] = *reinterpret_cast<const uint4*>(yp + ((t0 + rr) * k.ys + pcol) * EB);
+                }
             }
-        // the chunk: starting log-decay, dt of token `lane`, C rows (B operand, rows t) and y (rows
-        // past the sequence clamped to its last token; their stores are skipped)
-        const float lam0 = k.ws_lamc[c * BH + bh];
-        const int64_t row0 = seq_row0(k, b);
-        const T* dtp = reinterpret_cast<const T*>(k.dt) + row0 * k.dts + h;
-        const T dtr = dtp[(t0 + (lane < valid ? lane : valid - 1)) * k.dts];
-        const uint8_t* cp =
-            reinterpret_cast<const uint8_t*>(reinterpret_cast<const T*>(k.C) + row0 * k.bcs + (int64_t)g * N);
-        uint8_t* yp = reinterpret_cast<uint8_t*>(reinterpret_cast<T*>(k.y) + row0 * k.ys + (int64_t)h * P);
-        Frag<T> cf[NTB][KS_N];
-        uint4 yv[NTB][NPASS];
+            const float dtv = lane < valid ? dt_of(to_f32(dtr), k.dt_bias[h], k.dt_min, k.dt_max) : 0.0f;
+            const float lam = lam0 + wave_prefix_sum(dtv * k.A[h]);
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const int t = tb * 16 + li;
-            const int tr = t < valid ? t : valid - 1;
+            for (int tb = 0; tb < NTB; ++tb) {
+                // e^Lam_t (S_in . C_t) for the 16 rows t = tb*16 + li, into LDS as [row][p]
+                const float el = fast_exp(__shfl(lam, tb * 16 + li, 64));
 #pragma unroll
-            for (int ks = 0; ks < KS_N; ++ks) {
-                const int n0 = 32 * ks + 8 * q;
-                if (n0 < N) load8(cf[tb][ks], cp + ((t0 + tr) * k.bcs + n0) * EB);
-                else zero8(cf[tb][ks]);
-            }
+                for (int pb = 0; pb < NPB; ++pb) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ps = 0; ps < NPASS; ++ps) {
-                const int row = tb * 16 + ps * RPP + prow;
-                const int rr = row < valid ? row : valid - 1;
-                yv[tb][ps] = *reinterpret_cast<const uint4*>(yp + ((t0 + rr) * k.ys + pcol) * EB);
-            }
-        }
-        const float dtv = lane < valid ? dt_of(to_f32(dtr), k.dt_bias[h], k.dt_min, k.dt_max) : 0.0f;
-        const float lam = lam0 + wave_prefix_sum(dtv * k.A[h]);
+                    for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[tb][ks]);
+                    *reinterpret_cast<float4*>(acc_lds + li * RS + pb * 16 + 4 * q) =
+                        make_float4(el * acc[0], el * acc[1], el * acc[2], el * acc[3]);
+                }
+                // back in row pieces (LDS operations of one wave complete in order): y += term
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            // e^Lam_t (S_in . C_t) for the 16 rows t = tb*16 + li, into LDS as [row][p]
-            const float el = fast_exp(__shfl(lam, tb * 16 + li, 64));
-#pragma unroll
-            for (int pb = 0; pb < NPB; ++pb) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS_N; ++ks) mfma(acc, sa[pb][ks], cf[tb][ks]);
-                *reinterpret_cast<float4*>(acc_lds + li * RS + pb * 16 + 4 * q) =
-                    make_float4(el * acc[0], el * acc[1], el * acc[2], el * acc[3]);
-            }
-            // back in row pieces (LDS operations of one wave complete in order): y += term
-#pragma unroll
-            for (int ps = 0; ps < NPASS; ++ps) {
-                const int rloc = ps * RPP + prow;
-                const int row = tb * 16 + rloc;
-                if (rloc < 16 && row < valid) {
-                    const float* src = acc_lds + rloc * RS + pcol;
-                    uint8_t* dst = yp + ((t0 + row) * k.ys + pcol) * EB;
-                    const uint4 v = yv[tb][ps];
-                    if constexpr (EB == 2) {
-                        const float4 a = reinterpret_cast<const float4*>(src)[0];
-                        const float4 e = reinterpret_cast<const float4*>(src)[1];
-                        *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(lo_bf16(v.x) + a.x, hi_bf16(v.x) + a.y),
-                                                                    pack_bf16x2(lo_bf16(v.y) + a.z, hi_bf16(v.y) + a.w),
-                                                                    pack_bf16x2(lo_bf16(v.z) + e.x, hi_bf16(v.z) + e.y),
-                                                                    pack_bf16x2(lo_bf16(v.w) + e.z, hi_bf16(v.w) + e.w));
-                    } else {
-                        const float4 a = *reinterpret_cast<const float4*>(src);
-                        *reinterpret_cast<float4*>(dst) =
-                            make_float4(__uint_as_float(v.x) + a.x, __uint_as_float(v.y) + a.y,
-                                        __uint_as_float(v.z) + a.z, __uint_as_float(v.w) + a.w);
+                for (int ps = 0; ps < NPASS; ++ps) {
+                    const int rloc = ps * RPP + prow;
+                    const int row = tb * 16 + rloc;
+                    if (rloc < 16 && row < valid) {
+                        const float* src = acc_lds + rloc * RS + pcol;
+                        uint8_t* dst = yp + ((t0 + row) * k.ys + pcol) * EB;
+                        const uint4 v = yv[tb][ps];
+                        if constexpr (EB == 2) {
+                            const float4 a = reinterpret_cast<const float4*>(src)[0];
+                            const float4 e = reinterpret_cast<const float4*>(src)[1];
+                            *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(lo_bf16(v.x) + a.x, hi_bf16(v.x) + a.y),
+                                                                        pack_bf16x2(lo_bf16(v.y) + a.z, hi_bf16(v.y) + a.w),
+                                                                        pack_bf16x2(lo_bf16(v.z) + e.x, hi_bf16(v.z) + e.y),
+                                                                        pack_bf16x2(lo_bf16(v.w) + e.z, hi_bf16(v.w) + e.w));
+                        } else {
+                            const float4 a = *reinterpret_cast<const float4*>(src);
+                            *reinterpret_cast<float4*>(dst) =
+                                make_float4(__uint_as_float(v.x) + a.x, __uint_as_float(v.y) + a.y,
+                                            __uint_as_float(v.z) + a.z, __uint_as_float(v.w) + a.w);
+                        }
                     }
                 }
             }
         }
+        __syncthreads();
     }
 }
 
@@ -867,23 +850,19 @@ struct Plan {
 
 // Byte offsets of the workspace parts, from a 256-byte aligned base (the caller's pointer rounded up):
 // segment states [nseg][B*H][P*N] f32, segment log-decays [nseg][B*H] f32, per-chunk starting
-// log-decays [nchunks][B*H] f32, fix-up counts [nseg-1][B*H] i32, the work list's length, the work
-// list [(nseg-1)*B*H*cps] (pair, chunk), and for bf16 outputs the segments' initial states in bf16
-// [nseg-1][B*H][P*N].
+// log-decays [nchunks][B*H] f32, the segments' own end-state maxima and the bounds on their true ones
+// [nseg][B*H] f32 each, and for bf16 outputs the segments' initial states in bf16 [nseg-1][B*H][P*N].
 struct WsLayout {
-    size_t lam, emax, tmax, lamc, nfix, count, items, tin, total;
+    size_t lam, emax, tb, lamc, tin, total;
 };
-static WsLayout ws_layout(int64_t nseg, int64_t BH, int64_t PN, int64_t nchunks, int64_t cps, bool bf16) {
+static WsLayout ws_layout(int64_t nseg, int64_t BH, int64_t PN, int64_t nchunks, bool bf16) {
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     WsLayout w;
     w.lam = up((size_t)(nseg * BH * PN) * sizeof(float));
     w.emax = up(w.lam + (size_t)(nseg * BH) * sizeof(float));
-    w.tmax = up(w.emax + (size_t)(nseg * BH) * sizeof(float));
-    w.lamc = up(w.tmax + (size_t)(nseg * BH) * sizeof(unsigned));
-    w.nfix = up(w.lamc + (size_t)(nchunks * BH) * sizeof(float));
-    w.count = up(w.nfix + (size_t)((nseg - 1) * BH) * sizeof(int));
-    w.items = up(w.count + sizeof(int));
-    w.tin = up(w.items + (size_t)((nseg - 1) * BH * cps) * sizeof(uint2));
+    w.tb = up(w.emax + (size_t)(nseg * BH) * sizeof(float));
+    w.lamc = up(w.tb + (size_t)(nseg * BH) * sizeof(float));
+    w.tin = up(w.lamc + (size_t)(nchunks * BH) * sizeof(float));
     w.total = w.tin + (bf16 ? (size_t)((nseg - 1) * BH * PN) * sizeof(uint16_t) : 0);
     return w;
 }
@@ -917,7 +896,7 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, i
     const int64_t nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
     pl.nseg = (int)nseg;
     pl.cps = (int)cps;
-    pl.ws_bytes = nseg > 1 ? ws_layout(nseg, batch * H, N_P_N, nchunks, cps, bf16).total + 256 : 0;
+    pl.ws_bytes = nseg > 1 ? ws_layout(nseg, batch * H, N_P_N, nchunks, bf16).total + 256 : 0;
     return pl;
 }
 
@@ -954,23 +933,17 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     k.ws_state = nullptr;
     k.ws_lam = nullptr;
     k.ws_lamc = nullptr;
-    k.ws_nfix = nullptr;
-    k.fix_items = nullptr;
-    k.fix_count = nullptr;
     k.ws_tin = nullptr;
     k.ws_emax = nullptr;
-    k.ws_tmax = nullptr;
+    k.ws_tb = nullptr;
     if (pl.nseg > 1) {
-        const WsLayout w = ws_layout(pl.nseg, BH, P * N, (a.L + Q - 1) / Q, pl.cps, sizeof(T) == 2);
+        const WsLayout w = ws_layout(pl.nseg, BH, P * N, (a.L + Q - 1) / Q, sizeof(T) == 2);
         uint8_t* base = reinterpret_cast<uint8_t*>(((uintptr_t)a.ws + 255) & ~(uintptr_t)255);
         k.ws_state = reinterpret_cast<float*>(base);
         k.ws_lam = reinterpret_cast<float*>(base + w.lam);
         k.ws_emax = reinterpret_cast<float*>(base + w.emax);
-        k.ws_tmax = reinterpret_cast<unsigned*>(base + w.tmax);
+        k.ws_tb = reinterpret_cast<float*>(base + w.tb);
         k.ws_lamc = reinterpret_cast<float*>(base + w.lamc);
-        k.ws_nfix = reinterpret_cast<int*>(base + w.nfix);
-        k.fix_count = reinterpret_cast<int*>(base + w.count);
-        k.fix_items = reinterpret_cast<uint2*>(base + w.items);
         if (sizeof(T) == 2) k.ws_tin = reinterpret_cast<uint16_t*>(base + w.tin);
     }
     // every segment at once (later ones from a zero state), then, with several segments, the chain
@@ -988,12 +961,15 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     if (walk) e = launch_ssd_walk(k, conv, s);
     else e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
     if (e != hipSuccess || pl.nseg == 1) return e;
-    // one extra block row lists the fix-up's work
-    dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH + 1);
-    e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k.ws_state, (const float*)k.ws_lam, a.state_out,
-                      BH, pl.nseg, P * N, (const int*)k.ws_nfix, k.fix_items, k.fix_count, k.ws_tin, k.ws_tmax);
+    dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH);
+    e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k, BH, P * N);
     if (e != hipSuccess) return e;
-    return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3(kFixBlocks), dim3(kFixThreads), 0, s, k);
+    // about one listed chunk per wave on the work seen so far; at most one round of resident blocks
+    const int64_t ncand = (int64_t)(pl.nseg - 1) * BH * pl.cps;
+    int64_t nfb = (ncand + 63) / 64;
+    const int64_t cap = (int64_t)device_shape().cus * kFixBlocksPerCU;
+    nfb = nfb < cap ? nfb : cap;
+    return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3((unsigned)nfb), dim3(kFixThreads), 0, s, k);
 }
 
 template <typename T, int Q>

@@ -216,7 +216,6 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
     // `tbuf` into sSt[sbuf][w]; the chunk's wave-uniform values come back through dec_o (factor on
     // the stored state after the chunk's output) and lamend_o (its summed log-decay)
     float sig = 0.0f, lam_seg = 0.0f;
-    int nfix = 0;
     auto stats = [&](int i, int tbuf, int sbuf, float& dec_o, float& lamend_o) __attribute__((always_inline)) {
         const int left = nrows - i * Q;
         const int valid = left < Q ? left : Q;
@@ -232,7 +231,6 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
         sig = rescale ? 0.0f : sig_prev + lam_end;
         const float lam_before = lam_seg;
         lam_seg += lam_end;
-        nfix += lam_before >= fix_cut<bf16_t>() - kFixMargin ? 1 : 0;
         if (lane < Q) {
             float* st = &sSt[sbuf][w][0][lane];
             st[0 * Q] = lam * kLog2e;
@@ -531,9 +529,7 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
         emax = wave_max(emax);
         if (hvalid && lane == 0) {
             k.ws_emax[(int64_t)seg * BH + bh] = emax;
-            k.ws_tmax[(int64_t)seg * BH + bh] = 0u;
             k.ws_lam[(int64_t)seg * BH + bh] = lam_seg;
-            if (seg > 0) k.ws_nfix[(int64_t)(seg - 1) * BH + bh] = nfix;
         }
     }
     if constexpr (FUSED) {
