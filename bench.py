@@ -128,6 +128,24 @@ def measured_traffic(kernel):
         return None
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def measured_mfma(kernel):
+    """MFMA utilisation of the entry point's main pass from the committed rocprofv3 SQ-counter summary
+    (MFMA pipe busy fraction, achieved MFMA TFLOP/s and its fraction of the dense bf16 peak); None if
+    absent or taken on a different version of the kernel source."""
+    try:
+        with open(COUNTERS_FILE) as fh:
+            e = json.load(fh)["kernels"][kernel]
+        if e.get("source_sha256") != source_digest(kernel):
+            return None
+        return {k: e[k] for k in ("kernel", "mfma_busy", "mfma_tflops", "mfma_frac_of_peak", "valu_per_wave",
+                                  "mfma_per_wave")}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 COPY_CEILING = [None]   # GB/s of the library's streaming copy, measured first in this run
 
 
@@ -402,6 +420,8 @@ def main():
                                       "frac": v["roofline"]["frac"], "achieved_GBs": v["roofline"]["achieved"],
                                       "frac_of_copy": v["roofline"].get("frac_of_copy")}
                                   for n, v in k.items()}
+        for n in ("mixer_prefill", "ssd_scan"):
+            out["prefill_kernels"][n]["mfma"] = measured_mfma(n)
         out["prefill_path_roofline_frac"] = pre["path_roofline_frac"]
         out["prefill_fused_min_roofline_frac"] = pre["fused_min_roofline_frac"]
         out["prefill_two_kernel"] = pre["two_kernel"]
