@@ -5,11 +5,12 @@
 //     out[b,t,c] = SiLU(bias[c] + sum_{k<W} w[c,k] * x[b, t-(W-1)+k, c])
 //
 // Pure HBM stream (3 flop per byte).  Each lane owns VEC adjacent channels (one
-// 16-byte load per token) and walks 64 consecutive tokens, keeping the last W
-// inputs in registers, so every input is read from HBM once (plus a W-1 token
-// halo per tile).  A wave covers 64*VEC contiguous channels of one token, so each
-// load and store instruction moves one contiguous 1 KiB row segment; loads run one
-// group of 8 tokens ahead of the arithmetic.
+// 8-byte load per token for 4 bf16 channels) and walks TILE consecutive tokens (64;
+// 8 when there are too few tiles to fill the chip), keeping the last W inputs in
+// registers, so every input is read from HBM once (plus a W-1 token halo per tile).
+// A wave covers 64*VEC contiguous channels of one token, so each load and store
+// instruction moves one contiguous row segment; loads run one group of 8 tokens
+// ahead of the arithmetic.
 #include "m2_device.h"
 #include "m2_launch.h"
 

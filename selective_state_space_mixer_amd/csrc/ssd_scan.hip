@@ -610,8 +610,8 @@ ssd_chunk_scan_kernel(ScanK k)
 //   T[0] = E[0],  T[seg] = e^lam[seg] T[seg-1] + E[seg];
 // T[seg] (the initial state of segment seg+1) is written over E[seg] (or, for bf16 outputs, to a
 // bf16 copy), and T[nseg-1] is the final state.  Only the combine is sequential: the loads of a
-// batch of segments are issued together.
-// The block row past the last sequence-head writes the fix-up's work list instead.
+// batch of segments are issued together.  The first block of each sequence-head also chains the
+// bounds Tb[seg] on max|T[seg]| from the segments' recorded maxima (see fix_cut).
 __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(ScanK k, int BH, int PN)
 {
 #ifndef M2_CHAIN_BATCH
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
             const int64_t c = (int64_t)seg * k.cps + j;
             const int64_t t0 = c * Q;
             const int64_t left = seq_len(k, b) - t0;
-            const int valid = (int)(left < Q ? left : Q);  // >= 1: listed chunks lie inside the sequence
+            const int valid = (int)(left < Q ? left : Q);  // >= 1: tested chunks lie inside the sequence
 
             // S_in as the A operand of Y^T[p][t] = sum_n S[p][n] C[t][n] (rows p), from the chain's bf16
             // copy for bf16 outputs, else from its fp32 states
@@ -964,7 +964,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH);
     e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k, BH, P * N);
     if (e != hipSuccess) return e;
-    // about one listed chunk per wave on the work seen so far; at most one round of resident blocks
+    // about one chunk to fix per wave on the 32k prompt's figures; at most one round of resident blocks
     const int64_t ncand = (int64_t)(pl.nseg - 1) * BH * pl.cps;
     int64_t nfb = (ncand + 63) / 64;
     const int64_t cap = (int64_t)device_shape().cus * kFixBlocksPerCU;

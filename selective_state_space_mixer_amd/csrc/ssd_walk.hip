@@ -6,8 +6,8 @@
 //   y_t   = e^Lam_t (S_prev . C_t) + sum_{s<=t} e^(Lam_t - Lam_s) dt_s (C_t . B_s) x_s + D x_t
 //   S_new = e^Lam_end S_prev + sum_s e^(Lam_end - Lam_s) dt_s x_s (outer) B_s
 // and the segment contract is the same (segments after the first start from zero; their end
-// states, summed log-decays, per-chunk starting log-decays and fix-up counts go to the workspace
-// for the chain and fix-up kernels of ssd_scan.hip).
+// states and the maxima of those, summed log-decays and per-chunk starting log-decays go to the
+// workspace for the chain and fix-up kernels of ssd_scan.hip).
 //
 // What differs from the general kernel is the split of the work.  Each wave owns one head and
 // keeps the whole 64x64 fp32 state of that head in 64 accumulator registers (two waves per
