@@ -51,6 +51,8 @@ def _load():
         lib.oracle_softplus.argtypes = [f64]
         lib.oracle_softplus.restype = f64
         lib.oracle_gated_rmsnorm.argtypes = [i64, i64, i64, dp, dp, dp, f64, i64, dp]
+        lib.oracle_ssd_scan_bwd.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64] + [dp] * 3 + [dp] * 8
+        lib.oracle_ssd_scan_bwd.restype = None
         lib.oracle_gated_rmsnorm.restype = None
         _lib = lib
     return _lib
@@ -143,6 +145,38 @@ def ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None,
     _load().oracle_ssd_scan(Bn, L, H, P, N, G, _p(x), _p(Bm), _p(Cm), _p(dt_raw), _p(dt_bias), _p(A),
                             _p(D), float(dt_min), float(dt_max), _p(state_in), _p(y), _p(state_out), _p(lens))
     return y, state_out
+
+
+def ssd_scan_bwd(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None, dy=None, dstate_out=None,
+                 dt_min: float = 0.0, dt_max: float = float("inf")):
+    """Gradients of L = sum(dy * y) + sum(dstate_out * state_out) for ssd_scan's outputs.
+
+    Same inputs as ssd_scan, plus dy [B,L,H,P] and dstate_out [B,H,P,N] (None: zero).  Returns a dict
+    with dx [B,L,H,P], dB and dC [B,L,G,N], ddt_raw [B,L,H], ddt_bias, dA, dD [H] and dstate_in
+    [B,H,P,N]."""
+    x = _f64(x)
+    Bn, L, H, P = x.shape
+    Bm = _f64(Bm)
+    G, N = Bm.shape[2], Bm.shape[3]
+    Bm = _f64(Bm, (Bn, L, G, N))
+    Cm = _f64(Cm, (Bn, L, G, N))
+    dt_raw = _f64(dt_raw, (Bn, L, H))
+    dt_bias = _f64(dt_bias, (H,))
+    A = _f64(A, (H,))
+    D = _f64(D, (H,))
+    state_in = _f64(state_in, (Bn, H, P, N))
+    dy = _f64(dy, (Bn, L, H, P)) if dy is not None else np.zeros((Bn, L, H, P))
+    dstate_out = _f64(dstate_out, (Bn, H, P, N))
+    if H % G:
+        raise ValueError("oracle: nheads must be a multiple of n_groups")
+    out = {"dx": np.empty_like(x), "dB": np.empty((Bn, L, G, N)), "dC": np.empty((Bn, L, G, N)),
+           "ddt_raw": np.empty((Bn, L, H)), "ddt_bias": np.empty(H), "dA": np.empty(H), "dD": np.empty(H),
+           "dstate_in": np.empty((Bn, H, P, N))}
+    _load().oracle_ssd_scan_bwd(Bn, L, H, P, N, G, _p(x), _p(Bm), _p(Cm), _p(dt_raw), _p(dt_bias), _p(A),
+                                _p(D), float(dt_min), float(dt_max), _p(state_in), _p(dy), _p(dstate_out),
+                                _p(out["dx"]), _p(out["dB"]), _p(out["dC"]), _p(out["ddt_raw"]),
+                                _p(out["ddt_bias"]), _p(out["dA"]), _p(out["dD"]), _p(out["dstate_in"]))
+    return out
 
 
 def _cu(cu_seqlens, T):

@@ -19,6 +19,14 @@
  *           y_t = S_t . C_t + D_h * x_t
  *   step    the same for one token, with the conv window taken from a ring of the
  *           last W tokens (the cache of conv state + recurrent state, §三)
+ *   scan backward  the gradients of L = sum_t dy_t . y_t + <dS, S_final> with respect to every
+ *           input of the scan (the training path of the stateful mixer, §三), by the adjoint
+ *           recurrence in reverse time from the stored forward states:
+ *             Gt = adjoint of S_t:  Gt = a_{t+1} G_{t+1} + dy_t (outer) C_t,  G_{L-1} includes dS
+ *             dx_t = D dy_t + dt_t Gt B_t      dB_t = dt_t Gt^T x_t      dC_t = S_t^T dy_t
+ *             d(dt_t) = <Gt, x_t B_t^T> + A a_t <Gt, S_{t-1}>,   a_t = exp(dt_t A)
+ *             dA = sum_t dt_t a_t <Gt, S_{t-1}>   dD = sum_t dy_t . x_t   dstate_in = a_0 G_0
+ *           then through the clamp and softplus to dt_raw and dt_bias
  *   norm    the gated group RMSNorm after the scan (§三, the gated normalisation: group RMSNorm times
  *           SiLU of the gate z, over intermediate_size in groups; eps from §五 rms_norm_eps):
  *             gate first (norm_before_gate = 0):  g = y * SiLU(z),
@@ -228,4 +236,132 @@ void oracle_gated_rmsnorm(int64_t T, int64_t D, int64_t GS, const double* y, con
             }
         }
     }
+}
+
+/* Gradients of L = sum_t dy_t . y_t + <dstate_out, S_final> for the scan of oracle_ssd_scan
+ * (no lens).  dstate_out / state_in / D nullable (zero).  Outputs: dx [B,L,H,P], dB and dC
+ * [B,L,G,N] (summed over the heads of the group), ddt_raw [B,L,H], ddt_bias / dA / dD [H]
+ * (summed over the batch), dstate_in [B,H,P,N].  The forward states S_0..S_{L-1} of a
+ * (sequence, head) are kept, then the adjoint runs from t = L-1 down to 0.  The clamped
+ * softplus passes the gradient where dt_min <= softplus(v) <= dt_max, else 0. */
+void oracle_ssd_scan_bwd(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                         const double* x, const double* Bm, const double* Cm,
+                         const double* dt_raw, const double* dt_bias, const double* A, const double* D,
+                         double dt_min, double dt_max, const double* state_in,
+                         const double* dy, const double* dstate_out,
+                         double* dx, double* dB, double* dC, double* ddt_raw,
+                         double* ddt_bias, double* dA, double* dD, double* dstate_in)
+{
+    const int64_t hpg = H / G, PN = P * N;
+    /* per (sequence, head) partial sums, added up after the parallel loop */
+    double* pdB = (double*)calloc((size_t)(Bn * H * L * N), sizeof(double));
+    double* pdC = (double*)calloc((size_t)(Bn * H * L * N), sizeof(double));
+    double* pdA = (double*)calloc((size_t)(Bn * H), sizeof(double));
+    double* pdD = (double*)calloc((size_t)(Bn * H), sizeof(double));
+    double* pdb = (double*)calloc((size_t)(Bn * H), sizeof(double));
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t b = 0; b < Bn; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t g = h / hpg, bh = b * H + h;
+            const double Dh = D ? D[h] : 0.0;
+            /* forward: S[t + 1] is the state after token t, S[0] the initial state */
+            double* S = (double*)malloc((size_t)((L + 1) * PN) * sizeof(double));
+            double* dts = (double*)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
+            for (int64_t i = 0; i < PN; ++i) S[i] = state_in ? state_in[bh * PN + i] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t bt = b * L + t;
+                const double dt = step_size(dt_raw[bt * H + h], dt_bias[h], dt_min, dt_max);
+                const double a = exp(dt * A[h]);
+                const double* xt = x + (bt * H + h) * P;
+                const double* Bt = Bm + (bt * G + g) * N;
+                dts[t] = dt;
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n)
+                        S[(t + 1) * PN + p * N + n] = a * S[t * PN + p * N + n] + dt * xt[p] * Bt[n];
+            }
+            /* reverse: Gm is the adjoint of the state after token t */
+            double* Gm = (double*)malloc((size_t)PN * sizeof(double));
+            for (int64_t i = 0; i < PN; ++i) Gm[i] = dstate_out ? dstate_out[bh * PN + i] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const int64_t bt = b * L + t;
+                const double dt = dts[t];
+                const double a = exp(dt * A[h]);
+                const double* xt = x + (bt * H + h) * P;
+                const double* Bt = Bm + (bt * G + g) * N;
+                const double* Ct = Cm + (bt * G + g) * N;
+                const double* dyt = dy + (bt * H + h) * P;
+                const double* St = S + (t + 1) * PN;
+                const double* Sp = S + t * PN;
+                /* y_t = S_t C_t + D x_t: the state after t receives dy_t (outer) C_t */
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n) Gm[p * N + n] += dyt[p] * Ct[n];
+                for (int64_t n = 0; n < N; ++n) {
+                    double acc = 0.0;
+                    for (int64_t p = 0; p < P; ++p) acc += St[p * N + n] * dyt[p];
+                    pdC[(bh * L + t) * N + n] = acc;
+                }
+                double xdy = 0.0;
+                for (int64_t p = 0; p < P; ++p) xdy += dyt[p] * xt[p];
+                pdD[bh] += xdy;
+                /* S_t = a S_{t-1} + dt x_t B_t^T */
+                for (int64_t p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) acc += Gm[p * N + n] * Bt[n];
+                    dx[(bt * H + h) * P + p] = Dh * dyt[p] + dt * acc;
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    double acc = 0.0;
+                    for (int64_t p = 0; p < P; ++p) acc += Gm[p * N + n] * xt[p];
+                    pdB[(bh * L + t) * N + n] = dt * acc;
+                }
+                double gxb = 0.0, gs = 0.0;
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n) {
+                        gxb += Gm[p * N + n] * xt[p] * Bt[n];
+                        gs += Gm[p * N + n] * Sp[p * N + n];
+                    }
+                const double ddt = gxb + A[h] * a * gs;
+                pdA[bh] += dt * a * gs;
+                /* dt = clamp(softplus(v)), v = dt_raw + dt_bias; softplus'(v) = 1 / (1 + e^-v) */
+                const double v = dt_raw[bt * H + h] + dt_bias[h];
+                const double sp = softplus(v);
+                const double g_raw = (sp < dt_min || sp > dt_max) ? 0.0 : ddt / (1.0 + exp(-v));
+                ddt_raw[bt * H + h] = g_raw;
+                pdb[bh] += g_raw;
+                for (int64_t i = 0; i < PN; ++i) Gm[i] *= a;
+            }
+            for (int64_t i = 0; i < PN; ++i) dstate_in[bh * PN + i] = Gm[i];
+            free(Gm);
+            free(dts);
+            free(S);
+        }
+    }
+    for (int64_t b = 0; b < Bn; ++b)
+        for (int64_t t = 0; t < L; ++t)
+            for (int64_t g = 0; g < G; ++g)
+                for (int64_t n = 0; n < N; ++n) {
+                    double sb = 0.0, sc = 0.0;
+                    for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+                        sb += pdB[((b * H + h) * L + t) * N + n];
+                        sc += pdC[((b * H + h) * L + t) * N + n];
+                    }
+                    dB[((b * L + t) * G + g) * N + n] = sb;
+                    dC[((b * L + t) * G + g) * N + n] = sc;
+                }
+    for (int64_t h = 0; h < H; ++h) {
+        double sa = 0.0, sd = 0.0, sbias = 0.0;
+        for (int64_t b = 0; b < Bn; ++b) {
+            sa += pdA[b * H + h];
+            sd += pdD[b * H + h];
+            sbias += pdb[b * H + h];
+        }
+        dA[h] = sa;
+        dD[h] = sd;
+        ddt_bias[h] = sbias;
+    }
+    free(pdB);
+    free(pdC);
+    free(pdA);
+    free(pdD);
+    free(pdb);
 }
