@@ -16,6 +16,8 @@
  *   m2_mixer_prefill_fwd  the conv and the scan of a prompt in one pass, without
  *                    writing the conv output (§五: use_mem_eff_path)
  *   m2_gated_rmsnorm the gated group RMSNorm applied to the scan's output (§三)
+ *   m2_ssd_scan_bwd  the backward of the scan: the gradients a training step of the stateful
+ *                    mixer needs (§三)
  *
  * A batch of prompts of different lengths (the recurrent mask of §2.3) is given either
  * right-padded (seq_lens on m2_conv1d_fwd / m2_ssd_scan_fwd) or packed back to back
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define M2SSD_ABI_VERSION 4
+#define M2SSD_ABI_VERSION 5
 
 typedef enum {
     M2_OK = 0,
@@ -297,6 +299,52 @@ m2_status m2_gated_rmsnorm(int64_t ntok, int32_t d_inner, int32_t group_size, in
  * measured with a streaming kernel of this library, which the benchmark reports beside the HBM
  * peak as the reference for the kernels' bandwidth fractions. */
 m2_status m2_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Workspace bytes m2_ssd_scan_bwd needs for these dims (0 when the backward is not built for them:
+ * then it returns M2_ERR_UNSUPPORTED). */
+size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims);
+
+/* Backward of m2_ssd_scan_fwd (article §三: the Mamba2 mixer's chunked scan on the training path of
+ * the stateful model): the gradients of
+ *     L = sum_{b,t} dy_t . y_t + <dstate_out, state_out>
+ * with respect to every input of the scan, for y and state_out as m2_ssd_scan_fwd computes them
+ * from the same arguments.  Built for bf16 activations at headdim 64 and d_state 64 (the
+ * Zamba2-2.7B mixer shape), any batch, seqlen and n_groups dividing nheads; chunk_size is ignored
+ * (chunks of 64 tokens).  Other dims return M2_ERR_UNSUPPORTED.  Sequence lengths and packed batches
+ * are not supported: every sequence is seqlen tokens.
+ * Inputs as m2_ssd_scan_fwd (x, B, C, raw dt, dt_bias, A, D or NULL, dt_min, dt_max, state_in or
+ * NULL), plus
+ *   dy         [batch, seqlen, nheads*headdim] io, token stride dy_tok_stride: dL/dy
+ *   dstate_out [batch, nheads, headdim, d_state] fp32 or NULL (zero): dL/dstate_out
+ * Outputs (written, not accumulated):
+ *   dx         [batch, seqlen, nheads*headdim] io, token stride dx_tok_stride
+ *   dB, dC     [batch, seqlen, n_groups*d_state] io, token stride dbc_tok_stride: summed over the
+ *              heads of each group
+ *   ddt        [batch, seqlen, nheads] io, token stride ddt_tok_stride: dL/d(raw dt), zero where the
+ *              clamp holds dt at dt_min or dt_max
+ *   ddt_bias, dA, dD  [nheads] fp32, summed over the batch and the tokens (dD also when D is NULL)
+ *   dstate_in  [batch, nheads, headdim, d_state] fp32 or NULL: dL/dstate_in
+ * workspace: at least m2_ssd_scan_bwd_workspace(dims) bytes, any alignment, contents on entry
+ * irrelevant; calls that may run at the same time need separate workspaces.
+ * x, B, C, dy, dx, dB and dC must start on 16-byte boundaries with token strides that are multiples
+ * of 16 bytes (else M2_ERR_UNSUPPORTED).  No output may overlap an input, another output or the
+ * workspace (M2_ERR_ALIAS). */
+m2_status m2_ssd_scan_bwd(const m2_dims* dims,
+                          const void* x, int64_t x_tok_stride,
+                          const void* B, const void* C, int64_t bc_tok_stride,
+                          const void* dt, int64_t dt_tok_stride,
+                          const float* dt_bias, const float* A, const float* D,
+                          float dt_min, float dt_max,
+                          const float* state_in,
+                          const void* dy, int64_t dy_tok_stride,
+                          const float* dstate_out,
+                          void* dx, int64_t dx_tok_stride,
+                          void* dB, void* dC, int64_t dbc_tok_stride,
+                          void* ddt, int64_t ddt_tok_stride,
+                          float* ddt_bias, float* dA, float* dD,
+                          float* dstate_in,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Static text for a status code. */
 const char* m2_status_str(m2_status status);

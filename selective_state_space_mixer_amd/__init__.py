@@ -27,11 +27,12 @@ M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, 
     M2_ERR_LAUNCH, M2_ERR_TOO_LARGE = range(9)
 M2_STATIC_SCRATCH_BYTES = 64 << 20
 M2_F32, M2_BF16 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
            "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc",
            "m2_mixer_prefill_workspace", "m2_mixer_prefill_fwd", "m2_ssd_step", "m2_gated_rmsnorm", "m2_stream_copy",
+           "m2_ssd_scan_bwd_workspace", "m2_ssd_scan_bwd",
            "m2_status_str", "m2_abi_version", "m2_last_hip_error")
 
 
@@ -101,6 +102,11 @@ def _load() -> ctypes.CDLL:
     lib.m2_gated_rmsnorm.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp, i64, vp, f32,
                                      ctypes.c_int32, vp, i64, vp]
     lib.m2_gated_rmsnorm.restype = ctypes.c_int
+    lib.m2_ssd_scan_bwd_workspace.argtypes = [dp]
+    lib.m2_ssd_scan_bwd_workspace.restype = sz
+    lib.m2_ssd_scan_bwd.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, i64, vp, vp, i64,
+                                    vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.m2_ssd_scan_bwd.restype = ctypes.c_int
     lib.m2_stream_copy.argtypes = [vp, vp, sz, vp]
     lib.m2_stream_copy.restype = ctypes.c_int
     lib.m2_status_str.argtypes = [ctypes.c_int]
@@ -531,6 +537,48 @@ def m2_gated_rmsnorm(y, z, w, out, group_size: int, eps: float = 1e-5, norm_befo
     _, os_ = _rows(out, "out")
     _call("m2_gated_rmsnorm", int(ntok), int(D), int(group_size), M2_BF16 if io == torch.bfloat16 else M2_F32,
           _ptr(y), ys, _ptr(z), zs, _ptr(w), float(eps), int(bool(norm_before_gate)), _ptr(out), os_,
+          _stream(stream))
+
+
+def m2_ssd_scan_bwd_workspace(dims: M2Dims) -> int:
+    """Bytes of workspace m2_ssd_scan_bwd needs (0: not built for these dims)."""
+    return int(_lib.m2_ssd_scan_bwd_workspace(ctypes.byref(dims)))
+
+
+def m2_ssd_scan_bwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, dy, dx, dB, dC, ddt, ddt_bias, dA, dD,
+                    state_in=None, dstate_out=None, dstate_in=None, dt_min: float = 0.0, dt_max: float = float("inf"),
+                    workspace=None, stream=None) -> None:
+    """Backward of the scan; see include/m2ssd.h.
+
+    Inputs as m2_ssd_scan_fwd plus dy (like y) and dstate_out [B, H, P, N] f32 or None; outputs dx (like x),
+    dB/dC (like B/C, sharing one token stride), ddt (like dt), ddt_bias/dA/dD [H] f32 and dstate_in
+    [B, H, P, N] f32 or None; workspace: a uint8 GPU tensor of at least m2_ssd_scan_bwd_workspace(dims)
+    bytes."""
+    torch = _torch()
+    ins, _ = _scan_args(dims, x, B, C, dt, dt_bias, A, D, dy, state_in, None)
+    io = _io_dtype(dims)
+    H, P, N, G = dims.nheads, dims.headdim, dims.d_state, dims.n_groups
+    for n, t in (("dx", dx), ("dB", dB), ("dC", dC), ("ddt", ddt)):
+        _check(t, n, io)
+    for n, t in (("ddt_bias", ddt_bias), ("dA", dA), ("dD", dD), ("dstate_out", dstate_out), ("dstate_in", dstate_in)):
+        _check(t, n, torch.float32)
+    for n, t in (("ddt_bias", ddt_bias), ("dA", dA), ("dD", dD)):
+        if t is None or not t.is_contiguous() or t.numel() != H:
+            raise ValueError("%s must be a contiguous [nheads] tensor" % n)
+    for n, t in (("dstate_out", dstate_out), ("dstate_in", dstate_in)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, H, P, N)):
+            raise ValueError("%s must be contiguous [batch, nheads, headdim, d_state]" % n)
+    dys = _tok_stride(dy, "dy", dims, H * P)
+    dxs = _tok_stride(dx, "dx", dims, H * P)
+    dbs = _tok_stride(dB, "dB", dims, G * N)
+    if _tok_stride(dC, "dC", dims, G * N) != dbs:
+        raise ValueError("dB and dC must have the same token stride")
+    ddts = _tok_stride(ddt, "ddt", dims, H)
+    if workspace is None:
+        raise ValueError("m2_ssd_scan_bwd needs a workspace of %d bytes" % m2_ssd_scan_bwd_workspace(dims))
+    _call("m2_ssd_scan_bwd", ctypes.byref(dims), *ins, float(dt_min), float(dt_max), _ptr(state_in), _ptr(dy), dys,
+          _ptr(dstate_out), _ptr(dx), dxs, _ptr(dB), _ptr(dC), dbs, _ptr(ddt), ddts, _ptr(ddt_bias), _ptr(dA),
+          _ptr(dD), _ptr(dstate_in), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
           _stream(stream))
 
 

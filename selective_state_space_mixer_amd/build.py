@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libm2ssd.so")
-SOURCES = ["api.cpp", "conv1d.hip", "ssd_scan.hip", "ssd_walk.hip", "ssd_step.hip", "gated_norm.hip", "stream_copy.hip"]
+SOURCES = ["api.cpp", "conv1d.hip", "ssd_scan.hip", "ssd_walk.hip", "ssd_step.hip", "gated_norm.hip", "stream_copy.hip", "ssd_bwd.hip"]
 ARCH = os.environ.get("M2SSD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -402,6 +402,75 @@ m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stri
     return launched(m2::launch_ssd_step(a, (hipStream_t)stream));
 }
 
+size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims) {
+    Derived d;
+    if (derive(dims, d) != M2_OK || !m2::ssd_bwd_supported(d.P, d.N, d.bf16)) return 0;
+    return m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H);
+}
+
+m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B, const void* C,
+                          int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
+                          const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
+                          const void* dy, int64_t dy_tok_stride, const float* dstate_out, void* dx,
+                          int64_t dx_tok_stride, void* dB, void* dC, int64_t dbc_tok_stride, void* ddt,
+                          int64_t ddt_tok_stride, float* ddt_bias, float* dA, float* dD, float* dstate_in,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    const int64_t rows = d.batch * d.L;
+    const int GN = d.G * d.N;
+    if (!dt_bias || !A || !ddt_bias || !dA || !dD) return M2_ERR_NULL;
+    if (rows > 0 && (!x || !B || !C || !dt || !dy || !dx || !dB || !dC || !ddt)) return M2_ERR_NULL;
+    if (rows > 0 && (x_tok_stride < d.d_inner || bc_tok_stride < GN || dt_tok_stride < d.H ||
+                     dy_tok_stride < d.d_inner || dx_tok_stride < d.d_inner || dbc_tok_stride < GN ||
+                     ddt_tok_stride < d.H))
+        return M2_ERR_SHAPE;
+    if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return M2_ERR_SHAPE;
+    if (!m2::ssd_bwd_supported(d.P, d.N, d.bf16)) return M2_ERR_UNSUPPORTED;
+    // grid rows: (sequence, group) and (sequence, head) pairs
+    if (d.batch * d.H > 65535) return M2_ERR_UNSUPPORTED;
+    if (rows > 0 && (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(dy) || !aligned16(dx) ||
+                     !aligned16(dB) || !aligned16(dC) || (x_tok_stride * 2) % 16 || (bc_tok_stride * 2) % 16 ||
+                     (dy_tok_stride * 2) % 16 || (dx_tok_stride * 2) % 16 || (dbc_tok_stride * 2) % 16 ||
+                     ((uintptr_t)dt & 1u) || ((uintptr_t)ddt & 1u)))
+        return M2_ERR_UNSUPPORTED;
+    if (((uintptr_t)state_in & 3u) || ((uintptr_t)dstate_out & 3u) || ((uintptr_t)dstate_in & 3u))
+        return M2_ERR_UNSUPPORTED;
+    const size_t need = m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H);
+    if (!workspace || workspace_bytes < need) return M2_ERR_WORKSPACE;
+    const int64_t SS = (int64_t)d.P * d.N;
+    const Range ins[] = {span(x, rows, x_tok_stride, d.d_inner, 2), span(B, rows, bc_tok_stride, GN, 2),
+                         span(C, rows, bc_tok_stride, GN, 2), span(dt, rows, dt_tok_stride, d.H, 2),
+                         span(dy, rows, dy_tok_stride, d.d_inner, 2), span(dt_bias, 1, 0, d.H, 4),
+                         span(A, 1, 0, d.H, 4), span(D, 1, 0, d.H, 4), span(state_in, d.batch * d.H, SS, SS, 4),
+                         span(dstate_out, d.batch * d.H, SS, SS, 4)};
+    const Range outs[] = {span(dx, rows, dx_tok_stride, d.d_inner, 2), span(dB, rows, dbc_tok_stride, GN, 2),
+                          span(dC, rows, dbc_tok_stride, GN, 2), span(ddt, rows, ddt_tok_stride, d.H, 2),
+                          span(ddt_bias, 1, 0, d.H, 4), span(dA, 1, 0, d.H, 4), span(dD, 1, 0, d.H, 4),
+                          span(dstate_in, d.batch * d.H, SS, SS, 4), span(workspace, 1, 0, (int64_t)need, 1)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return M2_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(outs[i], outs[j])) return M2_ERR_ALIAS;
+    }
+    m2::BwdArgs a{};
+    a.x = (const uint16_t*)x; a.xs = x_tok_stride;
+    a.B = (const uint16_t*)B; a.C = (const uint16_t*)C; a.bcs = bc_tok_stride;
+    a.dt = (const uint16_t*)dt; a.dts = dt_tok_stride;
+    a.dy = (const uint16_t*)dy; a.dys = dy_tok_stride;
+    a.dt_bias = dt_bias; a.A = A; a.D = D; a.dt_min = dt_min; a.dt_max = dt_max;
+    a.state_in = state_in; a.dstate_out = dstate_out;
+    a.dx = (uint16_t*)dx; a.dxs = dx_tok_stride;
+    a.dB = (uint16_t*)dB; a.dC = (uint16_t*)dC; a.dbcs = dbc_tok_stride;
+    a.ddt = (uint16_t*)ddt; a.ddts = ddt_tok_stride;
+    a.ddt_bias = ddt_bias; a.dA = dA; a.dD = dD; a.dstate_in = dstate_in;
+    a.batch = d.batch; a.L = d.L; a.H = d.H; a.G = d.G;
+    a.ws = workspace;
+    return launched(m2::launch_ssd_scan_bwd(a, (hipStream_t)stream));
+}
+
 m2_status m2_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
     if (bytes == 0) return M2_OK;
     if (!dst || !src) return M2_ERR_NULL;

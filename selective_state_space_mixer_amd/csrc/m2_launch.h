@@ -72,6 +72,34 @@ DeviceShape device_shape();
 
 hipError_t launch_conv1d(const ConvArgs& a, hipStream_t s);
 hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s);
+
+// Backward of the scan (bf16 activations, headdim 64, d_state 64).  Arrays are bf16 bit patterns
+// with token strides in elements; ddt_bias, dA and dD are [H] fp32 and overwritten.
+struct BwdArgs {
+    const uint16_t* x; int64_t xs;
+    const uint16_t* B; const uint16_t* C; int64_t bcs;
+    const uint16_t* dt; int64_t dts;
+    const uint16_t* dy; int64_t dys;
+    const float* dt_bias; const float* A; const float* D;
+    float dt_min, dt_max;
+    const float* state_in; const float* dstate_out;
+    uint16_t* dx; int64_t dxs;
+    uint16_t* dB; uint16_t* dC; int64_t dbcs;
+    uint16_t* ddt; int64_t ddts;
+    float* ddt_bias; float* dA; float* dD; float* dstate_in;
+    int64_t batch, L;
+    int H, G;
+    void* ws;
+    // set by the launcher
+    int nch;
+    float* ws_es;     // [nch][batch*H][N][P] fp32: E_c, then the chunk's initial state
+    float* ws_fg;     // [nch][batch*H][N][P] fp32: F_c, then the adjoint of the chunk's end state
+    float* ws_lam;    // [nch][batch*H] summed log-decay of each chunk
+    float* ws_part;   // [3][batch*nch][H] per-chunk sums of dA, dD and dt_bias
+};
+bool ssd_bwd_supported(int P, int N, bool bf16);
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int H);
+hipError_t launch_ssd_scan_bwd(const BwdArgs& a, hipStream_t s);
 // total: tokens of a packed batch (L its longest sequence), or -1 for a padded one
 size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16,
                                 int64_t total);

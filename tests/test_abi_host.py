@@ -266,3 +266,35 @@ def test_fused_prefill_shapes_and_validation():
     assert call(dims(), dts=81) == m2.M2_ERR_UNSUPPORTED                       # odd dt token stride
     assert call(dims(), y=FAKE + 64) == m2.M2_ERR_ALIAS                         # y overlaps xbc
     assert call(dims(batch=1, seqlen=32768)) == m2.M2_ERR_WORKSPACE
+
+
+def test_scan_backward_shapes_and_validation():
+    """The scan's backward is built for bf16 headdim 64 / d_state 64: elsewhere it reports no workspace
+    and M2_ERR_UNSUPPORTED; argument, alignment, overlap and workspace errors come back before any
+    launch."""
+    lib = m2.lib()
+    assert m2.m2_ssd_scan_bwd_workspace(dims(batch=1, seqlen=32768)) > 0
+    for bad in (dict(d_state=128), dict(headdim=32), dict(io=m2.M2_F32)):
+        assert m2.m2_ssd_scan_bwd_workspace(dims(**bad)) == 0, bad
+    MB = 1 << 28
+
+    def call(d, x=FAKE, dx=FAKE + 5 * MB, dB=FAKE + 6 * MB, ws=FAKE + 9 * MB, wsb=1 << 40, dA=FAKE + 8 * MB,
+             xs=None, dt=FAKE + 3 * MB):
+        di = d.expand * d.d_model
+        H, GN = di // d.headdim, d.n_groups * d.d_state
+        return lib.m2_ssd_scan_bwd(ctypes.byref(d), x, xs or di, FAKE + 1 * MB, FAKE + 2 * MB, GN, dt, H,
+                                   FAKE + 4 * MB, FAKE + 4 * MB + 4096, None, 0.0, float("inf"), None,
+                                   FAKE + 10 * MB, di, None, dx, di, dB, FAKE + 7 * MB, GN, FAKE + 11 * MB, H,
+                                   dA - 8192, dA, dA + 8192, None, ws, wsb, None)
+    assert call(dims(d_state=128)) == m2.M2_ERR_UNSUPPORTED
+    assert call(dims(io=m2.M2_F32)) == m2.M2_ERR_UNSUPPORTED
+    assert call(dims(), x=None) == m2.M2_ERR_NULL
+    assert call(dims(), dA=0) == m2.M2_ERR_NULL
+    assert call(dims(), xs=8) == m2.M2_ERR_SHAPE                        # token stride below the row
+    assert call(dims(), x=FAKE + 8) == m2.M2_ERR_UNSUPPORTED            # x off a 16-byte boundary
+    assert call(dims(), dt=FAKE + 3 * MB + 1) == m2.M2_ERR_UNSUPPORTED  # dt off a bf16 boundary
+    assert call(dims(), dx=FAKE + 64) == m2.M2_ERR_ALIAS                 # dx overlaps x
+    assert call(dims(), dB=FAKE + 5 * MB + 128) == m2.M2_ERR_ALIAS       # dB overlaps dx
+    assert call(dims(), ws=FAKE + 6 * MB) == m2.M2_ERR_ALIAS             # workspace overlaps dB
+    assert call(dims(), ws=None) == m2.M2_ERR_WORKSPACE
+    assert call(dims(batch=1, seqlen=32768), wsb=1 << 20) == m2.M2_ERR_WORKSPACE

@@ -1,0 +1,154 @@
+"""GPU parity of the scan's backward (m2_ssd_scan_bwd) against the fp64 oracle's adjoint recurrence.
+
+The backward returns the gradients of sum(dy * y) + <dstate_out, state_out> for the scan of the
+Zamba2 mixer (article "Transformers 中 Zamba2 混合架构模型解析", §三, its training path).  Every case
+compares dx, dB, dC, d(raw dt), dt_bias, dA, dD and dstate_in with oracle.ssd_scan_bwd on the same
+seeded bf16 inputs, floored max-relative error <= 2e-2, and prints the errors it reaches:
+  - small shapes: a ragged last chunk, one whole chunk, one token, grouped heads, no D, no initial
+    state and no final adjoint, a dt clamp that binds at both bounds, and an empty prompt;
+  - the 2.7B mixer shape at 2 x 2048 tokens, every head;
+  - the 32768-token prompt in the launch configuration of the benchmark, on four sampled heads (a
+    second call with dy and dstate_out zero outside them gives dB and dC over those heads alone).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import selective_state_space_mixer_amd as m2
+    from gpu_util import dev, dev32, dims_of, host, nan_like
+
+TOL = 2e-2
+KEYS = ("dx", "dB", "dC", "ddt_raw", "ddt_bias", "dA", "dD", "dstate_in")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+
+
+def _split(d, inp):
+    x, b, c = inp.split()
+    lead = (d.batch, d.seqlen)
+    return (x.reshape(lead + (d.nheads, d.headdim)), b.reshape(lead + (d.n_groups, d.d_state)),
+            c.reshape(lead + (d.n_groups, d.d_state)))
+
+
+def run_bwd(d, x, b, c, dt_raw, dt_bias, A, D, state_in, dy, ds, dt_min=0.0, dt_max=float("inf")):
+    """The library's backward through the C ABI; every output starts as NaN so unwritten values show."""
+    dims = dims_of(d)
+    B, L, H, P, N, G = d.batch, d.seqlen, d.nheads, d.headdim, d.d_state, d.n_groups
+    out = {"dx": nan_like((B, L, H * P), "bf16"), "dB": nan_like((B, L, G * N), "bf16"),
+           "dC": nan_like((B, L, G * N), "bf16"), "ddt_raw": nan_like((B, L, H), "bf16")}
+    for k in ("ddt_bias", "dA", "dD"):
+        out[k] = torch.full((H,), float("nan"), device="cuda")
+    out["dstate_in"] = torch.full((B, H, P, N), float("nan"), device="cuda")
+    nws = m2.m2_ssd_scan_bwd_workspace(dims)
+    assert nws > 0
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    m2.m2_ssd_scan_bwd(dims, dev(x, "bf16"), dev(b, "bf16"), dev(c, "bf16"), dev(dt_raw, "bf16"), dev32(dt_bias),
+                       dev32(A), dev32(D), dev(dy, "bf16"), out["dx"], out["dB"], out["dC"], out["ddt_raw"],
+                       out["ddt_bias"], out["dA"], out["dD"], state_in=dev32(state_in), dstate_out=dev32(ds),
+                       dstate_in=out["dstate_in"], dt_min=dt_min, dt_max=dt_max, workspace=ws)
+    torch.cuda.synchronize()
+    res = {k: host(v) for k, v in out.items()}
+    res["dx"] = res["dx"].reshape(B, L, H, P)
+    res["dB"] = res["dB"].reshape(B, L, G, N)
+    res["dC"] = res["dC"].reshape(B, L, G, N)
+    return res
+
+
+def errors(got, ref, keys=KEYS):
+    return {k: oracle.max_rel_err(got[k], ref[k]) for k in keys}
+
+
+def report(tag, err):
+    print("%s: %s" % (tag, " ".join("%s %.2e" % kv for kv in err.items())))
+    assert max(err.values()) <= TOL, err
+
+
+SMALL = workloads.CONFIGS[2].dims.replace(d_model=256)   # 8 heads of 64 x 64, bf16
+CASES = [
+    ("ragged", dict(batch=2, seqlen=200), True, True, True, False),
+    ("one-chunk-no-state", dict(batch=1, seqlen=64), False, False, True, False),
+    ("one-token", dict(batch=2, seqlen=1), True, True, True, False),
+    ("groups2", dict(batch=2, seqlen=130, n_groups=2), True, True, True, False),
+    ("groups8", dict(batch=1, seqlen=100, n_groups=8), True, True, True, False),
+    ("no-D", dict(batch=1, seqlen=300), True, True, False, False),
+    ("clamp", dict(batch=2, seqlen=150), True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_scan_backward_small(case):
+    _need_gpu()
+    tag, over, cached, with_ds, with_D, clamp = case
+    d = SMALL.replace(**over)
+    inp = workloads.generate(d, 7100 + len(tag), cached)
+    x, b, c = _split(d, inp)
+    dy, ds = workloads.grad_inputs(d, 7200 + len(tag), with_ds)
+    D = inp.D if with_D else None
+    lo, hi = (0.03, 0.12) if clamp else (0.0, float("inf"))
+    if clamp:
+        sp = np.logaddexp(0.0, inp.dt_raw.astype(np.float64) + inp.dt_bias)
+        assert (sp < lo).sum() > 0 and (sp > hi).sum() > 0, "both clamp bounds must bind"
+    got = run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, D, inp.state0, dy, ds, lo, hi)
+    ref = oracle.ssd_scan_bwd(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, D, inp.state0, dy, ds, lo, hi)
+    report("backward %s %s" % (tag, over), errors(got, ref))
+
+
+def test_scan_backward_empty_prompt():
+    """seqlen 0: the final state's gradient passes to dstate_in unchanged; the parameter sums are zero."""
+    _need_gpu()
+    d = SMALL.replace(batch=2, seqlen=0)
+    rng = np.random.default_rng(3)
+    H, P, N = d.nheads, d.headdim, d.d_state
+    ds = rng.standard_normal((2, H, P, N)).astype(np.float32)
+    z = np.zeros((2, 0, H, P), np.float32)
+    zb = np.zeros((2, 0, 1, N), np.float32)
+    got = run_bwd(d, z, zb, zb, np.zeros((2, 0, H), np.float32), np.full(H, -3.0, np.float32),
+                  -np.ones(H, np.float32), np.ones(H, np.float32), None, z, ds)
+    assert np.array_equal(got["dstate_in"], ds.astype(np.float64))
+    for k in ("ddt_bias", "dA", "dD"):
+        assert np.array_equal(got[k], np.zeros(H)), k
+
+
+def test_scan_backward_2p7b_shape_every_head():
+    _need_gpu()
+    d = workloads.CONFIGS[2].dims.replace(batch=2, seqlen=2048)
+    inp = workloads.generate(d, 7301, True)
+    x, b, c = _split(d, inp)
+    dy, ds = workloads.grad_inputs(d, 7302)
+    got = run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds)
+    ref = oracle.ssd_scan_bwd(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds)
+    report("backward 2.7b 2x2048", errors(got, ref))
+
+
+def test_scan_backward_full_size_32k_sampled_heads():
+    """The 32768-token prompt (all 80 heads on the GPU, as the benchmark runs it); the oracle takes four
+    heads.  Per-head gradients are compared from the full call; dB and dC, sums over the heads, from a
+    second call whose dy and dstate_out are zero outside the sampled heads."""
+    _need_gpu()
+    d = workloads.CONFIGS[3].dims
+    inp = workloads.config_inputs(3)
+    x, b, c = _split(d, inp)
+    dy, ds = workloads.grad_inputs(d, 7401)
+    heads = [0, 27, 53, 79]
+    got = run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, None, dy, ds)
+    dy_m = np.zeros_like(dy)
+    dy_m[:, :, heads] = dy[:, :, heads]
+    ds_m = np.zeros_like(ds)
+    ds_m[:, heads] = ds[:, heads]
+    got_m = run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, None, dy_m, ds_m)
+    ref = oracle.ssd_scan_bwd(x[:, :, heads], b, c, inp.dt_raw[:, :, heads], inp.dt_bias[heads], inp.A[heads],
+                              inp.D[heads], None, dy[:, :, heads], ds[:, heads])
+    sel = {"dx": got["dx"][:, :, heads], "ddt_raw": got["ddt_raw"][:, :, heads], "ddt_bias": got["ddt_bias"][heads],
+           "dA": got["dA"][heads], "dD": got["dD"][heads], "dstate_in": got["dstate_in"][:, heads],
+           "dB": got_m["dB"], "dC": got_m["dC"]}
+    report("backward 32k, heads %s" % heads, errors(sel, ref))

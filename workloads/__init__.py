@@ -184,3 +184,16 @@ def norm_inputs(ntok: int, d_inner: int, seed: int, io: str):
     z = rng.standard_normal((ntok, d_inner), dtype=np.float32)
     w = (1.0 + 0.1 * rng.standard_normal(d_inner, dtype=np.float32)).astype(np.float32)
     return round_to(y, io), round_to(z, io), w
+
+
+def grad_inputs(dims: Dims, seed: int, with_state: bool = True):
+    """Upstream gradients for the scan's backward: dy shaped like the scan output [B, L, H, P] (~N(0,1),
+    rounded to the activation type) and, if with_state, the final state's gradient [B, H, P, N]
+    (~N(0, 0.1), fp32); else None."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dy = rng.standard_normal((dims.batch, dims.seqlen, dims.nheads, dims.headdim), dtype=np.float32)
+    ds = None
+    if with_state:
+        ds = (0.1 * rng.standard_normal((dims.batch, dims.nheads, dims.headdim, dims.d_state),
+                                        dtype=np.float32)).astype(np.float32)
+    return round_to(dy, dims.io), ds
