@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the oracle sample")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward"], default="all")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -64,6 +64,21 @@ def step_bytes(B, H, P, N, G, W, Cd):
     the new token, dt, y, parameters."""
     return (B * H * P * N * 4 * 2 + B * (W - 1) * Cd * 2 + B * Cd * 2 + B * Cd * 2 + B * H * 2 + B * H * P * 2
             + Cd * (W + 1) * 4 + 3 * H * 4)
+
+
+def bwd_bytes(B, L, H, P, N, G, with_state_in, with_dstate_out, with_dstate_in):
+    """Algorithmic HBM bytes of one m2_ssd_scan_bwd launch (bf16 activations): read x, B, C, dt and dy,
+    write dx, dB, dC and d(dt), the parameters and their gradients, and the states."""
+    b = B * L * 2 * (2 * (H * P + 2 * G * N + H) + H * P) + 3 * H * 4 + 3 * H * 4
+    return b + (B * H * P * N * 4) * (int(with_state_in) + int(with_dstate_out) + int(with_dstate_in))
+
+
+def bwd_flops(B, L, H):
+    """MFMA flops of one m2_ssd_scan_bwd launch at headdim 64 / d_state 64 as the kernels issue them
+    (16,384 per v_mfma_f32_16x16x32_bf16): per head and 64-token chunk 128 for the chunk's state and
+    adjoint contributions and 416 for the gradients, plus 32 per (sequence, group, chunk) for C.B."""
+    nch = (L + 63) // 64
+    return 16384 * (B * nch * H * (128 + 416))
 
 
 def time_events(torch, fns, steps, warmup):
@@ -100,7 +115,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _SCAN_SRC = ("ssd_scan.hip", "ssd_walk.hip", "ssd_common.h")
 KERNEL_SOURCES = {"ssd_scan": _SCAN_SRC, "conv1d": ("conv1d.hip",), "ssd_step": ("ssd_step.hip",),
                   "gated_rmsnorm": ("gated_norm.hip",), "ssd_scan_packed": _SCAN_SRC, "conv1d_packed": ("conv1d.hip",),
-                  "mixer_prefill": _SCAN_SRC + ("conv1d.hip",)}
+                  "mixer_prefill": _SCAN_SRC + ("conv1d.hip",), "ssd_scan_bwd": ("ssd_bwd.hip", "ssd_common.h")}
 
 
 def source_digest(kernel):
@@ -323,6 +338,50 @@ def bench_decode(torch, m2, workloads, args):
     }
 
 
+def bench_backward(torch, m2, workloads, args):
+    """The scan's backward (m2_ssd_scan_bwd) on the 32k prompt at the 2.7B mixer shape: the gradients of
+    a prefill's output and final state for all of its inputs (training path)."""
+    cfg = workloads.CONFIGS[3]
+    d = cfg.dims
+    inp = workloads.config_inputs(3)
+    B, L, H, P, N, G = d.batch, d.seqlen, d.nheads, d.headdim, d.d_state, d.n_groups
+    dims = m2.make_dims(B, L, d.d_model, d.expand, P, N, G, d.d_conv, d.chunk_size, d.io)
+    bf = torch.bfloat16
+    dy_np, ds_np = workloads.grad_inputs(d, 1005)
+    act = torch.from_numpy(inp.xbc).to("cuda", bf)
+    dt = torch.from_numpy(inp.dt_raw).to("cuda", bf)
+    dtb, A, D = (torch.from_numpy(a).cuda() for a in (inp.dt_bias, inp.A, inp.D))
+    dy = torch.from_numpy(dy_np.reshape(B, L, H * P)).to("cuda", bf)
+    ds = torch.from_numpy(ds_np).cuda()
+    del inp, dy_np, ds_np
+    xv, bv, cv = act[:, :, :H * P], act[:, :, H * P:H * P + G * N], act[:, :, H * P + G * N:]
+    dx = torch.empty((B, L, H * P), device="cuda", dtype=bf)
+    dBt = torch.empty((B, L, G * N), device="cuda", dtype=bf)
+    dCt = torch.empty((B, L, G * N), device="cuda", dtype=bf)
+    ddt = torch.empty((B, L, H), device="cuda", dtype=bf)
+    dtb_g, dA, dD = (torch.empty(H, device="cuda") for _ in range(3))
+    dsi = torch.empty((B, H, P, N), device="cuda")
+    ws = torch.empty(m2.m2_ssd_scan_bwd_workspace(dims), device="cuda", dtype=torch.uint8)
+
+    def bwd():
+        m2.m2_ssd_scan_bwd(dims, xv, bv, cv, dt, dtb, A, D, dy, dx, dBt, dCt, ddt, dtb_g,
+                           dA, dD, dstate_out=ds, dstate_in=dsi, workspace=ws)
+
+    (t,), _, _ = time_events(torch, [bwd], args.steps, args.warmup)
+    nb = bwd_bytes(B, L, H, P, N, G, False, True, True)
+    fl = bwd_flops(B, L, H)
+    r = roofline(nb, t, "ssd_scan_bwd")
+    return {"value": round(B * L / (t * 1e-3), 1), "unit": "tokens/s", "us": round(t * 1e3, 2), "bytes": nb,
+            "roofline": dict(r, kernel="ssd_scan_bwd"),
+            "mfma": {"flops": fl, "achieved_TFLOPs": round(fl / (t * 1e-3) / 1e12, 1),
+                     "peak_TFLOPs": 2500.0, "frac": round(fl / (t * 1e-3) / 2.5e15, 4)},
+            "workspace_bytes": ws.numel(),
+            "config": {"workload": "zamba2-2.7b scan backward, batch 1 x 32768 tokens (gradients of y and the final "
+                                   "state for x, B, C, dt, dt_bias, A, D and the initial state)",
+                       "batch": B, "seqlen": L, "nheads": H, "headdim": P, "d_state": N, "n_groups": G,
+                       "chunk": 64}}
+
+
 def copy_ceiling(torch, m2, mib=1024, reps=10):
     """GB/s (read + write bytes) of the library's streaming copy kernel over `mib` MiB: the attainable
     bandwidth reference beside the 8 TB/s vendor peak."""
@@ -447,6 +506,17 @@ def main():
             out["ms_per_step"] = round(dec["ms_per_step"], 4)
             out["config"] = dec["config"]
             out["roofline"] = out["decode"]["roofline"]
+    if args.only in ("all", "backward"):
+        bw = bench_backward(torch, m2, workloads, args)
+        print("scan backward: %.1f us, %.3e tok/s (%.0f GB/s algorithmic, %.0f MFMA TFLOP/s)" % (
+            bw["us"], bw["value"], bw["roofline"]["achieved"], bw["mfma"]["achieved_TFLOPs"]), file=sys.stderr,
+            flush=True)
+        out["backward"] = bw
+        if pre is None and dec is None:
+            out["value"] = bw["value"]
+            out["ms_per_step"] = round(bw["us"] / 1e3, 4)
+            out["config"] = bw["config"]
+            out["roofline"] = bw["roofline"]
     out["copy_ceiling_GBs"] = COPY_CEILING[0]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(workloads, args.cpu_seconds)

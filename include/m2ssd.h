@@ -328,7 +328,8 @@ size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims);
  * irrelevant; calls that may run at the same time need separate workspaces.
  * x, B, C, dy, dx, dB and dC must start on 16-byte boundaries with token strides that are multiples
  * of 16 bytes (else M2_ERR_UNSUPPORTED).  No output may overlap an input, another output or the
- * workspace (M2_ERR_ALIAS). */
+ * workspace (M2_ERR_ALIAS); overlap is judged on each array's byte range from its first to its last
+ * element, so dB and dC interleaved in one buffer count as overlapping: pass separate arrays. */
 m2_status m2_ssd_scan_bwd(const m2_dims* dims,
                           const void* x, int64_t x_tok_stride,
                           const void* B, const void* C, int64_t bc_tok_stride,

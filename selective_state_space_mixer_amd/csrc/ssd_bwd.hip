@@ -45,7 +45,8 @@ constexpr int Q = 64, P = 64, N = 64;
 constexpr int U = 8;               // 16-byte units per tile row (64 bf16)
 constexpr int RS = (U + 1) * 8;    // elements per LDS tile row (one unit of padding)
 constexpr int TE = Q * RS;         // elements per tile
-constexpr int THREADS = 256;
+constexpr int THREADS = 256;     // the per-chunk kernel: four waves
+constexpr int GTHREADS = 512;    // the gradient kernel: eight waves
 constexpr int PN = P * N;
 }  // namespace bwd
 
@@ -71,29 +72,32 @@ __device__ __forceinline__ float sum_over_li(float v) {
 __device__ __forceinline__ float lane_value(float v, int src) { return __shfl(v, src, 64); }
 
 // rows [0, 64) of a token-major bf16 array (`stride` elements between rows) starting at `base`,
-// 64 columns, into registers; rows at or past `rows` read as zero.  Each thread holds two 16-byte
-// units: unit u = threadIdx.x + 256 j is row u / 8, columns 8 (u % 8) .. +7.
-__device__ __forceinline__ void fetch_tile(uint4 (&v)[2], const uint16_t* base, int64_t stride, int rows) {
+// 64 columns, into registers of a block of NT threads; rows at or past `rows` read as zero.  Unit
+// u = threadIdx.x + NT j is row u / 8, columns 8 (u % 8) .. +7.
+template <int NT>
+__device__ __forceinline__ void fetch_tile(uint4 (&v)[512 / NT], const uint16_t* base, int64_t stride, int rows) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int u = (int)threadIdx.x + bwd::THREADS * j, r = u >> 3, c8 = u & 7;
+    for (int j = 0; j < 512 / NT; ++j) {
+        const int u = (int)threadIdx.x + NT * j, r = u >> 3, c8 = u & 7;
         v[j] = r < rows ? *reinterpret_cast<const uint4*>(base + (int64_t)r * stride + 8 * c8)
                         : make_uint4(0u, 0u, 0u, 0u);
     }
 }
-__device__ __forceinline__ void put_tile(uint16_t* tile, const uint4 (&v)[2]) {
+template <int NT>
+__device__ __forceinline__ void put_tile(uint16_t* tile, const uint4 (&v)[512 / NT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int u = (int)threadIdx.x + bwd::THREADS * j, r = u >> 3, c8 = u & 7;
+    for (int j = 0; j < 512 / NT; ++j) {
+        const int u = (int)threadIdx.x + NT * j, r = u >> 3, c8 = u & 7;
         *reinterpret_cast<uint4*>(tile + r * bwd::RS + 8 * c8) = v[j];
     }
 }
 
-// a 64 x 64 fp32 tile (contiguous rows of 64) into registers: unit u = threadIdx.x + 256 j is row u / 16,
-// columns 4 (u % 16) .. +3
-__device__ __forceinline__ void fetch_tile32(float4 (&v)[4], const float* base) {
+// a 64 x 64 fp32 tile (contiguous rows of 64) into registers: unit u = threadIdx.x + NT j is row
+// u / 16, columns 4 (u % 16) .. +3
+template <int NT>
+__device__ __forceinline__ void fetch_tile32(float4 (&v)[1024 / NT], const float* base) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = reinterpret_cast<const float4*>(base)[(int)threadIdx.x + bwd::THREADS * j];
+    for (int j = 0; j < 1024 / NT; ++j) v[j] = reinterpret_cast<const float4*>(base)[(int)threadIdx.x + NT * j];
 }
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
@@ -108,10 +112,11 @@ __device__ __forceinline__ void unpack4(float (&o)[4], uint2 v) {
     o[0] = lo_bf16(v.x); o[1] = hi_bf16(v.x); o[2] = lo_bf16(v.y); o[3] = hi_bf16(v.y);
 }
 // the fp32 tile of fetch_tile32 as bf16 hi and lo tiles
-__device__ __forceinline__ void put_tile_split(uint16_t* hi, uint16_t* lo, const float4 (&v)[4]) {
+template <int NT>
+__device__ __forceinline__ void put_tile_split(uint16_t* hi, uint16_t* lo, const float4 (&v)[1024 / NT]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int u = (int)threadIdx.x + bwd::THREADS * j, r = u >> 4, c4 = u & 15;
+    for (int j = 0; j < 1024 / NT; ++j) {
+        const int u = (int)threadIdx.x + NT * j, r = u >> 4, c4 = u & 15;
         const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint2 h2, l2;
         split4(h2, l2, f);
@@ -123,7 +128,8 @@ __device__ __forceinline__ void put_tile_split(uint16_t* hi, uint16_t* lo, const
 }  // namespace
 
 // ----------------------------------------------------------------------------------------------
-// 1. per chunk: E_c, F_c (stored [n][p] fp32) and the chunk's summed log-decay
+// 1. per chunk: E_c, F_c (stored [n][p] fp32) and the chunk's summed log-decay; a block takes every
+// gridDim.z-th head of its group
 
 __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_chunk_kernel(BwdArgs k)
 {
@@ -141,26 +147,28 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_chunk_kernel(BwdArgs k)
     const int64_t row0 = b * k.L + t0;
     {
         uint4 vb[2], vc[2];
-        fetch_tile(vb, k.B + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
-        fetch_tile(vc, k.C + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
-        put_tile(sB, vb);
-        put_tile(sC, vc);
+        fetch_tile<THREADS>(vb, k.B + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
+        fetch_tile<THREADS>(vc, k.C + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
+        put_tile<THREADS>(sB, vb);
+        put_tile<THREADS>(sC, vc);
     }
     uint4 vx[2], vy[2];
     auto fetch = [&](int h) __attribute__((always_inline)) {
-        fetch_tile(vx, k.x + row0 * k.xs + (int64_t)h * P, k.xs, rows);
-        fetch_tile(vy, k.dy + row0 * k.dys + (int64_t)h * P, k.dys, rows);
+        fetch_tile<THREADS>(vx, k.x + row0 * k.xs + (int64_t)h * P, k.xs, rows);
+        fetch_tile<THREADS>(vy, k.dy + row0 * k.dys + (int64_t)h * P, k.dys, rows);
     };
-    fetch(g * hpg);
-    for (int i = 0; i < hpg; ++i) {
+    // the group's heads blockIdx.z, blockIdx.z + gridDim.z, ...
+    const int hstep = gridDim.z;
+    if ((int)blockIdx.z < hpg) fetch(g * hpg + blockIdx.z);
+    for (int i = blockIdx.z; i < hpg; i += hstep) {
         const int h = g * hpg + i;
         __syncthreads();  // the previous head's tiles are no longer read
-        put_tile(sX, vx);
-        put_tile(sDY, vy);
+        put_tile<THREADS>(sX, vx);
+        put_tile<THREADS>(sDY, vy);
         const bool valid = lane < rows;
         const float raw = valid ? bits_to_f32(k.dt[(row0 + lane) * k.dts + h]) : 0.0f;
         __syncthreads();
-        if (i + 1 < hpg) fetch(h + 1);
+        if (i + hstep < hpg) fetch(h + hstep);
         const float dtv = valid ? dt_of(raw, k.dt_bias[h], k.dt_min, k.dt_max) : 0.0f;
         const float lam = wave_prefix_sum(dtv * k.A[h]);
         const float lamQ = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), 63));
@@ -216,36 +224,42 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_chunk_kernel(BwdArgs k)
 }
 
 // ----------------------------------------------------------------------------------------------
-// 2. the chain over chunks, four state entries ([n][p] order) per thread: forward for the initial
-// states, backward for the end adjoints, in place; the loads of a batch of chunks issued together
+// 2. the chain over chunks, four state entries ([n][p] order) per thread, in place: the first
+// PN / 1024 blocks of a sequence-head run forward for the initial states, the others backward for the
+// end adjoints; the loads of a batch of chunks are issued together
 
 __global__ __launch_bounds__(256) void ssd_bwd_chain_kernel(BwdArgs k)
 {
     using namespace bwd;
     constexpr int kBatch = 16;
+    constexpr int kHalf = PN / 1024;
     const int bh = blockIdx.y;
-    const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= PN) return;
+    const bool fwd = (int)blockIdx.x < kHalf;
+    const int i = (((int)blockIdx.x % kHalf) * 256 + threadIdx.x) * 4;
     const int n = i / P, p = i % P;
     const int BH = (int)k.batch * k.H;
     const int nch = k.nch;
+    float* const arr = fwd ? k.ws_es : k.ws_fg;
+    const float* const init = fwd ? k.state_in : k.dstate_out;
     float s[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] = k.state_in ? k.state_in[(int64_t)bh * PN + (p + e) * N + n] : 0.0f;
-    for (int c0 = 0; c0 < nch; c0 += kBatch) {
+    for (int e = 0; e < 4; ++e) s[e] = init ? init[(int64_t)bh * PN + (p + e) * N + n] : 0.0f;
+    // chunk order: 0 .. nch-1 forward, nch-1 .. 0 backward
+    for (int j0 = 0; j0 < nch; j0 += kBatch) {
         float4 v[kBatch];
         float lam[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int c = c0 + j < nch ? c0 + j : nch - 1;
-            v[j] = *reinterpret_cast<const float4*>(k.ws_es + ((int64_t)c * BH + bh) * PN + i);
+            const int jj = j0 + j < nch ? j0 + j : nch - 1;
+            const int c = fwd ? jj : nch - 1 - jj;
+            v[j] = *reinterpret_cast<const float4*>(arr + ((int64_t)c * BH + bh) * PN + i);
             lam[j] = k.ws_lam[(int64_t)c * BH + bh];
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int c = c0 + j;
-            if (c < nch) {
-                *reinterpret_cast<float4*>(k.ws_es + ((int64_t)c * BH + bh) * PN + i) = make_float4(s[0], s[1], s[2], s[3]);
+            if (j0 + j < nch) {
+                const int c = fwd ? j0 + j : nch - 1 - (j0 + j);
+                *reinterpret_cast<float4*>(arr + ((int64_t)c * BH + bh) * PN + i) = make_float4(s[0], s[1], s[2], s[3]);
                 const float d = fast_exp(lam[j]);
                 s[0] = d * s[0] + v[j].x;
                 s[1] = d * s[1] + v[j].y;
@@ -254,101 +268,83 @@ __global__ __launch_bounds__(256) void ssd_bwd_chain_kernel(BwdArgs k)
             }
         }
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] = k.dstate_out ? k.dstate_out[(int64_t)bh * PN + (p + e) * N + n] : 0.0f;
-    for (int c0 = nch - 1; c0 >= 0; c0 -= kBatch) {
-        float4 v[kBatch];
-        float lam[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int c = c0 - j >= 0 ? c0 - j : 0;
-            v[j] = *reinterpret_cast<const float4*>(k.ws_fg + ((int64_t)c * BH + bh) * PN + i);
-            lam[j] = k.ws_lam[(int64_t)c * BH + bh];
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int c = c0 - j;
-            if (c >= 0) {
-                *reinterpret_cast<float4*>(k.ws_fg + ((int64_t)c * BH + bh) * PN + i) = make_float4(s[0], s[1], s[2], s[3]);
-                const float d = fast_exp(lam[j]);
-                s[0] = d * s[0] + v[j].x;
-                s[1] = d * s[1] + v[j].y;
-                s[2] = d * s[2] + v[j].z;
-                s[3] = d * s[3] + v[j].w;
-            }
-        }
-    }
-    if (k.dstate_in) {
+    if (!fwd && k.dstate_in) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) k.dstate_in[(int64_t)bh * PN + (p + e) * N + n] = s[e];
     }
 }
 
 // ----------------------------------------------------------------------------------------------
-// 3. the gradients of one (sequence, group, chunk): four waves on one head at a time; wave w owns
-// output rows 16w .. 16w+15 of every 64 x 64 product
+// 3. the gradients of one (sequence, group, chunk): eight waves on one head at a time; wave w owns
+// output rows 16 rb .. 16 rb + 15 (rb = w % 4) and column tiles 2 ch, 2 ch + 1 (ch = w / 4) of every
+// 64 x 64 product
 
-__global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_grad_kernel(BwdArgs k)
+__global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
 {
     using namespace bwd;
+    constexpr int NT = GTHREADS;
     __shared__ __attribute__((aligned(16))) uint16_t sB[TE], sC[TE], sX[TE], sDY[TE];
     __shared__ __attribute__((aligned(16))) uint16_t sS0[TE], sS0l[TE], sGE[TE], sGEl[TE];  // [n][p] hi, lo
-    __shared__ __attribute__((aligned(16))) uint16_t sWh[TE], sWl[TE], sVh[TE], sVl[TE];  // W^T, V^T: [s][t]
-    __shared__ float rRow[Q], rCol[4][Q], rM0[4][Q], rQ[4][Q], rDd[4][Q], rQ0[4], rD[4];
+    __shared__ __attribute__((aligned(16))) uint16_t sWh[TE], sWl[TE], sVh[TE], sVl[TE];    // W^T, V^T: [s][t]
+    // partial sums: row sums of M per column half, and per row band the column sums of M, m0, q and
+    // x . dxr; <Ge, S0> and the diagonal of dy.x per wave
+    __shared__ float rRow[2][Q], rCol[4][Q], rM0[4][Q], rQ[4][Q], rDd[4][Q], rQ0[8], rD[8];
     const int c = blockIdx.x, bg = blockIdx.y;
     const int64_t b = bg / k.G;
     const int g = bg % k.G;
     const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rb = w & 3, ch = w >> 2;
     const int hpg = k.H / k.G;
     const int BH = (int)k.batch * k.H;
     const int64_t t0 = (int64_t)c * Q;
     const int rows = (int)(k.L - t0 < Q ? k.L - t0 : Q);
     const int64_t row0 = b * k.L + t0;
     {
-        uint4 vb[2], vc[2];
-        fetch_tile(vb, k.B + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
-        fetch_tile(vc, k.C + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
-        put_tile(sB, vb);
-        put_tile(sC, vc);
+        uint4 vb[1], vc[1];
+        fetch_tile<NT>(vb, k.B + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
+        fetch_tile<NT>(vc, k.C + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
+        put_tile<NT>(sB, vb);
+        put_tile<NT>(sC, vc);
     }
-    uint4 vx[2], vy[2];
-    float4 vs[4], vg[4];
+    uint4 vx[1], vy[1];
+    float4 vs[2], vg[2];
     auto fetch = [&](int h) __attribute__((always_inline)) {
         const int64_t so = ((int64_t)c * BH + b * k.H + h) * PN;
-        fetch_tile(vx, k.x + row0 * k.xs + (int64_t)h * P, k.xs, rows);
-        fetch_tile(vy, k.dy + row0 * k.dys + (int64_t)h * P, k.dys, rows);
-        fetch_tile32(vs, k.ws_es + so);
-        fetch_tile32(vg, k.ws_fg + so);
+        fetch_tile<NT>(vx, k.x + row0 * k.xs + (int64_t)h * P, k.xs, rows);
+        fetch_tile<NT>(vy, k.dy + row0 * k.dys + (int64_t)h * P, k.dys, rows);
+        fetch_tile32<NT>(vs, k.ws_es + so);
+        fetch_tile32<NT>(vg, k.ws_fg + so);
     };
     fetch(g * hpg);
     __syncthreads();
-    // C.B of the chunk (every head of the group shares it): rows t = 16w + 4q + r, columns s = 16 sb + li
-    f32x4 cb[4];
+    // C.B of the chunk (every head of the group shares it): rows t = 16 rb + 4q + r, columns
+    // s = 16 (2 ch + j) + li
+    f32x4 cb[2];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) cb[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < N; kb += 32) {
-        const Frag<bf16_t> a = frag_row<bf16_t, U>(sC, 16 * w + li, kb, N, q);
+        const Frag<bf16_t> a = frag_row<bf16_t, U>(sC, 16 * rb + li, kb, N, q);
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) mfma(cb[sb], a, frag_row<bf16_t, U>(sB, 16 * sb + li, kb, N, q));
+        for (int j = 0; j < 2; ++j) mfma(cb[j], a, frag_row<bf16_t, U>(sB, 16 * (2 * ch + j) + li, kb, N, q));
     }
-    // dB^T and dC^T of the chunk, summed over the group's heads: rows n = 16w + 4q + r, columns
-    // s (t) = 16 sb + li
-    f32x4 dBa[4], dCa[4];
+    // dB^T and dC^T of the chunk, summed over the group's heads: rows n = 16 rb + 4q + r, columns
+    // s (t) = 16 (2 ch + j) + li
+    f32x4 dBa[2], dCa[2];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        dBa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dCa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) {
+        dBa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dCa[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     for (int i = 0; i < hpg; ++i) {
         const int h = g * hpg + i;
         __syncthreads();  // the previous head is done with the tiles and the partial sums
-        put_tile(sX, vx);
-        put_tile(sDY, vy);
-        put_tile_split(sS0, sS0l, vs);
-        put_tile_split(sGE, sGEl, vg);
+        put_tile<NT>(sX, vx);
+        put_tile<NT>(sDY, vy);
+        put_tile_split<NT>(sS0, sS0l, vs);
+        put_tile_split<NT>(sGE, sGEl, vg);
         const bool valid = lane < rows;
         const float raw = valid ? bits_to_f32(k.dt[(row0 + lane) * k.dts + h]) : 0.0f;
         __syncthreads();
@@ -362,59 +358,58 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_grad_kernel(BwdArgs k)
         const float eQ = fast_exp(lamQ - lam);  // e^(LamQ - Lam_s)
         const float el = fast_exp(lam);         // e^(Lam_t)
 
-        // ---- dy.x: rows t = 16w + 4q + r, columns s = 16 sb + li
-        f32x4 dx_[4];
+        // ---- dy.x: rows t = 16 rb + 4q + r, columns s
+        f32x4 dx_[2];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) dx_[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+        for (int j = 0; j < 2; ++j) dx_[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
         for (int kb = 0; kb < P; kb += 32) {
-            const Frag<bf16_t> a = frag_row<bf16_t, U>(sDY, 16 * w + li, kb, P, q);
+            const Frag<bf16_t> a = frag_row<bf16_t, U>(sDY, 16 * rb + li, kb, P, q);
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) mfma(dx_[sb], a, frag_row<bf16_t, U>(sX, 16 * sb + li, kb, P, q));
+            for (int j = 0; j < 2; ++j) mfma(dx_[j], a, frag_row<bf16_t, U>(sX, 16 * (2 * ch + j) + li, kb, P, q));
         }
         // ---- W = L (C.B), V = L dt_s (dy.x), M = W dt_s (dy.x); row and column sums of M
         float lt[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lt[r] = lane_value(lam, 16 * w + 4 * q + r);
+        for (int r = 0; r < 4; ++r) lt[r] = lane_value(lam, 16 * rb + 4 * q + r);
         float rsum[4] = {0.f, 0.f, 0.f, 0.f};
         float dpart = 0.0f;
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            const int s = 16 * sb + li;
+        for (int j = 0; j < 2; ++j) {
+            const int s = 16 * (2 * ch + j) + li;
             const float ls = lane_value(lam, s), ds = lane_value(dtv, s);
             float wv[4], vv[4], csum = 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * w + 4 * q + r;
+                const int t = 16 * rb + 4 * q + r;
                 const float L = t >= s ? fast_exp(lt[r] - ls) : 0.0f;
-                wv[r] = cb[sb][r] * L;
-                vv[r] = dx_[sb][r] * ds * L;
-                const float m = wv[r] * ds * dx_[sb][r];
+                wv[r] = cb[j][r] * L;
+                vv[r] = dx_[j][r] * ds * L;
+                const float m = wv[r] * ds * dx_[j][r];
                 rsum[r] += m;
                 csum += m;
-                if (t == s) dpart += dx_[sb][r];
+                if (t == s) dpart += dx_[j][r];
             }
             uint2 hi, lo;
             split4(hi, lo, wv);
-            *reinterpret_cast<uint2*>(sWh + s * RS + 16 * w + 4 * q) = hi;
-            *reinterpret_cast<uint2*>(sWl + s * RS + 16 * w + 4 * q) = lo;
+            *reinterpret_cast<uint2*>(sWh + s * RS + 16 * rb + 4 * q) = hi;
+            *reinterpret_cast<uint2*>(sWl + s * RS + 16 * rb + 4 * q) = lo;
             split4(hi, lo, vv);
-            *reinterpret_cast<uint2*>(sVh + s * RS + 16 * w + 4 * q) = hi;
-            *reinterpret_cast<uint2*>(sVl + s * RS + 16 * w + 4 * q) = lo;
+            *reinterpret_cast<uint2*>(sVh + s * RS + 16 * rb + 4 * q) = hi;
+            *reinterpret_cast<uint2*>(sVl + s * RS + 16 * rb + 4 * q) = lo;
             csum = sum_over_q(csum);
-            if (q == 0) rCol[w][s] = csum;
+            if (q == 0) rCol[rb][s] = csum;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float v = sum_over_li(rsum[r]);
-            if (li == 0) rRow[16 * w + 4 * q + r] = v;
+            if (li == 0) rRow[ch][16 * rb + 4 * q + r] = v;
         }
         dpart = wave_sum(dpart);
-        // <Ge, S0> over rows n = 16w .. 16w+15 of the transposed states
+        // <Ge, S0> over rows n = 8w .. 8w+7 of the transposed states, eight columns per lane
         float g0 = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int o = (16 * w + li) * RS + 16 * q + 8 * u;
+        {
+            const int o = (8 * w + (lane >> 3)) * RS + 8 * (lane & 7);
             const uint4 a = *reinterpret_cast<const uint4*>(sGE + o), al = *reinterpret_cast<const uint4*>(sGEl + o);
             const uint4 bb = *reinterpret_cast<const uint4*>(sS0 + o), bl = *reinterpret_cast<const uint4*>(sS0l + o);
             const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, alw[4] = {al.x, al.y, al.z, al.w};
@@ -432,136 +427,136 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_grad_kernel(BwdArgs k)
         }
         __syncthreads();  // W^T and V^T are in LDS
 
-        // ---- dxr^T[p][s]: rows p = 16w + 4q + r, columns s = 16 sb + li
-        f32x4 xr[4];
+        // ---- dxr^T[p][s]: rows p = 16 rb + 4q + r, columns s = 16 (2 ch + j) + li
+        f32x4 xr[2];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) xr[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+        for (int j = 0; j < 2; ++j) xr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
         for (int kb = 0; kb < N; kb += 32) {  // Ge B_s (k = n)
-            const Frag<bf16_t> a = frag_col<bf16_t, U>(sGE, kb, N, 16 * w, q, li);
-            const Frag<bf16_t> al = frag_col<bf16_t, U>(sGEl, kb, N, 16 * w, q, li);
+            const Frag<bf16_t> a = frag_col<bf16_t, U>(sGE, kb, N, 16 * rb, q, li);
+            const Frag<bf16_t> al = frag_col<bf16_t, U>(sGEl, kb, N, 16 * rb, q, li);
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const Frag<bf16_t> bf = frag_row<bf16_t, U>(sB, 16 * sb + li, kb, N, q);
-                mfma(xr[sb], a, bf);
-                mfma(xr[sb], al, bf);
+            for (int j = 0; j < 2; ++j) {
+                const Frag<bf16_t> bf = frag_row<bf16_t, U>(sB, 16 * (2 * ch + j) + li, kb, N, q);
+                mfma(xr[j], a, bf);
+                mfma(xr[j], al, bf);
             }
         }
-        float xs4[4][4], dy4[4][4];  // x[s][p] and dy[s][p] at this lane's (p, s) positions
+        float xs4[2][4], dy4[2][4];  // x[s][p] and dy[s][p] at this lane's (p, s) positions
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            const int s = 16 * sb + li;
+        for (int j = 0; j < 2; ++j) {
+            const int s = 16 * (2 * ch + j) + li;
             const float e = lane_value(eQ, s), ds = lane_value(dtv, s);
-            unpack4(xs4[sb], *reinterpret_cast<const uint2*>(sX + s * RS + 16 * w + 4 * q));
-            unpack4(dy4[sb], *reinterpret_cast<const uint2*>(sDY + s * RS + 16 * w + 4 * q));
+            unpack4(xs4[j], *reinterpret_cast<const uint2*>(sX + s * RS + 16 * rb + 4 * q));
+            unpack4(dy4[j], *reinterpret_cast<const uint2*>(sDY + s * RS + 16 * rb + 4 * q));
             float qp = 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                xr[sb][r] *= e;
-                qp += xs4[sb][r] * xr[sb][r];
+                xr[j][r] *= e;
+                qp += xs4[j][r] * xr[j][r];
             }
             qp = sum_over_q(qp);
-            if (q == 0) rQ[w][s] = qp * ds;
+            if (q == 0) rQ[rb][s] = qp * ds;
         }
-#pragma unroll
+#pragma unroll 1
         for (int kb = 0; kb < Q; kb += 32) {  // sum_t W_ts dy_t (k = t)
-            const Frag<bf16_t> a = frag_col<bf16_t, U>(sDY, kb, Q, 16 * w, q, li);
+            const Frag<bf16_t> a = frag_col<bf16_t, U>(sDY, kb, Q, 16 * rb, q, li);
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                mfma(xr[sb], a, frag_row<bf16_t, U>(sWh, 16 * sb + li, kb, Q, q));
-                mfma(xr[sb], a, frag_row<bf16_t, U>(sWl, 16 * sb + li, kb, Q, q));
+            for (int j = 0; j < 2; ++j) {
+                mfma(xr[j], a, frag_row<bf16_t, U>(sWh, 16 * (2 * ch + j) + li, kb, Q, q));
+                mfma(xr[j], a, frag_row<bf16_t, U>(sWl, 16 * (2 * ch + j) + li, kb, Q, q));
             }
         }
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            const int s = 16 * sb + li;
+        for (int j = 0; j < 2; ++j) {
+            const int s = 16 * (2 * ch + j) + li;
             const float ds = lane_value(dtv, s);
             float dd = 0.0f, o[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                dd += xs4[sb][r] * xr[sb][r];
-                o[r] = ds * xr[sb][r] + D_h * dy4[sb][r];
+                dd += xs4[j][r] * xr[j][r];
+                o[r] = ds * xr[j][r] + D_h * dy4[j][r];
             }
             dd = sum_over_q(dd);
-            if (q == 0) rDd[w][s] = dd;
+            if (q == 0) rDd[rb][s] = dd;
             if (s < rows)
-                *reinterpret_cast<uint2*>(k.dx + (row0 + s) * k.dxs + (int64_t)h * P + 16 * w + 4 * q) =
+                *reinterpret_cast<uint2*>(k.dx + (row0 + s) * k.dxs + (int64_t)h * P + 16 * rb + 4 * q) =
                     pack4(o[0], o[1], o[2], o[3]);
         }
 
         // ---- dB^T[n][s] of this head: dt_s e^(LamQ - Lam_s) Ge^T x_s + sum_t V_ts C_t
-        f32x4 acc[4];
+        f32x4 acc[2];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
         for (int kb = 0; kb < P; kb += 32) {  // k = p
-            const Frag<bf16_t> a = frag_row<bf16_t, U>(sGE, 16 * w + li, kb, P, q);
-            const Frag<bf16_t> al = frag_row<bf16_t, U>(sGEl, 16 * w + li, kb, P, q);
+            const Frag<bf16_t> a = frag_row<bf16_t, U>(sGE, 16 * rb + li, kb, P, q);
+            const Frag<bf16_t> al = frag_row<bf16_t, U>(sGEl, 16 * rb + li, kb, P, q);
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const Frag<bf16_t> bx = frag_row<bf16_t, U>(sX, 16 * sb + li, kb, P, q);
-                mfma(acc[sb], a, bx);
-                mfma(acc[sb], al, bx);
+            for (int j = 0; j < 2; ++j) {
+                const Frag<bf16_t> bx = frag_row<bf16_t, U>(sX, 16 * (2 * ch + j) + li, kb, P, q);
+                mfma(acc[j], a, bx);
+                mfma(acc[j], al, bx);
             }
         }
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            const int s = 16 * sb + li;
+        for (int j = 0; j < 2; ++j) {
+            const int s = 16 * (2 * ch + j) + li;
             const float f = lane_value(eQ, s) * lane_value(dtv, s);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[sb][r] *= f;
+            for (int r = 0; r < 4; ++r) acc[j][r] *= f;
         }
-#pragma unroll
+#pragma unroll 1
         for (int kb = 0; kb < Q; kb += 32) {  // k = t
-            const Frag<bf16_t> a = frag_col<bf16_t, U>(sC, kb, Q, 16 * w, q, li);
+            const Frag<bf16_t> a = frag_col<bf16_t, U>(sC, kb, Q, 16 * rb, q, li);
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                mfma(acc[sb], a, frag_row<bf16_t, U>(sVh, 16 * sb + li, kb, Q, q));
-                mfma(acc[sb], a, frag_row<bf16_t, U>(sVl, 16 * sb + li, kb, Q, q));
+            for (int j = 0; j < 2; ++j) {
+                mfma(acc[j], a, frag_row<bf16_t, U>(sVh, 16 * (2 * ch + j) + li, kb, Q, q));
+                mfma(acc[j], a, frag_row<bf16_t, U>(sVl, 16 * (2 * ch + j) + li, kb, Q, q));
             }
         }
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) dBa[sb] += acc[sb];
+        for (int j = 0; j < 2; ++j) dBa[j] += acc[j];
 
         // ---- dC^T[n][t] of this head: e^(Lam_t) S0^T dy_t + sum_s V_ts B_s
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
         for (int kb = 0; kb < P; kb += 32) {  // k = p
-            const Frag<bf16_t> a = frag_row<bf16_t, U>(sS0, 16 * w + li, kb, P, q);
-            const Frag<bf16_t> al = frag_row<bf16_t, U>(sS0l, 16 * w + li, kb, P, q);
+            const Frag<bf16_t> a = frag_row<bf16_t, U>(sS0, 16 * rb + li, kb, P, q);
+            const Frag<bf16_t> al = frag_row<bf16_t, U>(sS0l, 16 * rb + li, kb, P, q);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const Frag<bf16_t> bd = frag_row<bf16_t, U>(sDY, 16 * tb + li, kb, P, q);
-                mfma(acc[tb], a, bd);
-                mfma(acc[tb], al, bd);
+            for (int j = 0; j < 2; ++j) {
+                const Frag<bf16_t> bd = frag_row<bf16_t, U>(sDY, 16 * (2 * ch + j) + li, kb, P, q);
+                mfma(acc[j], a, bd);
+                mfma(acc[j], al, bd);
             }
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const int t = 16 * tb + li;
+        for (int j = 0; j < 2; ++j) {
+            const int t = 16 * (2 * ch + j) + li;
             const float f = lane_value(el, t);
             float c4[4], m0 = 0.0f;
-            unpack4(c4, *reinterpret_cast<const uint2*>(sC + t * RS + 16 * w + 4 * q));
+            unpack4(c4, *reinterpret_cast<const uint2*>(sC + t * RS + 16 * rb + 4 * q));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                acc[tb][r] *= f;
-                m0 += c4[r] * acc[tb][r];
+                acc[j][r] *= f;
+                m0 += c4[r] * acc[j][r];
             }
             m0 = sum_over_q(m0);
-            if (q == 0) rM0[w][t] = m0;
+            if (q == 0) rM0[rb][t] = m0;
         }
-#pragma unroll
+#pragma unroll 1
         for (int kb = 0; kb < Q; kb += 32) {  // k = s
-            const Frag<bf16_t> a = frag_col<bf16_t, U>(sB, kb, Q, 16 * w, q, li);
+            const Frag<bf16_t> a = frag_col<bf16_t, U>(sB, kb, Q, 16 * rb, q, li);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                mfma(acc[tb], a, frag_col<bf16_t, U>(sVh, kb, Q, 16 * tb, q, li));
-                mfma(acc[tb], a, frag_col<bf16_t, U>(sVl, kb, Q, 16 * tb, q, li));
+            for (int j = 0; j < 2; ++j) {
+                mfma(acc[j], a, frag_col<bf16_t, U>(sVh, kb, Q, 16 * (2 * ch + j), q, li));
+                mfma(acc[j], a, frag_col<bf16_t, U>(sVl, kb, Q, 16 * (2 * ch + j), q, li));
             }
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) dCa[tb] += acc[tb];
+        for (int j = 0; j < 2; ++j) dCa[j] += acc[j];
         __syncthreads();  // the partial sums are in LDS
 
         // ---- d(Lam), d(dt), and the head's dA, dD, dt_bias sums (wave 0, token `lane`)
@@ -570,9 +565,15 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_grad_kernel(BwdArgs k)
             const float m0 = rM0[0][lane] + rM0[1][lane] + rM0[2][lane] + rM0[3][lane];
             const float qv = rQ[0][lane] + rQ[1][lane] + rQ[2][lane] + rQ[3][lane];
             const float dd = rDd[0][lane] + rDd[1][lane] + rDd[2][lane] + rDd[3][lane];
+            float q0s = 0.0f, dsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                q0s += rQ0[j];
+                dsum += rD[j];
+            }
             const float qsum = wave_sum(qv);
-            const float q0 = fast_exp(lamQ) * (rQ0[0] + rQ0[1] + rQ0[2] + rQ0[3]);
-            const float dlam = rRow[lane] - colsum + m0 - qv + (lane == Q - 1 ? q0 + qsum : 0.0f);
+            const float q0 = fast_exp(lamQ) * q0s;
+            const float dlam = rRow[0][lane] + rRow[1][lane] - colsum + m0 - qv + (lane == Q - 1 ? q0 + qsum : 0.0f);
             const float pre = wave_prefix_sum(dlam);
             const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pre), 63));
             const float R = tot - pre + dlam;  // sum of dLam over tokens lane .. 63
@@ -588,39 +589,51 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_grad_kernel(BwdArgs k)
                 const int64_t pr = (b * k.nch + c) * k.H + h;
                 const int64_t stride = k.batch * k.nch * k.H;
                 k.ws_part[pr] = dA_part;
-                k.ws_part[stride + pr] = rD[0] + rD[1] + rD[2] + rD[3];
+                k.ws_part[stride + pr] = dsum;
                 k.ws_part[2 * stride + pr] = db_part;
             }
         }
     }
-    // dB, dC rows of the chunk: row s, columns n = 16w + 4q .. +3
+    // dB, dC rows of the chunk: row s, columns n = 16 rb + 4q .. +3
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        const int s = 16 * sb + li;
+    for (int j = 0; j < 2; ++j) {
+        const int s = 16 * (2 * ch + j) + li;
         if (s < rows) {
-            const int64_t o = (row0 + s) * k.dbcs + (int64_t)g * N + 16 * w + 4 * q;
-            *reinterpret_cast<uint2*>(k.dB + o) = pack4(dBa[sb][0], dBa[sb][1], dBa[sb][2], dBa[sb][3]);
-            *reinterpret_cast<uint2*>(k.dC + o) = pack4(dCa[sb][0], dCa[sb][1], dCa[sb][2], dCa[sb][3]);
+            const int64_t o = (row0 + s) * k.dbcs + (int64_t)g * N + 16 * rb + 4 * q;
+            *reinterpret_cast<uint2*>(k.dB + o) = pack4(dBa[j][0], dBa[j][1], dBa[j][2], dBa[j][3]);
+            *reinterpret_cast<uint2*>(k.dC + o) = pack4(dCa[j][0], dCa[j][1], dCa[j][2], dCa[j][3]);
         }
     }
 }
 
 // ----------------------------------------------------------------------------------------------
-// 4. dA, dD and dt_bias: the per-(sequence, chunk) sums added up per head
+// 4. dA, dD and dt_bias: the per-(sequence, chunk) sums of one head (a block), added up
 
 __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs k)
 {
+    __shared__ float red[3][4];
+    const int h = blockIdx.x;
     const int64_t rows = k.batch * k.nch, stride = rows * k.H;
-    for (int h = threadIdx.x; h < k.H; h += 256) {
-        float a = 0.0f, d = 0.0f, bi = 0.0f;
-        for (int64_t r = 0; r < rows; ++r) {
-            a += k.ws_part[r * k.H + h];
-            d += k.ws_part[stride + r * k.H + h];
-            bi += k.ws_part[2 * stride + r * k.H + h];
-        }
-        k.dA[h] = a;
-        k.dD[h] = d;
-        k.ddt_bias[h] = bi;
+    float a = 0.0f, d = 0.0f, bi = 0.0f;
+    for (int64_t r = threadIdx.x; r < rows; r += 256) {
+        a += k.ws_part[r * k.H + h];
+        d += k.ws_part[stride + r * k.H + h];
+        bi += k.ws_part[2 * stride + r * k.H + h];
+    }
+    a = wave_sum(a);
+    d = wave_sum(d);
+    bi = wave_sum(bi);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][w] = a;
+        red[1][w] = d;
+        red[2][w] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        k.dA[h] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+        k.dD[h] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+        k.ddt_bias[h] = red[2][0] + red[2][1] + red[2][2] + red[2][3];
     }
 }
 
@@ -659,20 +672,23 @@ hipError_t launch_ssd_scan_bwd(const BwdArgs& a_in, hipStream_t s) {
     a.nch = (int)((a.L + bwd::Q - 1) / bwd::Q);
     hipError_t e = hipSuccess;
     if (a.nch > 0 && a.batch > 0) {
-        const dim3 grid((unsigned)a.nch, (unsigned)(a.batch * a.G));
+        // the group's heads over up to four blocks, so that the launch has several blocks per CU
+        const int hpg = a.H / a.G;
+        const int hsplit = hpg < 4 ? hpg : 4;
+        const dim3 grid((unsigned)a.nch, (unsigned)(a.batch * a.G), (unsigned)hsplit);
         e = launch_kernel(ssd_bwd_chunk_kernel, grid, dim3(bwd::THREADS), 0, s, a);
         if (e != hipSuccess) return e;
     }
     if (a.batch > 0) {
-        e = launch_kernel(ssd_bwd_chain_kernel, dim3(bwd::PN / 1024, (unsigned)(a.batch * a.H)), dim3(256), 0, s, a);
+        e = launch_kernel(ssd_bwd_chain_kernel, dim3(2 * bwd::PN / 1024, (unsigned)(a.batch * a.H)), dim3(256), 0, s, a);
         if (e != hipSuccess) return e;
     }
     if (a.nch > 0 && a.batch > 0) {
         const dim3 grid((unsigned)a.nch, (unsigned)(a.batch * a.G));
-        e = launch_kernel(ssd_bwd_grad_kernel, grid, dim3(bwd::THREADS), 0, s, a);
+        e = launch_kernel(ssd_bwd_grad_kernel, grid, dim3(bwd::GTHREADS), 0, s, a);
         if (e != hipSuccess) return e;
     }
-    return launch_kernel(ssd_bwd_reduce_kernel, dim3(1), dim3(256), 0, s, a);
+    return launch_kernel(ssd_bwd_reduce_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
 }
 
 }  // namespace m2
