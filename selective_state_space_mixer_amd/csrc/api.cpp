@@ -405,7 +405,7 @@ m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stri
 size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims) {
     Derived d;
     if (derive(dims, d) != M2_OK || !m2::ssd_bwd_supported(d.P, d.N, d.bf16)) return 0;
-    return m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H);
+    return m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H, d.G);
 }
 
 m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B, const void* C,
@@ -437,7 +437,7 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
         return M2_ERR_UNSUPPORTED;
     if (((uintptr_t)state_in & 3u) || ((uintptr_t)dstate_out & 3u) || ((uintptr_t)dstate_in & 3u))
         return M2_ERR_UNSUPPORTED;
-    const size_t need = m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H);
+    const size_t need = m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H, d.G);
     if (!workspace || workspace_bytes < need) return M2_ERR_WORKSPACE;
     const int64_t SS = (int64_t)d.P * d.N;
     const Range ins[] = {span(x, rows, x_tok_stride, d.d_inner, 2), span(B, rows, bc_tok_stride, GN, 2),

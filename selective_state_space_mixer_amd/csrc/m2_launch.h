@@ -91,14 +91,18 @@ struct BwdArgs {
     int H, G;
     void* ws;
     // set by the launcher
-    int nch;
-    float* ws_es;     // [nch][batch*H][N][P] fp32: E_c, then the chunk's initial state
-    float* ws_fg;     // [nch][batch*H][N][P] fp32: F_c, then the adjoint of the chunk's end state
-    float* ws_lam;    // [nch][batch*H] summed log-decay of each chunk
-    float* ws_part;   // [3][batch*nch][H] per-chunk sums of dA, dD and dt_bias
+    int nch, nseg, cps;  // 64-token chunks, segments of the walks, chunks per segment
+    float* ws_es;      // [nch][batch*H][N][P] fp32: each chunk's initial state from its segment's start
+    float* ws_fg;      // [nch][batch*H][N][P] fp32: the adjoint of each chunk's end state from its segment's end
+    float* ws_lamb;    // [nch][batch*H] summed log-decay of the segment before the chunk
+    float* ws_lame;    // [nch][batch*H] summed log-decay of the segment after the chunk
+    float* ws_sege;    // [nseg][batch*H][N][P]: segment end states, then the true segment initial states
+    float* ws_segf;    // [nseg][batch*H][N][P]: segment start adjoints, then the true segment end adjoints
+    float* ws_seglam;  // [nseg][batch*H] summed log-decay of each segment
+    float* ws_part;    // [3][batch*nch][H] per-chunk sums of dA, dD and dt_bias
 };
 bool ssd_bwd_supported(int P, int N, bool bf16);
-size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int H);
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int H, int G);
 hipError_t launch_ssd_scan_bwd(const BwdArgs& a, hipStream_t s);
 // total: tokens of a packed batch (L its longest sequence), or -1 for a padded one
 size_t ssd_scan_workspace_bytes(int64_t batch, int64_t L, int H, int P, int N, int G, int Q, bool bf16,

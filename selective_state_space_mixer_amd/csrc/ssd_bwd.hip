@@ -22,15 +22,17 @@
 //   Ge_{c-1} = e^(LamQ_c) Ge_c + F_c,   F_c = sum_t e^(Lam_t) dy_t (outer) C_t
 // and dstate_in = e^(LamQ_0) Ge_0 + F_0.
 //
-// Four kernels: the per-chunk E_c and F_c (one block per (sequence, group, chunk), the group's heads
-// in turn), the chain over chunks (elementwise, in place: E_c becomes S0_c and F_c becomes Ge_c), the
-// gradients (one block per (sequence, group, chunk), four waves on one head at a time, dB and dC
-// summed over the group's heads in registers), and a reduction of the per-chunk dA, dD and dt_bias
-// sums.  States in the workspace are fp32 and stored transposed, [n][p], so an accumulator's four
-// rows land as one 16-byte piece; they enter the products as bf16 hi + lo pairs (a single bf16
-// rounding of the chained adjoint left 2e-2 of dx, in an emulation of these kernels' rounding points
-// and on the GPU).
-//
+// Four kernels: walks over the chunks of segments of the sequence (four heads of one group per
+// block, the state or adjoint in accumulator registers; forward, each chunk's initial state from the
+// segment's start is stored before E_c is added; backward, each chunk's end adjoint from the
+// segment's end before F_c is added), a chain over the segments for what crosses segment boundaries,
+// the gradients (one block per (sequence, group, chunk), eight waves on one head at a time, the
+// boundary terms added as the states are loaded, dB and dC summed over the group's heads in
+// registers), and a reduction of the per-chunk dA, dD and dt_bias sums.  States in the workspace are
+// fp32 and stored transposed, [n][p], so an accumulator's four rows land as one 16-byte piece; they
+// enter the products as bf16 hi + lo pairs (a single bf16 rounding of the chained adjoint left 2e-2
+// of dx, in an emulation of these kernels' rounding points and on the GPU).
+
 // Operands follow the fragment convention of ssd_common.h (chunk 0: k = kbase + 4q + 0..3, chunk 1:
 // k = kbase + 16 + 4q + 0..3), read from row-major LDS tiles along a row (frag_row) or down the rows
 // with transposing reads (frag_col).  The decay-masked matrices that multiply another operand
@@ -128,149 +130,195 @@ __device__ __forceinline__ void put_tile_split(uint16_t* hi, uint16_t* lo, const
 }  // namespace
 
 // ----------------------------------------------------------------------------------------------
-// 1. per chunk: E_c, F_c (stored [n][p] fp32) and the chunk's summed log-decay; a block takes every
-// gridDim.z-th head of its group
+// 1. the walks over the chunks of a segment, four heads of one group per block (a wave each, the state
+// or adjoint in 64 accumulator registers): blockIdx.z = 0 runs forward (the chunk's initial state,
+// from the segment's start, is stored before the chunk's E_c is added), blockIdx.z = 1 backward (the
+// adjoint of the chunk's end state, from the segment's end, before F_c is added).  The first
+// segment's walk starts from the caller's state, the last segment's backward walk from dstate_out,
+// the others from zero; the segment chain adds what comes from across segment boundaries.
 
-__global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_chunk_kernel(BwdArgs k)
+__global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_walk_kernel(BwdArgs k)
 {
     using namespace bwd;
-    __shared__ __attribute__((aligned(16))) uint16_t sB[TE], sC[TE], sX[TE], sDY[TE];
-    const int c = blockIdx.x, bg = blockIdx.y;
-    const int64_t b = bg / k.G;
-    const int g = bg % k.G;
+    __shared__ __attribute__((aligned(16))) uint16_t sT[4][TE];  // x (dy) of the four heads
+    __shared__ __attribute__((aligned(16))) uint16_t sG[TE];     // B (C) of the group
+    const int seg = blockIdx.x;
+    const bool fwd = blockIdx.z == 0;
     const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hpg = k.H / k.G;
+    const int upg = (hpg + 3) / 4;               // head quads per group
+    const int64_t b = blockIdx.y / (k.G * upg);
+    const int hu = blockIdx.y % (k.G * upg);
+    const int g = hu / upg;
+    const int h0 = g * hpg + (hu % upg) * 4;
+    const int hcount = hpg - (hu % upg) * 4 < 4 ? hpg - (hu % upg) * 4 : 4;
+    const bool hvalid = w < hcount;
+    const int h = h0 + (hvalid ? w : hcount - 1);  // waves past the last head repeat it (results unused)
     const int BH = (int)k.batch * k.H;
-    const int64_t t0 = (int64_t)c * Q;
-    const int rows = (int)(k.L - t0 < Q ? k.L - t0 : Q);
-    const int64_t row0 = b * k.L + t0;
-    {
-        uint4 vb[2], vc[2];
-        fetch_tile<THREADS>(vb, k.B + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
-        fetch_tile<THREADS>(vc, k.C + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
-        put_tile<THREADS>(sB, vb);
-        put_tile<THREADS>(sC, vc);
-    }
-    uint4 vx[2], vy[2];
-    auto fetch = [&](int h) __attribute__((always_inline)) {
-        fetch_tile<THREADS>(vx, k.x + row0 * k.xs + (int64_t)h * P, k.xs, rows);
-        fetch_tile<THREADS>(vy, k.dy + row0 * k.dys + (int64_t)h * P, k.dys, rows);
+    const int bh = (int)b * k.H + h;
+    const int c0 = seg * k.cps;
+    const int c1 = c0 + k.cps < k.nch ? c0 + k.cps : k.nch;
+    const float A_h = k.A[h], bias_h = k.dt_bias[h];
+    const uint16_t* const src = fwd ? k.x : k.dy;
+    const int64_t srs = fwd ? k.xs : k.dys;
+    const uint16_t* const gsrc = fwd ? k.B : k.C;
+    float* const out = fwd ? k.ws_es : k.ws_fg;
+    float* const lamrun = fwd ? k.ws_lamb : k.ws_lame;
+
+    // the state (adjoint) in accumulator layout: acc[pb][nb] lane (q, li) = S[p = 16 pb + 4q + r][n = 16 nb + li]
+    f32x4 acc[4][4];
+    const float* init = fwd ? (seg == 0 ? k.state_in : nullptr) : (seg == k.nseg - 1 ? k.dstate_out : nullptr);
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[pb][nb][r] = init ? init[(int64_t)bh * PN + (16 * pb + 4 * q + r) * N + 16 * nb + li] : 0.0f;
+        }
+    float run = 0.0f;  // summed log-decay of the segment's chunks walked so far
+    // the next chunk's tiles and raw dt, fetched into registers while the current one is computed; the
+    // wave's own tile: unit u = lane + 64 m is row u / 8, columns 8 (u % 8) .. +7
+    uint4 vt[8], vg[2];
+    float raw_n = 0.0f;
+    auto fetch = [&](int c) __attribute__((always_inline)) {
+        const int64_t t0 = (int64_t)c * Q;
+        const int rows = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+        const int64_t row0 = b * k.L + t0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int u = lane + 64 * m, r = u >> 3, c8 = u & 7;
+            vt[m] = r < rows ? *reinterpret_cast<const uint4*>(src + (row0 + r) * srs + (int64_t)h * P + 8 * c8)
+                             : make_uint4(0u, 0u, 0u, 0u);
+        }
+        fetch_tile<THREADS>(vg, gsrc + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);
+        raw_n = lane < rows ? bits_to_f32(k.dt[(row0 + lane) * k.dts + h]) : 0.0f;
     };
-    // the group's heads blockIdx.z, blockIdx.z + gridDim.z, ...
-    const int hstep = gridDim.z;
-    if ((int)blockIdx.z < hpg) fetch(g * hpg + blockIdx.z);
-    for (int i = blockIdx.z; i < hpg; i += hstep) {
-        const int h = g * hpg + i;
-        __syncthreads();  // the previous head's tiles are no longer read
-        put_tile<THREADS>(sX, vx);
-        put_tile<THREADS>(sDY, vy);
+    if (c1 > c0) fetch(fwd ? c0 : c1 - 1);
+    for (int j = 0; j < c1 - c0; ++j) {
+        const int c = fwd ? c0 + j : c1 - 1 - j;
+        const int64_t t0 = (int64_t)c * Q;
+        const int rows = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+        __syncthreads();  // the previous chunk's tiles are no longer read
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int u = lane + 64 * m, r = u >> 3, c8 = u & 7;
+            *reinterpret_cast<uint4*>(sT[w] + r * RS + 8 * c8) = vt[m];
+        }
+        put_tile<THREADS>(sG, vg);
         const bool valid = lane < rows;
-        const float raw = valid ? bits_to_f32(k.dt[(row0 + lane) * k.dts + h]) : 0.0f;
+        const float raw = raw_n;
         __syncthreads();
-        if (i + hstep < hpg) fetch(h + hstep);
-        const float dtv = valid ? dt_of(raw, k.dt_bias[h], k.dt_min, k.dt_max) : 0.0f;
-        const float lam = wave_prefix_sum(dtv * k.A[h]);
+        if (j + 1 < c1 - c0) fetch(fwd ? c + 1 : c - 1);
+        // the chunk's state (adjoint) before its own contribution, as [n][p] fp32
+        if (hvalid) {
+            float* const o = out + ((int64_t)c * BH + bh) * PN;
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    *reinterpret_cast<float4*>(o + (16 * nb + li) * P + 16 * pb + 4 * q) =
+                        make_float4(acc[pb][nb][0], acc[pb][nb][1], acc[pb][nb][2], acc[pb][nb][3]);
+            if (lane == 0) lamrun[(int64_t)c * BH + bh] = run;
+        }
+        const float dtv = valid ? dt_of(raw, bias_h, k.dt_min, k.dt_max) : 0.0f;
+        const float lam = wave_prefix_sum(dtv * A_h);
         const float lamQ = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam), 63));
-        const float wgt = fast_exp(lamQ - lam) * dtv;  // weight of token s in E
-        const float fct = fast_exp(lam);               // weight of token t in F
-        // E[p][n] and F[p][n] for rows p = 16w + 4q + r, columns n = 16 nb + li
-        f32x4 aE[4], aF[4];
+        // token weights: e^(LamQ - Lam_s) dt_s forward (E_c), e^(Lam_t) backward (F_c)
+        const float wgt = fwd ? fast_exp(lamQ - lam) * dtv : fast_exp(lam);
+        const float d = fast_exp(lamQ);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            aE[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            aF[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pb][nb][r] *= d;
+#pragma unroll 1
         for (int kb = 0; kb < Q; kb += 32) {
-            // A operands: x and dy down the tokens (m = p = 16w + li, k = s), scaled per token
-            const Frag<bf16_t> xa = frag_col<bf16_t, U>(sX, kb, Q, 16 * w, q, li);
-            const Frag<bf16_t> ya = frag_col<bf16_t, U>(sDY, kb, Q, 16 * w, q, li);
-            Frag<bf16_t> xh, xl, yh, yl;
+            float ws8[2][4];
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                float vxs[4], vys[4];
+            for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = kb + 16 * cc + 4 * q + e;
-                    vxs[e] = xa.get(cc, e) * lane_value(wgt, s);
-                    vys[e] = ya.get(cc, e) * lane_value(fct, s);
+                for (int e = 0; e < 4; ++e) ws8[cc][e] = lane_value(wgt, kb + 16 * cc + 4 * q + e);
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                // A operand: the head's tile down the tokens (m = p, k = s), scaled per token, hi + lo
+                Frag<bf16_t> th, tl;
+                const Frag<bf16_t> ta = frag_col<bf16_t, U>(sT[w], kb, Q, 16 * pb, q, li);
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const float v4[4] = {ta.get(cc, 0) * ws8[cc][0], ta.get(cc, 1) * ws8[cc][1],
+                                         ta.get(cc, 2) * ws8[cc][2], ta.get(cc, 3) * ws8[cc][3]};
+                    uint2 h2, l2;
+                    split4(h2, l2, v4);
+                    th.w[2 * cc] = h2.x; th.w[2 * cc + 1] = h2.y;
+                    tl.w[2 * cc] = l2.x; tl.w[2 * cc + 1] = l2.y;
                 }
-                uint2 h2, l2;
-                split4(h2, l2, vxs);
-                xh.w[2 * cc] = h2.x; xh.w[2 * cc + 1] = h2.y; xl.w[2 * cc] = l2.x; xl.w[2 * cc + 1] = l2.y;
-                split4(h2, l2, vys);
-                yh.w[2 * cc] = h2.x; yh.w[2 * cc + 1] = h2.y; yl.w[2 * cc] = l2.x; yl.w[2 * cc + 1] = l2.y;
-            }
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const Frag<bf16_t> bb = frag_col<bf16_t, U>(sB, kb, Q, 16 * nb, q, li);
-                const Frag<bf16_t> cf = frag_col<bf16_t, U>(sC, kb, Q, 16 * nb, q, li);
-                mfma(aE[nb], xh, bb);
-                mfma(aE[nb], xl, bb);
-                mfma(aF[nb], yh, cf);
-                mfma(aF[nb], yl, cf);
+                for (int nb = 0; nb < 4; ++nb) {
+                    const Frag<bf16_t> gb = frag_col<bf16_t, U>(sG, kb, Q, 16 * nb, q, li);
+                    mfma(acc[pb][nb], th, gb);
+                    mfma(acc[pb][nb], tl, gb);
+                }
             }
         }
-        const int64_t base = ((int64_t)c * BH + b * k.H + h) * PN;
+        run += lamQ;
+    }
+    // the segment's end state (its adjoint at the segment's start) and summed log-decay
+    if (hvalid) {
+        float* const o = (fwd ? k.ws_sege : k.ws_segf) + ((int64_t)seg * BH + bh) * PN;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int64_t o = base + (int64_t)(16 * nb + li) * P + 16 * w + 4 * q;
-            *reinterpret_cast<float4*>(k.ws_es + o) = make_float4(aE[nb][0], aE[nb][1], aE[nb][2], aE[nb][3]);
-            *reinterpret_cast<float4*>(k.ws_fg + o) = make_float4(aF[nb][0], aF[nb][1], aF[nb][2], aF[nb][3]);
-        }
-        if (threadIdx.x == 0) k.ws_lam[(int64_t)c * BH + b * k.H + h] = lamQ;
+        for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                *reinterpret_cast<float4*>(o + (16 * nb + li) * P + 16 * pb + 4 * q) =
+                    make_float4(acc[pb][nb][0], acc[pb][nb][1], acc[pb][nb][2], acc[pb][nb][3]);
+        if (fwd && lane == 0) k.ws_seglam[(int64_t)seg * BH + bh] = run;
     }
 }
 
 // ----------------------------------------------------------------------------------------------
-// 2. the chain over chunks, four state entries ([n][p] order) per thread, in place: the first
-// PN / 1024 blocks of a sequence-head run forward for the initial states, the others backward for the
-// end adjoints; the loads of a batch of chunks are issued together
+// 2. the chain over segments, four entries ([n][p] order) per thread, in place: forward, T[s] = the
+// true state at segment s's start (s >= 1) = e^lam[s-1] T[s-1] + E[s-1] with T[1] = E[0] (the first
+// walk started from the caller's state); backward, U[s] = the true adjoint at segment s's end
+// (s <= nseg-2) = e^lam[s+1] U[s+1] + F[s+1] with U[nseg-2] = F[nseg-1]; dstate_in = F[0] + e^lam[0] U[0].
 
-__global__ __launch_bounds__(256) void ssd_bwd_chain_kernel(BwdArgs k)
+__global__ __launch_bounds__(256) void ssd_bwd_segchain_kernel(BwdArgs k)
 {
     using namespace bwd;
-    constexpr int kBatch = 16;
     constexpr int kHalf = PN / 1024;
     const int bh = blockIdx.y;
     const bool fwd = (int)blockIdx.x < kHalf;
     const int i = (((int)blockIdx.x % kHalf) * 256 + threadIdx.x) * 4;
     const int n = i / P, p = i % P;
     const int BH = (int)k.batch * k.H;
-    const int nch = k.nch;
-    float* const arr = fwd ? k.ws_es : k.ws_fg;
-    const float* const init = fwd ? k.state_in : k.dstate_out;
-    float s[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] = init ? init[(int64_t)bh * PN + (p + e) * N + n] : 0.0f;
-    // chunk order: 0 .. nch-1 forward, nch-1 .. 0 backward
-    for (int j0 = 0; j0 < nch; j0 += kBatch) {
-        float4 v[kBatch];
-        float lam[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const int jj = j0 + j < nch ? j0 + j : nch - 1;
-            const int c = fwd ? jj : nch - 1 - jj;
-            v[j] = *reinterpret_cast<const float4*>(arr + ((int64_t)c * BH + bh) * PN + i);
-            lam[j] = k.ws_lam[(int64_t)c * BH + bh];
+    const int nseg = k.nseg;
+    float* const arr = fwd ? k.ws_sege : k.ws_segf;
+    auto at = [&](int sg) __attribute__((always_inline)) { return arr + ((int64_t)sg * BH + bh) * PN + i; };
+    auto lam = [&](int sg) __attribute__((always_inline)) { return k.ws_seglam[(int64_t)sg * BH + bh]; };
+    if (fwd) {
+        float4 cur = *reinterpret_cast<const float4*>(at(0));
+        for (int sg = 1; sg < nseg; ++sg) {
+            const float4 e = *reinterpret_cast<const float4*>(at(sg));
+            *reinterpret_cast<float4*>(at(sg)) = cur;
+            const float d = fast_exp(lam(sg));
+            cur = make_float4(d * cur.x + e.x, d * cur.y + e.y, d * cur.z + e.z, d * cur.w + e.w);
         }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            if (j0 + j < nch) {
-                const int c = fwd ? j0 + j : nch - 1 - (j0 + j);
-                *reinterpret_cast<float4*>(arr + ((int64_t)c * BH + bh) * PN + i) = make_float4(s[0], s[1], s[2], s[3]);
-                const float d = fast_exp(lam[j]);
-                s[0] = d * s[0] + v[j].x;
-                s[1] = d * s[1] + v[j].y;
-                s[2] = d * s[2] + v[j].z;
-                s[3] = d * s[3] + v[j].w;
-            }
+    } else {
+        float4 cur = *reinterpret_cast<const float4*>(at(nseg - 1));
+        for (int sg = nseg - 2; sg >= 0; --sg) {
+            const float4 f = *reinterpret_cast<const float4*>(at(sg));
+            *reinterpret_cast<float4*>(at(sg)) = cur;
+            const float d = fast_exp(lam(sg));
+            cur = make_float4(d * cur.x + f.x, d * cur.y + f.y, d * cur.z + f.z, d * cur.w + f.w);
         }
-    }
-    if (!fwd && k.dstate_in) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) k.dstate_in[(int64_t)bh * PN + (p + e) * N + n] = s[e];
+        if (k.dstate_in) {
+            k.dstate_in[(int64_t)bh * PN + (p + 0) * N + n] = cur.x;
+            k.dstate_in[(int64_t)bh * PN + (p + 1) * N + n] = cur.y;
+            k.dstate_in[(int64_t)bh * PN + (p + 2) * N + n] = cur.z;
+            k.dstate_in[(int64_t)bh * PN + (p + 3) * N + n] = cur.w;
+        }
     }
 }
 
@@ -309,12 +357,36 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
     }
     uint4 vx[1], vy[1];
     float4 vs[2], vg[2];
+    // the chunk's true initial state and end adjoint: the walks' in-segment values plus what crosses the
+    // segment's boundaries, e^(log-decay from the segment's start) T[seg] and e^(log-decay to its end) U[seg]
+    const int seg = c / k.cps;
     auto fetch = [&](int h) __attribute__((always_inline)) {
-        const int64_t so = ((int64_t)c * BH + b * k.H + h) * PN;
+        const int64_t bh = b * k.H + h;
+        const int64_t so = ((int64_t)c * BH + bh) * PN, sg = ((int64_t)seg * BH + bh) * PN;
         fetch_tile<NT>(vx, k.x + row0 * k.xs + (int64_t)h * P, k.xs, rows);
         fetch_tile<NT>(vy, k.dy + row0 * k.dys + (int64_t)h * P, k.dys, rows);
         fetch_tile32<NT>(vs, k.ws_es + so);
         fetch_tile32<NT>(vg, k.ws_fg + so);
+        // a boundary term whose factor is below 2^-60 is below the fp32 resolution of any state it
+        // is added to (the states are finite), and is skipped
+        const float fb = fast_exp(k.ws_lamb[(int64_t)c * BH + bh]);
+        const float fe = fast_exp(k.ws_lame[(int64_t)c * BH + bh]);
+        if (seg > 0 && fb >= 0x1p-60f) {
+            float4 t[1024 / NT];
+            fetch_tile32<NT>(t, k.ws_sege + sg);
+            const float f = fb;
+#pragma unroll
+            for (int j = 0; j < 1024 / NT; ++j)
+                vs[j] = make_float4(vs[j].x + f * t[j].x, vs[j].y + f * t[j].y, vs[j].z + f * t[j].z, vs[j].w + f * t[j].w);
+        }
+        if (seg < k.nseg - 1 && fe >= 0x1p-60f) {
+            float4 t[1024 / NT];
+            fetch_tile32<NT>(t, k.ws_segf + sg);
+            const float f = fe;
+#pragma unroll
+            for (int j = 0; j < 1024 / NT; ++j)
+                vg[j] = make_float4(vg[j].x + f * t[j].x, vg[j].y + f * t[j].y, vg[j].z + f * t[j].z, vg[j].w + f * t[j].w);
+        }
     };
     fetch(g * hpg);
     __syncthreads();
@@ -638,54 +710,90 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs k)
 }
 
 // ----------------------------------------------------------------------------------------------
+// a prompt of no tokens: dstate_in = dstate_out (or zero), one block per sequence-head
+
+__global__ __launch_bounds__(256) void ssd_bwd_copy_state_kernel(BwdArgs k)
+{
+    const int64_t o = (int64_t)blockIdx.x * bwd::PN;
+    for (int i = threadIdx.x; i < bwd::PN; i += 256) k.dstate_in[o + i] = k.dstate_out ? k.dstate_out[o + i] : 0.0f;
+}
+
+// ----------------------------------------------------------------------------------------------
 // host side
 
 bool ssd_bwd_supported(int P, int N, bool bf16) { return bf16 && P == bwd::P && N == bwd::N; }
 
 namespace {
-struct BwdLayout {
-    size_t es, fg, lam, part, total;
+// Segments of the walks: at most two walk blocks (forward and backward together) per CU, the number
+// resident at once (46 KB of LDS, about 190 registers per lane), and at most one segment per chunk.
+struct BwdPlan {
+    int nch, nseg, cps;
 };
-BwdLayout bwd_layout(int64_t batch, int64_t L, int H) {
+BwdPlan bwd_plan(int64_t batch, int64_t L, int H, int G) {
+    BwdPlan pl;
+    pl.nch = (int)((L + bwd::Q - 1) / bwd::Q);
+    const int64_t quads = batch * G * ((H / G + 3) / 4);
+    const int64_t target = (int64_t)device_shape().cus * 2;
+    int64_t nseg = quads > 0 ? target / (2 * quads) : 1;
+    if (nseg > pl.nch) nseg = pl.nch;
+    if (nseg < 1) nseg = 1;
+    pl.cps = pl.nch > 0 ? (int)((pl.nch + nseg - 1) / nseg) : 1;
+    pl.nseg = pl.nch > 0 ? (pl.nch + pl.cps - 1) / pl.cps : 1;
+    return pl;
+}
+struct BwdLayout {
+    size_t es, fg, lamb, lame, sege, segf, seglam, part, total;
+};
+BwdLayout bwd_layout(int64_t batch, int64_t L, int H, int G) {
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    const int64_t nch = (L + bwd::Q - 1) / bwd::Q;
+    const BwdPlan pl = bwd_plan(batch, L, H, G);
+    const size_t BH = (size_t)(batch * H), st = (size_t)bwd::PN * 4;
     BwdLayout w;
     w.es = 0;
-    w.fg = up((size_t)(nch * batch * H * bwd::PN) * 4);
-    w.lam = up(w.fg + (size_t)(nch * batch * H * bwd::PN) * 4);
-    w.part = up(w.lam + (size_t)(nch * batch * H) * 4);
-    w.total = w.part + (size_t)(3 * batch * nch * H) * 4;
+    w.fg = up(pl.nch * BH * st);
+    w.lamb = up(w.fg + pl.nch * BH * st);
+    w.lame = up(w.lamb + pl.nch * BH * 4);
+    w.sege = up(w.lame + pl.nch * BH * 4);
+    w.segf = up(w.sege + pl.nseg * BH * st);
+    w.seglam = up(w.segf + pl.nseg * BH * st);
+    w.part = up(w.seglam + pl.nseg * BH * 4);
+    w.total = w.part + (size_t)(3 * batch * pl.nch * H) * 4;
     return w;
 }
 }  // namespace
 
-size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int H) { return bwd_layout(batch, L, H).total + 256; }
+size_t ssd_bwd_workspace_bytes(int64_t batch, int64_t L, int H, int G) { return bwd_layout(batch, L, H, G).total + 256; }
 
 hipError_t launch_ssd_scan_bwd(const BwdArgs& a_in, hipStream_t s) {
     BwdArgs a = a_in;
-    const BwdLayout lay = bwd_layout(a.batch, a.L, a.H);
+    const BwdPlan pl = bwd_plan(a.batch, a.L, a.H, a.G);
+    const BwdLayout lay = bwd_layout(a.batch, a.L, a.H, a.G);
     uint8_t* base = reinterpret_cast<uint8_t*>(((uintptr_t)a.ws + 255) & ~(uintptr_t)255);
     a.ws_es = reinterpret_cast<float*>(base + lay.es);
     a.ws_fg = reinterpret_cast<float*>(base + lay.fg);
-    a.ws_lam = reinterpret_cast<float*>(base + lay.lam);
+    a.ws_lamb = reinterpret_cast<float*>(base + lay.lamb);
+    a.ws_lame = reinterpret_cast<float*>(base + lay.lame);
+    a.ws_sege = reinterpret_cast<float*>(base + lay.sege);
+    a.ws_segf = reinterpret_cast<float*>(base + lay.segf);
+    a.ws_seglam = reinterpret_cast<float*>(base + lay.seglam);
     a.ws_part = reinterpret_cast<float*>(base + lay.part);
-    a.nch = (int)((a.L + bwd::Q - 1) / bwd::Q);
+    a.nch = pl.nch;
+    a.nseg = pl.nseg;
+    a.cps = pl.cps;
     hipError_t e = hipSuccess;
     if (a.nch > 0 && a.batch > 0) {
-        // the group's heads over up to four blocks, so that the launch has several blocks per CU
-        const int hpg = a.H / a.G;
-        const int hsplit = hpg < 4 ? hpg : 4;
-        const dim3 grid((unsigned)a.nch, (unsigned)(a.batch * a.G), (unsigned)hsplit);
-        e = launch_kernel(ssd_bwd_chunk_kernel, grid, dim3(bwd::THREADS), 0, s, a);
+        const int quads = (int)a.batch * a.G * ((a.H / a.G + 3) / 4);
+        e = launch_kernel(ssd_bwd_walk_kernel, dim3((unsigned)a.nseg, (unsigned)quads, 2), dim3(bwd::THREADS), 0, s, a);
         if (e != hipSuccess) return e;
-    }
-    if (a.batch > 0) {
-        e = launch_kernel(ssd_bwd_chain_kernel, dim3(2 * bwd::PN / 1024, (unsigned)(a.batch * a.H)), dim3(256), 0, s, a);
+        e = launch_kernel(ssd_bwd_segchain_kernel, dim3(2 * bwd::PN / 1024, (unsigned)(a.batch * a.H)), dim3(256), 0, s,
+                          a);
         if (e != hipSuccess) return e;
-    }
-    if (a.nch > 0 && a.batch > 0) {
-        const dim3 grid((unsigned)a.nch, (unsigned)(a.batch * a.G));
-        e = launch_kernel(ssd_bwd_grad_kernel, grid, dim3(bwd::GTHREADS), 0, s, a);
+        e = launch_kernel(ssd_bwd_grad_kernel, dim3((unsigned)a.nch, (unsigned)(a.batch * a.G)), dim3(bwd::GTHREADS), 0,
+                          s, a);
+        if (e != hipSuccess) return e;
+    } else if (a.batch > 0 && a.dstate_in) {
+        // no tokens: the final state's gradient reaches the initial state unchanged
+        e = launch_kernel(ssd_bwd_copy_state_kernel, dim3((unsigned)(a.batch * a.H)), dim3(256), 0, s, a);
         if (e != hipSuccess) return e;
     }
     return launch_kernel(ssd_bwd_reduce_kernel, dim3((unsigned)a.H), dim3(256), 0, s, a);
