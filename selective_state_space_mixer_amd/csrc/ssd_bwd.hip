@@ -54,21 +54,23 @@ constexpr int PN = P * N;
 
 namespace {
 
+// sum over the wave, the same value in every lane (DPP prefix sums, then the last lane)
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_prefix_sum(v)), 63));
+}
+// inclusive prefix sum inside each 16-lane row (DPP row shifts): lane 15 of a row holds the row's sum
+__device__ __forceinline__ float row_prefix_sum(float v) {
+    float x = v;
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+    return x;
 }
 // sum over the four 16-lane groups (lanes with the same lane % 16)
 __device__ __forceinline__ float sum_over_q(float v) {
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
-    return v;
-}
-// sum over the 16 lanes of a lane group
-__device__ __forceinline__ float sum_over_li(float v) {
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
 __device__ __forceinline__ float lane_value(float v, int src) { return __shfl(v, src, 64); }
@@ -417,6 +419,11 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
         put_tile<NT>(sDY, vy);
         put_tile_split<NT>(sS0, sS0l, vs);
         put_tile_split<NT>(sGE, sGEl, vg);
+        // <Ge, S0> from the fp32 tiles (both [n][p], the same entries in every thread)
+        float g0 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 1024 / NT; ++j)
+            g0 += vs[j].x * vg[j].x + vs[j].y * vg[j].y + vs[j].z * vg[j].z + vs[j].w * vg[j].w;
         const bool valid = lane < rows;
         const float raw = valid ? bits_to_f32(k.dt[(row0 + lane) * k.dts + h]) : 0.0f;
         __syncthreads();
@@ -474,24 +481,10 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float v = sum_over_li(rsum[r]);
-            if (li == 0) rRow[ch][16 * rb + 4 * q + r] = v;
+            const float v = row_prefix_sum(rsum[r]);  // lane 15 of the row: the sum over its 16 columns
+            if (li == 15) rRow[ch][16 * rb + 4 * q + r] = v;
         }
         dpart = wave_sum(dpart);
-        // <Ge, S0> over rows n = 8w .. 8w+7 of the transposed states, eight columns per lane
-        float g0 = 0.0f;
-        {
-            const int o = (8 * w + (lane >> 3)) * RS + 8 * (lane & 7);
-            const uint4 a = *reinterpret_cast<const uint4*>(sGE + o), al = *reinterpret_cast<const uint4*>(sGEl + o);
-            const uint4 bb = *reinterpret_cast<const uint4*>(sS0 + o), bl = *reinterpret_cast<const uint4*>(sS0l + o);
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, alw[4] = {al.x, al.y, al.z, al.w};
-            const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w}, blw[4] = {bl.x, bl.y, bl.z, bl.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                g0 += (lo_bf16(aw[e]) + lo_bf16(alw[e])) * (lo_bf16(bw[e]) + lo_bf16(blw[e]));
-                g0 += (hi_bf16(aw[e]) + hi_bf16(alw[e])) * (hi_bf16(bw[e]) + hi_bf16(blw[e]));
-            }
-        }
         g0 = wave_sum(g0);
         if (lane == 0) {
             rQ0[w] = g0;
