@@ -1,0 +1,95 @@
+"""GPU parity of the conv on long prompts (the kernel that sizes its token tile at launch) against
+the fp64 oracle.
+
+The conv of the Zamba2 mixer (article "Transformers 中 Zamba2 混合架构模型解析", §三: depthwise
+conv over the token axis, width mamba_d_conv, SiLU, its state carried as the last W inputs).  A
+launch takes the long-prompt kernel when the grid, made one resident round, would give every lane
+at least two turns of its load ring (32 tokens for bf16, 16 for fp32).  Every case below is sized so
+that this holds at any occupancy up to 8 blocks per CU on 256 CUs (more tokens per lane on fewer
+CUs), and so that the last tile of a sequence ends part-way through a ring turn:
+  - the 2.7B channel count (5248) at 16461 tokens, conv widths 4, 3 and 2, with ring history at a
+    non-zero phase;
+  - fp32 activations (io "f32");
+  - a right-padded batch (one sequence ends mid-tile, the other is full);
+  - a packed batch with a 3-token sequence (shorter than the window) and an empty one.
+Outputs within the floored max-relative bound (2e-2 bf16, 1e-4 fp32); rings bit-exact; padding left
+untouched.  Each test prints the error it reaches.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import selective_state_space_mixer_amd as m2
+    from gpu_util import dev, dev32, dims_of, host, nan_like, tol_for
+
+BASE = workloads.CONFIGS[3].dims   # d_model 2560: conv_dim 5248
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+
+
+@pytest.mark.parametrize("width,io", [(4, "bf16"), (3, "bf16"), (2, "bf16"), (4, "f32")])
+def test_long_prompt_conv(width, io):
+    _need_gpu()
+    d = BASE.replace(batch=1, seqlen=16461, d_conv=width, io=io)
+    inp = workloads.generate(d, 8100 + width, True)
+    phase = 2
+    ref, ref_ring = oracle.conv1d(inp.xbc, inp.conv_w, inp.conv_b, inp.ring0, phase)
+    out = nan_like((d.batch, d.seqlen, d.conv_dim), io)
+    ring_out = nan_like((d.batch, width, d.conv_dim), io)
+    m2.m2_conv1d_fwd(dims_of(d), dev(inp.xbc, io), dev32(inp.conv_w), dev32(inp.conv_b), out,
+                     dev(inp.ring0, io), phase, ring_out)
+    torch.cuda.synchronize()
+    e = oracle.max_rel_err(host(out), ref)
+    print("long conv W=%d %s, %d tokens x %d channels: %.2e" % (width, io, d.seqlen, d.conv_dim, e))
+    assert e <= tol_for(io)
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
+
+
+def test_long_prompt_conv_right_padded():
+    _need_gpu()
+    d = BASE.replace(batch=2, seqlen=12000)
+    lens = np.array([7777, 12000], np.int32)
+    inp = workloads.generate(d, 8201, True)
+    ref, ref_ring = oracle.conv1d(inp.xbc, inp.conv_w, inp.conv_b, inp.ring0, 1, seq_lens=lens)
+    out = nan_like((d.batch, d.seqlen, d.conv_dim), "bf16")
+    ring_out = nan_like((d.batch, d.d_conv, d.conv_dim), "bf16")
+    m2.m2_conv1d_fwd(dims_of(d), dev(inp.xbc, "bf16"), dev32(inp.conv_w), dev32(inp.conv_b), out,
+                     dev(inp.ring0, "bf16"), 1, ring_out, seq_lens=torch.as_tensor(lens, device="cuda"))
+    torch.cuda.synchronize()
+    got = host(out)
+    errs = []
+    for b, n in enumerate(lens):
+        errs.append(oracle.max_rel_err(got[b, :n], ref[b, :n]))
+        assert np.isnan(got[b, n:]).all(), "padding of sequence %d written" % b
+    print("long conv, right-padded %s: %s" % (lens.tolist(), " ".join("%.2e" % e for e in errs)))
+    assert max(errs) <= tol_for("bf16")
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
+
+
+def test_long_prompt_conv_packed():
+    _need_gpu()
+    lens = [9000, 3, 0, 6000]
+    d = BASE.replace(batch=len(lens), seqlen=max(lens))
+    inp = workloads.generate(d, 8301, True)
+    xp = np.concatenate([inp.xbc[b, :n] for b, n in enumerate(lens)], 0)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ref, ref_ring = oracle.conv1d_packed(xp, cu, inp.conv_w, inp.conv_b, inp.ring0, 3)
+    out = nan_like((len(xp), d.conv_dim), "bf16")
+    ring_out = nan_like((len(lens), d.d_conv, d.conv_dim), "bf16")
+    m2.m2_conv1d_fwd_packed(dims_of(d), torch.as_tensor(cu, device="cuda"), dev(xp, "bf16"), dev32(inp.conv_w),
+                            dev32(inp.conv_b), out, dev(inp.ring0, "bf16"), 3, ring_out)
+    torch.cuda.synchronize()
+    e = oracle.max_rel_err(host(out), ref)
+    print("long conv, packed %s: %.2e" % (lens, e))
+    assert e <= tol_for("bf16")
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
