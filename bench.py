@@ -8,8 +8,10 @@ resident in HBM, through the one-pass entry point m2_mixer_prefill_fwd (the conv
 written).  The same run times the two-kernel path (m2_conv1d_fwd then m2_ssd_scan_fwd) on the same
 prompt, the same tokens as 8 packed prompts, the gated RMSNorm, the fused decode step on 256
 sequences (the `decode` object) and the library's streaming copy (the attainable-bandwidth
-reference).  Each entry point's average time comes from HIP events recorded on the stream it runs on
-and is turned into a roofline fraction with the algorithmic bytes it must move.  The fp64 CPU oracle
+reference).  Each entry point's average time comes from HIP events recorded on the stream it runs on,
+around each of its calls in the order the path makes them, and is turned into a roofline fraction
+with the algorithmic bytes it must move (the two-kernel path's entry points are also timed repeated
+by themselves: `us_alone`).  The fp64 CPU oracle
 is timed on a bounded sample of the same prefill on the host cores (`cpu_baseline`).
 
     python bench.py [--steps K] [--warmup W] [--decode-steps S] [--no-cpu-baseline]
@@ -81,23 +83,37 @@ def bwd_flops(B, L, H):
     return 16384 * (B * nch * H * (128 + 416))
 
 
-def time_events(torch, fns, steps, warmup):
-    """Per-callable mean ms, each from `steps` back-to-back calls between one event pair on the current
-    stream (the queue stays ahead of the GPU, so host launch gaps are not counted), then the mean ms of
-    one pass of all callables in order, again over `steps` passes, plus the wall ms of that last region."""
+def time_events(torch, fns, steps, warmup, alone=None):
+    """Per-callable mean ms and the mean ms of one pass of all callables in order, over `steps` passes.
+
+    The per-callable times come from an event pair around each call inside those passes, so every
+    kernel is timed where the path runs it (the scan right after the conv whose output it reads).  The
+    pass time comes from a second region of `steps` passes with no events inside; the wall ms of that
+    region is returned too.  With `alone` (a list), the mean ms of `steps` back-to-back calls of each
+    callable by itself is appended to it (a repeated conv runs slower: each call's output is still
+    being written back from the caches when the next call starts)."""
     for _ in range(warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
-    per = []
-    for f in fns:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
+    if alone is not None:
+        for f in fns:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            alone.append(e0.elapsed_time(e1) / steps)
+    marks = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+             for _ in range(steps)]
+    for s in range(steps):
+        for (e0, e1), f in zip(marks[s], fns):
+            e0.record()
             f()
-        e1.record()
-        torch.cuda.synchronize()
-        per.append(e0.elapsed_time(e1) / steps)
+            e1.record()
+    torch.cuda.synchronize()
+    per = [sum(marks[s][i][0].elapsed_time(marks[s][i][1]) for s in range(steps)) / steps for i in range(len(fns))]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -211,7 +227,8 @@ def bench_prefill(torch, m2, workloads, args):
     # point's time (they are the same calls), so the roofline and ms_per_step agree
     _, fused_total, wall_ms = time_events(torch, [fused], args.steps, args.warmup)
     t_fused = fused_total / args.steps
-    (t_conv, t_scan), two_total, _ = time_events(torch, [conv, scan], args.steps, args.warmup)
+    alone = []
+    (t_conv, t_scan), two_total, _ = time_events(torch, [conv, scan], args.steps, args.warmup, alone)
     conv_b, scan_b = prefill_bytes(B, L, H, P, N, G, W, Cd, False, True)
     fused_b = fused_bytes(B, L, H, P, N, G, W, Cd, False, True)
     step_ms = fused_total / args.steps
@@ -223,8 +240,10 @@ def bench_prefill(torch, m2, workloads, args):
         "tokens_per_s": tok / (step_ms * 1e-3), "ms_per_step": step_ms, "wall_ms": wall_ms,
         "kernels": {"mixer_prefill": {"ms": t_fused, "bytes": fused_b,
                                       "roofline": roofline(fused_b, t_fused, "mixer_prefill")},
-                    "conv1d": {"ms": t_conv, "bytes": conv_b, "roofline": roofline(conv_b, t_conv, "conv1d")},
-                    "ssd_scan": {"ms": t_scan, "bytes": scan_b, "roofline": roofline(scan_b, t_scan, "ssd_scan")}},
+                    "conv1d": {"ms": t_conv, "bytes": conv_b, "roofline": roofline(conv_b, t_conv, "conv1d"),
+                               "ms_alone": alone[0]},
+                    "ssd_scan": {"ms": t_scan, "bytes": scan_b, "roofline": roofline(scan_b, t_scan, "ssd_scan"),
+                                 "ms_alone": alone[1]}},
         "two_kernel": {"ms_per_step": round(two_ms, 4), "tokens_per_s": round(tok / (two_ms * 1e-3), 1),
                        "path_roofline_frac": round((conv_b + scan_b) / (two_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "path_roofline_frac": round(tok / (step_ms * 1e-3) / roof_tok_s, 4),
@@ -479,6 +498,9 @@ def main():
                                       "frac": v["roofline"]["frac"], "achieved_GBs": v["roofline"]["achieved"],
                                       "frac_of_copy": v["roofline"].get("frac_of_copy")}
                                   for n, v in k.items()}
+        for n, v in k.items():
+            if "ms_alone" in v:
+                out["prefill_kernels"][n]["us_alone"] = round(v["ms_alone"] * 1e3, 2)
         for n in ("mixer_prefill", "ssd_scan"):
             out["prefill_kernels"][n]["mfma"] = measured_mfma(n)
         out["prefill_path_roofline_frac"] = pre["path_roofline_frac"]

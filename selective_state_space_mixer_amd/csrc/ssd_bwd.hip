@@ -358,11 +358,17 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
         put_tile<NT>(sC, vc);
     }
     uint4 vx[1], vy[1];
-    float4 vs[2], vg[2];
-    // the chunk's true initial state and end adjoint: the walks' in-segment values plus what crosses the
-    // segment's boundaries, e^(log-decay from the segment's start) T[seg] and e^(log-decay to its end) U[seg]
+    float4 vs[2], vg[2], ts[2], tg[2];
+    float fs = 0.0f, fg = 0.0f, raw_n = 0.0f, A_n = 0.0f, bias_n = 0.0f, D_n = 0.0f;
+    // The chunk's true initial state and end adjoint: the walks' in-segment values plus what crosses the
+    // segment's boundaries, e^(log-decay from the segment's start) T[seg] and e^(log-decay to its end)
+    // U[seg].  fetch(h) issues every load of head h and waits for none of them: the boundary tiles go to
+    // ts / tg with their factors in fs / fg and are added when the head's tiles are put in LDS, and a
+    // boundary term that is not needed reads through an empty buffer range (zeros, no memory access).
+    // Its log-decays come in one head earlier (lb_n, le_n), so the choice waits for no load either.
     const int seg = c / k.cps;
-    auto fetch = [&](int h) __attribute__((always_inline)) {
+    const int64_t lrow = (int64_t)c * BH + b * k.H;  // log-decays of head h at lrow + h
+    auto fetch = [&](int h, float lb, float le) __attribute__((always_inline)) {
         const int64_t bh = b * k.H + h;
         const int64_t so = ((int64_t)c * BH + bh) * PN, sg = ((int64_t)seg * BH + bh) * PN;
         fetch_tile<NT>(vx, k.x + row0 * k.xs + (int64_t)h * P, k.xs, rows);
@@ -371,26 +377,26 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
         fetch_tile32<NT>(vg, k.ws_fg + so);
         // a boundary term whose factor is below 2^-60 is below the fp32 resolution of any state it
         // is added to (the states are finite), and is skipped
-        const float fb = fast_exp(k.ws_lamb[(int64_t)c * BH + bh]);
-        const float fe = fast_exp(k.ws_lame[(int64_t)c * BH + bh]);
-        if (seg > 0 && fb >= 0x1p-60f) {
-            float4 t[1024 / NT];
-            fetch_tile32<NT>(t, k.ws_sege + sg);
-            const float f = fb;
+        const float fb = fast_exp(lb), fe = fast_exp(le);
+        const bool use_b = seg > 0 && fb >= 0x1p-60f, use_e = seg < k.nseg - 1 && fe >= 0x1p-60f;
+        const auto rs = make_rsrc(k.ws_sege + (use_b ? sg : 0), use_b ? PN * 4u : 0u);
+        const auto rg = make_rsrc(k.ws_segf + (use_e ? sg : 0), use_e ? PN * 4u : 0u);
 #pragma unroll
-            for (int j = 0; j < 1024 / NT; ++j)
-                vs[j] = make_float4(vs[j].x + f * t[j].x, vs[j].y + f * t[j].y, vs[j].z + f * t[j].z, vs[j].w + f * t[j].w);
+        for (int j = 0; j < 1024 / NT; ++j) {
+            const uint32_t off = (uint32_t)((int)threadIdx.x + NT * j) * 16u;
+            ts[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+            tg[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, (int)off, 0, 0));
         }
-        if (seg < k.nseg - 1 && fe >= 0x1p-60f) {
-            float4 t[1024 / NT];
-            fetch_tile32<NT>(t, k.ws_segf + sg);
-            const float f = fe;
-#pragma unroll
-            for (int j = 0; j < 1024 / NT; ++j)
-                vg[j] = make_float4(vg[j].x + f * t[j].x, vg[j].y + f * t[j].y, vg[j].z + f * t[j].z, vg[j].w + f * t[j].w);
-        }
+        fs = use_b ? fb : 0.0f;
+        fg = use_e ? fe : 0.0f;
+        raw_n = lane < rows ? bits_to_f32(k.dt[(row0 + lane) * k.dts + h]) : 0.0f;
+        A_n = k.A[h];
+        bias_n = k.dt_bias[h];
+        D_n = k.D ? k.D[h] : 0.0f;
     };
-    fetch(g * hpg);
+    fetch(g * hpg, k.ws_lamb[lrow + g * hpg], k.ws_lame[lrow + g * hpg]);
+    float lb_n = hpg > 1 ? k.ws_lamb[lrow + g * hpg + 1] : 0.0f;
+    float le_n = hpg > 1 ? k.ws_lame[lrow + g * hpg + 1] : 0.0f;
     __syncthreads();
     // C.B of the chunk (every head of the group shares it): rows t = 16 rb + 4q + r, columns
     // s = 16 (2 ch + j) + li
@@ -415,6 +421,11 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
     for (int i = 0; i < hpg; ++i) {
         const int h = g * hpg + i;
         __syncthreads();  // the previous head is done with the tiles and the partial sums
+#pragma unroll
+        for (int j = 0; j < 1024 / NT; ++j) {
+            vs[j] = make_float4(vs[j].x + fs * ts[j].x, vs[j].y + fs * ts[j].y, vs[j].z + fs * ts[j].z, vs[j].w + fs * ts[j].w);
+            vg[j] = make_float4(vg[j].x + fg * tg[j].x, vg[j].y + fg * tg[j].y, vg[j].z + fg * tg[j].z, vg[j].w + fg * tg[j].w);
+        }
         put_tile<NT>(sX, vx);
         put_tile<NT>(sDY, vy);
         put_tile_split<NT>(sS0, sS0l, vs);
@@ -425,11 +436,13 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
         for (int j = 0; j < 1024 / NT; ++j)
             g0 += vs[j].x * vg[j].x + vs[j].y * vg[j].y + vs[j].z * vg[j].z + vs[j].w * vg[j].w;
         const bool valid = lane < rows;
-        const float raw = valid ? bits_to_f32(k.dt[(row0 + lane) * k.dts + h]) : 0.0f;
+        const float raw = raw_n, A_h = A_n, bias_h = bias_n, D_h = D_n;
         __syncthreads();
-        if (i + 1 < hpg) fetch(h + 1);
-        const float A_h = k.A[h], bias_h = k.dt_bias[h];
-        const float D_h = k.D ? k.D[h] : 0.0f;
+        if (i + 1 < hpg) fetch(h + 1, lb_n, le_n);
+        if (i + 2 < hpg) {
+            lb_n = k.ws_lamb[lrow + h + 2];
+            le_n = k.ws_lame[lrow + h + 2];
+        }
         // statistics of token `lane`
         const float dtv = valid ? dt_of(raw, bias_h, k.dt_min, k.dt_max) : 0.0f;
         const float lam = wave_prefix_sum(dtv * A_h);
