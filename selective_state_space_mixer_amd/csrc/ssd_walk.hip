@@ -449,6 +449,43 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 mfma(accY[tb][pb], xf[pb], mh[tb]);
                 mfma(accY[tb][pb], xf[pb], ml[tb]);
             }
+        // ---- state update: S^T[n][p] = dec S^T[n][p] + sum_s B[s][n] (w_s X[s][p]), w_s x_s as bf16 hi + lo.
+        // One channel block of w_s x_s is split at a time and its products issued before the next block
+        // is split, so the split's VALU work runs beside the matrix cores; the y tile is staged and
+        // stored after all of them are issued.
+        if (dec != 1.0f) {
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) accS[pb][nb] *= dec;
+        }
+        Frag<bf16_t> bt[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const uint2 a = lds_read8_tr(Bt, col_off(0, nb)), c = lds_read8_tr(Bt, col_off(1, nb));
+            bt[nb].w[0] = a.x; bt[nb].w[1] = a.y; bt[nb].w[2] = c.x; bt[nb].w[3] = c.y;
+        }
+        const float4 w0 = *reinterpret_cast<const float4*>(wh + 4 * q);
+        const float4 w1 = *reinterpret_cast<const float4*>(wh + 16 + 4 * q);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            if constexpr (!FUSED) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const float4 wv = c == 0 ? w0 : w1;
+                    const float v0 = xf[pb].get(c, 0) * wv.x, v1 = xf[pb].get(c, 1) * wv.y;
+                    const float v2 = xf[pb].get(c, 2) * wv.z, v3 = xf[pb].get(c, 3) * wv.w;
+                    xwh[pb].set(c, v0, v1, v2, v3);
+                    xwl[pb].set(c, v0 - xwh[pb].get(c, 0), v1 - xwh[pb].get(c, 1), v2 - xwh[pb].get(c, 2),
+                                v3 - xwh[pb].get(c, 3));
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                mfma(accS[pb][nb], bt[nb], xwh[pb]);
+                mfma(accS[pb][nb], bt[nb], xwl[pb]);
+            }
+        }
         // y out: lane (q, li) holds y[t = 16 tb + li][p = 16 pb + 4q .. +3]; staged (in this wave's own
         // X tile, whose reads are done) so that each store instruction writes eight whole 128-byte rows
 #pragma unroll
@@ -468,38 +505,6 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
             __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)off, 0, 0);
         }
 
-        // ---- state update: S^T[n][p] = dec S^T[n][p] + sum_s B[s][n] (w_s X[s][p]), w_s x_s as bf16 hi + lo
-        if (dec != 1.0f) {
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) accS[pb][nb] *= dec;
-        }
-        const float4 w0 = *reinterpret_cast<const float4*>(wh + 4 * q);
-        const float4 w1 = *reinterpret_cast<const float4*>(wh + 16 + 4 * q);
-#pragma unroll
-        for (int pb = 0; pb < 4 && !FUSED; ++pb) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const float4 wv = c == 0 ? w0 : w1;
-                const float v0 = xf[pb].get(c, 0) * wv.x, v1 = xf[pb].get(c, 1) * wv.y;
-                const float v2 = xf[pb].get(c, 2) * wv.z, v3 = xf[pb].get(c, 3) * wv.w;
-                xwh[pb].set(c, v0, v1, v2, v3);
-                xwl[pb].set(c, v0 - xwh[pb].get(c, 0), v1 - xwh[pb].get(c, 1), v2 - xwh[pb].get(c, 2),
-                            v3 - xwh[pb].get(c, 3));
-            }
-        }
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            Frag<bf16_t> bt;
-            const uint2 a = lds_read8_tr(Bt, col_off(0, nb)), c = lds_read8_tr(Bt, col_off(1, nb));
-            bt.w[0] = a.x; bt.w[1] = a.y; bt.w[2] = c.x; bt.w[3] = c.y;
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-                mfma(accS[pb][nb], bt, xwh[pb]);
-                mfma(accS[pb][nb], bt, xwl[pb]);
-            }
-        }
         // Chunk i+1's tiles and chunk i+2's dt must be in LDS before the barrier: the dt load is the first
         // of chunk i+2's seven, so at most its six tile loads and this chunk's four y stores may still run.
         if (i + 2 < nc) wait_vmem<10>();
