@@ -420,7 +420,9 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
 
     for (int i = 0; i < hpg; ++i) {
         const int h = g * hpg + i;
-        __syncthreads();  // the previous head is done with the tiles and the partial sums
+        // No barrier here: the previous head's last one (before its d(Lam) tail) already has every wave
+        // past its reads of the tiles, and the tail reads only the partial sums, which this head writes
+        // after the next barrier, the one that waits for the tail's wave.
 #pragma unroll
         for (int j = 0; j < 1024 / NT; ++j) {
             vs[j] = make_float4(vs[j].x + fs * ts[j].x, vs[j].y + fs * ts[j].y, vs[j].z + fs * ts[j].z, vs[j].w + fs * ts[j].w);

@@ -11,7 +11,9 @@ CUs), and so that the last tile of a sequence ends part-way through a ring turn:
     non-zero phase;
   - fp32 activations (io "f32");
   - a right-padded batch (one sequence ends mid-tile, the other is full);
-  - a packed batch with a 3-token sequence (shorter than the window) and an empty one.
+  - a packed batch with a 3-token sequence (shorter than the window) and an empty one;
+  - one call against the same prompt in two calls continued through the ring, the second short
+    enough for the fixed-tile kernel: bit-identical outputs and rings.
 Outputs within the floored max-relative bound (2e-2 bf16, 1e-4 fp32); rings bit-exact; padding left
 untouched.  Each test prints the error it reaches.
 """
@@ -93,3 +95,34 @@ def test_long_prompt_conv_packed():
     print("long conv, packed %s: %.2e" % (lens, e))
     assert e <= tol_for("bf16")
     np.testing.assert_array_equal(host(ring_out), ref_ring)
+
+
+def test_long_prompt_conv_split_matches_whole_bit_for_bit():
+    """Both conv kernels form each output with the same taps in the same order, so a prompt convolved in
+    one call (16461 tokens: the long-prompt kernel) equals, bit for bit, the same prompt in two calls
+    continued through the ring: 9000 tokens (the long-prompt kernel), then 7461 tokens (at the five or
+    more resident blocks per CU the long-prompt kernel gets, one round would give fewer than 32 tokens
+    per lane there, so the fixed-tile kernel runs)."""
+    _need_gpu()
+    d = BASE.replace(batch=1, seqlen=16461)
+    inp = workloads.generate(d, 8401, True)
+    xbc = dev(inp.xbc, "bf16")
+    w, bias = dev32(inp.conv_w), dev32(inp.conv_b)
+    ring0 = dev(inp.ring0, "bf16")
+    whole = nan_like((1, d.seqlen, d.conv_dim), "bf16")
+    ring_whole = nan_like((1, d.d_conv, d.conv_dim), "bf16")
+    m2.m2_conv1d_fwd(dims_of(d), xbc, w, bias, whole, ring0, 1, ring_whole)
+    cut = 9000
+    d1, d2 = d.replace(seqlen=cut), d.replace(seqlen=d.seqlen - cut)
+    part = nan_like((1, d.seqlen, d.conv_dim), "bf16")
+    ring_mid = nan_like((1, d.d_conv, d.conv_dim), "bf16")
+    ring_end = nan_like((1, d.d_conv, d.conv_dim), "bf16")
+    m2.m2_conv1d_fwd(dims_of(d1), xbc[:, :cut], w, bias, part[:, :cut], ring0, 1, ring_mid)
+    m2.m2_conv1d_fwd(dims_of(d2), xbc[:, cut:], w, bias, part[:, cut:], ring_mid, 0, ring_end)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), part.view(torch.int16))
+    assert torch.equal(ring_whole.view(torch.int16), ring_end.view(torch.int16))
+    ref, _ = oracle.conv1d(inp.xbc, inp.conv_w, inp.conv_b, inp.ring0, 1)
+    e = oracle.max_rel_err(host(whole), ref)
+    print("long conv, one call vs two: bit-identical; against the oracle %.2e" % e)
+    assert e <= tol_for("bf16")
