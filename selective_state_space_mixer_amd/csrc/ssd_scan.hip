@@ -85,14 +85,8 @@ hipError_t static_scratch(void** ptr, size_t* bytes) {
 // (eight where the LDS budget allows: two such blocks fill a compute unit at four waves per SIMD).
 // Every wave forms the decay-masked matrix M of its own head from G = C B^T tiles it computes
 // itself, so the only data exchanged between waves are the tiles and the chunk statistics.
-#ifndef M2_SCAN_STATE_TILES
-#define M2_SCAN_STATE_TILES 8
-#endif
-constexpr int kMaxStateTiles = M2_SCAN_STATE_TILES;
-#ifndef M2_SCAN_WAVES
-#define M2_SCAN_WAVES 8
-#endif
-constexpr int kScanWaves = M2_SCAN_WAVES;  // waves per block, when the heads allow
+constexpr int kMaxStateTiles = 8;
+constexpr int kScanWaves = 8;  // waves per block, when the heads allow
 
 template <typename T, int Q, int P, int N>
 struct Cfg {
@@ -614,10 +608,7 @@ ssd_chunk_scan_kernel(ScanK k)
 // bounds Tb[seg] on max|T[seg]| from the segments' recorded maxima (see fix_cut).
 __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(ScanK k, int BH, int PN)
 {
-#ifndef M2_CHAIN_BATCH
-#define M2_CHAIN_BATCH 32
-#endif
-    constexpr int kBatch = M2_CHAIN_BATCH;  // segments whose loads are issued together
+    constexpr int kBatch = 32;  // segments whose loads are issued together
     const int nseg = k.nseg;
     const int bh = blockIdx.y;
     float* __restrict__ ws_state = k.ws_state;
@@ -906,11 +897,6 @@ static Plan plan_of(int64_t batch, int64_t L, int H, int G, int64_t total) {
     return plan_for(batch, L, H, G, P * N, Q, Cf::HPW, Cf::BPC, sizeof(T) == 2, total);
 }
 
-#ifndef M2_WALK_KERNEL
-#define M2_WALK_KERNEL 1
-#endif
-constexpr bool kWalkKernel = M2_WALK_KERNEL != 0;
-
 template <typename T, int Q, int P, int N>
 static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* conv = nullptr) {
     using Cf = Cfg<T, Q, P, N>;
@@ -952,7 +938,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     k.nxcd = device_shape().xcds;
     hipError_t e;
     bool walk = false;
-    if constexpr (sizeof(T) == 2 && Q == 32 && P == 64 && N == 64 && kWalkKernel) {
+    if constexpr (sizeof(T) == 2 && Q == 32 && P == 64 && N == 64) {
         static_assert(Cf::HPW == 4, "the walk kernel's block covers four heads");
         // its blocks hold four heads of one group each, and it reads dt two heads per dword
         walk = (a.H / a.G) % 4 == 0 && ((uintptr_t)a.dt & 3u) == 0 && (a.dts & 1) == 0;
@@ -1039,7 +1025,7 @@ hipError_t launch_ssd_scan(const ScanArgs& a, hipStream_t s) {
 // the fused prompt path
 
 bool mixer_fusable(int P, int N, int H, int G, bool bf16) {
-    return kWalkKernel && bf16 && P == 64 && N == 64 && G > 0 && (H / G) % 4 == 0;
+    return bf16 && P == 64 && N == 64 && G > 0 && (H / G) % 4 == 0;
 }
 
 bool mixer_dt_fusable(const void* dt, int64_t dts) { return ((uintptr_t)dt & 3u) == 0 && (dts & 1) == 0; }
