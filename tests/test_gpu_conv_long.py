@@ -13,7 +13,8 @@ CUs), and so that the last tile of a sequence ends part-way through a ring turn:
   - a right-padded batch (one sequence ends mid-tile, the other is full);
   - a packed batch with a 3-token sequence (shorter than the window) and an empty one;
   - one call against the same prompt in two calls continued through the ring, the second short
-    enough for the fixed-tile kernel: bit-identical outputs and rings.
+    enough for the fixed-tile kernel: bit-identical outputs and rings;
+  - input and output as column slices of wider rows (token strides above conv_dim).
 Outputs within the floored max-relative bound (2e-2 bf16, 1e-4 fp32); rings bit-exact; padding left
 untouched.  Each test prints the error it reaches.
 """
@@ -126,3 +127,29 @@ def test_long_prompt_conv_split_matches_whole_bit_for_bit():
     e = oracle.max_rel_err(host(whole), ref)
     print("long conv, one call vs two: bit-identical; against the oracle %.2e" % e)
     assert e <= tol_for("bf16")
+
+
+def test_long_prompt_conv_strided_views():
+    """The conv input as a column slice of a wider row (as xBC sits between the gate and dt in the
+    input projection's output) and the output written into a slice of a wider buffer: token strides
+    5248 + 512 and 5248 + 256 elements, both multiples of 8, so the vector path and the long-prompt
+    kernel run; the padding columns of the output buffer stay untouched."""
+    _need_gpu()
+    d = BASE.replace(batch=1, seqlen=12345)
+    inp = workloads.generate(d, 8501, True)
+    Cd, L = d.conv_dim, d.seqlen
+    src = np.zeros((1, L, Cd + 512), np.float32)
+    src[:, :, 256:256 + Cd] = inp.xbc
+    xbig = dev(src, "bf16")
+    obig = nan_like((1, L, Cd + 256), "bf16")
+    ring_out = nan_like((1, d.d_conv, Cd), "bf16")
+    m2.m2_conv1d_fwd(dims_of(d), xbig[:, :, 256:256 + Cd], dev32(inp.conv_w), dev32(inp.conv_b), obig[:, :, 128:128 + Cd],
+                     dev(inp.ring0, "bf16"), 2, ring_out)
+    torch.cuda.synchronize()
+    ref, ref_ring = oracle.conv1d(inp.xbc, inp.conv_w, inp.conv_b, inp.ring0, 2)
+    got = host(obig)
+    e = oracle.max_rel_err(got[:, :, 128:128 + Cd], ref)
+    print("long conv, strided views (token strides %d and %d): %.2e" % (Cd + 512, Cd + 256, e))
+    assert e <= tol_for("bf16")
+    assert np.isnan(got[:, :, :128]).all() and np.isnan(got[:, :, 128 + Cd:]).all(), "padding written"
+    np.testing.assert_array_equal(host(ring_out), ref_ring)
