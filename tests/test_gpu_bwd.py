@@ -6,7 +6,7 @@ compares dx, dB, dC, d(raw dt), dt_bias, dA, dD and dstate_in with oracle.ssd_sc
 seeded bf16 inputs, floored max-relative error <= 2e-2, and prints the errors it reaches:
   - small shapes: a ragged last chunk, one whole chunk, one token, grouped heads, no D, no initial
     state and no final adjoint, a dt clamp that binds at both bounds, and an empty prompt;
-  - the 2.7B mixer shape at 2 x 2048 tokens, every head;
+  - the 2.7B mixer shape at 2 x 2048 tokens, every head; with four B/C groups at 2 x 4096 tokens;
   - the 32768-token prompt in the launch configuration of the benchmark, on four sampled heads (a
     second call with dy and dstate_out zero outside them gives dB and dC over those heads alone).
 """
@@ -152,3 +152,17 @@ def test_scan_backward_full_size_32k_sampled_heads():
            "dA": got["dA"][heads], "dD": got["dD"][heads], "dstate_in": got["dstate_in"][:, heads],
            "dB": got_m["dB"], "dC": got_m["dC"]}
     report("backward 32k, heads %s" % heads, errors(sel, ref))
+
+
+def test_scan_backward_groups4_2x4096_every_head():
+    """Four B/C groups of 20 heads at the 2.7B head shape, 2 x 4096 tokens (several segments per
+    sequence, so the segment chains run), initial state and final adjoint given, every head and every
+    gradient against the oracle."""
+    _need_gpu()
+    d = workloads.CONFIGS[2].dims.replace(batch=2, seqlen=4096, n_groups=4)
+    inp = workloads.generate(d, 7501, True)
+    x, b, c = _split(d, inp)
+    dy, ds = workloads.grad_inputs(d, 7502)
+    got = run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds)
+    ref = oracle.ssd_scan_bwd(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds)
+    report("backward 4 groups 2x4096", errors(got, ref))
