@@ -12,7 +12,9 @@ dt = clamp(softplus(dt_raw + dt_bias)).  The pins:
   - A = 0 reduces the scan to causal linear attention; its gradients are written here as numpy
     matrix products from that closed form;
   - the backward of a prompt split in two calls, with the adjoint of the first call's final state
-    taken from the second call's dstate_in, equals the backward of the whole prompt.
+    taken from the second call's dstate_in, equals the backward of the whole prompt;
+  - every gradient equals PyTorch's reverse-mode autograd (fp64, CPU) through the token recurrence
+    written out with torch ops, with and without a clamp.
 """
 import numpy as np
 import pytest
@@ -158,3 +160,40 @@ def test_no_initial_state_and_no_final_adjoint():
     g0 = oracle.ssd_scan_bwd(**zero, dy=dy, dstate_out=np.zeros_like(dS))
     for k in g:
         assert np.array_equal(g[k], g0[k]), k
+
+
+@pytest.mark.parametrize("clamp", [False, True], ids=["no-clamp", "clamp"])
+def test_matches_autograd_of_the_token_recurrence(clamp):
+    """Every gradient, the nonlinear ones (dt_raw, dt_bias, A) included, against PyTorch's reverse-mode
+    autograd in fp64 on the CPU, run through the token recurrence written out here with torch ops
+    (S_t = e^(dt_t A) S_{t-1} + dt_t x_t B_t^T, y_t = S_t C_t + D x_t, dt = clamp(softplus(dt_raw +
+    dt_bias))): an independent differentiation, exact up to rounding.  With the clamp, its bounds are
+    set between token values so that no token sits on one (where the derivative is a convention)."""
+    torch = pytest.importorskip("torch")
+    c, dy, dS, _ = case(8, Bn=2, L=19, H=4, P=3, N=5, G=2)
+    lo, hi = 0.0, float("inf")
+    if clamp:
+        sp = np.sort(np.logaddexp(0.0, c["dt_raw"] + c["dt_bias"]).ravel())
+        lo, hi = (sp[30] + sp[31]) / 2, (sp[-31] + sp[-30]) / 2
+    g = oracle.ssd_scan_bwd(**c, dy=dy, dstate_out=dS, dt_min=lo, dt_max=hi)
+    T = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in c.items() if v is not None}
+    Bn, L, H, P = c["x"].shape
+    G = c["Bm"].shape[2]
+    dt = torch.nn.functional.softplus(T["dt_raw"] + T["dt_bias"], beta=1.0, threshold=1e30)
+    if clamp:
+        dt = torch.clamp(dt, lo, hi)
+    S = T["state_in"]
+    loss = torch.zeros((), dtype=torch.float64)
+    hg = torch.arange(H) // (H // G)
+    for t in range(L):
+        a = torch.exp(dt[:, t] * T["A"])                                   # [Bn, H]
+        Bt, Ct = T["Bm"][:, t][:, hg], T["Cm"][:, t][:, hg]                # [Bn, H, N]
+        S = a[..., None, None] * S + (dt[:, t][..., None] * T["x"][:, t])[..., None] * Bt[:, :, None, :]
+        y = (S * Ct[:, :, None, :]).sum(-1) + T["D"][None, :, None] * T["x"][:, t]
+        loss = loss + (y * torch.tensor(dy[:, t])).sum()
+    loss = loss + (S * torch.tensor(dS)).sum()
+    loss.backward()
+    pairs = {"dx": "x", "dB": "Bm", "dC": "Cm", "ddt_raw": "dt_raw", "ddt_bias": "dt_bias", "dA": "A",
+             "dD": "D", "dstate_in": "state_in"}
+    for gk, ck in pairs.items():
+        assert rel(g[gk], T[ck].grad.numpy()) < 1e-12, (gk, rel(g[gk], T[ck].grad.numpy()))
