@@ -51,7 +51,7 @@ def _load():
         lib.oracle_softplus.argtypes = [f64]
         lib.oracle_softplus.restype = f64
         lib.oracle_gated_rmsnorm.argtypes = [i64, i64, i64, dp, dp, dp, f64, i64, dp]
-        lib.oracle_ssd_scan_bwd.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64] + [dp] * 3 + [dp] * 8
+        lib.oracle_ssd_scan_bwd.argtypes = [i64] * 6 + [dp] * 7 + [f64, f64] + [dp] * 3 + [dp] * 8 + [dp]
         lib.oracle_ssd_scan_bwd.restype = None
         lib.oracle_gated_rmsnorm.restype = None
         _lib = lib
@@ -148,12 +148,13 @@ def ssd_scan(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None,
 
 
 def ssd_scan_bwd(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None, dy=None, dstate_out=None,
-                 dt_min: float = 0.0, dt_max: float = float("inf")):
+                 dt_min: float = 0.0, dt_max: float = float("inf"), seq_lens=None):
     """Gradients of L = sum(dy * y) + sum(dstate_out * state_out) for ssd_scan's outputs.
 
     Same inputs as ssd_scan, plus dy [B,L,H,P] and dstate_out [B,H,P,N] (None: zero).  Returns a dict
     with dx [B,L,H,P], dB and dC [B,L,G,N], ddt_raw [B,L,H], ddt_bias, dA, dD [H] and dstate_in
-    [B,H,P,N]."""
+    [B,H,P,N].  seq_lens [B] (optional): as for ssd_scan (state_out is the state after sequence b's
+    last real token); dx, dB, dC and ddt_raw past a sequence's length are NaN here."""
     x = _f64(x)
     Bn, L, H, P = x.shape
     Bm = _f64(Bm)
@@ -169,13 +170,14 @@ def ssd_scan_bwd(x, Bm, Cm, dt_raw, dt_bias, A, D=None, state_in=None, dy=None, 
     dstate_out = _f64(dstate_out, (Bn, H, P, N))
     if H % G:
         raise ValueError("oracle: nheads must be a multiple of n_groups")
-    out = {"dx": np.empty_like(x), "dB": np.empty((Bn, L, G, N)), "dC": np.empty((Bn, L, G, N)),
-           "ddt_raw": np.empty((Bn, L, H)), "ddt_bias": np.empty(H), "dA": np.empty(H), "dD": np.empty(H),
+    lens = _lens(seq_lens, Bn, L)
+    out = {"dx": np.full_like(x, np.nan), "dB": np.full((Bn, L, G, N), np.nan), "dC": np.full((Bn, L, G, N), np.nan),
+           "ddt_raw": np.full((Bn, L, H), np.nan), "ddt_bias": np.empty(H), "dA": np.empty(H), "dD": np.empty(H),
            "dstate_in": np.empty((Bn, H, P, N))}
     _load().oracle_ssd_scan_bwd(Bn, L, H, P, N, G, _p(x), _p(Bm), _p(Cm), _p(dt_raw), _p(dt_bias), _p(A),
                                 _p(D), float(dt_min), float(dt_max), _p(state_in), _p(dy), _p(dstate_out),
                                 _p(out["dx"]), _p(out["dB"]), _p(out["dC"]), _p(out["ddt_raw"]),
-                                _p(out["ddt_bias"]), _p(out["dA"]), _p(out["dD"]), _p(out["dstate_in"]))
+                                _p(out["ddt_bias"]), _p(out["dA"]), _p(out["dD"]), _p(out["dstate_in"]), _p(lens))
     return out
 
 

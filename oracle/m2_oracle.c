@@ -238,19 +238,21 @@ void oracle_gated_rmsnorm(int64_t T, int64_t D, int64_t GS, const double* y, con
     }
 }
 
-/* Gradients of L = sum_t dy_t . y_t + <dstate_out, S_final> for the scan of oracle_ssd_scan
- * (no lens).  dstate_out / state_in / D nullable (zero).  Outputs: dx [B,L,H,P], dB and dC
- * [B,L,G,N] (summed over the heads of the group), ddt_raw [B,L,H], ddt_bias / dA / dD [H]
- * (summed over the batch), dstate_in [B,H,P,N].  The forward states S_0..S_{L-1} of a
- * (sequence, head) are kept, then the adjoint runs from t = L-1 down to 0.  The clamped
- * softplus passes the gradient where dt_min <= softplus(v) <= dt_max, else 0. */
+/* Gradients of L = sum_t dy_t . y_t + <dstate_out, S_final> for the scan of oracle_ssd_scan.
+ * dstate_out / state_in / D nullable (zero).  Outputs: dx [B,L,H,P], dB and dC [B,L,G,N]
+ * (summed over the heads of the group), ddt_raw [B,L,H], ddt_bias / dA / dD [H] (summed over
+ * the batch), dstate_in [B,H,P,N].  The forward states of a (sequence, head) are kept, then
+ * the adjoint runs from its last token down to 0.  The clamped softplus passes the gradient
+ * where dt_min <= softplus(v) <= dt_max, else 0.  lens (nullable): sequence b consumes only
+ * its first lens[b] tokens, as in oracle_ssd_scan (S_final is the state after the last of
+ * them); per-token outputs past them are not written. */
 void oracle_ssd_scan_bwd(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                          const double* x, const double* Bm, const double* Cm,
                          const double* dt_raw, const double* dt_bias, const double* A, const double* D,
                          double dt_min, double dt_max, const double* state_in,
                          const double* dy, const double* dstate_out,
                          double* dx, double* dB, double* dC, double* ddt_raw,
-                         double* ddt_bias, double* dA, double* dD, double* dstate_in)
+                         double* ddt_bias, double* dA, double* dD, double* dstate_in, const int64_t* lens)
 {
     const int64_t hpg = H / G, PN = P * N;
     /* per (sequence, head) partial sums, added up after the parallel loop */
@@ -264,11 +266,12 @@ void oracle_ssd_scan_bwd(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t N,
         for (int64_t h = 0; h < H; ++h) {
             const int64_t g = h / hpg, bh = b * H + h;
             const double Dh = D ? D[h] : 0.0;
+            const int64_t Lb = lens ? lens[b] : L;
             /* forward: S[t + 1] is the state after token t, S[0] the initial state */
             double* S = (double*)malloc((size_t)((L + 1) * PN) * sizeof(double));
             double* dts = (double*)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
             for (int64_t i = 0; i < PN; ++i) S[i] = state_in ? state_in[bh * PN + i] : 0.0;
-            for (int64_t t = 0; t < L; ++t) {
+            for (int64_t t = 0; t < Lb; ++t) {
                 const int64_t bt = b * L + t;
                 const double dt = step_size(dt_raw[bt * H + h], dt_bias[h], dt_min, dt_max);
                 const double a = exp(dt * A[h]);
@@ -282,7 +285,7 @@ void oracle_ssd_scan_bwd(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t N,
             /* reverse: Gm is the adjoint of the state after token t */
             double* Gm = (double*)malloc((size_t)PN * sizeof(double));
             for (int64_t i = 0; i < PN; ++i) Gm[i] = dstate_out ? dstate_out[bh * PN + i] : 0.0;
-            for (int64_t t = L - 1; t >= 0; --t) {
+            for (int64_t t = Lb - 1; t >= 0; --t) {
                 const int64_t bt = b * L + t;
                 const double dt = dts[t];
                 const double a = exp(dt * A[h]);
@@ -337,7 +340,7 @@ void oracle_ssd_scan_bwd(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t N,
         }
     }
     for (int64_t b = 0; b < Bn; ++b)
-        for (int64_t t = 0; t < L; ++t)
+        for (int64_t t = 0; t < (lens ? lens[b] : L); ++t)
             for (int64_t g = 0; g < G; ++g)
                 for (int64_t n = 0; n < N; ++n) {
                     double sb = 0.0, sc = 0.0;

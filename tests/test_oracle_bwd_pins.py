@@ -197,3 +197,35 @@ def test_matches_autograd_of_the_token_recurrence(clamp):
              "dD": "D", "dstate_in": "state_in"}
     for gk, ck in pairs.items():
         assert rel(g[gk], T[ck].grad.numpy()) < 1e-12, (gk, rel(g[gk], T[ck].grad.numpy()))
+
+
+def test_right_padded_batch_equals_each_sequence_alone():
+    """Right padding (a per-sequence length, the reading the forward oracle follows): the backward of a
+    padded batch, with dstate_out the adjoint of the state after each sequence's last real token, equals
+    the backward of each sequence's real tokens alone (the case every pin above fixes), including an
+    empty sequence (dstate_in = dstate_out) and a full one; the per-token gradients past a length are
+    left unwritten, and junk in the padded positions changes nothing."""
+    c, dy, dS, r = case(9, Bn=4, L=21, H=4, P=3, N=5, G=2)
+    lens = np.array([21, 13, 0, 1])
+    junk = dict(c)
+    dyj = dy.copy()
+    for b, n in enumerate(lens):
+        for k in ("x", "Bm", "Cm", "dt_raw"):
+            junk[k] = junk[k].copy()
+            junk[k][b, n:] = r.normal(size=junk[k][b, n:].shape) * 7.0
+        dyj[b, n:] = r.normal(size=dyj[b, n:].shape) * 7.0
+    g = oracle.ssd_scan_bwd(**junk, dy=dyj, dstate_out=dS, seq_lens=lens)
+    sums = {k: np.zeros_like(g[k]) for k in ("ddt_bias", "dA", "dD")}
+    for b, n in enumerate(lens):
+        one = {k: (v[b:b + 1, :n] if k in ("x", "Bm", "Cm", "dt_raw") else v) for k, v in c.items()}
+        one["state_in"] = c["state_in"][b:b + 1]
+        gb = oracle.ssd_scan_bwd(**one, dy=dy[b:b + 1, :n], dstate_out=dS[b:b + 1])
+        for k in ("dx", "dB", "dC", "ddt_raw"):
+            assert rel(g[k][b, :n], gb[k][0]) < 1e-12 if n else True, (k, b)
+            assert np.isnan(g[k][b, n:]).all(), (k, b)
+        assert rel(g["dstate_in"][b], gb["dstate_in"][0]) < 1e-12, b
+        for k in sums:
+            sums[k] += gb[k]
+    assert np.array_equal(g["dstate_in"][2], dS[2]), "an empty sequence passes dstate_out through"
+    for k in sums:
+        assert rel(g[k], sums[k]) < 1e-12, k
