@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define M2SSD_ABI_VERSION 5
+#define M2SSD_ABI_VERSION 6
 
 typedef enum {
     M2_OK = 0,
@@ -310,8 +310,8 @@ size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims);
  * with respect to every input of the scan, for y and state_out as m2_ssd_scan_fwd computes them
  * from the same arguments.  Built for bf16 activations at headdim 64 and d_state 64 (the
  * Zamba2-2.7B mixer shape), any batch, seqlen and n_groups dividing nheads; chunk_size is ignored
- * (chunks of 64 tokens).  Other dims return M2_ERR_UNSUPPORTED.  Sequence lengths and packed batches
- * are not supported: every sequence is seqlen tokens.
+ * (chunks of 64 tokens).  Other dims return M2_ERR_UNSUPPORTED.  Right-padded batches are supported
+ * (seq_lens); packed batches are not.
  * Inputs as m2_ssd_scan_fwd (x, B, C, raw dt, dt_bias, A, D or NULL, dt_min, dt_max, state_in or
  * NULL), plus
  *   dy         [batch, seqlen, nheads*headdim] io, token stride dy_tok_stride: dL/dy
@@ -326,6 +326,11 @@ size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims);
  *   dstate_in  [batch, nheads, headdim, d_state] fp32 or NULL: dL/dstate_in
  * workspace: at least m2_ssd_scan_bwd_workspace(dims) bytes, any alignment, contents on entry
  * irrelevant; calls that may run at the same time need separate workspaces.
+ * seq_lens   [batch] int32 on the device, or NULL (every sequence is seqlen tokens): a right-padded
+ *            batch as in m2_ssd_scan_fwd.  Sequence b consumes only its first seq_lens[b] tokens
+ *            (clamped to [0, seqlen]), dstate_out is the adjoint of the state after the last of them,
+ *            and dx, dB, dC and ddt at later positions are left as they were; padded tokens add
+ *            nothing to ddt_bias, dA and dD.  4-byte aligned; must not overlap an output.
  * x, B, C, dy, dx, dB and dC must start on 16-byte boundaries with token strides that are multiples
  * of 16 bytes (else M2_ERR_UNSUPPORTED).  No output may overlap an input, another output or the
  * workspace (M2_ERR_ALIAS); overlap is judged on each array's byte range from its first to its last
@@ -345,6 +350,7 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims,
                           float* ddt_bias, float* dA, float* dD,
                           float* dstate_in,
                           void* workspace, size_t workspace_bytes,
+                          const int32_t* seq_lens,
                           void* stream);
 
 /* Static text for a status code. */

@@ -27,7 +27,7 @@ M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, 
     M2_ERR_LAUNCH, M2_ERR_TOO_LARGE = range(9)
 M2_STATIC_SCRATCH_BYTES = 64 << 20
 M2_F32, M2_BF16 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
            "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc",
@@ -105,7 +105,7 @@ def _load() -> ctypes.CDLL:
     lib.m2_ssd_scan_bwd_workspace.argtypes = [dp]
     lib.m2_ssd_scan_bwd_workspace.restype = sz
     lib.m2_ssd_scan_bwd.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, i64, vp, vp, i64,
-                                    vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+                                    vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.m2_ssd_scan_bwd.restype = ctypes.c_int
     lib.m2_stream_copy.argtypes = [vp, vp, sz, vp]
     lib.m2_stream_copy.restype = ctypes.c_int
@@ -547,13 +547,13 @@ def m2_ssd_scan_bwd_workspace(dims: M2Dims) -> int:
 
 def m2_ssd_scan_bwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, dy, dx, dB, dC, ddt, ddt_bias, dA, dD,
                     state_in=None, dstate_out=None, dstate_in=None, dt_min: float = 0.0, dt_max: float = float("inf"),
-                    workspace=None, stream=None) -> None:
+                    workspace=None, stream=None, seq_lens=None) -> None:
     """Backward of the scan; see include/m2ssd.h.
 
     Inputs as m2_ssd_scan_fwd plus dy (like y) and dstate_out [B, H, P, N] f32 or None; outputs dx (like x),
     dB/dC (like B/C, sharing one token stride), ddt (like dt), ddt_bias/dA/dD [H] f32 and dstate_in
     [B, H, P, N] f32 or None; workspace: a uint8 GPU tensor of at least m2_ssd_scan_bwd_workspace(dims)
-    bytes."""
+    bytes; seq_lens: int32 [B] GPU tensor of each right-padded sequence's length, or None."""
     torch = _torch()
     ins, _ = _scan_args(dims, x, B, C, dt, dt_bias, A, D, dy, state_in, None)
     io = _io_dtype(dims)
@@ -579,7 +579,7 @@ def m2_ssd_scan_bwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, dy, dx, dB, dC, dd
     _call("m2_ssd_scan_bwd", ctypes.byref(dims), *ins, float(dt_min), float(dt_max), _ptr(state_in), _ptr(dy), dys,
           _ptr(dstate_out), _ptr(dx), dxs, _ptr(dB), _ptr(dC), dbs, _ptr(ddt), ddts, _ptr(ddt_bias), _ptr(dA),
           _ptr(dD), _ptr(dstate_in), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-          _stream(stream))
+          _lens_ptr(seq_lens, dims), _stream(stream))
 
 
 def m2_stream_copy(dst, src, stream=None) -> None:

@@ -414,7 +414,7 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
                           const void* dy, int64_t dy_tok_stride, const float* dstate_out, void* dx,
                           int64_t dx_tok_stride, void* dB, void* dC, int64_t dbc_tok_stride, void* ddt,
                           int64_t ddt_tok_stride, float* ddt_bias, float* dA, float* dD, float* dstate_in,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
     Derived d;
     m2_status st = derive(dims, d);
     if (st != M2_OK) return st;
@@ -435,7 +435,8 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
                      (dy_tok_stride * 2) % 16 || (dx_tok_stride * 2) % 16 || (dbc_tok_stride * 2) % 16 ||
                      ((uintptr_t)dt & 1u) || ((uintptr_t)ddt & 1u)))
         return M2_ERR_UNSUPPORTED;
-    if (((uintptr_t)state_in & 3u) || ((uintptr_t)dstate_out & 3u) || ((uintptr_t)dstate_in & 3u))
+    if (((uintptr_t)state_in & 3u) || ((uintptr_t)dstate_out & 3u) || ((uintptr_t)dstate_in & 3u) ||
+        ((uintptr_t)seq_lens & 3u))
         return M2_ERR_UNSUPPORTED;
     const size_t need = m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H, d.G);
     if (!workspace || workspace_bytes < need) return M2_ERR_WORKSPACE;
@@ -444,7 +445,7 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
                          span(C, rows, bc_tok_stride, GN, 2), span(dt, rows, dt_tok_stride, d.H, 2),
                          span(dy, rows, dy_tok_stride, d.d_inner, 2), span(dt_bias, 1, 0, d.H, 4),
                          span(A, 1, 0, d.H, 4), span(D, 1, 0, d.H, 4), span(state_in, d.batch * d.H, SS, SS, 4),
-                         span(dstate_out, d.batch * d.H, SS, SS, 4)};
+                         span(dstate_out, d.batch * d.H, SS, SS, 4), span(seq_lens, d.batch, 1, 1, 4)};
     const Range outs[] = {span(dx, rows, dx_tok_stride, d.d_inner, 2), span(dB, rows, dbc_tok_stride, GN, 2),
                           span(dC, rows, dbc_tok_stride, GN, 2), span(ddt, rows, ddt_tok_stride, d.H, 2),
                           span(ddt_bias, 1, 0, d.H, 4), span(dA, 1, 0, d.H, 4), span(dD, 1, 0, d.H, 4),
@@ -467,6 +468,7 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
     a.ddt = (uint16_t*)ddt; a.ddts = ddt_tok_stride;
     a.ddt_bias = ddt_bias; a.dA = dA; a.dD = dD; a.dstate_in = dstate_in;
     a.batch = d.batch; a.L = d.L; a.H = d.H; a.G = d.G;
+    a.lens = seq_lens;
     a.ws = workspace;
     return launched(m2::launch_ssd_scan_bwd(a, (hipStream_t)stream));
 }

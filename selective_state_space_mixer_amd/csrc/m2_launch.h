@@ -89,6 +89,7 @@ struct BwdArgs {
     float* ddt_bias; float* dA; float* dD; float* dstate_in;
     int64_t batch, L;
     int H, G;
+    const int32_t* lens;  // [batch] valid tokens per sequence (device), or null
     void* ws;
     // set by the launcher
     int nch, nseg, cps;  // 64-token chunks, segments of the walks, chunks per segment

@@ -129,6 +129,20 @@ __device__ __forceinline__ void put_tile_split(uint16_t* hi, uint16_t* lo, const
     }
 }
 
+// Tokens of sequence b: seqlen, or its length in a right-padded batch (clamped to [0, seqlen]).  A
+// padded token reads as zero x, B, C, dy and dt, so it changes neither the state nor the adjoint, and
+// its gradients are not stored.
+__device__ __forceinline__ int64_t bwd_seq_len(const BwdArgs& k, int64_t b) {
+    if (!k.lens) return k.L;
+    const int64_t v = k.lens[b];
+    return v < 0 ? 0 : (v > k.L ? k.L : v);
+}
+// rows of chunk c (from token t0) that belong to a sequence of Lb tokens: 0 .. Q
+__device__ __forceinline__ int chunk_rows(int64_t Lb, int64_t t0) {
+    const int64_t r = Lb - t0;
+    return (int)(r < 0 ? 0 : (r < bwd::Q ? r : bwd::Q));
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------------------------
@@ -184,9 +198,10 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_walk_kernel(BwdArgs k)
     // wave's own tile: unit u = lane + 64 m is row u / 8, columns 8 (u % 8) .. +7
     uint4 vt[8], vg[2];
     float raw_n = 0.0f;
+    const int64_t Lb = bwd_seq_len(k, b);
     auto fetch = [&](int c) __attribute__((always_inline)) {
         const int64_t t0 = (int64_t)c * Q;
-        const int rows = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+        const int rows = chunk_rows(Lb, t0);
         const int64_t row0 = b * k.L + t0;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_walk_kernel(BwdArgs k)
     for (int j = 0; j < c1 - c0; ++j) {
         const int c = fwd ? c0 + j : c1 - 1 - j;
         const int64_t t0 = (int64_t)c * Q;
-        const int rows = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+        const int rows = chunk_rows(Lb, t0);
         __syncthreads();  // the previous chunk's tiles are no longer read
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -348,7 +363,8 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
     const int hpg = k.H / k.G;
     const int BH = (int)k.batch * k.H;
     const int64_t t0 = (int64_t)c * Q;
-    const int rows = (int)(k.L - t0 < Q ? k.L - t0 : Q);
+    // a chunk past its sequence's length still runs (its inputs read as zero) and records zero sums
+    const int rows = chunk_rows(bwd_seq_len(k, b), t0);
     const int64_t row0 = b * k.L + t0;
     {
         uint4 vb[1], vc[1];

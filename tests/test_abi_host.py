@@ -279,13 +279,13 @@ def test_scan_backward_shapes_and_validation():
     MB = 1 << 28
 
     def call(d, x=FAKE, dx=FAKE + 5 * MB, dB=FAKE + 6 * MB, ws=FAKE + 9 * MB, wsb=1 << 40, dA=FAKE + 8 * MB,
-             xs=None, dt=FAKE + 3 * MB):
+             xs=None, dt=FAKE + 3 * MB, lens=None):
         di = d.expand * d.d_model
         H, GN = di // d.headdim, d.n_groups * d.d_state
         return lib.m2_ssd_scan_bwd(ctypes.byref(d), x, xs or di, FAKE + 1 * MB, FAKE + 2 * MB, GN, dt, H,
                                    FAKE + 4 * MB, FAKE + 4 * MB + 4096, None, 0.0, float("inf"), None,
                                    FAKE + 10 * MB, di, None, dx, di, dB, FAKE + 7 * MB, GN, FAKE + 11 * MB, H,
-                                   dA - 8192, dA, dA + 8192, None, ws, wsb, None)
+                                   dA - 8192, dA, dA + 8192, None, ws, wsb, lens, None)
     assert call(dims(d_state=128)) == m2.M2_ERR_UNSUPPORTED
     assert call(dims(io=m2.M2_F32)) == m2.M2_ERR_UNSUPPORTED
     assert call(dims(), x=None) == m2.M2_ERR_NULL
@@ -298,3 +298,5 @@ def test_scan_backward_shapes_and_validation():
     assert call(dims(), ws=FAKE + 6 * MB) == m2.M2_ERR_ALIAS             # workspace overlaps dB
     assert call(dims(), ws=None) == m2.M2_ERR_WORKSPACE
     assert call(dims(batch=1, seqlen=32768), wsb=1 << 20) == m2.M2_ERR_WORKSPACE
+    assert call(dims(), lens=FAKE + 12 * MB + 2) == m2.M2_ERR_UNSUPPORTED  # lengths off a 4-byte boundary
+    assert call(dims(), lens=FAKE + 5 * MB + 64) == m2.M2_ERR_ALIAS        # lengths inside dx

@@ -8,7 +8,9 @@ seeded bf16 inputs, floored max-relative error <= 2e-2, and prints the errors it
     state and no final adjoint, a dt clamp that binds at both bounds, and an empty prompt;
   - the 2.7B mixer shape at 2 x 2048 tokens, every head; with four B/C groups at 2 x 4096 tokens;
   - the 32768-token prompt in the launch configuration of the benchmark, on four sampled heads (a
-    second call with dy and dstate_out zero outside them gives dB and dC over those heads alone).
+    second call with dy and dstate_out zero outside them gives dB and dC over those heads alone);
+  - right-padded batches (per-sequence lengths, padded positions left untouched), small and at the
+    2.7B shape.
 """
 import numpy as np
 import pytest
@@ -40,7 +42,7 @@ def _split(d, inp):
             c.reshape(lead + (d.n_groups, d.d_state)))
 
 
-def run_bwd(d, x, b, c, dt_raw, dt_bias, A, D, state_in, dy, ds, dt_min=0.0, dt_max=float("inf")):
+def run_bwd(d, x, b, c, dt_raw, dt_bias, A, D, state_in, dy, ds, dt_min=0.0, dt_max=float("inf"), seq_lens=None):
     """The library's backward through the C ABI; every output starts as NaN so unwritten values show."""
     dims = dims_of(d)
     B, L, H, P, N, G = d.batch, d.seqlen, d.nheads, d.headdim, d.d_state, d.n_groups
@@ -55,7 +57,8 @@ def run_bwd(d, x, b, c, dt_raw, dt_bias, A, D, state_in, dy, ds, dt_min=0.0, dt_
     m2.m2_ssd_scan_bwd(dims, dev(x, "bf16"), dev(b, "bf16"), dev(c, "bf16"), dev(dt_raw, "bf16"), dev32(dt_bias),
                        dev32(A), dev32(D), dev(dy, "bf16"), out["dx"], out["dB"], out["dC"], out["ddt_raw"],
                        out["ddt_bias"], out["dA"], out["dD"], state_in=dev32(state_in), dstate_out=dev32(ds),
-                       dstate_in=out["dstate_in"], dt_min=dt_min, dt_max=dt_max, workspace=ws)
+                       dstate_in=out["dstate_in"], dt_min=dt_min, dt_max=dt_max, workspace=ws,
+                       seq_lens=None if seq_lens is None else torch.as_tensor(np.asarray(seq_lens, np.int32), device="cuda"))
     torch.cuda.synchronize()
     res = {k: host(v) for k, v in out.items()}
     res["dx"] = res["dx"].reshape(B, L, H, P)
@@ -166,3 +169,40 @@ def test_scan_backward_groups4_2x4096_every_head():
     got = run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds)
     ref = oracle.ssd_scan_bwd(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds)
     report("backward 4 groups 2x4096", errors(got, ref))
+
+
+def _padded_errors(got, ref, lens):
+    """Errors over each sequence's real tokens; the per-token gradients past a length must be untouched."""
+    err = {}
+    for k in ("dx", "dB", "dC", "ddt_raw"):
+        e = 0.0
+        for bi, n in enumerate(lens):
+            if n:
+                e = max(e, oracle.max_rel_err(got[k][bi, :n], ref[k][bi, :n]))
+            assert np.isnan(got[k][bi, n:]).all(), "%s written past the length of sequence %d" % (k, bi)
+        err[k] = e
+    for k in ("ddt_bias", "dA", "dD", "dstate_in"):
+        err[k] = oracle.max_rel_err(got[k], ref[k])
+    return err
+
+
+@pytest.mark.parametrize("shape", ["small", "2.7b"])
+def test_scan_backward_right_padded(shape):
+    """Right-padded batches (per-sequence lengths): a full sequence, an empty one (its dstate_in is
+    dstate_out, bit for bit), one ending inside a chunk and one on a chunk boundary; and the 2.7B shape
+    at 2 x 2048 tokens with a 1000-token sequence, on a plan of several segments.  Every gradient
+    against the oracle with the same lengths; padded positions untouched."""
+    _need_gpu()
+    if shape == "small":
+        d, lens, seed = SMALL.replace(batch=4, seqlen=300), [300, 0, 131, 64], 7601
+    else:
+        d, lens, seed = workloads.CONFIGS[2].dims.replace(batch=2, seqlen=2048), [2048, 1000], 7611
+    inp = workloads.generate(d, seed, True)
+    x, b, c = _split(d, inp)
+    dy, ds = workloads.grad_inputs(d, seed + 1)
+    got = run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds, seq_lens=lens)
+    ref = oracle.ssd_scan_bwd(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds, seq_lens=lens)
+    for bi, n in enumerate(lens):
+        if n == 0:
+            assert np.array_equal(got["dstate_in"][bi], ds[bi].astype(np.float64)), "empty sequence %d" % bi
+    report("backward right-padded %s %s" % (shape, lens), _padded_errors(got, ref, lens))
