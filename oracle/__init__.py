@@ -228,6 +228,33 @@ def ssd_scan_packed(x, Bm, Cm, dt_raw, cu_seqlens, dt_bias, A, D=None, state_in=
     return y, (np.stack(states) if states else np.empty((0, H, P, N)))
 
 
+def ssd_scan_bwd_packed(x, Bm, Cm, dt_raw, cu_seqlens, dt_bias, A, D=None, state_in=None, dy=None,
+                        dstate_out=None, dt_min: float = 0.0, dt_max: float = float("inf")):
+    """Backward of ssd_scan_packed: each sequence's gradients from ssd_scan_bwd on its own rows (with
+    its own state_in[b] and dstate_out[b]); dx, dB, dC, ddt_raw [T, ...] by rows, ddt_bias, dA and dD
+    summed over the sequences, dstate_in [nseq, H, P, N]."""
+    x = _f64(x)
+    T, H, P = x.shape
+    G, N = np.asarray(Bm).shape[1], np.asarray(Bm).shape[2]
+    cu = _cu(cu_seqlens, T)
+    out = {"dx": np.empty_like(x), "dB": np.empty((T, G, N)), "dC": np.empty((T, G, N)), "ddt_raw": np.empty((T, H)),
+           "ddt_bias": np.zeros(H), "dA": np.zeros(H), "dD": np.zeros(H)}
+    dsi = []
+    for b in range(cu.size - 1):
+        sl = slice(cu[b], cu[b + 1])
+        one = lambda a: None if a is None else np.asarray(a)[b:b + 1]
+        gb = ssd_scan_bwd(x[None, sl], np.asarray(Bm)[None, sl], np.asarray(Cm)[None, sl], np.asarray(dt_raw)[None, sl],
+                          dt_bias, A, D, one(state_in), None if dy is None else np.asarray(dy)[None, sl],
+                          one(dstate_out), dt_min, dt_max)
+        for k in ("dx", "dB", "dC", "ddt_raw"):
+            out[k][sl] = gb[k][0]
+        for k in ("ddt_bias", "dA", "dD"):
+            out[k] += gb[k]
+        dsi.append(gb["dstate_in"][0])
+    out["dstate_in"] = np.stack(dsi) if dsi else np.empty((0, H, P, N))
+    return out
+
+
 def ssd_step(xbc_tok, dt_tok, w, bias, dt_bias, A, D, ring, step: int, state,
              H: int, P: int, N: int, G: int = 1,
              dt_min: float = 0.0, dt_max: float = float("inf")):

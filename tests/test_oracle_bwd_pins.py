@@ -229,3 +229,42 @@ def test_right_padded_batch_equals_each_sequence_alone():
     assert np.array_equal(g["dstate_in"][2], dS[2]), "an empty sequence passes dstate_out through"
     for k in sums:
         assert rel(g[k], sums[k]) < 1e-12, k
+
+
+def test_packed_batch_matches_derivatives_of_the_packed_forward():
+    """Packed batches (sequences back to back, each scanned on its own from its own state): the
+    gradients of L = sum dy . y + <dS, state_out> over the packed forward oracle, with an empty
+    sequence, a one-token one and two longer ones.  L is affine in x, B, C and the initial states, so
+    one step along a random direction gives the exact directional derivative; d(raw dt) and
+    dt_bias by central differences, sampled at each sequence's first and last tokens (a gradient that
+    leaked across a sequence boundary would show there)."""
+    r = np.random.default_rng(12)
+    lens = [7, 0, 1, 11]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, P, N, G = int(cu[-1]), 4, 3, 5, 2
+    c = dict(x=r.normal(size=(T, H, P)), Bm=r.normal(size=(T, G, N)) / np.sqrt(N),
+             Cm=r.normal(size=(T, G, N)) / np.sqrt(N), dt_raw=r.normal(size=(T, H)),
+             dt_bias=r.uniform(-3, -1, H), A=-np.exp(r.uniform(0, np.log(16), H)), D=r.normal(size=H),
+             state_in=r.normal(size=(len(lens), H, P, N)) * 0.5)
+    dy = r.normal(size=(T, H, P))
+    dS = r.normal(size=(len(lens), H, P, N))
+
+    def L(**over):
+        a = dict(c)
+        a.update(over)
+        y, s = oracle.ssd_scan_packed(cu_seqlens=cu, **a)
+        return float((y * dy).sum() + (s * dS).sum())
+
+    g = oracle.ssd_scan_bwd_packed(cu_seqlens=cu, **c, dy=dy, dstate_out=dS)
+    assert np.array_equal(g["dstate_in"][1], dS[1]), "an empty sequence passes dstate_out through"
+    for name, grad in (("x", "dx"), ("Bm", "dB"), ("Cm", "dC"), ("state_in", "dstate_in"), ("D", "dD")):
+        e = r.normal(size=np.shape(c[name]))
+        lhs = L(**{name: c[name] + e}) - L()
+        assert lhs == pytest.approx(float((g[grad] * e).sum()), rel=1e-9, abs=1e-9), name
+    for t in (0, 6, 7, 8, 18):
+        for h in (0, 3):
+            num = _central(lambda v: L(dt_raw=v), c["dt_raw"], (t, h), 1e-5)
+            assert num == pytest.approx(g["ddt_raw"][t, h], rel=1e-5, abs=1e-7), (t, h)
+    for h in range(H):
+        num = _central(lambda v: L(dt_bias=v), c["dt_bias"], (h,), 1e-5)
+        assert num == pytest.approx(g["ddt_bias"][h], rel=1e-5, abs=1e-7), h
