@@ -20,8 +20,9 @@
  *                    mixer needs (§三)
  *
  * A batch of prompts of different lengths (the recurrent mask of §2.3) is given either
- * right-padded (seq_lens on m2_conv1d_fwd / m2_ssd_scan_fwd) or packed back to back
- * (m2_conv1d_fwd_packed / m2_ssd_scan_fwd_packed with cu_seqlens offsets).
+ * right-padded (seq_lens on m2_conv1d_fwd / m2_ssd_scan_fwd / m2_ssd_scan_bwd) or packed back
+ * to back (m2_conv1d_fwd_packed / m2_ssd_scan_fwd_packed / m2_ssd_scan_bwd_packed with
+ * cu_seqlens offsets).
  *
  * The recurrence, per batch element b and head h, for t = 0..L-1:
  *     dt_t = softplus(dt_raw_t + dt_bias[h])        (then clamped to [dt_min, dt_max])
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define M2SSD_ABI_VERSION 6
+#define M2SSD_ABI_VERSION 7
 
 typedef enum {
     M2_OK = 0,
@@ -310,8 +311,8 @@ size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims);
  * with respect to every input of the scan, for y and state_out as m2_ssd_scan_fwd computes them
  * from the same arguments.  Built for bf16 activations at headdim 64 and d_state 64 (the
  * Zamba2-2.7B mixer shape), any batch, seqlen and n_groups dividing nheads; chunk_size is ignored
- * (chunks of 64 tokens).  Other dims return M2_ERR_UNSUPPORTED.  Right-padded batches are supported
- * (seq_lens); packed batches are not.
+ * (chunks of 64 tokens).  Other dims return M2_ERR_UNSUPPORTED.  Right-padded batches take
+ * seq_lens; packed batches take m2_ssd_scan_bwd_packed.
  * Inputs as m2_ssd_scan_fwd (x, B, C, raw dt, dt_bias, A, D or NULL, dt_min, dt_max, state_in or
  * NULL), plus
  *   dy         [batch, seqlen, nheads*headdim] io, token stride dy_tok_stride: dL/dy
@@ -352,6 +353,33 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims,
                           void* workspace, size_t workspace_bytes,
                           const int32_t* seq_lens,
                           void* stream);
+
+/* Packed batch: the same as m2_ssd_scan_bwd for dims.batch sequences back to back in arrays of
+ * total_tokens rows (x, dy, dx [total_tokens, nheads*headdim]; B, C, dB, dC [total_tokens,
+ * n_groups*d_state]; dt, ddt [total_tokens, nheads]; token strides and alignment as in
+ * m2_ssd_scan_bwd), the backward of m2_ssd_scan_fwd_packed on the same arguments.  cu_seqlens as
+ * in m2_conv1d_fwd_packed (each offset clamped to [0, total_tokens], a sequence's end to at least
+ * its start and its length to dims.seqlen); dims.seqlen is the longest sequence; workspace holds
+ * at least m2_ssd_scan_bwd_workspace(dims) bytes.  Sequence b starts from state_in[b] (or zero),
+ * dstate_out[b] is the adjoint of its state after its last token and dstate_in[b] receives the
+ * adjoint of state_in[b]; rows that no sequence covers are left as they were.  Sequences never
+ * see one another's tokens. */
+m2_status m2_ssd_scan_bwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                                 const void* x, int64_t x_tok_stride,
+                                 const void* B, const void* C, int64_t bc_tok_stride,
+                                 const void* dt, int64_t dt_tok_stride,
+                                 const float* dt_bias, const float* A, const float* D,
+                                 float dt_min, float dt_max,
+                                 const float* state_in,
+                                 const void* dy, int64_t dy_tok_stride,
+                                 const float* dstate_out,
+                                 void* dx, int64_t dx_tok_stride,
+                                 void* dB, void* dC, int64_t dbc_tok_stride,
+                                 void* ddt, int64_t ddt_tok_stride,
+                                 float* ddt_bias, float* dA, float* dD,
+                                 float* dstate_in,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* Static text for a status code. */
 const char* m2_status_str(m2_status status);

@@ -10,8 +10,8 @@ library is missing, importing this package raises.
 Names and semantics follow the C ABI:
     m2_conv1d_fwd, m2_conv1d_fwd_packed, m2_ssd_scan_workspace, m2_ssd_scan_fwd,
     m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_scan_fwd_noalloc, m2_mixer_prefill_workspace,
-    m2_mixer_prefill_fwd, m2_ssd_step, m2_gated_rmsnorm, m2_stream_copy, m2_status_str, m2_abi_version,
-    m2_last_hip_error
+    m2_mixer_prefill_fwd, m2_ssd_step, m2_gated_rmsnorm, m2_ssd_scan_bwd_workspace, m2_ssd_scan_bwd,
+    m2_ssd_scan_bwd_packed, m2_stream_copy, m2_status_str, m2_abi_version, m2_last_hip_error
 """
 from __future__ import annotations
 
@@ -27,12 +27,12 @@ M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, 
     M2_ERR_LAUNCH, M2_ERR_TOO_LARGE = range(9)
 M2_STATIC_SCRATCH_BYTES = 64 << 20
 M2_F32, M2_BF16 = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
            "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc",
            "m2_mixer_prefill_workspace", "m2_mixer_prefill_fwd", "m2_ssd_step", "m2_gated_rmsnorm", "m2_stream_copy",
-           "m2_ssd_scan_bwd_workspace", "m2_ssd_scan_bwd",
+           "m2_ssd_scan_bwd_workspace", "m2_ssd_scan_bwd", "m2_ssd_scan_bwd_packed",
            "m2_status_str", "m2_abi_version", "m2_last_hip_error")
 
 
@@ -107,6 +107,9 @@ def _load() -> ctypes.CDLL:
     lib.m2_ssd_scan_bwd.argtypes = [dp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp, i64, vp, vp, i64,
                                     vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.m2_ssd_scan_bwd.restype = ctypes.c_int
+    lib.m2_ssd_scan_bwd_packed.argtypes = [dp, i64, vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, f32, f32, vp, vp,
+                                           i64, vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.m2_ssd_scan_bwd_packed.restype = ctypes.c_int
     lib.m2_stream_copy.argtypes = [vp, vp, sz, vp]
     lib.m2_stream_copy.restype = ctypes.c_int
     lib.m2_status_str.argtypes = [ctypes.c_int]
@@ -580,6 +583,50 @@ def m2_ssd_scan_bwd(dims: M2Dims, x, B, C, dt, dt_bias, A, D, dy, dx, dB, dC, dd
           _ptr(dstate_out), _ptr(dx), dxs, _ptr(dB), _ptr(dC), dbs, _ptr(ddt), ddts, _ptr(ddt_bias), _ptr(dA),
           _ptr(dD), _ptr(dstate_in), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
           _lens_ptr(seq_lens, dims), _stream(stream))
+
+
+def m2_ssd_scan_bwd_packed(dims: M2Dims, cu_seqlens, x, B, C, dt, dt_bias, A, D, dy, dx, dB, dC, ddt, ddt_bias, dA,
+                           dD, state_in=None, dstate_out=None, dstate_in=None, dt_min: float = 0.0,
+                           dt_max: float = float("inf"), workspace=None, stream=None) -> None:
+    """Backward of the packed scan; see include/m2ssd.h.  dims.batch sequences, dims.seqlen the longest;
+    x/dy/dx [T, H, P] (or [T, H*P]), B/C/dB/dC [T, G, N], dt/ddt [T, H] (token-strided views allowed, B and
+    C sharing one stride, dB and dC another); cu_seqlens int32 [batch + 1] on the GPU; state_in,
+    dstate_out, dstate_in [batch, H, P, N] f32 or None; ddt_bias/dA/dD [H] f32; workspace: a uint8 GPU
+    tensor of at least m2_ssd_scan_bwd_workspace(dims) bytes."""
+    torch = _torch()
+    io = _io_dtype(dims)
+    H, P, N, G = dims.nheads, dims.headdim, dims.d_state, dims.n_groups
+    for n, t in (("x", x), ("B", B), ("C", C), ("dt", dt), ("dy", dy), ("dx", dx), ("dB", dB), ("dC", dC),
+                 ("ddt", ddt)):
+        _check(t, n, io)
+    for n, t in (("dt_bias", dt_bias), ("A", A), ("D", D), ("ddt_bias", ddt_bias), ("dA", dA), ("dD", dD),
+                 ("state_in", state_in), ("dstate_out", dstate_out), ("dstate_in", dstate_in)):
+        _check(t, n, torch.float32)
+    for n, t in (("dt_bias", dt_bias), ("A", A), ("D", D), ("ddt_bias", ddt_bias), ("dA", dA), ("dD", dD)):
+        if (t is None and n != "D") or (t is not None and (not t.is_contiguous() or t.numel() != H)):
+            raise ValueError("%s must be a contiguous [nheads] tensor" % n)
+    for n, t in (("state_in", state_in), ("dstate_out", dstate_out), ("dstate_in", dstate_in)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, H, P, N)):
+            raise ValueError("%s must be contiguous [batch, nheads, headdim, d_state]" % n)
+    T = int(x.shape[0])
+    xs = _packed_stride(x, "x", T, H * P)
+    bs = _packed_stride(B, "B", T, G * N)
+    if _packed_stride(C, "C", T, G * N) != bs:
+        raise ValueError("B and C must have the same token stride")
+    dts = _packed_stride(dt, "dt", T, H)
+    dys = _packed_stride(dy, "dy", T, H * P)
+    dxs = _packed_stride(dx, "dx", T, H * P)
+    dbs = _packed_stride(dB, "dB", T, G * N)
+    if _packed_stride(dC, "dC", T, G * N) != dbs:
+        raise ValueError("dB and dC must have the same token stride")
+    ddts = _packed_stride(ddt, "ddt", T, H)
+    if workspace is None:
+        raise ValueError("m2_ssd_scan_bwd_packed needs a workspace of %d bytes" % m2_ssd_scan_bwd_workspace(dims))
+    _call("m2_ssd_scan_bwd_packed", ctypes.byref(dims), T, _cu_ptr(cu_seqlens, dims), _ptr(x), xs, _ptr(B), _ptr(C),
+          bs, _ptr(dt), dts, _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min), float(dt_max), _ptr(state_in), _ptr(dy),
+          dys, _ptr(dstate_out), _ptr(dx), dxs, _ptr(dB), _ptr(dC), dbs, _ptr(ddt), ddts, _ptr(ddt_bias), _ptr(dA),
+          _ptr(dD), _ptr(dstate_in), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+          _stream(stream))
 
 
 def m2_stream_copy(dst, src, stream=None) -> None:

@@ -408,17 +408,19 @@ size_t m2_ssd_scan_bwd_workspace(const m2_dims* dims) {
     return m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H, d.G);
 }
 
-m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B, const void* C,
-                          int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
-                          const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
-                          const void* dy, int64_t dy_tok_stride, const float* dstate_out, void* dx,
-                          int64_t dx_tok_stride, void* dB, void* dC, int64_t dbc_tok_stride, void* ddt,
-                          int64_t ddt_tok_stride, float* ddt_bias, float* dA, float* dD, float* dstate_in,
-                          void* workspace, size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
-    Derived d;
-    m2_status st = derive(dims, d);
-    if (st != M2_OK) return st;
-    const int64_t rows = d.batch * d.L;
+}  // extern "C"
+
+namespace {
+
+// The backward for a right-padded batch (cu null, rows = batch * seqlen) or a packed one (rows = its
+// token count): argument checks over `rows` rows, then the launches.
+m2_status bwd_run(const Derived& d, int64_t rows, const int32_t* cu, const void* x, int64_t x_tok_stride,
+                  const void* B, const void* C, int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride,
+                  const float* dt_bias, const float* A, const float* D, float dt_min, float dt_max,
+                  const float* state_in, const void* dy, int64_t dy_tok_stride, const float* dstate_out, void* dx,
+                  int64_t dx_tok_stride, void* dB, void* dC, int64_t dbc_tok_stride, void* ddt,
+                  int64_t ddt_tok_stride, float* ddt_bias, float* dA, float* dD, float* dstate_in,
+                  void* workspace, size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
     const int GN = d.G * d.N;
     if (!dt_bias || !A || !ddt_bias || !dA || !dD) return M2_ERR_NULL;
     if (rows > 0 && (!x || !B || !C || !dt || !dy || !dx || !dB || !dC || !ddt)) return M2_ERR_NULL;
@@ -436,7 +438,7 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
                      ((uintptr_t)dt & 1u) || ((uintptr_t)ddt & 1u)))
         return M2_ERR_UNSUPPORTED;
     if (((uintptr_t)state_in & 3u) || ((uintptr_t)dstate_out & 3u) || ((uintptr_t)dstate_in & 3u) ||
-        ((uintptr_t)seq_lens & 3u))
+        ((uintptr_t)seq_lens & 3u) || ((uintptr_t)cu & 3u))
         return M2_ERR_UNSUPPORTED;
     const size_t need = m2::ssd_bwd_workspace_bytes(d.batch, d.L, d.H, d.G);
     if (!workspace || workspace_bytes < need) return M2_ERR_WORKSPACE;
@@ -445,7 +447,8 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
                          span(C, rows, bc_tok_stride, GN, 2), span(dt, rows, dt_tok_stride, d.H, 2),
                          span(dy, rows, dy_tok_stride, d.d_inner, 2), span(dt_bias, 1, 0, d.H, 4),
                          span(A, 1, 0, d.H, 4), span(D, 1, 0, d.H, 4), span(state_in, d.batch * d.H, SS, SS, 4),
-                         span(dstate_out, d.batch * d.H, SS, SS, 4), span(seq_lens, d.batch, 1, 1, 4)};
+                         span(dstate_out, d.batch * d.H, SS, SS, 4), span(seq_lens, d.batch, 1, 1, 4),
+                         span(cu, d.batch + 1, 1, 1, 4)};
     const Range outs[] = {span(dx, rows, dx_tok_stride, d.d_inner, 2), span(dB, rows, dbc_tok_stride, GN, 2),
                           span(dC, rows, dbc_tok_stride, GN, 2), span(ddt, rows, ddt_tok_stride, d.H, 2),
                           span(ddt_bias, 1, 0, d.H, 4), span(dA, 1, 0, d.H, 4), span(dD, 1, 0, d.H, 4),
@@ -469,8 +472,48 @@ m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stri
     a.ddt_bias = ddt_bias; a.dA = dA; a.dD = dD; a.dstate_in = dstate_in;
     a.batch = d.batch; a.L = d.L; a.H = d.H; a.G = d.G;
     a.lens = seq_lens;
+    a.cu = cu;
+    a.total = cu ? rows : 0;
     a.ws = workspace;
     return launched(m2::launch_ssd_scan_bwd(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+m2_status m2_ssd_scan_bwd(const m2_dims* dims, const void* x, int64_t x_tok_stride, const void* B, const void* C,
+                          int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
+                          const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
+                          const void* dy, int64_t dy_tok_stride, const float* dstate_out, void* dx,
+                          int64_t dx_tok_stride, void* dB, void* dC, int64_t dbc_tok_stride, void* ddt,
+                          int64_t ddt_tok_stride, float* ddt_bias, float* dA, float* dD, float* dstate_in,
+                          void* workspace, size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    return bwd_run(d, d.batch * d.L, nullptr, x, x_tok_stride, B, C, bc_tok_stride, dt, dt_tok_stride, dt_bias, A, D,
+                   dt_min, dt_max, state_in, dy, dy_tok_stride, dstate_out, dx, dx_tok_stride, dB, dC, dbc_tok_stride,
+                   ddt, ddt_tok_stride, ddt_bias, dA, dD, dstate_in, workspace, workspace_bytes, seq_lens, stream);
+}
+
+m2_status m2_ssd_scan_bwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                                 const void* x, int64_t x_tok_stride, const void* B, const void* C,
+                                 int64_t bc_tok_stride, const void* dt, int64_t dt_tok_stride, const float* dt_bias,
+                                 const float* A, const float* D, float dt_min, float dt_max, const float* state_in,
+                                 const void* dy, int64_t dy_tok_stride, const float* dstate_out, void* dx,
+                                 int64_t dx_tok_stride, void* dB, void* dC, int64_t dbc_tok_stride, void* ddt,
+                                 int64_t ddt_tok_stride, float* ddt_bias, float* dA, float* dD, float* dstate_in,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    if (total_tokens < 0) return M2_ERR_SHAPE;
+    if (d.batch > 0 && !cu_seqlens) return M2_ERR_NULL;
+    return bwd_run(d, total_tokens, cu_seqlens, x, x_tok_stride, B, C, bc_tok_stride, dt, dt_tok_stride, dt_bias, A,
+                   D, dt_min, dt_max, state_in, dy, dy_tok_stride, dstate_out, dx, dx_tok_stride, dB, dC,
+                   dbc_tok_stride, ddt, ddt_tok_stride, ddt_bias, dA, dD, dstate_in, workspace, workspace_bytes,
+                   nullptr, stream);
 }
 
 m2_status m2_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {

@@ -90,6 +90,8 @@ struct BwdArgs {
     int64_t batch, L;
     int H, G;
     const int32_t* lens;  // [batch] valid tokens per sequence (device), or null
+    const int32_t* cu;    // packed batch: [batch+1] first row of each sequence (device), or null
+    int64_t total;        // packed batch: rows of the packed arrays
     void* ws;
     // set by the launcher
     int nch, nseg, cps;  // 64-token chunks, segments of the walks, chunks per segment

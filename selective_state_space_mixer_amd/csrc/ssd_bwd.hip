@@ -129,10 +129,21 @@ __device__ __forceinline__ void put_tile_split(uint16_t* hi, uint16_t* lo, const
     }
 }
 
-// Tokens of sequence b: seqlen, or its length in a right-padded batch (clamped to [0, seqlen]).  A
-// padded token reads as zero x, B, C, dy and dt, so it changes neither the state nor the adjoint, and
-// its gradients are not stored.
+// Sequence b: its first row (b * seqlen, or cu[b] in a packed batch) and its tokens (seqlen, its
+// length in a right-padded batch, or the offset difference in a packed one; clamped to the rows that
+// exist and to seqlen).  A token past the length reads as zero x, B, C, dy and dt, so it changes
+// neither the state nor the adjoint, and its gradients are not stored.
+__device__ __forceinline__ int64_t bwd_row0(const BwdArgs& k, int64_t b) {
+    if (!k.cu) return b * k.L;
+    const int64_t r0 = k.cu[b];
+    return r0 < 0 ? 0 : (r0 > k.total ? k.total : r0);
+}
 __device__ __forceinline__ int64_t bwd_seq_len(const BwdArgs& k, int64_t b) {
+    if (k.cu) {
+        const int64_t row0 = bwd_row0(k, b), r1 = k.cu[b + 1];
+        const int64_t end = r1 < row0 ? row0 : (r1 > k.total ? k.total : r1);
+        return end - row0 < k.L ? end - row0 : k.L;
+    }
     if (!k.lens) return k.L;
     const int64_t v = k.lens[b];
     return v < 0 ? 0 : (v > k.L ? k.L : v);
@@ -198,11 +209,11 @@ __global__ __launch_bounds__(bwd::THREADS) void ssd_bwd_walk_kernel(BwdArgs k)
     // wave's own tile: unit u = lane + 64 m is row u / 8, columns 8 (u % 8) .. +7
     uint4 vt[8], vg[2];
     float raw_n = 0.0f;
-    const int64_t Lb = bwd_seq_len(k, b);
+    const int64_t Lb = bwd_seq_len(k, b), srow = bwd_row0(k, b);
     auto fetch = [&](int c) __attribute__((always_inline)) {
         const int64_t t0 = (int64_t)c * Q;
         const int rows = chunk_rows(Lb, t0);
-        const int64_t row0 = b * k.L + t0;
+        const int64_t row0 = srow + t0;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int u = lane + 64 * m, r = u >> 3, c8 = u & 7;
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(bwd::GTHREADS) void ssd_bwd_grad_kernel(BwdArgs k)
     const int64_t t0 = (int64_t)c * Q;
     // a chunk past its sequence's length still runs (its inputs read as zero) and records zero sums
     const int rows = chunk_rows(bwd_seq_len(k, b), t0);
-    const int64_t row0 = b * k.L + t0;
+    const int64_t row0 = bwd_row0(k, b) + t0;
     {
         uint4 vb[1], vc[1];
         fetch_tile<NT>(vb, k.B + row0 * k.bcs + (int64_t)g * N, k.bcs, rows);

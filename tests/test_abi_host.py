@@ -300,3 +300,29 @@ def test_scan_backward_shapes_and_validation():
     assert call(dims(batch=1, seqlen=32768), wsb=1 << 20) == m2.M2_ERR_WORKSPACE
     assert call(dims(), lens=FAKE + 12 * MB + 2) == m2.M2_ERR_UNSUPPORTED  # lengths off a 4-byte boundary
     assert call(dims(), lens=FAKE + 5 * MB + 64) == m2.M2_ERR_ALIAS        # lengths inside dx
+
+
+def test_packed_scan_backward_validation():
+    """The packed backward checks its token count, offsets pointer and packed rows before any launch;
+    an empty batch, or a batch with no tokens, is a valid no-op."""
+    lib = m2.lib()
+    MB = 1 << 28
+
+    def call(d, T=4096, cu=FAKE + 12 * MB, x=FAKE, dx=FAKE + 5 * MB, xs=None, ws=FAKE + 9 * MB, wsb=1 << 40):
+        di = d.expand * d.d_model
+        H, GN = di // d.headdim, d.n_groups * d.d_state
+        return lib.m2_ssd_scan_bwd_packed(ctypes.byref(d), T, cu, x, xs or di, FAKE + 1 * MB, FAKE + 2 * MB, GN,
+                                          FAKE + 3 * MB, H, FAKE + 4 * MB, FAKE + 4 * MB + 4096, None, 0.0,
+                                          float("inf"), None, FAKE + 10 * MB, di, None, dx, di, FAKE + 6 * MB,
+                                          FAKE + 7 * MB, GN, FAKE + 11 * MB, H, FAKE + 8 * MB - 8192, FAKE + 8 * MB,
+                                          FAKE + 8 * MB + 8192, None, ws, wsb, None)
+    assert call(dims(), T=-1) == m2.M2_ERR_SHAPE
+    assert call(dims(), cu=None) == m2.M2_ERR_NULL
+    assert call(dims(), cu=FAKE + 12 * MB + 2) == m2.M2_ERR_UNSUPPORTED  # offsets off a 4-byte boundary
+    assert call(dims(), cu=FAKE + 5 * MB + 64) == m2.M2_ERR_ALIAS        # offsets inside dx
+    assert call(dims(), x=None) == m2.M2_ERR_NULL
+    assert call(dims(), xs=8) == m2.M2_ERR_SHAPE
+    assert call(dims(d_state=128)) == m2.M2_ERR_UNSUPPORTED
+    assert call(dims(), ws=None) == m2.M2_ERR_WORKSPACE
+    # dx spans the packed rows: an x starting in its last of 512 rows overlaps it
+    assert call(dims(batch=8, seqlen=4096), T=512, dx=FAKE, x=FAKE + 511 * 5120 * 2) == m2.M2_ERR_ALIAS

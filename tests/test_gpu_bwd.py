@@ -10,7 +10,10 @@ seeded bf16 inputs, floored max-relative error <= 2e-2, and prints the errors it
   - the 32768-token prompt in the launch configuration of the benchmark, on four sampled heads (a
     second call with dy and dstate_out zero outside them gives dB and dC over those heads alone);
   - right-padded batches (per-sequence lengths, padded positions left untouched), small and at the
-    2.7B shape.
+    2.7B shape;
+  - packed batches (sequences back to back at cu_seqlens offsets, each from its own state) against
+    oracle.ssd_scan_bwd_packed, small (an empty, a one-token, a mid-chunk and a chunk-aligned
+    sequence) and at the 2.7B shape; rows after the last sequence left untouched.
 """
 import numpy as np
 import pytest
@@ -206,3 +209,49 @@ def test_scan_backward_right_padded(shape):
         if n == 0:
             assert np.array_equal(got["dstate_in"][bi], ds[bi].astype(np.float64)), "empty sequence %d" % bi
     report("backward right-padded %s %s" % (shape, lens), _padded_errors(got, ref, lens))
+
+
+@pytest.mark.parametrize("shape", ["small", "2.7b"])
+def test_scan_backward_packed(shape):
+    """Packed batches through m2_ssd_scan_bwd_packed: each sequence's gradients on its own rows, from its
+    own state_in and dstate_out; an empty sequence's dstate_in is its dstate_out, bit for bit.  The
+    packed arrays carry 5 spare rows past the last sequence, which must stay untouched."""
+    _need_gpu()
+    if shape == "small":
+        lens, base, seed = [130, 0, 1, 64, 77], SMALL, 7701
+    else:
+        lens, base, seed = [1500, 64, 2048, 333], workloads.CONFIGS[2].dims, 7711
+    d = base.replace(batch=len(lens), seqlen=max(lens))
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    inp = workloads.generate(d, seed, True)
+    x, b, c = _split(d, inp)
+    dy, ds = workloads.grad_inputs(d, seed + 1)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pack = lambda a: np.concatenate([a[i, :n] for i, n in enumerate(lens)], 0)
+    xp, bp, cp, dtp, dyp = pack(x), pack(b), pack(c), pack(inp.dt_raw), pack(dy)
+    T, spare = int(cu[-1]), 5
+    dims = dims_of(d)
+    out = {"dx": nan_like((T + spare, H * P), "bf16"), "dB": nan_like((T + spare, G * N), "bf16"),
+           "dC": nan_like((T + spare, G * N), "bf16"), "ddt_raw": nan_like((T + spare, H), "bf16")}
+    for k in ("ddt_bias", "dA", "dD"):
+        out[k] = torch.full((H,), float("nan"), device="cuda")
+    out["dstate_in"] = torch.full((d.batch, H, P, N), float("nan"), device="cuda")
+    ws = torch.empty(m2.m2_ssd_scan_bwd_workspace(dims), dtype=torch.uint8, device="cuda")
+    m2.m2_ssd_scan_bwd_packed(dims, torch.as_tensor(cu, device="cuda"), dev(xp, "bf16"), dev(bp, "bf16"),
+                              dev(cp, "bf16"), dev(dtp, "bf16"), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D),
+                              dev(dyp, "bf16"), out["dx"][:T], out["dB"][:T], out["dC"][:T], out["ddt_raw"][:T],
+                              out["ddt_bias"], out["dA"], out["dD"], state_in=dev32(inp.state0),
+                              dstate_out=dev32(ds), dstate_in=out["dstate_in"], workspace=ws)
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in out.items()}
+    for k in ("dx", "dB", "dC", "ddt_raw"):
+        assert np.isnan(got[k][T:]).all(), "%s written past the last sequence" % k
+        got[k] = got[k][:T]
+    got["dx"] = got["dx"].reshape(T, H, P)
+    got["dB"] = got["dB"].reshape(T, G, N)
+    got["dC"] = got["dC"].reshape(T, G, N)
+    ref = oracle.ssd_scan_bwd_packed(xp, bp, cp, dtp, cu, inp.dt_bias, inp.A, inp.D, inp.state0, dyp, ds)
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert np.array_equal(got["dstate_in"][i], ds[i].astype(np.float64)), "empty sequence %d" % i
+    report("backward packed %s %s" % (shape, lens), errors(got, ref))
