@@ -48,6 +48,7 @@
 #include "ssd_common.h"
 
 #include <mutex>
+#include <numeric>
 
 namespace m2 {
 
@@ -950,11 +951,16 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH);
     e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k, BH, P * N);
     if (e != hipSuccess) return e;
-    // about one chunk to fix per wave on the 32k prompt's figures; at most one round of resident blocks
+    // about one chunk to fix per wave on the 32k prompt's figures; at most one round of resident
+    // blocks.  Block b takes candidates b, b + nblocks, ... of the (segment, head, chunk) order, so a
+    // block count sharing a factor f with the chunks per segment would give each block only chunks
+    // j = b (mod f) of their segments, and the blocks holding the leading chunks (the ones that
+    // need the term) would carry f times their share: the count is made coprime to cps.
     const int64_t ncand = (int64_t)(pl.nseg - 1) * BH * pl.cps;
     int64_t nfb = (ncand + 63) / 64;
     const int64_t cap = (int64_t)device_shape().cus * kFixBlocksPerCU;
     nfb = nfb < cap ? nfb : cap;
+    while (nfb > 1 && std::gcd(nfb, (int64_t)pl.cps) > 1) --nfb;
     return launch_kernel(ssd_segment_fix_kernel<T, Q, P, N>, dim3((unsigned)nfb), dim3(kFixThreads), 0, s, k);
 }
 
