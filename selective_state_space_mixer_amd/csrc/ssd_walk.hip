@@ -90,7 +90,10 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
     const int64_t row_begin = c_begin * Q;
     const int64_t row_end = Lb < row_begin + (int64_t)nc * Q ? Lb : row_begin + (int64_t)nc * Q;
     const float bias_h = k.dt_bias[h], A_h = k.A[h];
-    const float D_h = k.D ? k.D[h] : 0.0f;
+    // the fused kernel's x operands carry a factor log2(e) (see the conv below); every factor that
+    // multiplies x (D here, dt, w and gs in the statistics) carries ln 2 to cancel it
+    constexpr float xs_inv = FUSED ? 0.6931471805599453f : 1.0f;
+    const float D_h = (k.D ? k.D[h] : 0.0f) * xs_inv;
 
     // ---- tile loads: piece m (0..3) of this wave's X tile (rows 8m..8m+7), piece w of B and of C, and
     // the raw dt of tokens 8w..8w+7 for the block's four heads.
@@ -128,6 +131,8 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
 
     // ---- fused: this lane's conv taps and bias for its four x channels p = 16 pb + li of head h, taps
     // right-aligned (tap 3 multiplies the current token; a narrower conv leaves the first taps zero).
+    // The taps and the bias are scaled by log2(e), so the conv gives b = log2(e) a and SiLU needs no
+    // scale before the base-2 exponential.
     // Transposing reads of raw rows 4g .. 4g+3 of column block cb sit at base(g) ^ (2 cb << 4); the
     // lanes of q-group q read row groups q-1, q (tokens 4q-4 .. 4q+3) and q+3, q+4 (16+4q-4 .. 16+4q+3).
     // Group -1 is the halo: the last raw rows of the chunk before, kept as rows 28..31 in sHalo.
@@ -138,8 +143,8 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
         for (int pb = 0; pb < 4; ++pb) {
             const int64_t c = (int64_t)h * P + 16 * pb + li;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) cw[pb][t] = t >= 4 - cv.W ? cv.w[c * cv.W + (t - (4 - cv.W))] : 0.0f;
-            cb4[pb] = cv.bias ? cv.bias[c] : 0.0f;
+            for (int t = 0; t < 4; ++t) cw[pb][t] = t >= 4 - cv.W ? cv.w[c * cv.W + (t - (4 - cv.W))] * kLog2e : 0.0f;
+            cb4[pb] = cv.bias ? cv.bias[c] * kLog2e : 0.0f;
         }
         auto gbase = [&](int r) __attribute__((always_inline)) {
             return r * ROWB + ((((li >> 1) & 1) ^ rowperm(r)) << 4) + 8 * (li & 1);
@@ -234,10 +239,11 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
         if (lane < Q) {
             float* st = &sSt[sbuf][w][0][lane];
             st[0 * Q] = lam * kLog2e;
-            st[1 * Q] = dtv;
-            st[2 * Q] = fast_exp(wexp) * dtv;
+            const float dtx = dtv * xs_inv;
+            st[1 * Q] = dtx;
+            st[2 * Q] = fast_exp(wexp) * dtx;
             st[3 * Q] = fast_exp(lam + sig_prev);
-            st[4 * Q] = fast_exp(lam_blk - lam) * dtv;
+            st[4 * Q] = fast_exp(lam_blk - lam) * dtx;
         }
         if (lane == 0 && k.ws_lamc && hvalid) k.ws_lamc[(c_begin + i) * BH + bh] = lam_before;
         dec_o = rescale ? fast_exp(sig_prev + lam_end) : 1.0f;
@@ -286,7 +292,6 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
         const float dec = dec_n;
         const bool split_diag = lamend_n > -60.0f;  // every e^(Lam_t - Lam_s) splits into two finite factors
         if (i + 2 < nc) stream(i + 2, tnext2);
-        if (i + 1 < nc) stats(i + 1, tnext, sbuf ^ 1, dec_n, lamend_n);
         uint8_t* const T = &tiles[tcur * BUFB];
         uint8_t* const Xt = T + w * TILEB;
         const uint8_t* const Bt = T + BOFF;
@@ -305,6 +310,9 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 const uint2 a = lds_read8(Ct, row_off(tb, ks, 0)), c = lds_read8(Ct, row_off(tb, ks, 1));
                 cf[tb][ks].w[0] = a.x; cf[tb][ks].w[1] = a.y; cf[tb][ks].w[2] = c.x; cf[tb][ks].w[3] = c.y;
             }
+        // Raised wave priority around the MFMA bursts: of the two waves on a SIMD, the one with matrix
+        // products to issue goes first, and the other's VALU work fills in beside them.
+        __builtin_amdgcn_s_setprio(1);
         // state part: Y^T[p][t] = sum_n S[p][n] C[t][n], the state's bf16 copy as the A operand
         f32x4 accY[2][4];
 #pragma unroll
@@ -339,6 +347,7 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                     mfma(g11, bf, cf[1][ks]);
                 }
             }
+        __builtin_amdgcn_s_setprio(0);
         // X columns (k = token s): A operand of the intra part, and the source of w_s x_s
         Frag<bf16_t> xf[4];
         Frag<bf16_t> xwh[4], xwl[4];  // w_s x_s as bf16 hi + lo (fused: from the fp32 conv output)
@@ -362,13 +371,14 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 v[1][4] = lo_bf16(rd.x); v[1][5] = hi_bf16(rd.x); v[1][6] = lo_bf16(rd.y); v[1][7] = hi_bf16(rd.y);
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    float xo[4];
+                    float xo[4];  // log2(e) SiLU(conv) of tokens 4q+j (c = 0) or 16+4q+j (c = 1)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        float a = cb4[pb];
+                        float bv = cb4[pb];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) a = fmaf(cw[pb][t], v[c][j + 1 + t], a);
-                        xo[j] = silu(a);
+                        for (int t = 0; t < 4; ++t) bv = fmaf(cw[pb][t], v[c][j + 1 + t], bv);
+                        // log2(e) a / (1 + e^-a) with bv = log2(e) a
+                        xo[j] = bv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-bv));
                     }
                     xf[pb].set(c, xo[0], xo[1], xo[2], xo[3]);
                     const float4 wv = c == 0 ? w0 : w1;
@@ -441,6 +451,7 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 ml[tb].w[2 * sb + 1] = pack_bf16x2(m[2] - lo_bf16(h23), m[3] - hi_bf16(h23));
             }
         }
+        __builtin_amdgcn_s_setprio(1);
         // intra part: Y^T[p][t] += sum_s X[s][p] M[t][s]
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -486,6 +497,10 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 mfma(accS[pb][nb], bt[nb], xwl[pb]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
+        // the next chunk's statistics, issued behind the state-update products (they write the other
+        // statistics buffer, which this chunk does not read)
+        if (i + 1 < nc) stats(i + 1, tnext, sbuf ^ 1, dec_n, lamend_n);
         // y out: lane (q, li) holds y[t = 16 tb + li][p = 16 pb + 4q .. +3]; staged (in this wave's own
         // X tile, whose reads are done) so that each store instruction writes eight whole 128-byte rows
 #pragma unroll
