@@ -605,11 +605,13 @@ ssd_chunk_scan_kernel(ScanK k)
 //   T[0] = E[0],  T[seg] = e^lam[seg] T[seg-1] + E[seg];
 // T[seg] (the initial state of segment seg+1) is written over E[seg] (or, for bf16 outputs, to a
 // bf16 copy), and T[nseg-1] is the final state.  Only the combine is sequential: the loads of a
-// batch of segments are issued together.  The first block of each sequence-head also chains the
-// bounds Tb[seg] on max|T[seg]| from the segments' recorded maxima (see fix_cut).
+// batch of segments are issued together (kBatch of them: 8 for the few segments of a packed batch's
+// plan, whose registers then leave room for more waves, else 32), and only segments that exist are
+// loaded.  The first block of each sequence-head also chains the bounds Tb[seg] on max|T[seg]| from
+// the segments' recorded maxima (see fix_cut).
+template <int kBatch>
 __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(ScanK k, int BH, int PN)
 {
-    constexpr int kBatch = 32;  // segments whose loads are issued together
     const int nseg = k.nseg;
     const int bh = blockIdx.y;
     float* __restrict__ ws_state = k.ws_state;
@@ -628,10 +630,12 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(ScanK k, int BH,
         float dec[kBatch], em[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const int seg = seg0 + j < nseg ? seg0 + j : nseg - 1;
-            loc[j] = *reinterpret_cast<const float4*>(ws_state + ((int64_t)seg * BH + bh) * PN + i);
-            dec[j] = ws_lam[(int64_t)seg * BH + bh];
-            em[j] = ws_emax[(int64_t)seg * BH + bh];
+            const int seg = seg0 + j;
+            if (seg < nseg) {
+                loc[j] = *reinterpret_cast<const float4*>(ws_state + ((int64_t)seg * BH + bh) * PN + i);
+                dec[j] = ws_lam[(int64_t)seg * BH + bh];
+                em[j] = ws_emax[(int64_t)seg * BH + bh];
+            }
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
@@ -949,7 +953,8 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     else e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
     if (e != hipSuccess || pl.nseg == 1) return e;
     dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH);
-    e = launch_kernel(ssd_segment_chain_kernel, g2, dim3(256), 0, s, k, BH, P * N);
+    e = pl.nseg <= 8 ? launch_kernel(ssd_segment_chain_kernel<8>, g2, dim3(256), 0, s, k, BH, P * N)
+                     : launch_kernel(ssd_segment_chain_kernel<32>, g2, dim3(256), 0, s, k, BH, P * N);
     if (e != hipSuccess) return e;
     // about one chunk to fix per wave on the 32k prompt's figures; at most one round of resident
     // blocks.  Block b takes candidates b, b + nblocks, ... of the (segment, head, chunk) order, so a
