@@ -184,6 +184,10 @@ def roofline(bytes_per_launch, ms, kernel=None):
     gbs = bytes_per_launch / (ms * 1e-3) / 1e9
     r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel) if kernel else None}
+    if r["traffic"] is not None:
+        # the counters are not collected in this run: the figure is the committed rocprofv3 summary's, valid
+        # while the kernel sources hash to what was profiled
+        r["traffic_source"] = "profiles/traffic.json (rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)"
     if COPY_CEILING[0]:
         r["frac_of_copy"] = round(gbs / COPY_CEILING[0], 4)
     return r
