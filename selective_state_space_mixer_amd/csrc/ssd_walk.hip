@@ -451,7 +451,7 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 ml[tb].w[2 * sb + 1] = pack_bf16x2(m[2] - lo_bf16(h23), m[3] - hi_bf16(h23));
             }
         }
-        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_setprio(2);
         // intra part: Y^T[p][t] += sum_s X[s][p] M[t][s]
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
