@@ -7,6 +7,7 @@
   (the Zamba2 article §七: the token-by-token path must agree with the chunked prefill);
 - a bf16 decode step at headdim 64 / d_state 128 (the 130m-like shape);
 - every channel of the full-size conv (32k prompt and the 8 x 4096 batch with history).
+- plans of more segments than the segment chain loads at once (down to one chunk per segment).
 Floored max-relative-error bar 2e-2 for bf16 activations with fp32 state; conv rings bit-exact."""
 import numpy as np
 import pytest
@@ -315,3 +316,30 @@ def test_large_initial_state_across_segments_per_token(idx, over, scale):
     print("initial state x%.0e: worst token after the first segment (from token %d) %.2e, state %.2e"
           % (scale, first, et, es))
     assert et <= TOL and es <= TOL
+
+
+@pytest.mark.parametrize("idx,over", [(0, dict(seqlen=1000)), (3, dict(d_model=128, seqlen=1300))],
+                         ids=["tiny-f32-63-segments", "2.7b-4-heads-bf16-41-segments"])
+def test_scan_plan_of_more_segments_than_one_load_batch(idx, over):
+    """Few heads and a long prompt: the plan cuts the sequence into more segments than the chain kernel
+    loads at once (32), down to one chunk per segment, so the chain runs over several load batches and
+    nearly every chunk is a segment's first.  Checked against the oracle with a random initial state."""
+    _need_gpu()
+    d = workloads.CONFIGS[idx].dims.replace(**over)
+    inp = workloads.generate(d, 6900 + idx, True)
+    x, b, c = _split(d, inp)
+    dims = dims_of(d)
+    # the workspace holds one fp32 state per (segment, sequence, head): more than 32 segments
+    per_seg = d.batch * d.nheads * d.headdim * d.d_state * 4
+    assert m2.m2_ssd_scan_workspace(dims) > 33 * per_seg, "expected a plan of more than 32 segments"
+    y = nan_like((d.batch, d.seqlen, d.d_inner), d.io)
+    s = torch.full((d.batch, d.nheads, d.headdim, d.d_state), float("nan"), device="cuda")
+    m2.m2_ssd_scan_fwd(dims, dev(x, d.io), dev(b, d.io), dev(c, d.io), dev(inp.dt_raw, d.io), dev32(inp.dt_bias),
+                       dev32(inp.A), dev32(inp.D), y, dev32(inp.state0), s, workspace=workspace(dims))
+    torch.cuda.synchronize()
+    yr, sr = oracle.ssd_scan(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0)
+    ey = oracle.max_rel_err(host(y).reshape(yr.shape), yr)
+    es = oracle.max_rel_err(host(s), sr)
+    tol = 1e-4 if d.io == "f32" else TOL
+    print("plan of many segments (%s): y %.2e state %.2e (bar %.0e)" % (d.io, ey, es, tol))
+    assert ey <= tol and es <= tol
