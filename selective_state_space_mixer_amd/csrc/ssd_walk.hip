@@ -310,8 +310,9 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
                 const uint2 a = lds_read8(Ct, row_off(tb, ks, 0)), c = lds_read8(Ct, row_off(tb, ks, 1));
                 cf[tb][ks].w[0] = a.x; cf[tb][ks].w[1] = a.y; cf[tb][ks].w[2] = c.x; cf[tb][ks].w[3] = c.y;
             }
-        // Raised wave priority around the MFMA bursts: of the two waves on a SIMD, the one with matrix
-        // products to issue goes first, and the other's VALU work fills in beside them.
+        // Raised wave priority around the MFMA bursts (1 for the state part and G, 2 for the intra part
+        // and the state update): of the two waves on a SIMD, the one with matrix products to issue goes
+        // first, and the other's VALU work fills in beside them.
         __builtin_amdgcn_s_setprio(1);
         // state part: Y^T[p][t] = sum_n S[p][n] C[t][n], the state's bf16 copy as the A operand
         f32x4 accY[2][4];
