@@ -70,6 +70,9 @@ FUSED_CASES = [
     (dict(batch=2, seqlen=130, d_conv=2), True, 0, True),  # conv width 2
     (dict(batch=2, seqlen=200, n_groups=2), True, 0, True),
     (dict(batch=1, seqlen=700, n_groups=4), False, 0, True),
+    # four heads and 41 chunks: 41 one-chunk segments, every block a segment start taking its conv
+    # window from memory, and a segment chain longer than one load batch
+    (dict(batch=1, seqlen=1300, d_model=128), True, 1, True),
 ]
 
 
