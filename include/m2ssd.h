@@ -20,9 +20,9 @@
  *                    mixer needs (§三)
  *
  * A batch of prompts of different lengths (the recurrent mask of §2.3) is given either
- * right-padded (seq_lens on m2_conv1d_fwd / m2_ssd_scan_fwd / m2_ssd_scan_bwd) or packed back
- * to back (m2_conv1d_fwd_packed / m2_ssd_scan_fwd_packed / m2_ssd_scan_bwd_packed with
- * cu_seqlens offsets).
+ * right-padded (seq_lens on m2_conv1d_fwd / m2_ssd_scan_fwd / m2_mixer_prefill_fwd /
+ * m2_ssd_scan_bwd) or packed back to back (m2_conv1d_fwd_packed / m2_ssd_scan_fwd_packed /
+ * m2_mixer_prefill_fwd_packed / m2_ssd_scan_bwd_packed with cu_seqlens offsets).
  *
  * The recurrence, per batch element b and head h, for t = 0..L-1:
  *     dt_t = softplus(dt_raw_t + dt_bias[h])        (then clamped to [dt_min, dt_max])
@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define M2SSD_ABI_VERSION 7
+#define M2SSD_ABI_VERSION 8
 
 typedef enum {
     M2_OK = 0,
@@ -231,6 +231,31 @@ m2_status m2_mixer_prefill_fwd(const m2_dims* dims,
                                void* workspace, size_t workspace_bytes,
                                const int32_t* seq_lens,
                                void* stream);
+
+/* Workspace bytes m2_mixer_prefill_fwd_packed needs for dims (dims.seqlen the longest sequence) and
+ * total_tokens rows (0 when the fused path is not built for these dims, or if the arguments are
+ * invalid).  It sizes the scan's segments from the total, as m2_ssd_scan_workspace_packed does. */
+size_t m2_mixer_prefill_workspace_packed(const m2_dims* dims, int64_t total_tokens);
+
+/* Packed batch: the same as m2_mixer_prefill_fwd for dims.batch sequences back to back in arrays of
+ * total_tokens rows (xbc [total_tokens, conv_dim], dt [total_tokens, nheads], y [total_tokens,
+ * nheads*headdim], with token strides and alignment as in m2_mixer_prefill_fwd).  cu_seqlens as in
+ * m2_conv1d_fwd_packed; dims.seqlen is the longest sequence; workspace holds at least
+ * m2_mixer_prefill_workspace_packed(dims, total_tokens) bytes.  Each sequence starts from its own
+ * conv history ring_in[b] and state_in[b] (or zeros) and returns ring_out[b] and state_out[b], as
+ * m2_conv1d_fwd_packed and m2_ssd_scan_fwd_packed do.  Sequences never see one another's tokens. */
+m2_status m2_mixer_prefill_fwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                                      const void* xbc, int64_t xbc_tok_stride,
+                                      const float* conv_w, const float* conv_b,
+                                      const void* ring_in, int64_t ring_in_step,
+                                      void* ring_out,
+                                      const void* dt, int64_t dt_tok_stride,
+                                      const float* dt_bias, const float* A, const float* D,
+                                      float dt_min, float dt_max,
+                                      const float* state_in, float* state_out,
+                                      void* y, int64_t y_tok_stride,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* m2_ssd_scan_fwd without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The

@@ -10,7 +10,7 @@ library is missing, importing this package raises.
 Names and semantics follow the C ABI:
     m2_conv1d_fwd, m2_conv1d_fwd_packed, m2_ssd_scan_workspace, m2_ssd_scan_fwd,
     m2_ssd_scan_workspace_packed, m2_ssd_scan_fwd_packed, m2_ssd_scan_fwd_noalloc, m2_mixer_prefill_workspace,
-    m2_mixer_prefill_fwd, m2_ssd_step, m2_gated_rmsnorm, m2_ssd_scan_bwd_workspace, m2_ssd_scan_bwd,
+    m2_mixer_prefill_fwd, m2_mixer_prefill_workspace_packed, m2_mixer_prefill_fwd_packed, m2_ssd_step, m2_gated_rmsnorm, m2_ssd_scan_bwd_workspace, m2_ssd_scan_bwd,
     m2_ssd_scan_bwd_packed, m2_stream_copy, m2_status_str, m2_abi_version, m2_last_hip_error
 """
 from __future__ import annotations
@@ -27,11 +27,12 @@ M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIAS, M2_ERR_WORKSPACE, 
     M2_ERR_LAUNCH, M2_ERR_TOO_LARGE = range(9)
 M2_STATIC_SCRATCH_BYTES = 64 << 20
 M2_F32, M2_BF16 = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 EXPORTS = ("m2_conv1d_fwd", "m2_conv1d_fwd_packed", "m2_ssd_scan_workspace", "m2_ssd_scan_fwd",
            "m2_ssd_scan_workspace_packed", "m2_ssd_scan_fwd_packed", "m2_ssd_scan_fwd_noalloc",
-           "m2_mixer_prefill_workspace", "m2_mixer_prefill_fwd", "m2_ssd_step", "m2_gated_rmsnorm", "m2_stream_copy",
+           "m2_mixer_prefill_workspace", "m2_mixer_prefill_fwd", "m2_mixer_prefill_workspace_packed",
+           "m2_mixer_prefill_fwd_packed", "m2_ssd_step", "m2_gated_rmsnorm", "m2_stream_copy",
            "m2_ssd_scan_bwd_workspace", "m2_ssd_scan_bwd", "m2_ssd_scan_bwd_packed",
            "m2_status_str", "m2_abi_version", "m2_last_hip_error")
 
@@ -97,6 +98,11 @@ def _load() -> ctypes.CDLL:
     lib.m2_mixer_prefill_fwd.argtypes = [dp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, f32, f32, vp, vp, vp,
                                          i64, vp, sz, vp, vp]
     lib.m2_mixer_prefill_fwd.restype = ctypes.c_int
+    lib.m2_mixer_prefill_workspace_packed.argtypes = [dp, i64]
+    lib.m2_mixer_prefill_workspace_packed.restype = sz
+    lib.m2_mixer_prefill_fwd_packed.argtypes = [dp, i64, vp, vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp, f32,
+                                                f32, vp, vp, vp, i64, vp, sz, vp]
+    lib.m2_mixer_prefill_fwd_packed.restype = ctypes.c_int
     lib.m2_ssd_step.argtypes = [dp, vp, i64, vp, i64, vp, vp, vp, vp, vp, f32, f32, vp, i64, vp, vp, vp]
     lib.m2_ssd_step.restype = ctypes.c_int
     lib.m2_gated_rmsnorm.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, i64, vp, i64, vp, f32,
@@ -457,6 +463,56 @@ def m2_ssd_scan_fwd_packed(dims: M2Dims, cu_seqlens, x, B, C, dt, dt_bias, A, D,
     _call("m2_ssd_scan_fwd_packed", ctypes.byref(dims), T, _cu_ptr(cu_seqlens, dims), _ptr(x), xs, _ptr(B), _ptr(C),
           bs, _ptr(dt), dts, _ptr(dt_bias), _ptr(A), _ptr(D), float(dt_min), float(dt_max), _ptr(state_in),
           _ptr(state_out), _ptr(y), ys, ws_ptr, ws_bytes, _stream(stream))
+
+
+def m2_mixer_prefill_workspace_packed(dims: M2Dims, total_tokens: int) -> int:
+    return int(_lib.m2_mixer_prefill_workspace_packed(ctypes.byref(dims), int(total_tokens)))
+
+
+def m2_mixer_prefill_fwd_packed(dims: M2Dims, cu_seqlens, xbc, w, bias, dt, dt_bias, A, D, y, ring_in=None,
+                                ring_in_step: int = 0, ring_out=None, state_in=None, state_out=None,
+                                dt_min: float = 0.0, dt_max: float = float("inf"), workspace=None,
+                                stream=None) -> None:
+    """Packed batch, one pass; see include/m2ssd.h.  dims.batch sequences, dims.seqlen the longest;
+    xbc [T, conv_dim] raw conv input, dt [T, H], y [T, H*P] (token-strided views allowed); cu_seqlens
+    int32 [batch + 1] on the GPU; w, bias, ring_in / ring_out, dt_bias, A, D and the states as in
+    m2_mixer_prefill_fwd; workspace: a uint8 GPU tensor of at least
+    m2_mixer_prefill_workspace_packed(dims, T) bytes."""
+    torch = _torch()
+    io = _io_dtype(dims)
+    H, P, N, Cd = dims.nheads, dims.headdim, dims.d_state, dims.conv_dim
+    for n, t in (("xbc", xbc), ("dt", dt), ("y", y), ("ring_in", ring_in), ("ring_out", ring_out)):
+        _check(t, n, io)
+    for n, t in (("w", w), ("bias", bias), ("dt_bias", dt_bias), ("A", A), ("D", D), ("state_in", state_in),
+                 ("state_out", state_out)):
+        _check(t, n, torch.float32)
+    if not w.is_contiguous() or tuple(w.shape) != (Cd, dims.d_conv):
+        raise ValueError("w must be contiguous [conv_dim, d_conv]")
+    if bias is not None and (not bias.is_contiguous() or bias.numel() != Cd):
+        raise ValueError("bias must be contiguous [conv_dim]")
+    for n, t in (("ring_in", ring_in), ("ring_out", ring_out)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, dims.d_conv, Cd)):
+            raise ValueError("%s must be contiguous [batch, d_conv, conv_dim]" % n)
+    for n, t in (("dt_bias", dt_bias), ("A", A), ("D", D)):
+        if t is not None and (not t.is_contiguous() or t.numel() != H):
+            raise ValueError("%s must be contiguous [nheads]" % n)
+    for n, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (dims.batch, H, P, N)):
+            raise ValueError("%s must be contiguous [batch, nheads, headdim, d_state]" % n)
+    T = int(xbc.shape[0])
+    xs = _packed_stride(xbc, "xbc", T, Cd)
+    dts = _packed_stride(dt, "dt", T, H)
+    ys = _packed_stride(y, "y", T, H * P)
+    need = m2_mixer_prefill_workspace_packed(dims, T)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    elif need > 0:
+        raise ValueError("m2_mixer_prefill_fwd_packed needs a workspace of %d bytes" % need)
+    _call("m2_mixer_prefill_fwd_packed", ctypes.byref(dims), T, _cu_ptr(cu_seqlens, dims), _ptr(xbc), xs, _ptr(w),
+          _ptr(bias), _ptr(ring_in), int(ring_in_step), _ptr(ring_out), _ptr(dt), dts, _ptr(dt_bias), _ptr(A),
+          _ptr(D), float(dt_min), float(dt_max), _ptr(state_in), _ptr(state_out), _ptr(y), ys, ws_ptr, ws_bytes,
+          _stream(stream))
 
 
 def m2_ssd_step(dims: M2Dims, xbc_tok, dt_tok, w, bias, dt_bias, A, D, ring, step: int, state, y,

@@ -308,16 +308,25 @@ size_t m2_mixer_prefill_workspace(const m2_dims* dims) {
            m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, 32, d.bf16, -1);
 }
 
-m2_status m2_mixer_prefill_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_stride, const float* conv_w,
-                               const float* conv_b, const void* ring_in, int64_t ring_in_step, void* ring_out,
-                               const void* dt, int64_t dt_tok_stride, const float* dt_bias, const float* A,
-                               const float* D, float dt_min, float dt_max, const float* state_in, float* state_out,
-                               void* y, int64_t y_tok_stride, void* workspace, size_t workspace_bytes,
-                               const int32_t* seq_lens, void* stream) {
+size_t m2_mixer_prefill_workspace_packed(const m2_dims* dims, int64_t total_tokens) {
     Derived d;
-    m2_status st = derive(dims, d);
-    if (st != M2_OK) return st;
-    const int64_t rows = d.batch * d.L;
+    if (derive(dims, d) != M2_OK || total_tokens < 0 || !m2::mixer_fusable(d.P, d.N, d.H, d.G, d.bf16)) return 0;
+    return m2::mixer_act_bytes(1, total_tokens, d.G, d.N) +
+           m2::ssd_scan_workspace_bytes(d.batch, d.L, d.H, d.P, d.N, d.G, 32, d.bf16, total_tokens);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared by the padded and the packed one-pass entry points (rows and cu as for conv_run; need is the
+// workspace the entry point reports for these dims).
+m2_status mixer_run(const Derived& d, int64_t rows, const int32_t* cu, size_t need, const void* xbc,
+                    int64_t xbc_tok_stride, const float* conv_w, const float* conv_b, const void* ring_in,
+                    int64_t ring_in_step, void* ring_out, const void* dt, int64_t dt_tok_stride,
+                    const float* dt_bias, const float* A, const float* D, float dt_min, float dt_max,
+                    const float* state_in, float* state_out, void* y, int64_t y_tok_stride, void* workspace,
+                    size_t workspace_bytes, const int32_t* seq_lens, void* stream) {
     if (!conv_w || !dt_bias || !A) return M2_ERR_NULL;
     if (rows > 0 && (!xbc || !dt || !y)) return M2_ERR_NULL;
     if (rows > 0 && (xbc_tok_stride < d.Cd || dt_tok_stride < d.H || y_tok_stride < d.d_inner)) return M2_ERR_SHAPE;
@@ -332,8 +341,7 @@ m2_status m2_mixer_prefill_fwd(const m2_dims* dims, const void* xbc, int64_t xbc
     const Range rro = span(ring_out, d.batch * d.W, d.Cd, d.Cd, d.esize);
     const Range rs_in = span(state_in, d.batch * d.H, (int64_t)d.P * d.N, (int64_t)d.P * d.N, 4);
     const Range rs_out = span(state_out, d.batch * d.H, (int64_t)d.P * d.N, (int64_t)d.P * d.N, 4);
-    const Range rl = span(seq_lens, d.batch, 1, 1, 4);
-    const size_t need = m2_mixer_prefill_workspace(dims);
+    const Range rl = cu ? span(cu, d.batch + 1, 1, 1, 4) : span(seq_lens, d.batch, 1, 1, 4);
     const Range rws = span(workspace, 1, 0, (int64_t)need, 1);
     const Range outs[] = {ry, rro, rs_out, rws};
     const Range ins[] = {rx, rdt, rri, rs_in, rl};
@@ -343,22 +351,24 @@ m2_status m2_mixer_prefill_fwd(const m2_dims* dims, const void* xbc, int64_t xbc
     if (overlap(ry, rro) || overlap(ry, rs_out) || overlap(ry, rws) || overlap(rro, rs_out) || overlap(rro, rws) ||
         overlap(rs_out, rws))
         return M2_ERR_ALIAS;
-    if (!aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)seq_lens & 3u)) return M2_ERR_UNSUPPORTED;
+    if (!aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)seq_lens & 3u) || ((uintptr_t)cu & 3u))
+        return M2_ERR_UNSUPPORTED;
     // raw x rows and y move in 16-byte pieces; dt is read two heads per dword; rings in 16-byte pieces
     if (rows > 0 && (!aligned16(xbc) || !aligned16(y) || (xbc_tok_stride * d.esize) % 16 ||
                      (y_tok_stride * d.esize) % 16 || !m2::mixer_dt_fusable(dt, dt_tok_stride)))
         return M2_ERR_UNSUPPORTED;
     if (!aligned16(ring_in) || !aligned16(ring_out)) return M2_ERR_UNSUPPORTED;
     if (need > 0 && (!workspace || workspace_bytes < need)) return M2_ERR_WORKSPACE;
-    // the workspace, from a 256-byte boundary: the B/C activation, then the scan's own part
+    // the workspace, from a 256-byte boundary: the B/C activation (one row per token), then the scan's
+    // own part
     uint8_t* base = reinterpret_cast<uint8_t*>(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
-    const size_t act_bytes = m2::mixer_act_bytes(d.batch, d.L, d.G, d.N);
+    const size_t act_bytes = cu ? m2::mixer_act_bytes(1, rows, d.G, d.N) : m2::mixer_act_bytes(d.batch, d.L, d.G, d.N);
     m2::ConvArgs c;
     c.xbc = rows > 0 ? xbc : nullptr; c.xs = xbc_tok_stride; c.L = d.L; c.Cd = d.Cd; c.W = d.W; c.batch = d.batch;
     c.w = conv_w; c.bias = conv_b; c.ring_in = ring_in;
     c.ring_phase = (int)(((ring_in_step % d.W) + d.W) % d.W);
     c.ring_out = ring_out; c.rs = d.Cd; c.out = nullptr; c.os = 2 * GN; c.lens = seq_lens; c.bf16 = true;
-    c.cu = nullptr; c.total = 0;
+    c.cu = cu; c.total = cu ? rows : 0;
     c.vec = (d.Cd % 8 == 0) && (rows == 0 || (xbc_tok_stride % 8 == 0 && aligned16(xbc)));
     m2::ScanArgs a;
     a.batch = d.batch; a.L = d.L; a.H = d.H; a.P = d.P; a.N = d.N; a.G = d.G; a.Q = 32;
@@ -367,8 +377,43 @@ m2_status m2_mixer_prefill_fwd(const m2_dims* dims, const void* xbc, int64_t xbc
     a.dt_bias = dt_bias; a.A = A; a.D = D; a.dt_min = dt_min; a.dt_max = dt_max;
     a.state_in = state_in; a.state_out = state_out; a.y = y; a.ys = y_tok_stride;
     a.ws = base + act_bytes; a.ws_bytes = workspace_bytes > act_bytes + 255 ? workspace_bytes - act_bytes - 255 : 0;
-    a.lens = seq_lens; a.bf16 = true; a.cu = nullptr; a.total = 0;
+    a.lens = seq_lens; a.bf16 = true; a.cu = cu; a.total = cu ? rows : 0;
     return launched(m2::launch_mixer_prefill(c, a, base, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+m2_status m2_mixer_prefill_fwd(const m2_dims* dims, const void* xbc, int64_t xbc_tok_stride, const float* conv_w,
+                               const float* conv_b, const void* ring_in, int64_t ring_in_step, void* ring_out,
+                               const void* dt, int64_t dt_tok_stride, const float* dt_bias, const float* A,
+                               const float* D, float dt_min, float dt_max, const float* state_in, float* state_out,
+                               void* y, int64_t y_tok_stride, void* workspace, size_t workspace_bytes,
+                               const int32_t* seq_lens, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    return mixer_run(d, d.batch * d.L, nullptr, m2_mixer_prefill_workspace(dims), xbc, xbc_tok_stride, conv_w, conv_b,
+                     ring_in, ring_in_step, ring_out, dt, dt_tok_stride, dt_bias, A, D, dt_min, dt_max, state_in,
+                     state_out, y, y_tok_stride, workspace, workspace_bytes, seq_lens, stream);
+}
+
+m2_status m2_mixer_prefill_fwd_packed(const m2_dims* dims, int64_t total_tokens, const int32_t* cu_seqlens,
+                                      const void* xbc, int64_t xbc_tok_stride, const float* conv_w,
+                                      const float* conv_b, const void* ring_in, int64_t ring_in_step, void* ring_out,
+                                      const void* dt, int64_t dt_tok_stride, const float* dt_bias, const float* A,
+                                      const float* D, float dt_min, float dt_max, const float* state_in,
+                                      float* state_out, void* y, int64_t y_tok_stride, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    Derived d;
+    m2_status st = derive(dims, d);
+    if (st != M2_OK) return st;
+    if (total_tokens < 0) return M2_ERR_SHAPE;
+    if (d.batch > 0 && !cu_seqlens) return M2_ERR_NULL;
+    return mixer_run(d, total_tokens, cu_seqlens, m2_mixer_prefill_workspace_packed(dims, total_tokens), xbc,
+                     xbc_tok_stride, conv_w, conv_b, ring_in, ring_in_step, ring_out, dt, dt_tok_stride, dt_bias, A, D,
+                     dt_min, dt_max, state_in, state_out, y, y_tok_stride, workspace, workspace_bytes, nullptr, stream);
 }
 
 m2_status m2_ssd_step(const m2_dims* dims, const void* xbc_tok, int64_t xbc_stride, const void* dt_tok,

@@ -268,6 +268,34 @@ def test_fused_prefill_shapes_and_validation():
     assert call(dims(batch=1, seqlen=32768)) == m2.M2_ERR_WORKSPACE
 
 
+def test_packed_fused_prefill_shapes_and_validation():
+    """The packed one-pass path: its workspace follows the total (B/C activation rows plus the packed
+    scan's plan), it is built where the one-pass path is, and it checks its token count, offsets and
+    packed rows before any launch."""
+    lib = m2.lib()
+    d = dims(batch=8, seqlen=8192)
+    need = m2.m2_mixer_prefill_workspace_packed(d, 32768)
+    assert need >= m2.m2_ssd_scan_workspace_packed(d, 32768) + 32768 * 2 * d.n_groups * d.d_state * 2
+    assert m2.m2_mixer_prefill_workspace_packed(d, -1) == 0
+    for bad in (dict(d_state=128), dict(headdim=32), dict(io=m2.M2_F32)):
+        assert m2.m2_mixer_prefill_workspace_packed(dims(**bad), 100) == 0, bad
+
+    def call(d, T=256, cu=FAKE + 0x5000_0000_0, xbc=FAKE, y=FAKE + 0x4000_0000_00, ws=FAKE + 0x6000_0000_00,
+             wsb=1 << 40):
+        di = d.expand * d.d_model
+        return lib.m2_mixer_prefill_fwd_packed(ctypes.byref(d), T, cu, xbc, d.conv_dim, FAKE + 0x1000_0000_0, None,
+                                               None, 0, None, FAKE + 0x2000_0000_0, di // d.headdim,
+                                               FAKE + 0x3000_0000_0, FAKE + 0x3000_1000_0, None, 0.0, float("inf"),
+                                               None, None, y, di, ws, wsb, None)
+    assert call(dims(d_state=128)) == m2.M2_ERR_UNSUPPORTED
+    assert call(dims(), T=-1) == m2.M2_ERR_SHAPE
+    assert call(dims(), cu=None) == m2.M2_ERR_NULL
+    assert call(dims(), cu=FAKE + 0x5000_0000_2) == m2.M2_ERR_UNSUPPORTED     # offsets off a 4-byte boundary
+    assert call(dims(), y=FAKE + 64) == m2.M2_ERR_ALIAS                         # y overlaps xbc
+    assert call(dims(), cu=FAKE + 0x4000_0000_00 + 64) == m2.M2_ERR_ALIAS       # offsets inside y
+    assert call(dims(batch=8, seqlen=8192), T=32768, wsb=1 << 20) == m2.M2_ERR_WORKSPACE
+
+
 def test_scan_backward_shapes_and_validation():
     """The scan's backward is built for bf16 headdim 64 / d_state 64: elsewhere it reports no workspace
     and M2_ERR_UNSUPPORTED; argument, alignment, overlap and workspace errors come back before any

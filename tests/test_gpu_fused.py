@@ -177,3 +177,106 @@ def test_full_size_fused_prefill(idx):
     print("fused full size %d: y %.2e state %.2e" % (idx, ey, es))
     assert ey <= TOL and es <= TOL
     np.testing.assert_array_equal(ring, ringr)
+
+
+def _pack(a, lens):
+    """[batch, seqlen, ...] -> the first lens[b] tokens of each row, back to back."""
+    return np.concatenate([a[b, :n] for b, n in enumerate(lens)], axis=0)
+
+
+def _fused_packed(d, lens, xbc_p, dt_p, inp, ring_in, phase, state_in):
+    H, P, N, W, Cd = d.nheads, d.headdim, d.d_state, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    T = int(sum(lens))
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    y = nan_like((T, H * P), "bf16")
+    s_out = torch.full((len(lens), H, P, N), float("nan"), device="cuda")
+    ring_out = nan_like((len(lens), W, Cd), "bf16")
+    n = m2.m2_mixer_prefill_workspace_packed(dims, T)
+    ws = torch.empty(max(n, 1), device="cuda", dtype=torch.uint8)
+    m2.m2_mixer_prefill_fwd_packed(dims, cu, dev(xbc_p, "bf16"), dev32(inp.conv_w), dev32(inp.conv_b),
+                                   dev(dt_p, "bf16"), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y,
+                                   dev(ring_in, "bf16"), phase, ring_out, dev32(state_in), s_out, workspace=ws)
+    torch.cuda.synchronize()
+    return host(y).reshape(T, H, P), host(s_out), host(ring_out), cu
+
+
+def _two_kernels_packed(d, lens, xbc_p, dt_p, inp, ring_in, phase, state_in, cu):
+    H, P, N, G, W, Cd = d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    T = int(sum(lens))
+    act = torch.empty((T, Cd), device="cuda", dtype=torch.bfloat16)
+    ring_out = torch.empty((len(lens), W, Cd), device="cuda", dtype=torch.bfloat16)
+    m2.m2_conv1d_fwd_packed(dims, cu, dev(xbc_p, "bf16"), dev32(inp.conv_w), dev32(inp.conv_b), act,
+                            dev(ring_in, "bf16"), phase, ring_out)
+    y = torch.empty((T, H * P), device="cuda", dtype=torch.bfloat16)
+    s_out = torch.empty((len(lens), H, P, N), device="cuda")
+    m2.m2_ssd_scan_fwd_packed(dims, cu, act[:, :H * P], act[:, H * P:H * P + G * N], act[:, H * P + G * N:],
+                              dev(dt_p, "bf16"), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(state_in),
+                              s_out, workspace=workspace(dims, T))
+    torch.cuda.synchronize()
+    return host(y).reshape(T, H, P), host(s_out), host(ring_out)
+
+
+PACKED_FUSED_CASES = [
+    [300, 0, 17, 129, 301, 1],   # an empty and a one-token prompt, ragged ends
+    [2, 3, 40],                  # prompts shorter than the conv window take their history from the ring
+    [4096, 1500, 0, 2500],       # several segments per prompt, empty segments
+]
+
+
+@pytest.mark.parametrize("lens", PACKED_FUSED_CASES, ids=lambda l: "-".join(map(str, l)))
+def test_fused_prefill_packed_parity(lens):
+    """Packed prompts through the one-pass path, each from its own conv history (ring phase 2) and
+    initial state, against the oracle's conv -> scan of each prompt; and equal to the two-kernel packed
+    path within rounding."""
+    _need_gpu()
+    d = workloads.CONFIGS[2].dims.replace(batch=len(lens), seqlen=max(lens))
+    inp = workloads.generate(d, 5700 + len(lens), True)
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    xbc_p, dt_p = _pack(inp.xbc, lens), _pack(inp.dt_raw, lens)
+    y, s, ring, cu = _fused_packed(d, lens, xbc_p, dt_p, inp, inp.ring0, 2, inp.state0)
+    worst = [0.0, 0.0]
+    for b, n in enumerate(lens):
+        yr, sr, ringr, _ = oracle.mixer_prefill(inp.xbc[b:b + 1, :n], inp.dt_raw[b:b + 1, :n], inp.conv_w,
+                                                inp.conv_b, inp.dt_bias, inp.A, inp.D, H, P, N, G,
+                                                inp.ring0[b:b + 1], 2, inp.state0[b:b + 1])
+        t0 = int(sum(lens[:b]))
+        if n > 0:
+            worst[0] = max(worst[0], oracle.max_rel_err(y[t0:t0 + n][None], yr))
+        worst[1] = max(worst[1], oracle.max_rel_err(s[b:b + 1], sr))
+        np.testing.assert_array_equal(ring[b:b + 1], ringr)
+    y2, s2, r2 = _two_kernels_packed(d, lens, xbc_p, dt_p, inp, inp.ring0, 2, inp.state0, cu)
+    e2 = max(oracle.max_rel_err(y, y2), oracle.max_rel_err(s, s2))
+    print("fused packed %s: y %.2e state %.2e; vs two-kernel packed path %.2e" % (lens, worst[0], worst[1], e2))
+    assert worst[0] <= TOL and worst[1] <= TOL and e2 <= TOL
+    np.testing.assert_array_equal(ring, r2)
+
+
+def test_full_size_fused_prefill_packed():
+    """The 8 packed prompts of the benchmark (8192 ... 1024 tokens, 32768 in all, zero history and
+    state) at the 2.7B shape: every prompt against the two-kernel packed path, and the shortest and a
+    middle one against the oracle's conv -> scan over every head."""
+    _need_gpu()
+    lens = [8192, 6144, 5120, 4096, 3584, 2560, 2048, 1024]
+    d1 = workloads.CONFIGS[3].dims
+    T = sum(lens)
+    inp = workloads.generate(d1.replace(seqlen=T), 1003, False)
+    d = d1.replace(batch=len(lens), seqlen=max(lens))
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    xbc_p, dt_p = inp.xbc[0], inp.dt_raw[0]
+    y, s, ring, cu = _fused_packed(d, lens, xbc_p, dt_p, inp, None, 0, None)
+    y2, s2, r2 = _two_kernels_packed(d, lens, xbc_p, dt_p, inp, None, 0, None, cu)
+    e2 = max(oracle.max_rel_err(y, y2), oracle.max_rel_err(s, s2))
+    np.testing.assert_array_equal(ring, r2)
+    worst = [0.0, 0.0]
+    for b in (7, 4):
+        t0, n = int(sum(lens[:b])), lens[b]
+        yr, sr, ringr, _ = oracle.mixer_prefill(xbc_p[None, t0:t0 + n], dt_p[None, t0:t0 + n], inp.conv_w,
+                                                inp.conv_b, inp.dt_bias, inp.A, inp.D, H, P, N, G, None, 0, None)
+        worst[0] = max(worst[0], oracle.max_rel_err(y[t0:t0 + n][None], yr))
+        worst[1] = max(worst[1], oracle.max_rel_err(s[b:b + 1], sr))
+        np.testing.assert_array_equal(ring[b:b + 1], ringr)
+    print("fused packed full size: sampled prompts y %.2e state %.2e; all prompts vs two-kernel path %.2e"
+          % (worst[0], worst[1], e2))
+    assert worst[0] <= TOL and worst[1] <= TOL and e2 <= TOL
