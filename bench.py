@@ -6,7 +6,7 @@ batch-1, 32768-token prompt at the Zamba2-2.7B mixer shape (d_model 2560, expand
 headdim 64, d_state 64, one B/C group, conv width 4), bf16 activations and fp32 state, inputs
 resident in HBM, through the one-pass entry point m2_mixer_prefill_fwd (the conv output is never
 written).  The same run times the two-kernel path (m2_conv1d_fwd then m2_ssd_scan_fwd) on the same
-prompt, the same tokens as 8 packed prompts, the gated RMSNorm, the fused decode step on 256
+prompt, the same tokens as 8 packed prompts (two kernels, and one pass), the gated RMSNorm, the fused decode step on 256
 sequences (the `decode` object) and the library's streaming copy (the attainable-bandwidth
 reference).  Each entry point's average time comes from HIP events recorded on the stream it runs on,
 around each of its calls in the order the path makes them, and is turned into a roofline fraction
@@ -130,6 +130,7 @@ def time_events(torch, fns, steps, warmup, alone=None):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _SCAN_SRC = ("ssd_scan.hip", "ssd_walk.hip", "ssd_common.h")
 KERNEL_SOURCES = {"ssd_scan": _SCAN_SRC, "conv1d": ("conv1d.hip",), "ssd_step": ("ssd_step.hip",),
+                  "mixer_prefill_packed": _SCAN_SRC + ("conv1d.hip",),
                   "gated_rmsnorm": ("gated_norm.hip",), "ssd_scan_packed": _SCAN_SRC, "conv1d_packed": ("conv1d.hip",),
                   "mixer_prefill": _SCAN_SRC + ("conv1d.hip",), "ssd_scan_bwd": ("ssd_bwd.hip", "ssd_common.h")}
 
@@ -297,7 +298,23 @@ def bench_varlen(torch, m2, workloads, args):
     conv_b += (Bn - 1) * W * Cd * 2           # one ring per prompt
     scan_b += (Bn - 1) * H * P * N * 4        # one final state per prompt
     step_ms = total_ms / args.steps
+
+    # the same prompts through the one-pass path (the conv output of x never written)
+    nwf = m2.m2_mixer_prefill_workspace_packed(dims, T)
+    wsf = torch.empty(max(nwf, 1), device="cuda", dtype=torch.uint8)
+    y2, s_out2, ring2 = torch.empty_like(y), torch.empty_like(s_out), torch.empty_like(ring_out)
+
+    def fused():
+        m2.m2_mixer_prefill_fwd_packed(dims, cu, xbc, cw, cb, dt, dtb, A, D, y2, None, 0, ring2, None, s_out2,
+                                       workspace=wsf)
+
+    (t_fused,), fused_ms, _ = time_events(torch, [fused], args.steps, args.warmup)
+    fused_b = fused_bytes(1, T, H, P, N, G, W, Cd, False, True) + (Bn - 1) * (W * Cd * 2 + H * P * N * 4)
+    fused_step = fused_ms / args.steps
     return {"value": round(T / (step_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(step_ms, 4),
+            "one_pass": {"value": round(T / (fused_step * 1e-3), 1), "unit": "tokens/s",
+                         "ms_per_step": round(fused_step, 4),
+                         "roofline": roofline(fused_b, t_fused, "mixer_prefill_packed")},
             "kernels": {"conv1d_packed": {"us": round(t_conv * 1e3, 2),
                                           "roofline": roofline(conv_b, t_conv, "conv1d_packed")},
                         "ssd_scan_packed": {"us": round(t_scan * 1e3, 2),
@@ -512,7 +529,8 @@ def main():
         out["prefill_two_kernel"] = pre["two_kernel"]
     if args.only in ("all", "prefill"):
         vl = bench_varlen(torch, m2, workloads, args)
-        print("packed prompts: %.3f ms/step, %.3e tok/s" % (vl["ms_per_step"], vl["value"]), file=sys.stderr,
+        print("packed prompts: %.3f ms/step, %.3e tok/s (one pass: %.3f ms/step)" % (
+            vl["ms_per_step"], vl["value"], vl["one_pass"]["ms_per_step"]), file=sys.stderr,
               flush=True)
         out["varlen"] = vl
         nrm = bench_norm(torch, m2, workloads, args)
