@@ -280,3 +280,21 @@ def test_full_size_fused_prefill_packed():
     print("fused packed full size: sampled prompts y %.2e state %.2e; all prompts vs two-kernel path %.2e"
           % (worst[0], worst[1], e2))
     assert worst[0] <= TOL and worst[1] <= TOL and e2 <= TOL
+
+
+def test_fused_prefill_packed_all_empty():
+    """Packed prompts that are all empty (zero rows): each state passes through and each ring is a copy
+    of its history, as for an empty prompt of the padded entry point."""
+    _need_gpu()
+    lens = [0, 0, 0]
+    d = workloads.CONFIGS[2].dims.replace(batch=len(lens), seqlen=1)
+    inp = workloads.generate(d, 5800, True)
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    xbc_p, dt_p = inp.xbc[0, :0], inp.dt_raw[0, :0]
+    _, s, ring, _ = _fused_packed(d, lens, xbc_p, dt_p, inp, inp.ring0, 3, inp.state0)
+    np.testing.assert_array_equal(s, inp.state0.astype(np.float64))
+    for b in range(len(lens)):
+        _, _, ringr, _ = oracle.mixer_prefill(inp.xbc[b:b + 1, :0], inp.dt_raw[b:b + 1, :0], inp.conv_w, inp.conv_b,
+                                              inp.dt_bias, inp.A, inp.D, H, P, N, G, inp.ring0[b:b + 1], 3,
+                                              inp.state0[b:b + 1])
+        np.testing.assert_array_equal(ring[b:b + 1], ringr)
