@@ -1,0 +1,150 @@
+"""Seeded random cases against the fp64 oracle, across the option space that the hand-picked tests cover
+one corner at a time: 1-5 prompts of lengths 0 ... 3000 tokens (on and off chunk and window boundaries),
+1, 2 or 4 B/C groups, 4-32 heads, conv widths 2-4, with or without conv history at ring phases 0-5 and
+an initial state.
+
+- the one-pass prompt path, right-padded (seq_lens) and packed (cu_seqlens), each prompt against the
+  oracle's conv -> scan (y, final state; rings bit-exact; padding untouched);
+- the scan backward, right-padded and packed, every gradient against the oracle's adjoint recurrence.
+
+The case list is drawn from a fixed seed when the tests are collected, so a failure names its case."""
+import random
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import selective_state_space_mixer_amd as m2
+    from gpu_util import dev, dev32, dims_of, host, nan_like
+    import test_gpu_bwd as tb
+
+TOL = 2e-2
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+
+
+def _fwd_cases(seed=7, n=40):
+    rng, out = random.Random(seed), []
+    while len(out) < n:
+        nb = rng.randint(1, 5)
+        lens = [rng.choice([0, 1, 2, 3, 5, 31, 32, 33, 64, 100, 257, 700, 1500, 3000]) for _ in range(nb)]
+        groups, d_model, d_conv = rng.choice([1, 2, 4]), rng.choice([128, 256, 512]), rng.choice([2, 3, 4])
+        cached, phase = rng.random() < 0.7, rng.randint(0, 5)
+        if (2 * d_model // 64 // groups) % 4:   # the one-pass path takes heads per group in fours
+            continue
+        out.append((lens, groups, d_model, d_conv, cached, phase, 9000 + len(out)))
+    return out
+
+
+def _bwd_cases(seed=11, n=16):
+    rng, out = random.Random(seed), []
+    while len(out) < n:
+        nb = rng.randint(1, 4)
+        lens = [rng.choice([0, 1, 2, 63, 64, 65, 100, 300, 1000, 2100]) for _ in range(nb)]
+        groups, d_model = rng.choice([1, 2, 4]), rng.choice([128, 256, 512])
+        if (2 * d_model // 64) % groups:
+            continue
+        out.append((lens, groups, d_model, 9500 + len(out)))
+    return out
+
+
+@pytest.mark.parametrize("case", _fwd_cases(), ids=lambda c: "L%s-G%d-dm%d-W%d-h%d-ph%d" % (
+    "_".join(map(str, c[0])), c[1], c[2], c[3], c[4], c[5]))
+def test_random_one_pass_prefill(case):
+    _need_gpu()
+    lens, groups, d_model, d_conv, cached, phase, seed = case
+    nb = len(lens)
+    d = workloads.CONFIGS[2].dims.replace(batch=nb, seqlen=max(1, max(lens)), n_groups=groups, d_model=d_model,
+                                          d_conv=d_conv)
+    inp = workloads.generate(d, seed, cached)
+    ring_in = inp.ring0 if cached else None
+    s_in = inp.state0 if cached else None
+    H, P, N, G, W, Cd = d.nheads, d.headdim, d.d_state, d.n_groups, d.d_conv, d.conv_dim
+    dims = dims_of(d)
+    # packed
+    T = sum(lens)
+    xbc_p = np.concatenate([inp.xbc[b, :n] for b, n in enumerate(lens)], axis=0)
+    dt_p = np.concatenate([inp.dt_raw[b, :n] for b, n in enumerate(lens)], axis=0)
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    y = nan_like((T, H * P), "bf16")
+    s = torch.full((nb, H, P, N), float("nan"), device="cuda")
+    ring = nan_like((nb, W, Cd), "bf16")
+    ws = torch.empty(max(m2.m2_mixer_prefill_workspace_packed(dims, T), 1), device="cuda", dtype=torch.uint8)
+    m2.m2_mixer_prefill_fwd_packed(dims, cu, dev(xbc_p, "bf16"), dev32(inp.conv_w), dev32(inp.conv_b),
+                                   dev(dt_p, "bf16"), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y,
+                                   dev(ring_in, "bf16"), phase, ring, dev32(s_in), s, workspace=ws)
+    # right-padded
+    yq = nan_like((nb, d.seqlen, H * P), "bf16")
+    sq = torch.full((nb, H, P, N), float("nan"), device="cuda")
+    ringq = nan_like((nb, W, Cd), "bf16")
+    wsq = torch.empty(max(m2.m2_mixer_prefill_workspace(dims), 1), device="cuda", dtype=torch.uint8)
+    m2.m2_mixer_prefill_fwd(dims, dev(inp.xbc, "bf16"), dev32(inp.conv_w), dev32(inp.conv_b), dev(inp.dt_raw, "bf16"),
+                            dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), yq, dev(ring_in, "bf16"), phase, ringq,
+                            dev32(s_in), sq, workspace=wsq,
+                            seq_lens=torch.as_tensor(np.asarray(lens, np.int32), device="cuda"))
+    torch.cuda.synchronize()
+    yh, sh, rh = host(y).reshape(T, H, P), host(s), host(ring)
+    yqh, sqh, rqh = host(yq).reshape(nb, d.seqlen, H, P), host(sq), host(ringq)
+    worst = 0.0
+    for b, n in enumerate(lens):
+        yr, sr, rr, _ = oracle.mixer_prefill(inp.xbc[b:b + 1, :n], inp.dt_raw[b:b + 1, :n], inp.conv_w, inp.conv_b,
+                                             inp.dt_bias, inp.A, inp.D, H, P, N, G,
+                                             None if ring_in is None else ring_in[b:b + 1], phase,
+                                             None if s_in is None else s_in[b:b + 1])
+        t0 = sum(lens[:b])
+        errs = [oracle.max_rel_err(sh[b:b + 1], sr), oracle.max_rel_err(sqh[b:b + 1], sr)]
+        if n > 0:
+            errs += [oracle.max_rel_err(yh[t0:t0 + n][None], yr), oracle.max_rel_err(yqh[b:b + 1, :n], yr)]
+        worst = max([worst] + errs)
+        assert max(errs) <= TOL, (b, errs)
+        np.testing.assert_array_equal(rh[b:b + 1], rr)
+        np.testing.assert_array_equal(rqh[b:b + 1], rr)
+        assert np.isnan(yqh[b, n:]).all(), "padding of sequence %d written" % b
+    print("random one-pass %s: worst %.2e" % (lens, worst))
+
+
+@pytest.mark.parametrize("case", _bwd_cases(), ids=lambda c: "L%s-G%d-dm%d" % ("_".join(map(str, c[0])), c[1], c[2]))
+def test_random_scan_backward(case):
+    _need_gpu()
+    lens, groups, d_model, seed = case
+    d = workloads.CONFIGS[2].dims.replace(batch=len(lens), seqlen=max(1, max(lens)), n_groups=groups, d_model=d_model)
+    inp = workloads.generate(d, seed, True)
+    x, b, c = tb._split(d, inp)
+    dy, ds = workloads.grad_inputs(d, seed + 100)
+    H, P, N, G = d.nheads, d.headdim, d.d_state, d.n_groups
+    got = tb.run_bwd(d, x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds, seq_lens=lens)
+    ref = oracle.ssd_scan_bwd(x, b, c, inp.dt_raw, inp.dt_bias, inp.A, inp.D, inp.state0, dy, ds, seq_lens=lens)
+    e1 = tb._padded_errors(got, ref, lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pack = lambda a: np.concatenate([a[i, :n] for i, n in enumerate(lens)], 0)
+    xp, bp, cp, dtp, dyp = pack(x), pack(b), pack(c), pack(inp.dt_raw), pack(dy)
+    T, dims = int(cu[-1]), dims_of(d)
+    out = {"dx": nan_like((T, H * P), "bf16"), "dB": nan_like((T, G * N), "bf16"),
+           "dC": nan_like((T, G * N), "bf16"), "ddt_raw": nan_like((T, H), "bf16")}
+    for k in ("ddt_bias", "dA", "dD"):
+        out[k] = torch.full((H,), float("nan"), device="cuda")
+    out["dstate_in"] = torch.full((d.batch, H, P, N), float("nan"), device="cuda")
+    ws = torch.empty(m2.m2_ssd_scan_bwd_workspace(dims), dtype=torch.uint8, device="cuda")
+    m2.m2_ssd_scan_bwd_packed(dims, torch.as_tensor(cu, device="cuda"), dev(xp, "bf16"), dev(bp, "bf16"),
+                              dev(cp, "bf16"), dev(dtp, "bf16"), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D),
+                              dev(dyp, "bf16"), out["dx"], out["dB"], out["dC"], out["ddt_raw"], out["ddt_bias"],
+                              out["dA"], out["dD"], state_in=dev32(inp.state0), dstate_out=dev32(ds),
+                              dstate_in=out["dstate_in"], workspace=ws)
+    torch.cuda.synchronize()
+    g2 = {k: host(v) for k, v in out.items()}
+    g2["dx"], g2["dB"], g2["dC"] = g2["dx"].reshape(T, H, P), g2["dB"].reshape(T, G, N), g2["dC"].reshape(T, G, N)
+    r2 = oracle.ssd_scan_bwd_packed(xp, bp, cp, dtp, cu, inp.dt_bias, inp.A, inp.D, inp.state0, dyp, ds)
+    e2 = tb.errors(g2, r2)
+    print("random backward %s G%d: padded %.2e packed %.2e" % (lens, groups, max(e1.values()), max(e2.values())))
+    assert max(e1.values()) <= TOL, e1
+    assert max(e2.values()) <= TOL, e2
