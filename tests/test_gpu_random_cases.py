@@ -5,7 +5,9 @@ an initial state.
 
 - the one-pass prompt path, right-padded (seq_lens) and packed (cu_seqlens), each prompt against the
   oracle's conv -> scan (y, final state; rings bit-exact; padding untouched);
-- the scan backward, right-padded and packed, every gradient against the oracle's adjoint recurrence.
+- the scan backward, right-padded and packed, every gradient against the oracle's adjoint recurrence;
+- the scan on its own, right-padded and packed, over every built (headdim, d_state, chunk, dtype), 1-12
+  heads in 1, 2 or 4 groups, against the oracle per sequence (2e-2 for bf16, 1e-4 for fp32).
 
 The case list is drawn from a fixed seed when the tests are collected, so a failure names its case."""
 import random
@@ -24,6 +26,8 @@ if torch.cuda.is_available():
     import selective_state_space_mixer_amd as m2
     from gpu_util import dev, dev32, dims_of, host, nan_like
     import test_gpu_bwd as tb
+    import test_gpu_parity as tp
+    from gpu_util import tol_for, workspace
 
 TOL = 2e-2
 
@@ -55,6 +59,18 @@ def _bwd_cases(seed=11, n=16):
         if (2 * d_model // 64) % groups:
             continue
         out.append((lens, groups, d_model, 9500 + len(out)))
+    return out
+
+
+def _scan_cases(seed=5, n=30):
+    from test_gpu_parity import SHAPE_CASES
+    rng, out = random.Random(seed), []
+    for _ in range(n):
+        io, P, N, Q = rng.choice(SHAPE_CASES)
+        nb = rng.randint(1, 4)
+        lens = [rng.choice([0, 1, Q - 1, Q, Q + 1, 3 * Q + 5, 200, 700, 1600]) for _ in range(nb)]
+        G = rng.choice([1, 2, 4])
+        out.append((io, P, N, Q, G, G * rng.choice([1, 2, 3]), lens, rng.random() < 0.7, 9900 + len(out)))
     return out
 
 
@@ -148,3 +164,39 @@ def test_random_scan_backward(case):
     print("random backward %s G%d: padded %.2e packed %.2e" % (lens, groups, max(e1.values()), max(e2.values())))
     assert max(e1.values()) <= TOL, e1
     assert max(e2.values()) <= TOL, e2
+
+
+@pytest.mark.parametrize("case", _scan_cases(), ids=lambda c: "%s-P%d-N%d-Q%d-G%d-H%d-L%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "_".join(map(str, c[6]))))
+def test_random_scan(case):
+    _need_gpu()
+    io, P, N, Q, G, H, lens, cached, seed = case
+    nb = len(lens)
+    d = workloads.Dims(nb, max(1, max(lens)), H * P // 2, 2, P, N, G, 4, Q, io)
+    inp, x, b, c = tp._scan_inputs(d, seed, cached)
+    s0 = inp.state0
+    dims, tol = dims_of(d), tol_for(io)
+    yq, sq = tp._run_scan(d, inp, x, b, c, s0, seq_lens=lens)
+    pack = lambda a: np.concatenate([a[i, :n] for i, n in enumerate(lens)], 0)
+    xp, bp, cp, dtp = pack(x), pack(b), pack(c), pack(inp.dt_raw)
+    T = len(xp)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    y = nan_like((T, H * P), io)
+    s = torch.full((nb, H, P, N), float("nan"), device="cuda")
+    m2.m2_ssd_scan_fwd_packed(dims, torch.as_tensor(cu, device="cuda"), dev(xp, io), dev(bp, io), dev(cp, io),
+                              dev(dtp, io), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(s0), s,
+                              workspace=workspace(dims, T))
+    torch.cuda.synchronize()
+    errs = []
+    for bi, n in enumerate(lens):
+        yr, sr = oracle.ssd_scan(x[bi:bi + 1, :n], b[bi:bi + 1, :n], c[bi:bi + 1, :n], inp.dt_raw[bi:bi + 1, :n],
+                                 inp.dt_bias, inp.A, inp.D, None if s0 is None else s0[bi:bi + 1])
+        errs.append(oracle.max_rel_err(sq[bi:bi + 1], sr))
+        if n:
+            errs.append(oracle.max_rel_err(yq[bi:bi + 1, :n], yr))
+    yr2, sr2 = oracle.ssd_scan_packed(xp, bp, cp, dtp, cu, inp.dt_bias, inp.A, inp.D, s0)
+    errs.append(oracle.max_rel_err(host(s), sr2))
+    if T:
+        errs.append(oracle.max_rel_err(host(y).reshape(T, H, P), yr2))
+    print("random scan %s P%d N%d Q%d G%d H%d %s: worst %.2e (bar %.0e)" % (io, P, N, Q, G, H, lens, max(errs), tol))
+    assert max(errs) <= tol, errs
