@@ -7,7 +7,9 @@ an initial state.
   oracle's conv -> scan (y, final state; rings bit-exact; padding untouched);
 - the scan backward, right-padded and packed, every gradient against the oracle's adjoint recurrence;
 - the scan on its own, right-padded and packed, over every built (headdim, d_state, chunk, dtype), 1-12
-  heads in 1, 2 or 4 groups, against the oracle per sequence (2e-2 for bf16, 1e-4 for fp32).
+  heads in 1, 2 or 4 groups, against the oracle per sequence (2e-2 for bf16, 1e-4 for fp32);
+- chains of decode steps over head sizes 8-256, d_state 16-256, conv widths 2-4, both dtypes, from any
+  ring phase, each step's output and the final state and ring against the oracle's step chain.
 
 The case list is drawn from a fixed seed when the tests are collected, so a failure names its case."""
 import random
@@ -200,3 +202,40 @@ def test_random_scan(case):
         errs.append(oracle.max_rel_err(host(y).reshape(T, H, P), yr2))
     print("random scan %s P%d N%d Q%d G%d H%d %s: worst %.2e (bar %.0e)" % (io, P, N, Q, G, H, lens, max(errs), tol))
     assert max(errs) <= tol, errs
+
+
+def _step_cases(seed=13, n=24):
+    rng, out = random.Random(seed), []
+    while len(out) < n:
+        io = rng.choice(["bf16", "f32"])
+        P, N = rng.choice([8, 16, 24, 32, 48, 64, 80, 96, 128, 256]), rng.choice([16, 32, 64, 128, 256])
+        if P * (N // 4) > 8 * 256 or P + 2 * N > 1024:   # the shapes the decode kernel builds
+            continue
+        G = rng.choice([1, 2, 4])
+        out.append((io, P, N, G, G * rng.choice([1, 2]), rng.choice([2, 3, 4]), rng.randint(1, 4),
+                    rng.randint(2, 6), rng.randint(0, 5), rng.random() < 0.8, 9700 + len(out)))
+    return out
+
+
+@pytest.mark.parametrize("case", _step_cases(), ids=lambda c: "%s-P%d-N%d-G%d-H%d-W%d-B%d-S%d-from%d" % c[:9])
+def test_random_decode_chain(case):
+    _need_gpu()
+    io, P, N, G, H, W, Bn, steps, first, cached, seed = case
+    d = workloads.Dims(Bn, 1, H * P // 2, 2, P, N, G, W, 0, io)
+    inp = workloads.generate(d, seed, cached, steps)
+    ys, ring, state = tp._gpu_chain(d, inp, steps, inp.ring0, inp.state0, first_step=first)
+    Cd = d.conv_dim
+    r_ring = inp.ring0.astype(np.float64) if inp.ring0 is not None else np.zeros((Bn, W, Cd))
+    r_state = inp.state0.astype(np.float64) if inp.state0 is not None else np.zeros((Bn, H, P, N))
+    tol = tol_for(io)
+    worst = 0.0
+    for t in range(steps):
+        yr, r_ring, r_state = oracle.ssd_step(inp.xbc[t], inp.dt_raw[t], inp.conv_w, inp.conv_b, inp.dt_bias, inp.A,
+                                              inp.D, r_ring, first + t, r_state, H, P, N, G)
+        e = oracle.max_rel_err(ys[t], yr)
+        worst = max(worst, e)
+        assert e <= tol, "step %d: %.2e" % (t, e)
+    es = oracle.max_rel_err(state, r_state)
+    print("random decode chain %s P%d N%d G%d H%d W%d: y %.2e state %.2e" % (io, P, N, G, H, W, worst, es))
+    assert es <= tol
+    np.testing.assert_array_equal(ring, r_ring)
