@@ -204,6 +204,9 @@ struct ScanK {
     int64_t L;
     int batch, H, G;
     int nseg, cps;     // segments per sequence, chunks per segment
+    const int* plan;   // packed batch with a device plan (ssd_packed_plan_kernel), else null:
+                       // [0] chunks per segment, [1] pairs with work, then those (sequence, segment)
+                       // pairs as int2, sequence by sequence
     int win;           // chunks per buffer-resource window (byte offsets inside one stay below 2^31)
     int nblocks;       // blocks in this launch
     int nxcd;          // XCDs the launch's blocks are dealt over (round-robin in launch order)
@@ -215,6 +218,9 @@ __device__ __forceinline__ int64_t seq_row0(const ScanK& k, int64_t b) {
     const int64_t r0 = k.cu[b];
     return r0 < 0 ? 0 : (r0 > k.total ? k.total : r0);
 }
+// Chunks per segment: the host's figure, or for a packed batch the one its plan kernel picked.
+__device__ __forceinline__ int seg_chunks(const ScanK& k) { return k.plan ? *k.plan : k.cps; }
+
 // Tokens of sequence b: L; its length clamped to [0, L] in a right-padded batch; in a packed
 // batch cu[b+1] - cu[b], clamped to the rows that exist and to L.
 __device__ __forceinline__ int64_t seq_len(const ScanK& k, int64_t b) {
@@ -255,6 +261,30 @@ __device__ __forceinline__ int logical_block(int nblocks, int nx) {
     if (nx <= 1) return i;
     const int x = i % nx, per = nblocks / nx, extra = nblocks % nx;
     return x * per + (x < extra ? x : extra) + i / nx;
+}
+
+// Block -> (head unit, sequence, segment); false for a block with nothing to do.  With a packed plan
+// the first plan[1] * nhu blocks hold the (sequence, segment) pairs with work: one round of resident
+// blocks spread evenly over the XCDs, each XCD a contiguous run of them (the head units of a pair
+// share its B/C rows in one L2).  Otherwise: uniform sequences as logical_block deals them, variable
+// lengths round-robin in launch order (the busy first segments come first).
+__device__ __forceinline__ bool block_unit(const ScanK& k, int nhu, int& hu, int64_t& b, int& seg) {
+    if (k.plan) {
+        const int nbusy = k.plan[1] * nhu;
+        if ((int)blockIdx.x >= nbusy) return false;
+        const int u = logical_block(nbusy, k.nxcd);
+        hu = u % nhu;
+        const int2 e = reinterpret_cast<const int2*>(k.plan + 2)[u / nhu];
+        b = e.x;
+        seg = e.y;
+        return true;
+    }
+    const int unit = (k.lens || k.cu) ? (int)blockIdx.x : logical_block(k.nblocks, k.nxcd);
+    hu = unit % nhu;
+    const int sb = unit / nhu;
+    b = sb % k.batch;
+    seg = sb / k.batch;
+    return true;
 }
 
 // The conv of the x channels when the main pass takes the raw conv input (the fused prompt path):

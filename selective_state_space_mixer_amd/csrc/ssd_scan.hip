@@ -173,19 +173,18 @@ ssd_chunk_scan_kernel(ScanK k)
     const int pblk0 = (wave / HPW) * PW;            // first p-block of this wave
     const bool stats_writer = wave < HPW;
 
-    // logical unit -> (segment, sequence, head group)
+    // block -> (segment, sequence, head group)
     // Uniform sequences: each XCD takes a contiguous run of units (head groups sharing B/C rows in
-    // one L2).  Variable lengths: which units have work is known only here, and the units of the
+    // one L2).  Right-padded lengths: which units have work is known only here, and the units of the
     // first segments (nearly all busy) come first; dealt round-robin as launched, they spread
-    // evenly over the XCDs, where contiguous runs would pile them onto the first few.
-    const int unit = (k.lens || k.cu) ? (int)blockIdx.x : logical_block(k.nblocks, k.nxcd);
+    // evenly over the XCDs, where contiguous runs would pile them onto the first few.  A packed
+    // batch's plan lists the units with work (block_unit).
     const int hpg = k.H / k.G;
     const int upg = (hpg + HPW - 1) / HPW;          // head units per group
     const int nhu = k.G * upg;
-    const int hu = unit % nhu;
-    const int sb_ = unit / nhu;
-    const int64_t b = sb_ % k.batch;
-    const int seg = sb_ / k.batch;
+    int hu, seg;
+    int64_t b;
+    if (!block_unit(k, nhu, hu, b, seg)) return;
     const int g = hu / upg;
     const int h0 = g * hpg + (hu % upg) * HPW;
     const int hcount = hpg - (hu % upg) * HPW < HPW ? hpg - (hu % upg) * HPW : HPW;  // heads present
@@ -197,8 +196,9 @@ ssd_chunk_scan_kernel(ScanK k)
     // starts past it runs none (end state = start state, log-decay 0)
     const int64_t Lb = seq_len(k, b);
     const int64_t nchunks = (Lb + Q - 1) / Q;
-    const int64_t c_begin = (int64_t)seg * k.cps;
-    const int64_t c_stop = c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks;
+    const int cps = seg_chunks(k);
+    const int64_t c_begin = (int64_t)seg * cps;
+    const int64_t c_stop = c_begin + cps < nchunks ? c_begin + cps : nchunks;
     const int nc = c_stop > c_begin ? (int)(c_stop - c_begin) : 0;  // chunks here
     const int64_t row_begin = c_begin * Q;                       // first token of the segment
     const int64_t row_end = Lb < row_begin + (int64_t)nc * Q ? Lb : row_begin + (int64_t)nc * Q;
@@ -604,16 +604,21 @@ ssd_chunk_scan_kernel(ScanK k)
 // the caller's state), lam[seg] its summed log-decay.  The true end states follow
 //   T[0] = E[0],  T[seg] = e^lam[seg] T[seg-1] + E[seg];
 // T[seg] (the initial state of segment seg+1) is written over E[seg] (or, for bf16 outputs, to a
-// bf16 copy), and T[nseg-1] is the final state.  Only the combine is sequential: the loads of a
-// batch of segments are issued together (kBatch of them: 8 for the few segments of a packed batch's
-// plan, whose registers then leave room for more waves, else 32), and only segments that exist are
-// loaded.  The first block of each sequence-head also chains the bounds Tb[seg] on max|T[seg]| from
-// the segments' recorded maxima (see fix_cut).
+// bf16 copy), and T of the sequence's last segment is the final state.  A sequence's segments past
+// its last chunk hold nothing (end state = start state, log-decay 0), so the chain stops at its last
+// segment with work.  Only the combine is sequential: the loads of a batch of segments are issued
+// together (kBatch of them: 8 for the few segments of a packed batch's plan, whose registers then
+// leave room for more waves, else 32), and only segments that exist are loaded.  The first block of
+// each sequence-head also chains the bounds Tb[seg] on max|T[seg]| from the segments' recorded
+// maxima (see fix_cut).
 template <int kBatch>
-__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(ScanK k, int BH, int PN)
+__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(ScanK k, int BH, int PN, int Q)
 {
-    const int nseg = k.nseg;
     const int bh = blockIdx.y;
+    const int cps = seg_chunks(k);
+    const int64_t cb = (seq_len(k, bh / k.H) + Q - 1) / Q;
+    const int64_t sb = (cb + cps - 1) / cps;
+    const int nseg = sb < 1 ? 1 : (sb < k.nseg ? (int)sb : k.nseg);
     float* __restrict__ ws_state = k.ws_state;
     const float* __restrict__ ws_lam = k.ws_lam;
     const float* __restrict__ ws_emax = k.ws_emax;
@@ -706,21 +711,36 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
     const int BH = k.batch * k.H;
     // Candidates: chunk j of pair = (later segment - 1) * BH + bh is cand = pair * cps + j.  Block b
     // tests b, b + nblocks, ..., a thread each, lists in LDS the ones that pass, and its waves share
-    // the list.
+    // the list.  A block count sharing a factor f with cps would give each block only chunks
+    // j = b (mod f) of their segments, and the blocks holding the leading chunks (the ones that need
+    // the term) would carry f times their share: the blocks past the largest count coprime to cps
+    // sit out (the host makes its own count coprime to its cps; a packed plan may pick another).
     __shared__ int sItem[kFixThreads];
     __shared__ int sCount;
     const int npairs = (k.nseg - 1) * BH;
-    const int64_t ncand = (int64_t)npairs * k.cps;
-    const int64_t nblk = gridDim.x;
+    const int cps = seg_chunks(k);
+    const int64_t ncand = (int64_t)npairs * cps;
+    auto gcd = [](int a, int b) {
+        while (b) {
+            const int t = a % b;
+            a = b;
+            b = t;
+        }
+        return a;
+    };
+    int nb = (int)gridDim.x;
+    while (nb > 1 && gcd(nb, cps) > 1) --nb;
+    if ((int)blockIdx.x >= nb) return;
+    const int64_t nblk = nb;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (int64_t base = blockIdx.x; base < ncand; base += nblk * kFixThreads) {
         bool act = false;
         {
             const int64_t cand = base + (int64_t)threadIdx.x * nblk;
-            const int pair = (int)(cand / k.cps), j = (int)(cand % k.cps);
+            const int pair = (int)(cand / cps), j = (int)(cand % cps);
             if (cand < ncand && pair < npairs) {
                 const int seg = 1 + pair / BH, bh = pair % BH;
-                const int64_t c = (int64_t)seg * k.cps + j;
+                const int64_t c = (int64_t)seg * cps + j;
                 // chunks past the sequence have no recorded log-decay and nothing to fix
                 if (c * Q < seq_len(k, bh / k.H)) {
                     const float tb = k.ws_tb[pair], em = k.ws_emax[pair + BH], lb = k.ws_lamc[c * BH + bh];
@@ -742,11 +762,11 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
         const int nitems = sCount;
         for (int it = wave; it < nitems; it += kFixThreads / 64) {
             const int64_t cand = base + (int64_t)sItem[it] * nblk;
-            const int pair = (int)(cand / k.cps), j = (int)(cand % k.cps);
+            const int pair = (int)(cand / cps), j = (int)(cand % cps);
             const int seg = 1 + pair / BH, bh = pair % BH;
             const int64_t b = bh / k.H;
             const int h = bh % k.H, g = h / (k.H / k.G);
-            const int64_t c = (int64_t)seg * k.cps + j;
+            const int64_t c = (int64_t)seg * cps + j;
             const int64_t t0 = c * Q;
             const int64_t left = seq_len(k, b) - t0;
             const int valid = (int)(left < Q ? left : Q);  // >= 1: tested chunks lie inside the sequence
@@ -836,22 +856,84 @@ __global__ __launch_bounds__(kFixThreads) void ssd_segment_fix_kernel(ScanK k)
     }
 }
 
+// The plan of a packed batch, from its lengths (which only the device holds).  Chunks per segment:
+// the least cps in [lo, hi] for which the (sequence, segment) pairs, sum_b max(1, ceil(c_b / cps)),
+// fit the `pairs` that one round of resident blocks holds.  hi always fits (the host's bound for any
+// lengths), and lo is the least any lengths of the batch's total could call for, so the host's grid
+// and workspace, sized for lo, cover the choice.  Then the pairs themselves, sequence by sequence
+// (an empty sequence keeps one, which passes its initial state on).  One block; uniform over it.
+__global__ __launch_bounds__(256) void ssd_packed_plan_kernel(ScanK k, int Q, int pairs, int lo, int hi, int* plan)
+{
+    __shared__ int sRed[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    auto chunks = [&](int64_t b) { return (seq_len(k, b) + Q - 1) / Q; };
+    auto segs_of = [](int64_t c, int cps) {
+        const int64_t n = (c + cps - 1) / cps;
+        return (int)(n < 1 ? 1 : n);
+    };
+    auto segs = [&](int64_t b, int cps) { return segs_of(chunks(b), cps); };
+    // a batch of at most one block's threads: each thread's sequence is read once
+    const bool one = k.batch <= 256;
+    const int64_t cmine = one && (int)threadIdx.x < k.batch ? chunks(threadIdx.x) : 0;
+    while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        int n = 0;
+        if (one) n = (int)threadIdx.x < k.batch ? segs_of(cmine, mid) : 0;
+        else
+            for (int b = threadIdx.x; b < k.batch; b += 256) n += segs(b, mid);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) n += __shfl_xor(n, o, 64);
+        if (lane == 0) sRed[wave] = n;
+        __syncthreads();
+        const int tot = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+        __syncthreads();
+        if (tot <= pairs) hi = mid;
+        else lo = mid + 1;
+    }
+    int2* table = reinterpret_cast<int2*>(plan + 2);
+    int base = 0;
+    for (int b0 = 0; b0 < k.batch; b0 += 256) {
+        const int b = b0 + (int)threadIdx.x;
+        const int n = b < k.batch ? segs(b, hi) : 0;
+        int x = n;  // inclusive prefix sum over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) sRed[wave] = x;
+        __syncthreads();
+        int off = base + x - n;
+        for (int j = 0; j < wave; ++j) off += sRed[j];
+        const int tot = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+        __syncthreads();
+        for (int j = 0; j < n; ++j) table[off + j] = make_int2(b, j);
+        base += tot;
+    }
+    if (threadIdx.x == 0) {
+        plan[0] = hi;
+        plan[1] = base;
+    }
+}
+
 // ----------------------------------------------------------------------------------------------
 // host side
 
 struct Plan {
     int nseg, cps, nhu;
+    int cps_lo, pairs;  // packed batch: the device picks cps in [cps_lo, cps] (equal: no pick)
     size_t ws_bytes;
 };
 
 // Byte offsets of the workspace parts, from a 256-byte aligned base (the caller's pointer rounded up):
 // segment states [nseg][B*H][P*N] f32, segment log-decays [nseg][B*H] f32, per-chunk starting
 // log-decays [nchunks][B*H] f32, the segments' own end-state maxima and the bounds on their true ones
-// [nseg][B*H] f32 each, and for bf16 outputs the segments' initial states in bf16 [nseg-1][B*H][P*N].
+// [nseg][B*H] f32 each, for bf16 outputs the segments' initial states in bf16 [nseg-1][B*H][P*N],
+// and a packed batch's plan: two ints and up to nseg * batch (sequence, segment) pairs.
 struct WsLayout {
-    size_t lam, emax, tb, lamc, tin, total;
+    size_t lam, emax, tb, lamc, tin, plan, total;
 };
-static WsLayout ws_layout(int64_t nseg, int64_t BH, int64_t PN, int64_t nchunks, bool bf16) {
+static WsLayout ws_layout(int64_t nseg, int64_t batch, int64_t BH, int64_t PN, int64_t nchunks, bool bf16) {
     auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
     WsLayout w;
     w.lam = up((size_t)(nseg * BH * PN) * sizeof(float));
@@ -859,14 +941,18 @@ static WsLayout ws_layout(int64_t nseg, int64_t BH, int64_t PN, int64_t nchunks,
     w.tb = up(w.emax + (size_t)(nseg * BH) * sizeof(float));
     w.lamc = up(w.tb + (size_t)(nseg * BH) * sizeof(float));
     w.tin = up(w.lamc + (size_t)(nchunks * BH) * sizeof(float));
-    w.total = w.tin + (bf16 ? (size_t)((nseg - 1) * BH * PN) * sizeof(uint16_t) : 0);
+    w.plan = up(w.tin + (bf16 ? (size_t)((nseg - 1) * BH * PN) * sizeof(uint16_t) : 0));
+    w.total = w.plan + 2 * sizeof(int) + (size_t)(nseg * batch) * 2 * sizeof(int);
     return w;
 }
 
 // Segments: enough (sequence, head group, segment) units for one round of resident blocks.
-// A packed batch (total >= 0 tokens, L the longest sequence) sizes its segments from the total:
-// every (sequence, segment) pair with work should fit in one round of resident blocks, and
-// sum_b ceil(c_b / cps) <= (total chunks + batch) / cps + batch bounds their number.
+// A packed batch (total >= 0 tokens, L the longest sequence): every (sequence, segment) pair with
+// work should fit in one round of resident blocks.  For any lengths, sum_b ceil(c_b / cps) <=
+// (total chunks + batch) / cps + batch bounds their number, which gives the upper bound cps; no
+// lengths can fit fewer than cps_lo = ceil(total chunks / pairs).  The lengths are device memory, so
+// the plan kernel picks the least that fits between the two, and the grid and the workspace are
+// sized for cps_lo.
 static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, int hpw, int bpc, bool bf16,
                      int64_t total) {
     Plan pl;
@@ -876,11 +962,15 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, i
     pl.nhu = G * ((hpg + hpw - 1) / hpw);
     const int64_t units = batch * pl.nhu;
     const int64_t target = (int64_t)cus * bpc;  // blocks resident at once
-    int64_t cps;
+    int64_t cps, cps_lo = 0;
+    pl.pairs = 0;
     if (total >= 0) {
         const int64_t pairs = target / pl.nhu;                  // (sequence, segment) pairs per round
-        const int64_t tchunks = (total + Q - 1) / Q + batch;
+        const int64_t rchunks = (total + Q - 1) / Q;
+        const int64_t tchunks = rchunks + batch;
         cps = pairs > batch ? (tchunks + (pairs - batch) - 1) / (pairs - batch) : nchunks;
+        cps_lo = pairs > batch ? (rchunks + pairs - 1) / pairs : cps;
+        pl.pairs = (int)(pairs < INT32_MAX ? pairs : INT32_MAX);
     } else {
         int64_t nseg = units > 0 ? target / units : 1;
         if (nseg > nchunks) nseg = nchunks;
@@ -889,10 +979,13 @@ static Plan plan_for(int64_t batch, int64_t L, int H, int G, int N_P_N, int Q, i
     }
     if (cps > nchunks) cps = nchunks;
     if (cps < 1) cps = 1;
-    const int64_t nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;
+    if (total < 0 || cps_lo > cps) cps_lo = cps;
+    if (cps_lo < 1) cps_lo = 1;
+    const int64_t nseg = nchunks > 0 ? (nchunks + cps_lo - 1) / cps_lo : 1;
     pl.nseg = (int)nseg;
     pl.cps = (int)cps;
-    pl.ws_bytes = nseg > 1 ? ws_layout(nseg, batch * H, N_P_N, nchunks, bf16).total + 256 : 0;
+    pl.cps_lo = (int)cps_lo;
+    pl.ws_bytes = nseg > 1 ? ws_layout(nseg, batch, batch * H, N_P_N, nchunks, bf16).total + 256 : 0;
     return pl;
 }
 
@@ -927,8 +1020,9 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
     k.ws_tin = nullptr;
     k.ws_emax = nullptr;
     k.ws_tb = nullptr;
+    k.plan = nullptr;
     if (pl.nseg > 1) {
-        const WsLayout w = ws_layout(pl.nseg, BH, P * N, (a.L + Q - 1) / Q, sizeof(T) == 2);
+        const WsLayout w = ws_layout(pl.nseg, a.batch, BH, P * N, (a.L + Q - 1) / Q, sizeof(T) == 2);
         uint8_t* base = reinterpret_cast<uint8_t*>(((uintptr_t)a.ws + 255) & ~(uintptr_t)255);
         k.ws_state = reinterpret_cast<float*>(base);
         k.ws_lam = reinterpret_cast<float*>(base + w.lam);
@@ -936,6 +1030,7 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
         k.ws_tb = reinterpret_cast<float*>(base + w.tb);
         k.ws_lamc = reinterpret_cast<float*>(base + w.lamc);
         if (sizeof(T) == 2) k.ws_tin = reinterpret_cast<uint16_t*>(base + w.tin);
+        if (pl.cps_lo < pl.cps) k.plan = reinterpret_cast<int*>(base + w.plan);
     }
     // every segment at once (later ones from a zero state), then, with several segments, the chain
     // of their end states and the fix-up of the later segments' leading chunks
@@ -949,18 +1044,21 @@ static hipError_t run_scan(const ScanArgs& a, hipStream_t s, const WalkConv* con
         walk = (a.H / a.G) % 4 == 0 && ((uintptr_t)a.dt & 3u) == 0 && (a.dts & 1) == 0;
     }
     if (conv && !walk) return hipErrorInvalidValue;  // the fused path needs the walk kernel
+    if (k.plan) {
+        e = launch_kernel(ssd_packed_plan_kernel, dim3(1), dim3(256), 0, s, k, Q, pl.pairs, pl.cps_lo, pl.cps,
+                          const_cast<int*>(k.plan));
+        if (e != hipSuccess) return e;
+    }
     if (walk) e = launch_ssd_walk(k, conv, s);
     else e = launch_kernel(ssd_chunk_scan_kernel<T, Q, P, N>, dim3(k.nblocks), dim3(Cf::THREADS), 0, s, k);
     if (e != hipSuccess || pl.nseg == 1) return e;
     dim3 g2((unsigned)((P * N / 4 + 255) / 256), (unsigned)BH);
-    e = pl.nseg <= 8 ? launch_kernel(ssd_segment_chain_kernel<8>, g2, dim3(256), 0, s, k, BH, P * N)
-                     : launch_kernel(ssd_segment_chain_kernel<32>, g2, dim3(256), 0, s, k, BH, P * N);
+    e = pl.nseg <= 8 ? launch_kernel(ssd_segment_chain_kernel<8>, g2, dim3(256), 0, s, k, BH, P * N, Q)
+                     : launch_kernel(ssd_segment_chain_kernel<32>, g2, dim3(256), 0, s, k, BH, P * N, Q);
     if (e != hipSuccess) return e;
     // about one chunk to fix per wave on the 32k prompt's figures; at most one round of resident
-    // blocks.  Block b takes candidates b, b + nblocks, ... of the (segment, head, chunk) order, so a
-    // block count sharing a factor f with the chunks per segment would give each block only chunks
-    // j = b (mod f) of their segments, and the blocks holding the leading chunks (the ones that
-    // need the term) would carry f times their share: the count is made coprime to cps.
+    // blocks (the candidates are counted with the upper bound on the chunks per segment); the count
+    // coprime to cps (see the kernel)
     const int64_t ncand = (int64_t)(pl.nseg - 1) * BH * pl.cps;
     int64_t nfb = (ncand + 63) / 64;
     const int64_t cap = (int64_t)device_shape().cus * kFixBlocksPerCU;

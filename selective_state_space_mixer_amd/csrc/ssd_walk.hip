@@ -65,15 +65,13 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
     const int lane = threadIdx.x & 63, q = lane >> 4, li = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // logical unit -> (segment, sequence, head group); see the general kernel
-    const int unit = (k.lens || k.cu) ? (int)blockIdx.x : logical_block(k.nblocks, k.nxcd);
+    // block -> (segment, sequence, head group)
     const int hpg = k.H / k.G;
     const int upg = (hpg + HPB - 1) / HPB;
     const int nhu = k.G * upg;
-    const int hu = unit % nhu;
-    const int sb_ = unit / nhu;
-    const int64_t b = sb_ % k.batch;
-    const int seg = sb_ / k.batch;
+    int hu, seg;
+    int64_t b;
+    if (!block_unit(k, nhu, hu, b, seg)) return;
     const int g = hu / upg;
     const int h0 = g * hpg + (hu % upg) * HPB;
     const int hcount = hpg - (hu % upg) * HPB < HPB ? hpg - (hu % upg) * HPB : HPB;
@@ -84,8 +82,9 @@ ssd_walk_kernel(ScanK k, WalkConv cv)
     const int BH = k.batch * k.H;
     const int64_t Lb = seq_len(k, b);
     const int64_t nchunks = (Lb + Q - 1) / Q;
-    const int64_t c_begin = (int64_t)seg * k.cps;
-    const int64_t c_stop = c_begin + k.cps < nchunks ? c_begin + k.cps : nchunks;
+    const int cps = seg_chunks(k);
+    const int64_t c_begin = (int64_t)seg * cps;
+    const int64_t c_stop = c_begin + cps < nchunks ? c_begin + cps : nchunks;
     const int nc = c_stop > c_begin ? (int)(c_stop - c_begin) : 0;
     const int64_t row_begin = c_begin * Q;
     const int64_t row_end = Lb < row_begin + (int64_t)nc * Q ? Lb : row_begin + (int64_t)nc * Q;

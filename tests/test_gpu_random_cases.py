@@ -239,3 +239,33 @@ def test_random_decode_chain(case):
     print("random decode chain %s P%d N%d G%d H%d W%d: y %.2e state %.2e" % (io, P, N, G, H, W, worst, es))
     assert es <= tol
     np.testing.assert_array_equal(ring, r_ring)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_packed_scan_many_sequences(io):
+    """260 packed prompts, two of 640 tokens among short and empty ones, at a small shape: more
+    sequences than one block of the plan kernel covers, and a chunks-per-segment pick that splits
+    the long prompts into many short segments; every output and final state against the oracle."""
+    _need_gpu()
+    rng = random.Random(17)
+    nb, P, N, Q, G, H = 260, 16, 16, 16, 1, 4
+    lens = [rng.choice([0, 1, 5, 15, 16, 17, 40]) for _ in range(nb)]
+    lens[3] = lens[200] = 640
+    d = workloads.Dims(nb, max(lens), H * P // 2, 2, P, N, G, 4, Q, io)
+    inp, x, b, c = tp._scan_inputs(d, 9990 + (io == "bf16"), True)
+    s0 = inp.state0
+    dims, tol = dims_of(d), tol_for(io)
+    pack = lambda a: np.concatenate([a[i, :n] for i, n in enumerate(lens)], 0)
+    xp, bp, cp, dtp = pack(x), pack(b), pack(c), pack(inp.dt_raw)
+    T = len(xp)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    y = nan_like((T, H * P), io)
+    s = torch.full((nb, H, P, N), float("nan"), device="cuda")
+    m2.m2_ssd_scan_fwd_packed(dims, torch.as_tensor(cu, device="cuda"), dev(xp, io), dev(bp, io), dev(cp, io),
+                              dev(dtp, io), dev32(inp.dt_bias), dev32(inp.A), dev32(inp.D), y, dev32(s0), s,
+                              workspace=workspace(dims, T))
+    torch.cuda.synchronize()
+    yr, sr = oracle.ssd_scan_packed(xp, bp, cp, dtp, cu, inp.dt_bias, inp.A, inp.D, s0)
+    errs = [oracle.max_rel_err(host(s), sr), oracle.max_rel_err(host(y).reshape(T, H, P), yr)]
+    print("packed scan, %d prompts (%d tokens) %s: state %.2e y %.2e (bar %.0e)" % (nb, T, io, errs[0], errs[1], tol))
+    assert max(errs) <= tol, errs
