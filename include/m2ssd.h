@@ -178,7 +178,9 @@ m2_status m2_ssd_scan_fwd(const m2_dims* dims,
 
 /* Workspace bytes m2_ssd_scan_fwd_packed needs for dims (dims.seqlen the longest sequence) and
  * total_tokens rows (0 if none, or if the arguments are invalid).  The packed scan sizes its
- * segments from the total, so this can differ from m2_ssd_scan_workspace(dims). */
+ * segments from the total, so this can differ from m2_ssd_scan_workspace(dims): the segment length
+ * is picked on the device from the lengths in cu_seqlens, and the workspace covers the shortest
+ * one any lengths adding up to total_tokens could call for. */
 size_t m2_ssd_scan_workspace_packed(const m2_dims* dims, int64_t total_tokens);
 
 /* Packed batch: the same as m2_ssd_scan_fwd for dims.batch sequences back to back in arrays of
