@@ -269,3 +269,22 @@ def test_packed_scan_many_sequences(io):
     errs = [oracle.max_rel_err(host(s), sr), oracle.max_rel_err(host(y).reshape(T, H, P), yr)]
     print("packed scan, %d prompts (%d tokens) %s: state %.2e y %.2e (bar %.0e)" % (nb, T, io, errs[0], errs[1], tol))
     assert max(errs) <= tol, errs
+
+
+def _many_prompt_cases(seed=47, n=3):
+    """12-40 prompts at 16-32 heads: enough chunks against the resident blocks that the packed scan
+    picks its segment length on the device (padded and packed, through the one-pass test's body)."""
+    rng, out = random.Random(seed), []
+    for i in range(n):
+        nb = rng.randint(12, 40)
+        maxlen = rng.choice([600, 1000, 1500])
+        lens = [rng.choice([0, 1, 3, 31, 33, 100, 257, maxlen // 2, maxlen]) for _ in range(nb)]
+        d_model = rng.choice([512, 1024]) if nb <= 24 else 512
+        groups = rng.choice([1, 2])
+        out.append((lens, groups, d_model, rng.choice([2, 3, 4]), rng.random() < 0.7, rng.randint(0, 5), 30000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _many_prompt_cases(), ids=lambda c: "n%d-G%d-dm%d" % (len(c[0]), c[1], c[2]))
+def test_one_pass_prefill_many_prompts(case):
+    test_random_one_pass_prefill(case)
